@@ -1,0 +1,146 @@
+"""CPU oracle for the MLA KV prolog -- test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product library never does, and
+this package never imports the product library.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, built by
+``oracle/build_oracle.py``); this module only converts numpy arrays to the
+pointer form that file takes.  What each step computes, and from which
+passage of the pages, is documented in ``oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        from . import build_oracle
+
+        build_oracle.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, i32, dbl, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
+    lib.oracle_round_to_dtype.argtypes = [vp, vp, i64, i32]
+    lib.oracle_round_to_dtype.restype = i32
+    lib.oracle_kv_prolog_fp.argtypes = (
+        [i64] * 7 + [vp] * 5 + [dbl, dbl, i32] + [vp] * 4 + [i32]
+    )
+    lib.oracle_kv_prolog_fp.restype = i32
+    lib.oracle_kv_prolog_w8a8.argtypes = (
+        [i64] * 7 + [vp] * 7 + [dbl, dbl] + [vp] * 4 + [vp] * 6 + [i32]
+    )
+    lib.oracle_kv_prolog_w8a8.restype = i32
+    lib.oracle_num_threads.argtypes = [i32]
+    lib.oracle_num_threads.restype = i32
+    _lib = lib
+    return lib
+
+
+DTYPE_CODE = {"f16": 1, "bf16": 2}
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+def round_to_dtype(x, dtype: str) -> np.ndarray:
+    """Round float64 values to the nearest fp16 / bf16 value (ties to even);
+    returns float64 holding the rounded values."""
+    x = _c(x, np.float64)
+    out = np.empty_like(x)
+    rc = _load().oracle_round_to_dtype(_ptr(x), _ptr(out), x.size, DTYPE_CODE[dtype])
+    if rc != 0:
+        raise ValueError(f"oracle_round_to_dtype failed: {rc}")
+    return out
+
+
+def num_threads(n: int = 0) -> int:
+    return _load().oracle_num_threads(int(n))
+
+
+def kv_prolog_fp(X, Wa, gamma, Wb, pos, *, r, dr, nh, dn, dv, eps, theta,
+                 dtype: str, nthreads: int = 0, want_kv: bool = True):
+    """fp16/bf16 KV prolog in fp64.  Inputs are arrays of the stored values
+    (any float dtype; they are widened exactly to float64).  Returns a dict of
+    float64 arrays k_nope [T,nh,dn], value [T,nh,dv], k_pe [T,dr],
+    ckv [T,r], all before the final rounding to the output dtype."""
+    X = _c(X, np.float64)
+    T, H = X.shape
+    Wa = _c(Wa, np.float64)
+    gamma = _c(gamma, np.float64)
+    Wb = _c(Wb, np.float64)
+    pos = _c(pos, np.int32)
+    assert Wa.shape == (H, r + dr) and gamma.shape == (r,)
+    assert Wb.shape == (r, nh * (dn + dv)) and pos.shape == (T,)
+    out = {
+        "k_nope": np.empty((T, nh, dn)) if want_kv else None,
+        "value": np.empty((T, nh, dv)) if want_kv else None,
+        "k_pe": np.empty((T, dr)),
+        "ckv": np.empty((T, r)),
+    }
+    rc = _load().oracle_kv_prolog_fp(
+        T, H, r, dr, nh, dn, dv, _ptr(X), _ptr(Wa), _ptr(gamma), _ptr(Wb),
+        _ptr(pos), float(eps), float(theta), DTYPE_CODE[dtype],
+        _ptr(out["k_nope"]), _ptr(out["value"]), _ptr(out["k_pe"]),
+        _ptr(out["ckv"]), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_kv_prolog_fp failed: {rc}")
+    return out
+
+
+def kv_prolog_w8a8(X, Wqa, swa, gamma, Wqb, swb, pos, *, r, dr, nh, dn, dv,
+                   eps, theta, nthreads: int = 0, want_kv: bool = True,
+                   want_acc: bool = True, want_codes: bool = False):
+    """W8A8 KV prolog.  X and gamma hold bf16 values (widened exactly to
+    float32 here); Wqa/Wqb int8 with float32 per-output-column scales.
+    Returns float64 references plus the exact int32 accumulators."""
+    X = _c(X, np.float32)
+    T, H = X.shape
+    N1 = r + dr
+    N2 = nh * (dn + dv)
+    Wqa = _c(Wqa, np.int8)
+    swa = _c(swa, np.float32)
+    gamma = _c(gamma, np.float32)
+    Wqb = _c(Wqb, np.int8)
+    swb = _c(swb, np.float32)
+    pos = _c(pos, np.int32)
+    assert Wqa.shape == (H, N1) and swa.shape == (N1,) and gamma.shape == (r,)
+    assert Wqb.shape == (r, N2) and swb.shape == (N2,) and pos.shape == (T,)
+    out = {
+        "k_nope": np.empty((T, nh, dn)) if want_kv else None,
+        "value": np.empty((T, nh, dv)) if want_kv else None,
+        "k_pe": np.empty((T, dr)),
+        "ckv": np.empty((T, r)),
+        "acc1": np.empty((T, N1), np.int32) if want_acc else None,
+        "acc2": np.empty((T, N2), np.int32) if (want_acc and want_kv) else None,
+        "qx": np.empty((T, H), np.int8) if want_codes else None,
+        "sx": np.empty((T,), np.float32) if want_codes else None,
+        "qz": np.empty((T, r), np.int8) if want_codes else None,
+        "sz": np.empty((T,), np.float32) if want_codes else None,
+    }
+    rc = _load().oracle_kv_prolog_w8a8(
+        T, H, r, dr, nh, dn, dv, _ptr(X), _ptr(Wqa), _ptr(swa), _ptr(gamma),
+        _ptr(Wqb), _ptr(swb), _ptr(pos), float(eps), float(theta),
+        _ptr(out["k_nope"]), _ptr(out["value"]), _ptr(out["k_pe"]),
+        _ptr(out["ckv"]), _ptr(out["acc1"]), _ptr(out["acc2"]),
+        _ptr(out["qx"]), _ptr(out["sx"]), _ptr(out["qz"]), _ptr(out["sz"]),
+        int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_kv_prolog_w8a8 failed: {rc}")
+    return out
