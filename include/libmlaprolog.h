@@ -1,0 +1,159 @@
+/*
+ * libmlaprolog -- the MLA (Multi-head Latent Attention) KV prolog on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The prolog turns each token's hidden state into the key/value inputs of
+ * MLA attention, in seven steps (DeepSeek-V2-Lite-Chat MLA KV Prolog
+ * migration guide, dpshk.com, section "Background"; data flow in section
+ * "Source-level principle"):
+ *
+ *   1. kv_a_proj      A = X . W_kv_a               [T,H] x [H, r+dr]
+ *   2. split          c = A[:, :r]  (compressed_kv),  p = A[:, r:]  (k_pe)
+ *   3. RMSNorm        y = c / sqrt(mean(c^2) + eps) * gamma
+ *   4. kv_b_proj      B = y . W_kv_b               [T,r] x [r, nh*(dn+dv)]
+ *   5. reshape+split  B -> [T, nh, dn+dv]; k_nope = [..., :dn], value = [..., dn:]
+ *   6. RoPE on p      rotate-half form, pairs (i, i + dr/2),
+ *                     angle pos * theta^(-2i/dr)  (section "Precision
+ *                     verification": the standard x*cos + x_rot*sin form)
+ *   7. assemble       write k_nope, value, k_pe and the normalised
+ *                     compressed_kv
+ *
+ * The W8A8 entry point is the same prolog with int8 weights (per-output-
+ * column fp32 scales) and per-token dynamic int8 activations, accumulating
+ * in int32 (the quantised-weight modes of the DeepSeek-R1 inference-recipe
+ * page, section "Weight conversion").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is a DEVICE pointer, allocated and owned by the
+ *   caller; the library never allocates, frees or keeps a pointer past the
+ *   call.  Scratch memory is the caller's `workspace` (size from the
+ *   matching *_workspace_size query).
+ * - Tensors are contiguous, row-major, in exactly the shapes given.  W_kv_b's
+ *   columns come in per-head blocks [k_nope_h (dn) | value_h (dv)].
+ *   Outputs are token-major: k_nope [T,nh,dn], value [T,nh,dv],
+ *   k_pe [T,dr] (one rope key per token, shared by all heads),
+ *   compressed_kv [T,r].
+ * - Every pointer must be 16-byte aligned.  Outputs must not alias inputs
+ *   or each other or the workspace.
+ * - Supported by the GPU kernels: r = 512, dr = 64, dn = dv = 128,
+ *   1 <= nh <= 1024, H a multiple of 64 with 64 <= H <= 65536,
+ *   0 <= T <= MLA_MAX_TOKENS.  Anything else returns MLA_ERR_UNSUPPORTED.
+ * - Every host-checkable condition (null pointer, dims, alignment,
+ *   workspace size, eps/theta) is checked before anything is launched; on
+ *   failure nothing is launched and a status is returned.  T == 0 returns
+ *   MLA_OK and launches nothing.  Launch failures return MLA_ERR_HIP.
+ * - Device-side contents are preconditions, not checked: positions >= 0,
+ *   finite inputs.
+ * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *   stream) and never synchronise.  Two calls that share a workspace must
+ *   be ordered (same stream, or synchronised).
+ * - The library holds no per-call state and is safe to call from several
+ *   host threads (apart from mla_kv_prolog_force_path, a test hook).
+ */
+#ifndef LIBMLAPROLOG_H
+#define LIBMLAPROLOG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_MAX_TOKENS (1 << 22)
+
+typedef enum {
+    MLA_OK = 0,
+    MLA_ERR_INVALID_ARG = -1, /* null pointer, negative T, bad eps/theta, unknown dtype */
+    MLA_ERR_UNSUPPORTED = -2, /* dims outside what the kernels implement */
+    MLA_ERR_MISALIGNED = -3,  /* a pointer not 16-byte aligned */
+    MLA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than the query says */
+    MLA_ERR_HIP = -5          /* a HIP launch or runtime call failed */
+} mla_status_t;
+
+typedef enum { MLA_F16 = 1, MLA_BF16 = 2 } mla_dtype_t;
+
+typedef struct {
+    int32_t H;  /* hidden size */
+    int32_t r;  /* kv_lora_rank (compressed latent width) */
+    int32_t dr; /* rope dim */
+    int32_t nh; /* heads */
+    int32_t dn; /* qk_nope_head_dim */
+    int32_t dv; /* v_head_dim */
+} mla_dims_t;
+
+/* Bytes of workspace mla_kv_prolog needs for T tokens (0 for T == 0).
+ * Returns 0 as well for unsupported dims or dtype (the call then fails). */
+size_t mla_kv_prolog_workspace_size(int64_t T, mla_dims_t d, mla_dtype_t dt);
+
+/*
+ * fp16 / bf16 KV prolog (steps 1-7 above, all in one call).
+ *   hidden      [T, H]            dt
+ *   W_kv_a      [H, r+dr]         dt   (the kv_a_proj weight, already transposed)
+ *   gamma       [r]               dt   (RMSNorm weight)
+ *   W_kv_b      [r, nh*(dn+dv)]   dt
+ *   positions   [T]               int32, >= 0
+ *   eps         RMSNorm epsilon (finite, >= 0), theta RoPE base (finite, > 0)
+ *   k_nope      [T, nh, dn]       dt   (out)
+ *   value       [T, nh, dv]       dt   (out)
+ *   k_pe        [T, dr]           dt   (out, after RoPE)
+ *   compressed_kv [T, r]          dt   (out, the normalised latent that
+ *                                       kv_b_proj consumes)
+ * Accumulation is fp32; intermediates never leave fp32 except the
+ * normalised latent, which is rounded to dt (it is an output) before
+ * kv_b_proj.
+ */
+mla_status_t mla_kv_prolog(const void* hidden, const void* W_kv_a, const void* gamma,
+                           const void* W_kv_b, const int32_t* positions, int64_t T,
+                           mla_dims_t d, mla_dtype_t dt, float eps, float theta,
+                           void* k_nope, void* value, void* k_pe, void* compressed_kv,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace mla_kv_prolog_w8a8 needs for T tokens. */
+size_t mla_kv_prolog_w8a8_workspace_size(int64_t T, mla_dims_t d);
+
+/*
+ * W8A8 KV prolog.  bf16 activations, gamma and outputs; int8 weights with
+ * fp32 per-output-column scales (weight = code * scale[column]).
+ *   hidden_bf16 [T, H]; Wq_kv_a int8 [H, r+dr], s_kv_a fp32 [r+dr];
+ *   gamma_bf16 [r]; Wq_kv_b int8 [r, nh*(dn+dv)], s_kv_b fp32 [nh*(dn+dv)].
+ * Steps, every one in IEEE fp32 with round-to-nearest-even:
+ *   qx = clamp(rint(x * (127/amax_t)), +-127), sx = amax_t/127, amax_t =
+ *   max_k |x[t,k]| (a zero row gives codes 0, scale 0);
+ *   acc1 = qx . Wq_kv_a (int32, exact); A = (float(acc1) * sx) * s_kv_a[n];
+ *   z = c * gamma; qz, sz = the same per-token quantisation of z;
+ *   acc2 = qz . Wq_kv_b (int32, exact); inv_t = 1/sqrt(mean(c^2) + eps);
+ *   k_nope/value = bf16(((float(acc2) * sz) * inv_t) * s_kv_b[m]);
+ *   compressed_kv = bf16(z * inv_t); k_pe = bf16(RoPE(A[:, r:])).
+ * Debug export (both may be NULL): for token rows
+ * [dbg_row_begin, dbg_row_begin + dbg_rows) the exact int32 accumulators
+ * are written to dbg_acc1 [dbg_rows, r+dr] and dbg_acc2 [dbg_rows,
+ * nh*(dn+dv)].  Rows outside [0, T) are an MLA_ERR_INVALID_ARG.
+ */
+mla_status_t mla_kv_prolog_w8a8(const void* hidden_bf16, const int8_t* Wq_kv_a,
+                                const float* s_kv_a, const void* gamma_bf16,
+                                const int8_t* Wq_kv_b, const float* s_kv_b,
+                                const int32_t* positions, int64_t T, mla_dims_t d,
+                                float eps, float theta, void* k_nope, void* value,
+                                void* k_pe, void* compressed_kv, int32_t* dbg_acc1,
+                                int32_t* dbg_acc2, int64_t dbg_row_begin, int64_t dbg_rows,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* The kernel family the dispatcher picks for T tokens: 0 = decode
+ * (weight-streaming, small T), 1 = prefill (MFMA-tiled, large T). */
+int mla_kv_prolog_selected_path(int64_t T, mla_dims_t d);
+
+/* Test / benchmark hook: force every later call in this process onto one
+ * kernel family (0 or 1), or back to the dispatcher's choice (-1).  Returns
+ * the previous setting.  Not for concurrent use. */
+int mla_kv_prolog_force_path(int path);
+
+/* Static, human-readable name of a status code. */
+const char* mla_status_string(mla_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMLAPROLOG_H */

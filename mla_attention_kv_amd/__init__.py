@@ -1,0 +1,268 @@
+"""Python binding of libmlaprolog, the MLA KV prolog for MI355X (gfx950).
+
+Argument marshalling only: every step of the prolog runs in the library's
+HIP kernels.  PyTorch provides device memory and the current stream; the
+functions below check tensor dtypes / shapes / devices, allocate outputs and
+workspace when they are not given, and call the C entry points of the same
+names (declared in include/libmlaprolog.h).
+
+If the shared library has not been built, importing works but every call
+raises: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmlaprolog.so")
+
+MLA_OK = 0
+MLA_ERR_INVALID_ARG = -1
+MLA_ERR_UNSUPPORTED = -2
+MLA_ERR_MISALIGNED = -3
+MLA_ERR_WORKSPACE = -4
+MLA_ERR_HIP = -5
+MLA_F16 = 1
+MLA_BF16 = 2
+MLA_MAX_TOKENS = 1 << 22
+
+# entry points declared in include/libmlaprolog.h
+EXPORTS = (
+    "mla_kv_prolog_workspace_size",
+    "mla_kv_prolog",
+    "mla_kv_prolog_w8a8_workspace_size",
+    "mla_kv_prolog_w8a8",
+    "mla_kv_prolog_selected_path",
+    "mla_kv_prolog_force_path",
+    "mla_status_string",
+)
+
+
+class mla_dims_t(ctypes.Structure):
+    _fields_ = [("H", ctypes.c_int32), ("r", ctypes.c_int32), ("dr", ctypes.c_int32),
+                ("nh", ctypes.c_int32), ("dn", ctypes.c_int32), ("dv", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class Dims:
+    H: int
+    nh: int
+    r: int = 512
+    dr: int = 64
+    dn: int = 128
+    dv: int = 128
+
+    def c(self) -> mla_dims_t:
+        return mla_dims_t(self.H, self.r, self.dr, self.nh, self.dn, self.dv)
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {mla_status_string(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded shared library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first (python -m mla_attention_kv_amd.build_lib "
+            "or __graft_entry__.build()); there is no fallback implementation")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, i32, f32, vp, sz = (ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
+                             ctypes.c_size_t)
+    L.mla_kv_prolog_workspace_size.argtypes = [i64, mla_dims_t, i32]
+    L.mla_kv_prolog_workspace_size.restype = sz
+    L.mla_kv_prolog_w8a8_workspace_size.argtypes = [i64, mla_dims_t]
+    L.mla_kv_prolog_w8a8_workspace_size.restype = sz
+    L.mla_kv_prolog.argtypes = [vp, vp, vp, vp, vp, i64, mla_dims_t, i32, f32, f32,
+                                vp, vp, vp, vp, vp, sz, vp]
+    L.mla_kv_prolog.restype = i32
+    L.mla_kv_prolog_w8a8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, mla_dims_t, f32, f32,
+                                     vp, vp, vp, vp, vp, vp, i64, i64, vp, sz, vp]
+    L.mla_kv_prolog_w8a8.restype = i32
+    L.mla_kv_prolog_selected_path.argtypes = [i64, mla_dims_t]
+    L.mla_kv_prolog_selected_path.restype = i32
+    L.mla_kv_prolog_force_path.argtypes = [i32]
+    L.mla_kv_prolog_force_path.restype = i32
+    L.mla_status_string.argtypes = [i32]
+    L.mla_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def mla_status_string(status: int) -> str:
+    return lib().mla_status_string(int(status)).decode()
+
+
+def mla_kv_prolog_workspace_size(T: int, dims: Dims, dtype: int = MLA_F16) -> int:
+    return int(lib().mla_kv_prolog_workspace_size(int(T), dims.c(), int(dtype)))
+
+
+def mla_kv_prolog_w8a8_workspace_size(T: int, dims: Dims) -> int:
+    return int(lib().mla_kv_prolog_w8a8_workspace_size(int(T), dims.c()))
+
+
+def mla_kv_prolog_selected_path(T: int, dims: Dims) -> int:
+    return int(lib().mla_kv_prolog_selected_path(int(T), dims.c()))
+
+
+def mla_kv_prolog_force_path(path: int) -> int:
+    return int(lib().mla_kv_prolog_force_path(int(path)))
+
+
+# ---------------------------------------------------------------------------
+# torch-tensor front ends
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _check(t, name, dtype, shape, device):
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _stream_ptr(device, stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dims_from(hidden, W_kv_b, gamma, W_kv_a, dn=128, dv=128) -> Dims:
+    H = hidden.shape[1]
+    r = gamma.shape[0]
+    dr = W_kv_a.shape[1] - r
+    N2 = W_kv_b.shape[1]
+    if N2 % (dn + dv):
+        raise ValueError(f"W_kv_b has {N2} columns, not a multiple of dn+dv={dn + dv}")
+    return Dims(H=H, nh=N2 // (dn + dv), r=r, dr=dr, dn=dn, dv=dv)
+
+
+def _outputs(T, d, dtype, device, k_nope, value, k_pe, compressed_kv):
+    torch = _torch()
+    if k_nope is None:
+        k_nope = torch.empty((T, d.nh, d.dn), dtype=dtype, device=device)
+    if value is None:
+        value = torch.empty((T, d.nh, d.dv), dtype=dtype, device=device)
+    if k_pe is None:
+        k_pe = torch.empty((T, d.dr), dtype=dtype, device=device)
+    if compressed_kv is None:
+        compressed_kv = torch.empty((T, d.r), dtype=dtype, device=device)
+    _check(k_nope, "k_nope", dtype, (T, d.nh, d.dn), device)
+    _check(value, "value", dtype, (T, d.nh, d.dv), device)
+    _check(k_pe, "k_pe", dtype, (T, d.dr), device)
+    _check(compressed_kv, "compressed_kv", dtype, (T, d.r), device)
+    return k_nope, value, k_pe, compressed_kv
+
+
+def _workspace(nbytes, device, workspace):
+    torch = _torch()
+    if workspace is None:
+        workspace = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace: contiguous uint8 tensor expected")
+    if workspace.numel() < nbytes:
+        raise ValueError(f"workspace: {workspace.numel()} bytes, need {nbytes}")
+    return workspace
+
+
+def mla_kv_prolog(hidden, W_kv_a, gamma, W_kv_b, positions, eps: float = 1e-6,
+                  theta: float = 10000.0, *, k_nope=None, value=None, k_pe=None,
+                  compressed_kv=None, workspace=None, stream=None, dn: int = 128,
+                  dv: int = 128):
+    """fp16 / bf16 KV prolog on torch tensors (all on one GPU).
+
+    hidden [T,H], W_kv_a [H,r+dr], gamma [r], W_kv_b [r,nh*(dn+dv)] of one
+    dtype (float16 or bfloat16); positions [T] int32.  Returns
+    (k_nope [T,nh,dn], value [T,nh,dv], k_pe [T,dr], compressed_kv [T,r])."""
+    torch = _torch()
+    dtype = hidden.dtype
+    code = {torch.float16: MLA_F16, torch.bfloat16: MLA_BF16}.get(dtype)
+    if code is None:
+        raise ValueError(f"hidden: dtype {dtype}, expected float16 or bfloat16")
+    dev = hidden.device
+    if hidden.dim() != 2:
+        raise ValueError("hidden must be [T, H]")
+    T = hidden.shape[0]
+    d = _dims_from(hidden, W_kv_b, gamma, W_kv_a, dn, dv)
+    _check(hidden, "hidden", dtype, (T, d.H), dev)
+    _check(W_kv_a, "W_kv_a", dtype, (d.H, d.r + d.dr), dev)
+    _check(gamma, "gamma", dtype, (d.r,), dev)
+    _check(W_kv_b, "W_kv_b", dtype, (d.r, d.nh * (d.dn + d.dv)), dev)
+    _check(positions, "positions", torch.int32, (T,), dev)
+    outs = _outputs(T, d, dtype, dev, k_nope, value, k_pe, compressed_kv)
+    nbytes = mla_kv_prolog_workspace_size(T, d, code)
+    if T > 0 and nbytes == 0:
+        raise MlaError(MLA_ERR_UNSUPPORTED, "mla_kv_prolog_workspace_size")
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib().mla_kv_prolog(
+        hidden.data_ptr(), W_kv_a.data_ptr(), gamma.data_ptr(), W_kv_b.data_ptr(),
+        positions.data_ptr(), T, d.c(), code, float(eps), float(theta),
+        outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(), outs[3].data_ptr(),
+        ws.data_ptr(), ws.numel(), _stream_ptr(dev, stream))
+    if st != MLA_OK:
+        raise MlaError(st, "mla_kv_prolog")
+    return outs
+
+
+def mla_kv_prolog_w8a8(hidden, Wq_kv_a, s_kv_a, gamma, Wq_kv_b, s_kv_b, positions,
+                       eps: float = 1e-6, theta: float = 10000.0, *, k_nope=None,
+                       value=None, k_pe=None, compressed_kv=None, dbg_acc1=None,
+                       dbg_acc2=None, dbg_row_begin: int = 0, dbg_rows: int = 0,
+                       workspace=None, stream=None, dn: int = 128, dv: int = 128):
+    """W8A8 KV prolog on torch tensors: hidden/gamma bfloat16, int8 weights
+    with float32 per-output-column scales, bfloat16 outputs.  dbg_acc1
+    [dbg_rows, r+dr] / dbg_acc2 [dbg_rows, nh*(dn+dv)] int32 (optional)
+    receive the exact accumulators of rows [dbg_row_begin, +dbg_rows)."""
+    torch = _torch()
+    dev = hidden.device
+    if hidden.dim() != 2:
+        raise ValueError("hidden must be [T, H]")
+    T = hidden.shape[0]
+    d = _dims_from(hidden, Wq_kv_b, gamma, Wq_kv_a, dn, dv)
+    N1, N2 = d.r + d.dr, d.nh * (d.dn + d.dv)
+    _check(hidden, "hidden", torch.bfloat16, (T, d.H), dev)
+    _check(Wq_kv_a, "Wq_kv_a", torch.int8, (d.H, N1), dev)
+    _check(s_kv_a, "s_kv_a", torch.float32, (N1,), dev)
+    _check(gamma, "gamma", torch.bfloat16, (d.r,), dev)
+    _check(Wq_kv_b, "Wq_kv_b", torch.int8, (d.r, N2), dev)
+    _check(s_kv_b, "s_kv_b", torch.float32, (N2,), dev)
+    _check(positions, "positions", torch.int32, (T,), dev)
+    if dbg_acc1 is not None:
+        _check(dbg_acc1, "dbg_acc1", torch.int32, (dbg_rows, N1), dev)
+    if dbg_acc2 is not None:
+        _check(dbg_acc2, "dbg_acc2", torch.int32, (dbg_rows, N2), dev)
+    outs = _outputs(T, d, torch.bfloat16, dev, k_nope, value, k_pe, compressed_kv)
+    nbytes = mla_kv_prolog_w8a8_workspace_size(T, d)
+    if T > 0 and nbytes == 0:
+        raise MlaError(MLA_ERR_UNSUPPORTED, "mla_kv_prolog_w8a8_workspace_size")
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib().mla_kv_prolog_w8a8(
+        hidden.data_ptr(), Wq_kv_a.data_ptr(), s_kv_a.data_ptr(), gamma.data_ptr(),
+        Wq_kv_b.data_ptr(), s_kv_b.data_ptr(), positions.data_ptr(), T, d.c(), float(eps),
+        float(theta), outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
+        outs[3].data_ptr(), dbg_acc1.data_ptr() if dbg_acc1 is not None else None,
+        dbg_acc2.data_ptr() if dbg_acc2 is not None else None, int(dbg_row_begin),
+        int(dbg_rows), ws.data_ptr(), ws.numel(), _stream_ptr(dev, stream))
+    if st != MLA_OK:
+        raise MlaError(st, "mla_kv_prolog_w8a8")
+    return outs

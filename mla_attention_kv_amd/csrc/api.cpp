@@ -1,0 +1,183 @@
+// C-ABI of libmlaprolog: argument validation, launch planning (the
+// decode / prefill dispatcher), workspace sizing, and the calls into the
+// gfx950 launchers.  Every host-checkable condition is checked here, before
+// anything reaches the GPU.
+#include <atomic>
+#include <cmath>
+
+#include "../../include/libmlaprolog.h"
+#include "mla_common.h"
+
+using namespace mla;
+
+namespace {
+
+std::atomic<int> g_force_path{-1};
+
+// Token counts up to this many take the decode tiling (small M tiles,
+// split-K over the hidden dimension so that the weight stream is spread
+// over the whole chip); larger counts take the prefill tiling.  The pages'
+// own short/long split is by sequence length as well (the migration guide's
+// note on dynamic selection); the threshold here is the widest decode batch
+// of the benchmarked workloads.
+constexpr int64_t kDecodeMaxT = 64;
+
+int select_path(int64_t T) {
+    const int f = g_force_path.load(std::memory_order_relaxed);
+    if (f == 0 || f == 1) return f;
+    return T <= kDecodeMaxT ? 0 : 1;
+}
+
+int kslabs_a(int H, bool int8) { return int8 ? H / 128 : H * 2 / 128; }
+
+Plan make_plan(int64_t T, int H, bool int8, int path) {
+    Plan p;
+    p.path = path;
+    const int ks = kslabs_a(H, int8);
+    if (path == 0) {
+        p.bm1 = T <= 16 ? 16 : (T <= 32 ? 32 : 64);
+        p.bm2 = p.bm1;
+        p.bn2 = 64;
+    } else {
+        p.bm1 = 128;
+        p.bm2 = 128;
+        p.bn2 = 128;
+    }
+    // split kv_a_proj's K so that at least ~256 workgroups stream W_kv_a,
+    // keeping at least two K slabs per split
+    const int64_t tiles = ((T + p.bm1 - 1) / p.bm1) * (kN1 / 64);
+    int64_t s = (256 + tiles - 1) / tiles;
+    const int64_t smax = ks >= 2 ? ks / 2 : 1;
+    if (s > smax) s = smax;
+    if (s < 1) s = 1;
+    // equalise the slabs per split
+    const int per = (int)((ks + s - 1) / s);
+    p.s1 = (ks + per - 1) / per;
+    return p;
+}
+
+bool dims_supported(const mla_dims_t& d) {
+    return d.r == kR && d.dr == kDR && d.dn == kDN && d.dv == kDV && d.nh >= 1 &&
+           d.nh <= 1024 && d.H >= 64 && d.H <= 65536 && (d.H % 64) == 0;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t ws_fp_max(int64_t T, const mla_dims_t& d) {
+    size_t m = 0;
+    for (int path = 0; path < 2; ++path) {
+        size_t b = ws_fp(T, make_plan(T, d.H, false, path)).total;
+        if (b > m) m = b;
+    }
+    return m;
+}
+size_t ws_w8_max(int64_t T, const mla_dims_t& d) {
+    size_t m = 0;
+    for (int path = 0; path < 2; ++path) {
+        size_t b = ws_w8(T, d.H, make_plan(T, d.H, true, path)).total;
+        if (b > m) m = b;
+    }
+    return m;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_kv_prolog_workspace_size(int64_t T, mla_dims_t d, mla_dtype_t dt) {
+    if (T <= 0 || T > MLA_MAX_TOKENS || !dims_supported(d)) return 0;
+    if (dt != MLA_F16 && dt != MLA_BF16) return 0;
+    return ws_fp_max(T, d);
+}
+
+size_t mla_kv_prolog_w8a8_workspace_size(int64_t T, mla_dims_t d) {
+    if (T <= 0 || T > MLA_MAX_TOKENS || !dims_supported(d) || (d.H % 128) != 0) return 0;
+    return ws_w8_max(T, d);
+}
+
+int mla_kv_prolog_selected_path(int64_t T, mla_dims_t) { return select_path(T); }
+
+int mla_kv_prolog_force_path(int path) {
+    if (path != 0 && path != 1) path = -1;
+    return g_force_path.exchange(path);
+}
+
+const char* mla_status_string(mla_status_t s) {
+    switch (s) {
+        case MLA_OK: return "MLA_OK";
+        case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: null pointer, bad T, eps, theta or dtype";
+        case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: dims outside what the kernels implement";
+        case MLA_ERR_MISALIGNED: return "MLA_ERR_MISALIGNED: a pointer is not 16-byte aligned";
+        case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
+        case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP launch or runtime call failed";
+    }
+    return "unknown mla_status_t";
+}
+
+mla_status_t mla_kv_prolog(const void* hidden, const void* W_kv_a, const void* gamma,
+                           const void* W_kv_b, const int32_t* positions, int64_t T,
+                           mla_dims_t d, mla_dtype_t dt, float eps, float theta,
+                           void* k_nope, void* value, void* k_pe, void* compressed_kv,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    if (T < 0 || T > MLA_MAX_TOKENS) return MLA_ERR_INVALID_ARG;
+    if (dt != MLA_F16 && dt != MLA_BF16) return MLA_ERR_INVALID_ARG;
+    if (!std::isfinite(eps) || eps < 0.f || !std::isfinite(theta) || theta <= 0.f)
+        return MLA_ERR_INVALID_ARG;
+    if (!dims_supported(d)) return MLA_ERR_UNSUPPORTED;
+    if (T == 0) return MLA_OK;
+    const void* ptrs[] = {hidden, W_kv_a, gamma, W_kv_b, positions,
+                          k_nope, value, k_pe, compressed_kv};
+    for (const void* p : ptrs)
+        if (p == nullptr) return MLA_ERR_INVALID_ARG;
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return MLA_ERR_MISALIGNED;
+    if (workspace == nullptr) return MLA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MLA_ERR_MISALIGNED;
+    const Plan plan = make_plan(T, d.H, false, select_path(T));
+    if (workspace_bytes < ws_fp(T, plan).total) return MLA_ERR_WORKSPACE;
+    hipError_t e = launch_fp((int)dt, hidden, W_kv_a, gamma, W_kv_b, positions, T, d.H, d.nh,
+                             eps, theta, k_nope, value, k_pe, compressed_kv, workspace, plan,
+                             (hipStream_t)stream);
+    return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_kv_prolog_w8a8(const void* hidden_bf16, const int8_t* Wq_kv_a,
+                                const float* s_kv_a, const void* gamma_bf16,
+                                const int8_t* Wq_kv_b, const float* s_kv_b,
+                                const int32_t* positions, int64_t T, mla_dims_t d, float eps,
+                                float theta, void* k_nope, void* value, void* k_pe,
+                                void* compressed_kv, int32_t* dbg_acc1, int32_t* dbg_acc2,
+                                int64_t dbg_row_begin, int64_t dbg_rows, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    if (T < 0 || T > MLA_MAX_TOKENS) return MLA_ERR_INVALID_ARG;
+    if (!std::isfinite(eps) || eps < 0.f || !std::isfinite(theta) || theta <= 0.f)
+        return MLA_ERR_INVALID_ARG;
+    if (!dims_supported(d) || (d.H % 128) != 0) return MLA_ERR_UNSUPPORTED;
+    if (T == 0) return MLA_OK;
+    const void* ptrs[] = {hidden_bf16, Wq_kv_a, s_kv_a, gamma_bf16, Wq_kv_b, s_kv_b,
+                          positions, k_nope, value, k_pe, compressed_kv};
+    for (const void* p : ptrs)
+        if (p == nullptr) return MLA_ERR_INVALID_ARG;
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return MLA_ERR_MISALIGNED;
+    if (dbg_acc1 != nullptr || dbg_acc2 != nullptr) {
+        if (dbg_rows < 0 || dbg_row_begin < 0 || dbg_row_begin + dbg_rows > T)
+            return MLA_ERR_INVALID_ARG;
+        if ((dbg_acc1 && !aligned16(dbg_acc1)) || (dbg_acc2 && !aligned16(dbg_acc2)))
+            return MLA_ERR_MISALIGNED;
+    } else {
+        dbg_rows = 0;
+        dbg_row_begin = 0;
+    }
+    if (workspace == nullptr) return MLA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MLA_ERR_MISALIGNED;
+    const Plan plan = make_plan(T, d.H, true, select_path(T));
+    if (workspace_bytes < ws_w8(T, d.H, plan).total) return MLA_ERR_WORKSPACE;
+    hipError_t e = launch_w8a8(hidden_bf16, Wq_kv_a, s_kv_a, gamma_bf16, Wq_kv_b, s_kv_b,
+                               positions, T, d.H, d.nh, eps, theta, k_nope, value, k_pe,
+                               compressed_kv, dbg_acc1, dbg_acc2, dbg_row_begin, dbg_rows,
+                               workspace, plan, (hipStream_t)stream);
+    return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // extern "C"

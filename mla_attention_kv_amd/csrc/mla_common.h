@@ -1,0 +1,130 @@
+// Internal definitions shared by the gfx950 kernels and the C-ABI layer of
+// libmlaprolog.  Not a public header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef int i4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+
+// element kinds of the two projections' operands
+enum Elem : int { kF16 = 1, kBF16 = 2, kI8 = 3 };
+
+// fixed widths of the prolog (DeepSeek-V2-Lite / R1 MLA)
+constexpr int kR = 512;   // kv_lora_rank
+constexpr int kDR = 64;   // rope dim
+constexpr int kN1 = kR + kDR;
+constexpr int kDN = 128;  // k_nope per head
+constexpr int kDV = 128;  // value per head
+constexpr int kHeadW = kDN + kDV;
+
+// ---------------------------------------------------------------------------
+// conversions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+    _Float16 v = __builtin_bit_cast(_Float16, h);
+    return (float)v;
+}
+// round-to-nearest-even fp32 -> bf16 (inputs are finite here)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+    _Float16 h = (_Float16)f;  // v_cvt_f16_f32, round to nearest even
+    return __builtin_bit_cast(uint16_t, h);
+}
+template <int E>
+__device__ __forceinline__ float ld_to_f32(uint16_t b) {
+    if constexpr (E == kF16) return f16_to_f32(b);
+    else return bf16_to_f32(b);
+}
+template <int E>
+__device__ __forceinline__ uint16_t f32_to_st(float f) {
+    if constexpr (E == kF16) return f32_to_f16(f);
+    else return f32_to_bf16(f);
+}
+
+// ---------------------------------------------------------------------------
+// wave reductions (64 lanes)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// launch plan and workspace layout (host)
+// ---------------------------------------------------------------------------
+struct Plan {
+    int path;       // 0 decode, 1 prefill
+    int bm1, s1;    // kv_a_proj: rows per tile, split-K count (BN = 64)
+    int bm2, bn2;   // kv_b_proj tile
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// fp path: [s1][T][576] fp32 split-K partial sums of kv_a_proj
+struct WsFp {
+    size_t p1, total;
+};
+inline WsFp ws_fp(int64_t T, const Plan& p) {
+    WsFp w;
+    w.p1 = 0;
+    w.total = align256((size_t)p.s1 * (size_t)T * kN1 * 4);
+    return w;
+}
+
+// W8A8 path: int8 codes of x [T][H], their scales [T], int32 split-K partials
+// [s1][T][576], int8 codes of z [T][512], their scales [T], RMS factors [T]
+struct WsW8 {
+    size_t qx, sx, p1, qz, sz, inv, total;
+};
+inline WsW8 ws_w8(int64_t T, int H, const Plan& p) {
+    WsW8 w;
+    size_t o = 0;
+    w.qx = o; o += align256((size_t)T * H);
+    w.sx = o; o += align256((size_t)T * 4);
+    w.p1 = o; o += align256((size_t)p.s1 * (size_t)T * kN1 * 4);
+    w.qz = o; o += align256((size_t)T * kR);
+    w.sz = o; o += align256((size_t)T * 4);
+    w.inv = o; o += align256((size_t)T * 4);
+    w.total = o;
+    return w;
+}
+
+// ---------------------------------------------------------------------------
+// host-side launchers (defined in the .hip files)
+// ---------------------------------------------------------------------------
+
+hipError_t launch_fp(int dt, const void* X, const void* Wa, const void* gamma,
+                     const void* Wb, const int32_t* pos, int64_t T, int H, int nh,
+                     float eps, float theta, void* k_nope, void* value, void* k_pe,
+                     void* ckv, void* ws, const Plan& plan, hipStream_t st);
+
+hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa,
+                       const void* gamma, const int8_t* Wqb, const float* swb,
+                       const int32_t* pos, int64_t T, int H, int nh, float eps,
+                       float theta, void* k_nope, void* value, void* k_pe, void* ckv,
+                       int32_t* dbg1, int32_t* dbg2, int64_t dbg_begin, int64_t dbg_rows,
+                       void* ws, const Plan& plan, hipStream_t st);
+
+}  // namespace mla

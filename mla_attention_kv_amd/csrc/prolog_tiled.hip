@@ -1,0 +1,524 @@
+// Tiled gfx950 kernels of the MLA KV prolog: both projections as MFMA GEMMs
+// (LDS-staged tiles, register prefetch of the next K slab, optional split-K),
+// plus the per-token kernels that finish kv_a_proj (split, RMSNorm, RoPE) and,
+// on the W8A8 path, quantise the activations.
+//
+// Steps follow the DeepSeek-V2-Lite-Chat MLA KV Prolog migration guide
+// (dpshk.com), sections "Background" and "Source-level principle"; RoPE is
+// the rotate-half x*cos + x_rot*sin form of its "Precision verification"
+// section.  The W8A8 scheme is the per-token / per-output-column int8 one
+// stated in include/libmlaprolog.h.
+#include "mla_common.h"
+
+namespace mla {
+
+// ---------------------------------------------------------------------------
+// MFMA 16x16 step over 64 bytes of K per lane group:
+//   fp16/bf16: v_mfma_f32_16x16x32_{f16,bf16}  (8 elements per lane)
+//   int8:      v_mfma_i32_16x16x64_i8          (16 elements per lane)
+// Operand lane layout: lane l supplies row (A) / column (B) l%16 and the
+// 16-byte K slice (l/16); result lane l holds rows 4*(l/16)+i, column l%16.
+// ---------------------------------------------------------------------------
+template <int E>
+struct Acc { typedef f4_t type; };
+template <>
+struct Acc<kI8> { typedef i4_t type; };
+
+template <int E>
+__device__ __forceinline__ typename Acc<E>::type mfma16(u4_t a, u4_t b, typename Acc<E>::type c) {
+    if constexpr (E == kF16) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, a),
+                                                      __builtin_bit_cast(h8_t, b), c, 0, 0, 0);
+    } else if constexpr (E == kBF16) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8_t, a),
+                                                       __builtin_bit_cast(b8_t, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i4_t, a),
+                                                     __builtin_bit_cast(i4_t, b), c, 0, 0, 0);
+    }
+}
+
+// 8x8 transpose of 16-bit values: in[i] = row i (8 columns), out[j] = column
+// j (8 rows).
+__device__ __forceinline__ void transpose8x8_b16(const u4_t in[8], u4_t out[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            uint32_t lo = in[2 * v][j >> 1], hi = in[2 * v + 1][j >> 1];
+            out[j][v] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u))
+                                : ((lo & 0xFFFFu) | (hi << 16));
+        }
+    }
+}
+
+// 16x16 transpose of bytes: in[i] = row i (16 columns), out[j] = column j.
+__device__ __forceinline__ void transpose16x16_b8(const u4_t in[16], u4_t out[16]) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int w = j >> 2, sh = (j & 3) * 8;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            uint32_t b0 = (in[4 * v + 0][w] >> sh) & 0xFFu;
+            uint32_t b1 = (in[4 * v + 1][w] >> sh) & 0xFFu;
+            uint32_t b2 = (in[4 * v + 2][w] >> sh) & 0xFFu;
+            uint32_t b3 = (in[4 * v + 3][w] >> sh) & 0xFFu;
+            out[j][v] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Epilogues: called once per accumulator element.
+// ---------------------------------------------------------------------------
+struct EpiPartialF32 {  // kv_a_proj split-K partial, fp32 [s][T][576]
+    float* out;
+    int64_t T;
+    __device__ __forceinline__ void operator()(int row, int col, int s, float v) const {
+        out[((int64_t)s * T + row) * kN1 + col] = v;
+    }
+};
+struct EpiPartialI32 {  // kv_a_proj split-K partial, int32 [s][T][576]
+    int32_t* out;
+    int64_t T;
+    __device__ __forceinline__ void operator()(int row, int col, int s, int v) const {
+        out[((int64_t)s * T + row) * kN1 + col] = v;
+    }
+};
+// kv_b_proj result column `col` = head col/256, slot col%256: slots [0,128)
+// are k_nope, [128,256) are value.
+template <int E>
+struct EpiKvFp {
+    uint16_t* k_nope;
+    uint16_t* value;
+    int nh;
+    __device__ __forceinline__ void operator()(int row, int col, int, float v) const {
+        const int h = col >> 8, s = col & 255;
+        uint16_t* dst = (s < kDN) ? k_nope : value;
+        dst[((int64_t)row * nh + h) * kDN + (s & 127)] = f32_to_st<E>(v);
+    }
+};
+struct EpiKvW8 {
+    uint16_t* k_nope;
+    uint16_t* value;
+    int nh;
+    const float* sz;
+    const float* inv_t;
+    const float* swb;
+    int32_t* dbg;
+    int64_t dbg_begin, dbg_rows;
+    __device__ __forceinline__ void operator()(int row, int col, int, int acc) const {
+        float v = (((float)acc * sz[row]) * inv_t[row]) * swb[col];
+        const int h = col >> 8, s = col & 255;
+        uint16_t* dst = (s < kDN) ? k_nope : value;
+        dst[((int64_t)row * nh + h) * kDN + (s & 127)] = f32_to_bf16(v);
+        if (dbg != nullptr && row >= dbg_begin && row < dbg_begin + dbg_rows)
+            dbg[(row - dbg_begin) * (int64_t)nh * kHeadW + col] = acc;
+    }
+};
+
+// ---------------------------------------------------------------------------
+// C[M, N] = A[M, K] . B[K, N]; A and B row-major, K consumed in 128-byte
+// slabs (64 fp16/bf16 or 128 int8 elements = two MFMA K steps).
+// Grid: x = M tiles, y = N tiles, z = split-K index.  256 threads, 4 waves
+// laid out (BM/WM) x (BN/WN), each wave owning a WM x WN block of 16x16
+// MFMA tiles.  The B slab is transposed into LDS as [n][k] so that both
+// operands are read as 16-byte K slices.  While one slab is multiplied, the
+// next is already being fetched into registers.
+// ---------------------------------------------------------------------------
+template <int E, int BM, int BN, int WM, int WN, class Epi>
+__global__ __launch_bounds__(256) void gemm_tiled_kernel(
+    const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
+    int M, int kslabs_per_split, int kslabs_total, Epi epi) {
+    constexpr int KB = 128;           // bytes of K per slab
+    constexpr int ST = KB + 16;       // LDS row stride in bytes (padding vs bank conflicts)
+    constexpr int ES = (E == kI8) ? 1 : 2;
+    constexpr int KE = KB / ES;       // K elements per slab
+    constexpr int WAVES_N = BN / WN;
+    static_assert((BM / WM) * WAVES_N == 4, "4 waves");
+    constexpr int TM = WM / 16, TN = WN / 16;
+    constexpr int A_CHUNKS = BM * (KB / 16);           // 16-byte chunks in an A slab
+    constexpr int A_PER_T = (A_CHUNKS + 255) / 256;
+    constexpr int BR = (E == kI8) ? 16 : 8;             // rows per B block
+    constexpr int BC = 16 / ES;                         // columns per B block
+    constexpr int B_BLOCKS = (KE / BR) * (BN / BC);
+    static_assert(B_BLOCKS <= 256, "one B block per thread at most");
+
+    __shared__ __align__(16) uint8_t As[BM * ST];
+    __shared__ __align__(16) uint8_t Bs[BN * ST];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm0 = (wave / WAVES_N) * WM, wn0 = (wave % WAVES_N) * WN;
+    const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN, s = blockIdx.z;
+    const int kc0 = s * kslabs_per_split;
+    const int kc1 = min(kc0 + kslabs_per_split, kslabs_total);
+
+    typedef typename Acc<E>::type acc_t;
+    acc_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
+
+    u4_t ra[A_PER_T];
+    u4_t rb[BR];
+    const int b_rb = tid / (BN / BC), b_cb = tid % (BN / BC);
+
+    auto gload = [&](int kc) {
+#pragma unroll
+        for (int i = 0; i < A_PER_T; ++i) {
+            const int c = tid + i * 256;
+            if (c < A_CHUNKS) {
+                const int row = c >> 3, c16 = c & 7;
+                u4_t v = {0u, 0u, 0u, 0u};
+                if (m0 + row < M)
+                    v = *(const u4_t*)(A + (int64_t)(m0 + row) * lda + (int64_t)kc * KB + c16 * 16);
+                ra[i] = v;
+            }
+        }
+        if (tid < B_BLOCKS) {
+            const uint8_t* src = B + ((int64_t)kc * KE + b_rb * BR) * ldb + (int64_t)(n0 + b_cb * BC) * ES;
+#pragma unroll
+            for (int i = 0; i < BR; ++i) rb[i] = *(const u4_t*)(src + (int64_t)i * ldb);
+        }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int i = 0; i < A_PER_T; ++i) {
+            const int c = tid + i * 256;
+            if (c < A_CHUNKS) {
+                const int row = c >> 3, c16 = c & 7;
+                *(u4_t*)(As + row * ST + c16 * 16) = ra[i];
+            }
+        }
+        if (tid < B_BLOCKS) {
+            u4_t t[BR];
+            if constexpr (E == kI8) transpose16x16_b8(rb, t);
+            else transpose8x8_b16(rb, t);
+#pragma unroll
+            for (int j = 0; j < BC; ++j)
+                *(u4_t*)(Bs + (b_cb * BC + j) * ST + b_rb * 16) = t[j];
+        }
+    };
+
+    if (kc0 < kc1) gload(kc0);
+    for (int kc = kc0; kc < kc1; ++kc) {
+        lstore();
+        __syncthreads();
+        if (kc + 1 < kc1) gload(kc + 1);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            u4_t a[TM], b[TN];
+            const int kofs = ks * 64 + (lane >> 4) * 16;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                a[i] = *(const u4_t*)(As + (wm0 + i * 16 + (lane & 15)) * ST + kofs);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                b[j] = *(const u4_t*)(Bs + (wn0 + j * 16 + (lane & 15)) * ST + kofs);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i][j] = mfma16<E>(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int row = m0 + wm0 + i * 16 + (lane >> 4) * 4 + v;
+                const int col = n0 + wn0 + j * 16 + (lane & 15);
+                if (row < M) epi(row, col, s, acc[i][j][v]);
+            }
+}
+
+// ---------------------------------------------------------------------------
+// Per-token finish of kv_a_proj, fp16/bf16 path.  One wave per token: lane l
+// owns latent columns 8l..8l+7 and rope column l.
+//   c, p  = sum of the split-K partials (split order ascending)
+//   y     = c / sqrt(sum(c^2)/512 + eps) * gamma      -> compressed_kv
+//   k_pe  = rotate-half RoPE of p at the token's position
+// The rope angle pos * theta^(-2i/64) and its sine / cosine are evaluated in
+// double, then rounded to fp32 for the rotation.
+// ---------------------------------------------------------------------------
+template <int E>
+__global__ __launch_bounds__(64) void finish_a_fp_kernel(
+    const float* __restrict__ P, int S, int64_t T, const uint16_t* __restrict__ gamma,
+    const int32_t* __restrict__ pos, float eps, float theta, uint16_t* __restrict__ ckv,
+    uint16_t* __restrict__ kpe) {
+    const int64_t t = blockIdx.x;
+    const int lane = threadIdx.x;
+    float c[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float p = 0.f;
+    for (int s = 0; s < S; ++s) {
+        const float* row = P + ((int64_t)s * T + t) * kN1;
+        const f4_t v0 = *(const f4_t*)(row + 8 * lane);
+        const f4_t v1 = *(const f4_t*)(row + 8 * lane + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            c[i] += v0[i];
+            c[4 + i] += v1[i];
+        }
+        p += row[kR + lane];
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += c[i] * c[i];
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)kR + eps);
+    const u4_t g = *(const u4_t*)(gamma + 8 * lane);
+    u4_t o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const float g0 = ld_to_f32<E>((uint16_t)(g[w] & 0xFFFFu));
+        const float g1 = ld_to_f32<E>((uint16_t)(g[w] >> 16));
+        const uint32_t y0 = f32_to_st<E>((c[2 * w] * inv) * g0);
+        const uint32_t y1 = f32_to_st<E>((c[2 * w + 1] * inv) * g1);
+        o[w] = y0 | (y1 << 16);
+    }
+    *(u4_t*)(ckv + t * kR + 8 * lane) = o;
+
+    const float partner = __shfl_xor(p, 32, 64);
+    const int i = lane & 31;
+    const double f = pow((double)theta, -2.0 * (double)i / (double)kDR);
+    const double ang = (double)pos[t] * f;
+    const float cs = (float)cos(ang), sn = (float)sin(ang);
+    const float out = (lane < 32) ? (p * cs - partner * sn) : (p * cs + partner * sn);
+    kpe[t * kDR + lane] = f32_to_st<E>(out);
+}
+
+// ---------------------------------------------------------------------------
+// W8A8: per-token activation quantisation (one 256-thread block per token).
+//   amax = max |x|;  q = clamp(rint(x * (127/amax)), -127, 127);
+//   scale = amax / 127;  amax == 0 -> q = 0, scale = 0.
+// fp32 with IEEE division and round-half-even rint.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_rows_bf16_kernel(const uint16_t* __restrict__ X,
+                                                              int H, int8_t* __restrict__ Q,
+                                                              float* __restrict__ scale) {
+    __shared__ float red[4];
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const uint16_t* row = X + t * H;
+    float amax = 0.f;
+    for (int k = tid * 8; k < H; k += 256 * 8) {
+        const u4_t v = *(const u4_t*)(row + k);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            amax = fmaxf(amax, fabsf(bf16_to_f32((uint16_t)(v[w] & 0xFFFFu))));
+            amax = fmaxf(amax, fabsf(bf16_to_f32((uint16_t)(v[w] >> 16))));
+        }
+    }
+    amax = wave_max(amax);
+    if ((tid & 63) == 0) red[tid >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float inv = (amax > 0.f) ? (127.0f / amax) : 0.f;
+    for (int k = tid * 8; k < H; k += 256 * 8) {
+        const u4_t v = *(const u4_t*)(row + k);
+        u2_t q;
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            uint32_t packed = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int e = w * 4 + b;
+                const uint32_t bits = (v[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+                float r = rintf(bf16_to_f32((uint16_t)bits) * inv);
+                r = fminf(fmaxf(r, -127.f), 127.f);
+                packed |= ((uint32_t)(uint8_t)(int8_t)(int)r) << (8 * b);
+            }
+            q[w] = packed;
+        }
+        *(u2_t*)(Q + t * H + k) = q;
+    }
+    if (tid == 0) scale[t] = (amax > 0.f) ? (amax / 127.0f) : 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// W8A8 per-token finish of kv_a_proj.  One wave per token.
+//   acc1 = sum of int32 partials (exact);  A = (float(acc1) * sx) * s_kv_a
+//   z = c * gamma;  qz, sz = per-token quantisation of z
+//   inv_t = 1/sqrt(sum(c^2)/512 + eps);  compressed_kv = bf16(z * inv_t)
+//   k_pe = RoPE(p)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void finish_a_w8_kernel(
+    const int32_t* __restrict__ P, int S, int64_t T, const float* __restrict__ sx,
+    const float* __restrict__ swa, const uint16_t* __restrict__ gamma,
+    const int32_t* __restrict__ pos, float eps, float theta, int8_t* __restrict__ QZ,
+    float* __restrict__ sz, float* __restrict__ inv_out, uint16_t* __restrict__ ckv,
+    uint16_t* __restrict__ kpe, int32_t* __restrict__ dbg, int64_t dbg_begin, int64_t dbg_rows) {
+    const int64_t t = blockIdx.x;
+    const int lane = threadIdx.x;
+    int a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int ap = 0;
+    for (int s = 0; s < S; ++s) {
+        const int32_t* row = P + ((int64_t)s * T + t) * kN1;
+        const i4_t v0 = *(const i4_t*)(row + 8 * lane);
+        const i4_t v1 = *(const i4_t*)(row + 8 * lane + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            a[i] += v0[i];
+            a[4 + i] += v1[i];
+        }
+        ap += row[kR + lane];
+    }
+    if (dbg != nullptr && t >= dbg_begin && t < dbg_begin + dbg_rows) {
+        int32_t* d = dbg + (t - dbg_begin) * kN1;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d[8 * lane + i] = a[i];
+        d[kR + lane] = ap;
+    }
+    const float sxt = sx[t];
+    float c[8], z[8];
+    float ss = 0.f, az = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int col = 8 * lane + i;
+        c[i] = ((float)a[i] * sxt) * swa[col];
+        const uint16_t gb = gamma[col];
+        z[i] = c[i] * bf16_to_f32(gb);
+        ss += c[i] * c[i];
+        az = fmaxf(az, fabsf(z[i]));
+    }
+    const float p = ((float)ap * sxt) * swa[kR + lane];
+    ss = wave_sum(ss);
+    az = wave_max(az);
+    const float inv_t = 1.0f / sqrtf(ss / (float)kR + eps);
+    const float inv2 = (az > 0.f) ? (127.0f / az) : 0.f;
+    u2_t q;
+    u4_t o;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            float r = rintf(z[w * 4 + b] * inv2);
+            r = fminf(fmaxf(r, -127.f), 127.f);
+            packed |= ((uint32_t)(uint8_t)(int8_t)(int)r) << (8 * b);
+        }
+        q[w] = packed;
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+        o[w] = (uint32_t)f32_to_bf16(z[2 * w] * inv_t) | ((uint32_t)f32_to_bf16(z[2 * w + 1] * inv_t) << 16);
+    *(u2_t*)(QZ + t * kR + 8 * lane) = q;
+    *(u4_t*)(ckv + t * kR + 8 * lane) = o;
+    if (lane == 0) {
+        sz[t] = (az > 0.f) ? (az / 127.0f) : 0.f;
+        inv_out[t] = inv_t;
+    }
+    const float partner = __shfl_xor(p, 32, 64);
+    const int i = lane & 31;
+    const double f = pow((double)theta, -2.0 * (double)i / (double)kDR);
+    const double ang = (double)pos[t] * f;
+    const float cs = (float)cos(ang), sn = (float)sin(ang);
+    const float out = (lane < 32) ? (p * cs - partner * sn) : (p * cs + partner * sn);
+    kpe[t * kDR + lane] = f32_to_bf16(out);
+}
+
+// ---------------------------------------------------------------------------
+// launch helpers
+// ---------------------------------------------------------------------------
+template <int E, int BM, int BN, int WM, int WN, class Epi>
+static void gemm_launch(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M,
+                        int N, int kslabs, int S, Epi epi, hipStream_t st) {
+    const int per = (kslabs + S - 1) / S;
+    dim3 grid((unsigned)((M + BM - 1) / BM), (unsigned)(N / BN), (unsigned)S);
+    hipLaunchKernelGGL((gemm_tiled_kernel<E, BM, BN, WM, WN, Epi>), grid, dim3(256), 0, st,
+                       (const uint8_t*)A, lda, (const uint8_t*)B, ldb, (int)M, per, kslabs, epi);
+}
+
+// kv_a_proj tiles: BN = 64 always (576 = 9 x 64)
+template <int E, class Epi>
+static void gemm1_dispatch(int bm, const void* A, int64_t lda, const void* B, int64_t M,
+                           int kslabs, int S, Epi epi, hipStream_t st) {
+    const int64_t ldb = (int64_t)kN1 * ((E == kI8) ? 1 : 2);
+    switch (bm) {
+        case 16: gemm_launch<E, 16, 64, 16, 16>(A, lda, B, ldb, M, kN1, kslabs, S, epi, st); break;
+        case 32: gemm_launch<E, 32, 64, 16, 32>(A, lda, B, ldb, M, kN1, kslabs, S, epi, st); break;
+        case 64: gemm_launch<E, 64, 64, 32, 32>(A, lda, B, ldb, M, kN1, kslabs, S, epi, st); break;
+        default: gemm_launch<E, 128, 64, 64, 32>(A, lda, B, ldb, M, kN1, kslabs, S, epi, st); break;
+    }
+}
+
+// kv_b_proj tiles
+template <int E, class Epi>
+static void gemm2_dispatch(int bm, int bn, const void* A, int64_t lda, const void* B, int64_t M,
+                           int N2, Epi epi, hipStream_t st) {
+    const int64_t ldb = (int64_t)N2 * ((E == kI8) ? 1 : 2);
+    const int kslabs = (E == kI8) ? kR / 128 : kR * 2 / 128;
+    if (bn == 128) {
+        gemm_launch<E, 128, 128, 64, 64>(A, lda, B, ldb, M, N2, kslabs, 1, epi, st);
+        return;
+    }
+    switch (bm) {
+        case 16: gemm_launch<E, 16, 64, 16, 16>(A, lda, B, ldb, M, N2, kslabs, 1, epi, st); break;
+        case 32: gemm_launch<E, 32, 64, 16, 32>(A, lda, B, ldb, M, N2, kslabs, 1, epi, st); break;
+        case 64: gemm_launch<E, 64, 64, 32, 32>(A, lda, B, ldb, M, N2, kslabs, 1, epi, st); break;
+        default: gemm_launch<E, 128, 64, 64, 32>(A, lda, B, ldb, M, N2, kslabs, 1, epi, st); break;
+    }
+}
+
+template <int E>
+static hipError_t launch_fp_t(const void* X, const void* Wa, const void* gamma, const void* Wb,
+                              const int32_t* pos, int64_t T, int H, int nh, float eps,
+                              float theta, void* k_nope, void* value, void* k_pe, void* ckv,
+                              void* ws, const Plan& plan, hipStream_t st) {
+    const WsFp w = ws_fp(T, plan);
+    float* P1 = (float*)((uint8_t*)ws + w.p1);
+    const int kslabs1 = H * 2 / 128;
+    gemm1_dispatch<E>(plan.bm1, X, (int64_t)H * 2, Wa, T, kslabs1, plan.s1,
+                      EpiPartialF32{P1, T}, st);
+    hipLaunchKernelGGL(finish_a_fp_kernel<E>, dim3((unsigned)T), dim3(64), 0, st, P1, plan.s1, T,
+                       (const uint16_t*)gamma, pos, eps, theta, (uint16_t*)ckv, (uint16_t*)k_pe);
+    const int N2 = nh * kHeadW;
+    gemm2_dispatch<E>(plan.bm2, plan.bn2, ckv, (int64_t)kR * 2, Wb, T, N2,
+                      EpiKvFp<E>{(uint16_t*)k_nope, (uint16_t*)value, nh}, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_fp(int dt, const void* X, const void* Wa, const void* gamma, const void* Wb,
+                     const int32_t* pos, int64_t T, int H, int nh, float eps, float theta,
+                     void* k_nope, void* value, void* k_pe, void* ckv, void* ws,
+                     const Plan& plan, hipStream_t st) {
+    if (dt == kF16)
+        return launch_fp_t<kF16>(X, Wa, gamma, Wb, pos, T, H, nh, eps, theta, k_nope, value,
+                                 k_pe, ckv, ws, plan, st);
+    return launch_fp_t<kBF16>(X, Wa, gamma, Wb, pos, T, H, nh, eps, theta, k_nope, value, k_pe,
+                              ckv, ws, plan, st);
+}
+
+hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa, const void* gamma,
+                       const int8_t* Wqb, const float* swb, const int32_t* pos, int64_t T, int H,
+                       int nh, float eps, float theta, void* k_nope, void* value, void* k_pe,
+                       void* ckv, int32_t* dbg1, int32_t* dbg2, int64_t dbg_begin,
+                       int64_t dbg_rows, void* ws, const Plan& plan, hipStream_t st) {
+    const WsW8 w = ws_w8(T, H, plan);
+    uint8_t* base = (uint8_t*)ws;
+    int8_t* QX = (int8_t*)(base + w.qx);
+    float* sx = (float*)(base + w.sx);
+    int32_t* P1 = (int32_t*)(base + w.p1);
+    int8_t* QZ = (int8_t*)(base + w.qz);
+    float* sz = (float*)(base + w.sz);
+    float* inv = (float*)(base + w.inv);
+    hipLaunchKernelGGL(quant_rows_bf16_kernel, dim3((unsigned)T), dim3(256), 0, st,
+                       (const uint16_t*)X, H, QX, sx);
+    gemm1_dispatch<kI8>(plan.bm1, QX, (int64_t)H, Wqa, T, H / 128, plan.s1,
+                        EpiPartialI32{P1, T}, st);
+    hipLaunchKernelGGL(finish_a_w8_kernel, dim3((unsigned)T), dim3(64), 0, st, P1, plan.s1, T, sx,
+                       swa, (const uint16_t*)gamma, pos, eps, theta, QZ, sz, inv,
+                       (uint16_t*)ckv, (uint16_t*)k_pe, dbg1, dbg_begin, dbg_rows);
+    const int N2 = nh * kHeadW;
+    gemm2_dispatch<kI8>(plan.bm2, plan.bn2, QZ, (int64_t)kR, Wqb, T, N2,
+                        EpiKvW8{(uint16_t*)k_nope, (uint16_t*)value, nh, sz, inv, swb, dbg2,
+                                dbg_begin, dbg_rows},
+                        st);
+    return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,147 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every entry
+point the public header declares, and rejects bad arguments before anything
+reaches a GPU (no call here launches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_attention_kv_amd as mla
+from mla_attention_kv_amd import Dims
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libmlaprolog.h")
+
+V2 = Dims(H=2048, nh=16)
+R1 = Dims(H=7168, nh=128)
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_match_header():
+    L = mla.lib()
+    names = header_functions()
+    assert set(names) == set(mla.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        s = mla.mla_status_string(code)
+        assert s.startswith("MLA_")
+    assert "unknown" in mla.mla_status_string(42)
+
+
+def test_workspace_sizes():
+    assert mla.mla_kv_prolog_workspace_size(0, V2) == 0
+    assert mla.mla_kv_prolog_workspace_size(-1, V2) == 0
+    assert mla.mla_kv_prolog_workspace_size(1 << 23, V2) == 0
+    assert mla.mla_kv_prolog_workspace_size(64, V2, 7) == 0  # bad dtype
+    prev = 0
+    for T in (1, 16, 64, 65, 1000, 4096, 20000):
+        b = mla.mla_kv_prolog_workspace_size(T, V2)
+        assert b > 0 and b % 256 == 0
+        assert mla.mla_kv_prolog_w8a8_workspace_size(T, R1) > 0
+        prev = b
+    assert prev > 0
+    assert mla.mla_kv_prolog_workspace_size(64, Dims(H=2048, nh=16, r=256)) == 0
+    assert mla.mla_kv_prolog_w8a8_workspace_size(4, Dims(H=64, nh=1)) == 0  # H % 128
+
+
+def test_dispatcher_and_force_hook():
+    assert mla.mla_kv_prolog_selected_path(1, V2) == 0
+    assert mla.mla_kv_prolog_selected_path(64, V2) == 0
+    assert mla.mla_kv_prolog_selected_path(65, V2) == 1
+    assert mla.mla_kv_prolog_selected_path(4096, V2) == 1
+    try:
+        assert mla.mla_kv_prolog_force_path(1) == -1
+        assert mla.mla_kv_prolog_selected_path(1, V2) == 1
+        assert mla.mla_kv_prolog_force_path(0) == 1
+        assert mla.mla_kv_prolog_selected_path(4096, V2) == 0
+    finally:
+        mla.mla_kv_prolog_force_path(-1)
+    assert mla.mla_kv_prolog_selected_path(1, V2) == 0
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
+
+
+def call_fp(T=4, d=V2, dt=1, eps=1e-6, theta=1e4, ptrs=None, ws=FAKE, wsb=1 << 40):
+    p = [FAKE] * 9 if ptrs is None else ptrs
+    return mla.lib().mla_kv_prolog(p[0], p[1], p[2], p[3], p[4], T, d.c(), dt, eps, theta,
+                                   p[5], p[6], p[7], p[8], ws, wsb, None)
+
+
+@pytest.mark.parametrize("i", range(9))
+def test_null_pointer_rejected(i):
+    p = [FAKE] * 9
+    p[i] = None
+    assert call_fp(ptrs=p) == mla.MLA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("i", range(9))
+def test_misaligned_pointer_rejected(i):
+    p = [FAKE] * 9
+    p[i] = FAKE + 2
+    assert call_fp(ptrs=p) == mla.MLA_ERR_MISALIGNED
+
+
+def test_argument_errors():
+    assert call_fp(T=-1) == mla.MLA_ERR_INVALID_ARG
+    assert call_fp(T=(1 << 22) + 1) == mla.MLA_ERR_INVALID_ARG
+    assert call_fp(dt=3) == mla.MLA_ERR_INVALID_ARG
+    assert call_fp(eps=float("nan")) == mla.MLA_ERR_INVALID_ARG
+    assert call_fp(eps=-1.0) == mla.MLA_ERR_INVALID_ARG
+    assert call_fp(theta=0.0) == mla.MLA_ERR_INVALID_ARG
+    assert call_fp(theta=float("inf")) == mla.MLA_ERR_INVALID_ARG
+    for bad in (Dims(H=2048, nh=16, r=256), Dims(H=2048, nh=16, dr=32),
+                Dims(H=2048, nh=16, dn=64), Dims(H=2048, nh=16, dv=64),
+                Dims(H=2000, nh=16), Dims(H=0, nh=16), Dims(H=2048, nh=0),
+                Dims(H=2048, nh=2048), Dims(H=1 << 17, nh=1)):
+        assert call_fp(d=bad) == mla.MLA_ERR_UNSUPPORTED, bad
+    assert call_fp(ws=None) == mla.MLA_ERR_WORKSPACE
+    assert call_fp(ws=FAKE + 4) == mla.MLA_ERR_MISALIGNED
+    assert call_fp(wsb=0) == mla.MLA_ERR_WORKSPACE
+    need = mla.mla_kv_prolog_workspace_size(4, V2)
+    assert call_fp(wsb=need - 1) == mla.MLA_ERR_WORKSPACE
+
+
+def test_zero_tokens_ok_without_pointers():
+    assert call_fp(T=0, ptrs=[None] * 9, ws=None, wsb=0) == mla.MLA_OK
+    # unsupported dims are still reported at T == 0
+    assert call_fp(T=0, d=Dims(H=100, nh=1)) == mla.MLA_ERR_UNSUPPORTED
+
+
+def call_w8(T=4, d=R1, ptrs=None, dbg=(None, None, 0, 0), ws=FAKE, wsb=1 << 40):
+    p = [FAKE] * 11 if ptrs is None else ptrs
+    return mla.lib().mla_kv_prolog_w8a8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], T, d.c(),
+                                        1e-6, 1e4, p[7], p[8], p[9], p[10], dbg[0], dbg[1],
+                                        dbg[2], dbg[3], ws, wsb, None)
+
+
+def test_w8a8_argument_errors():
+    for i in range(11):
+        p = [FAKE] * 11
+        p[i] = None
+        assert call_w8(ptrs=p) == mla.MLA_ERR_INVALID_ARG
+        p[i] = FAKE + 8
+        assert call_w8(ptrs=p) == mla.MLA_ERR_MISALIGNED
+    assert call_w8(d=Dims(H=64, nh=1)) == mla.MLA_ERR_UNSUPPORTED
+    assert call_w8(dbg=(FAKE, None, 2, 3)) == mla.MLA_ERR_INVALID_ARG   # rows past T
+    assert call_w8(dbg=(FAKE, None, -1, 1)) == mla.MLA_ERR_INVALID_ARG
+    assert call_w8(dbg=(None, FAKE + 4, 0, 1)) == mla.MLA_ERR_MISALIGNED
+    assert call_w8(wsb=16) == mla.MLA_ERR_WORKSPACE
+    assert call_w8(T=0, ptrs=[None] * 11, ws=None, wsb=0) == mla.MLA_OK
+
+
+def test_python_binding_checks_tensors():
+    torch = pytest.importorskip("torch")
+    X = torch.zeros(2, 64, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        mla.mla_kv_prolog(X, X, X, X, X)

@@ -1,0 +1,190 @@
+"""GPU parity: the HIP library against the CPU oracle, element by element.
+
+Every case is a seeded synthetic workload from ``workloads``.  Small cases
+compare every output row; the full-size workloads compare a sample of token
+rows (every output row depends only on its own token, so the oracle can
+compute sampled rows one by one) on outputs produced by a full-size launch.
+The W8A8 int32 accumulators are compared bit for bit.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from workloads import V2LITE, R1, Dims
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mla_attention_kv_amd as mla
+
+    mla.lib()
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(autouse=True)
+def _reset_path():
+    yield
+    try:
+        import mla_attention_kv_amd as mla
+
+        mla.mla_kv_prolog_force_path(-1)
+    except Exception:
+        pass
+
+
+from parity import compare, gpu_rows, run_lib, run_oracle, sample_rows, upload  # noqa: E402
+
+
+def check_full(w, dev, label, path=None, dbg=False):
+    import mla_attention_kv_amd as mla
+
+    if path is not None:
+        mla.mla_kv_prolog_force_path(path)
+    print(f"[parity] {label} T={w.T} path={path}", flush=True)
+    t = upload(w, dev)
+    outs, accs = run_lib(w, t, dbg_rows=(0, w.T) if dbg else None)
+    torch.cuda.synchronize()
+    ref = run_oracle(w)
+    stats = compare(gpu_rows(outs), ref, label)
+    if dbg:
+        np.testing.assert_array_equal(accs[0].cpu().numpy(), ref["acc1"])
+        np.testing.assert_array_equal(accs[1].cpu().numpy(), ref["acc2"])
+    return stats, outs
+
+
+# ---------------------------------------------------------------------------
+# the five benchmark workloads at full size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_config_decode_full(dev, idx):
+    w = workloads.make_config(idx)
+    check_full(w, dev, f"config{idx}")
+
+
+@pytest.mark.parametrize("idx,nsample", [(2, 40), (3, 24)])
+def test_config_large_sampled(dev, idx, nsample):
+    w = workloads.make_config(idx)
+    print(f"[parity] config{idx} T={w.T} sampled {nsample}", flush=True)
+    t = upload(w, dev)
+    outs, _ = run_lib(w, t)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.T, nsample, seed=idx)
+    compare(gpu_rows(outs, rows), run_oracle(w, rows), f"config{idx}")
+
+
+def test_config4_w8a8_sampled_and_exact_accumulators(dev):
+    w = workloads.make_config(4)
+    # debug rows straddle the first sequence boundary
+    L0 = int(w.seq_lens[0])
+    b, n = L0 - 3, 6
+    print(f"[parity] config4 T={w.T} lens={list(w.seq_lens)} dbg rows {b}..{b + n}", flush=True)
+    t = upload(w, dev)
+    outs, (d1, d2) = run_lib(w, t, dbg_rows=(b, n))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([sample_rows(w.T, 20, seed=4), np.arange(b, b + n)]))
+    ref = run_oracle(w, rows)
+    compare(gpu_rows(outs, rows), ref, "config4")
+    sel = np.searchsorted(rows, np.arange(b, b + n))
+    np.testing.assert_array_equal(d1.cpu().numpy(), ref["acc1"][sel])
+    np.testing.assert_array_equal(d2.cpu().numpy(), ref["acc2"][sel])
+
+
+# ---------------------------------------------------------------------------
+# ragged token counts, both kernel families
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("path", [0, 1])
+@pytest.mark.parametrize("T", [1, 2, 3, 15, 16, 17, 33, 63, 64, 65, 127, 129])
+def test_v2lite_fp16_token_counts(dev, T, path):
+    w = workloads.make_custom(V2LITE, T, dtype="f16", seed=100 + T)
+    check_full(w, dev, f"v2lite_f16_T{T}", path=path)
+
+
+@pytest.mark.parametrize("path", [0, 1])
+@pytest.mark.parametrize("T", [1, 7, 64, 130])
+def test_bf16_token_counts(dev, T, path):
+    d = Dims(H=1024, nh=8)
+    w = workloads.make_custom(d, T, dtype="bf16", seed=200 + T, wstd=0.03)
+    check_full(w, dev, f"bf16_T{T}", path=path)
+
+
+@pytest.mark.parametrize("path", [0, 1])
+@pytest.mark.parametrize("T", [1, 5, 64, 131])
+def test_w8a8_token_counts_exact(dev, T, path):
+    d = Dims(H=1024, nh=4)
+    w = workloads.make_custom(d, T, kind="w8a8", dtype="bf16", seed=300 + T, wstd=0.02)
+    check_full(w, dev, f"w8a8_T{T}", path=path, dbg=True)
+
+
+# ---------------------------------------------------------------------------
+# edge shapes
+# ---------------------------------------------------------------------------
+
+def test_minimal_hidden_single_head(dev):
+    d = Dims(H=64, nh=1)
+    w = workloads.make_custom(d, 5, dtype="f16", seed=400, wstd=0.1)
+    check_full(w, dev, "H64_nh1")
+
+
+def test_r1_shapes_small_T(dev):
+    w = workloads.make_custom(R1, 3, dtype="bf16", seed=401, wstd=0.01, max_pos=32768)
+    check_full(w, dev, "r1_T3")
+
+
+def test_large_positions(dev):
+    T = 32
+    pos = np.array([0, 1, 2, 4095, 32767, 65535, 1 << 20, (1 << 31) - 1] * 4, np.int32)
+    w = workloads.make_custom(V2LITE, T, dtype="f16", seed=402, positions=pos)
+    check_full(w, dev, "large_positions")
+
+
+def test_zero_tokens_is_noop(dev):
+    import mla_attention_kv_amd as mla
+
+    w = workloads.make_custom(V2LITE, 1, dtype="f16", seed=403)
+    t = upload(w, dev)
+    X0 = t["X"][:0]
+    outs = mla.mla_kv_prolog(X0, t["Wa"], t["gamma"], t["Wb"], t["pos"][:0])
+    assert all(o.shape[0] == 0 for o in outs)
+
+
+def test_zero_row_w8a8(dev):
+    """A token whose hidden row is all zeros: codes 0, scale 0, outputs 0."""
+    d = Dims(H=256, nh=2)
+    w = workloads.make_custom(d, 4, kind="w8a8", dtype="bf16", seed=404)
+    w.X[2, :] = 0
+    check_full(w, dev, "w8a8_zero_row", dbg=True)
+
+
+def test_deterministic(dev):
+    w = workloads.make_config(1)
+    t = upload(w, dev)
+    a, _ = run_lib(w, t)
+    b, _ = run_lib(w, t)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_nondefault_stream_and_reused_workspace(dev):
+    import mla_attention_kv_amd as mla
+
+    w = workloads.make_config(1)
+    t = upload(w, dev)
+    ws = torch.empty(mla.mla_kv_prolog_workspace_size(w.T, mla.Dims(H=2048, nh=16)),
+                     dtype=torch.uint8, device=dev)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        outs1 = mla.mla_kv_prolog(t["X"], t["Wa"], t["gamma"], t["Wb"], t["pos"], workspace=ws)
+        outs2 = mla.mla_kv_prolog(t["X"], t["Wa"], t["gamma"], t["Wb"], t["pos"], workspace=ws)
+    s.synchronize()
+    for x, y in zip(outs1, outs2):
+        assert torch.equal(x, y)
+    compare(gpu_rows(outs2), run_oracle(w), "stream")
