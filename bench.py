@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Benchmark of the MLA KV prolog on one MI355X.
+
+One step = one call of the whole prolog (kv_a_proj, split, RMSNorm,
+kv_b_proj, reshape/split, RoPE, assemble) over one batch of seeded synthetic
+input.  Default workload: DeepSeek-V2-Lite shapes, fp16 decode of 32
+sequences x 2 query tokens (T = 64).
+
+Timing: inputs, weights, outputs and workspace are replicated over enough
+distinct buffers (>= 512 MB in total) that the 256 MB last-level cache
+cannot serve a repeated call; successive steps rotate through them.  The K
+timed steps are launched as HIP graph replays (launch overhead removed, as
+a serving loop would) on one stream and bracketed by synchronisation and
+HIP events on that stream.  value = T * K / elapsed (tokens/s).
+
+Prints ONE JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "i8": 5000.0}
+ROTATE_BYTES = 512e6
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "mla_attention_kv_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None
+    when they are absent or were taken on different kernel sources."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("src_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+class Sets:
+    """n_sets device copies of one workload's tensors plus output buffers and
+    workspace, with ready-made C argument tuples."""
+
+    def __init__(self, w, n_sets, dev):
+        import torch
+
+        import mla_attention_kv_amd as mla
+        from tests.parity import upload
+
+        self.mla = mla
+        self.w = w
+        d = w.dims
+        self.dims = mla.Dims(H=d.H, nh=d.nh, r=d.r, dr=d.dr, dn=d.dn, dv=d.dv)
+        base = upload(w, dev)
+        odt = torch.float16 if w.dtype == "f16" else torch.bfloat16
+        if w.kind == "fp":
+            code = mla.MLA_F16 if w.dtype == "f16" else mla.MLA_BF16
+            nbytes = mla.mla_kv_prolog_workspace_size(w.T, self.dims, code)
+        else:
+            code = None
+            nbytes = mla.mla_kv_prolog_w8a8_workspace_size(w.T, self.dims)
+        self.keep = []
+        self.args = []
+        for i in range(n_sets):
+            t = {k: v.clone() for k, v in base.items()}
+            outs = (torch.empty((w.T, d.nh, d.dn), dtype=odt, device=dev),
+                    torch.empty((w.T, d.nh, d.dv), dtype=odt, device=dev),
+                    torch.empty((w.T, d.dr), dtype=odt, device=dev),
+                    torch.empty((w.T, d.r), dtype=odt, device=dev))
+            ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+            self.keep.append((t, outs, ws))
+            if w.kind == "fp":
+                a = (t["X"].data_ptr(), t["Wa"].data_ptr(), t["gamma"].data_ptr(),
+                     t["Wb"].data_ptr(), t["pos"].data_ptr(), w.T, self.dims.c(), code,
+                     w.eps, w.theta, outs[0].data_ptr(), outs[1].data_ptr(),
+                     outs[2].data_ptr(), outs[3].data_ptr(), ws.data_ptr(), ws.numel())
+            else:
+                a = (t["X"].data_ptr(), t["Wqa"].data_ptr(), t["swa"].data_ptr(),
+                     t["gamma"].data_ptr(), t["Wqb"].data_ptr(), t["swb"].data_ptr(),
+                     t["pos"].data_ptr(), w.T, self.dims.c(), w.eps, w.theta,
+                     outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
+                     outs[3].data_ptr(), None, None, 0, 0, ws.data_ptr(), ws.numel())
+            self.args.append(a)
+        self.fn = mla.lib().mla_kv_prolog if w.kind == "fp" else mla.lib().mla_kv_prolog_w8a8
+
+    def call(self, i, stream_ptr):
+        st = self.fn(*self.args[i % len(self.args)], ctypes.c_void_p(stream_ptr))
+        if st != 0:
+            raise RuntimeError(f"library call failed: {self.mla.mla_status_string(st)}")
+
+
+def time_graph(sets, steps, warmup, dev):
+    """Capture one rotation cycle (and the remainder) as HIP graphs, replay
+    so that exactly `steps` calls run; return elapsed ms (events)."""
+    import torch
+
+    n = len(sets.args)
+    cap = torch.cuda.Stream(device=dev)
+    graphs = {}
+
+    def make(count):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            sp = torch.cuda.current_stream(dev).cuda_stream
+            for i in range(count):
+                sets.call(i, sp)
+        return g
+
+    full = make(n)
+    rem = steps % n
+    part = make(rem) if rem else None
+    torch.cuda.synchronize()
+    wfull = max(1, math.ceil(warmup / n)) if warmup > 0 else 0
+    for _ in range(wfull):
+        full.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps // n):
+        full.replay()
+    if part is not None:
+        part.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del graphs
+    return e0.elapsed_time(e1)
+
+
+def time_eager(sets, steps, warmup, dev):
+    import torch
+
+    sp = torch.cuda.current_stream(dev).cuda_stream
+    for i in range(warmup):
+        sets.call(i, sp)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        sets.call(i, sp)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def cpu_baseline(w, seconds):
+    """The CPU oracle, as it stands, on a bounded sample of the same
+    workload: whole batches (or a prefix of token rows) repeated until about
+    `seconds` have elapsed."""
+    import numpy as np
+
+    import oracle
+    from tests.parity import run_oracle
+
+    nthreads = oracle.num_threads(0)
+    rows = None
+    if w.T > 256:
+        rows = np.arange(256)
+    ntok = w.T if rows is None else len(rows)
+    t0 = time.perf_counter()
+    run_oracle(w, rows)
+    one = time.perf_counter() - t0
+    reps = max(1, min(200, int(seconds / max(one, 1e-6))))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        run_oracle(w, rows)
+    dt = time.perf_counter() - t0
+    sample = (f"{reps} x {'all ' if rows is None else 'the first '}{ntok} token rows of the "
+              f"same seeded workload ({dt:.1f} s)")
+    return {"value": ntok * reps / dt, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": sample}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=7000)
+    ap.add_argument("--warmup", type=int, default=700)
+    ap.add_argument("--config", type=int, default=1, help="workload index (default 1)")
+    ap.add_argument("--eager", action="store_true", help="time direct calls, not graph replays")
+    ap.add_argument("--path", type=int, default=-1, help="force kernel family 0/1 (A/B runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: the KV prolog needs no communication and "
+              f"this build runs on a single MI355X (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mla_attention_kv_amd as mla
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mla.lib()
+    if args.path in (0, 1):
+        mla.mla_kv_prolog_force_path(args.path)
+
+    cfg = workloads.CONFIGS[args.config]
+    log(f"generating workload {cfg['name']}")
+    w = workloads.make_config(args.config)
+    d = w.dims
+    alg_bytes = workloads.algorithmic_bytes(d, w.T, w.kind, w.dtype)
+    alg_flops = workloads.algorithmic_flops(d, w.T)
+    n_sets = max(1, math.ceil(ROTATE_BYTES / alg_bytes))
+    log(f"T={w.T} algorithmic bytes/step={alg_bytes} flops/step={alg_flops} sets={n_sets}")
+    sets = Sets(w, n_sets, dev)
+    torch.cuda.synchronize()
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    steps, warmup = args.steps, args.warmup
+    if args.eager:
+        ms = time_eager(sets, steps, warmup, dev)
+        eager_ms = ms
+    else:
+        ms = time_graph(sets, steps, warmup, dev)
+        eager_ms = time_eager(sets, min(steps, 2000), min(warmup, 200), dev) * steps / min(steps, 2000)
+    ms_per_step = ms / steps
+    value = w.T * steps / (ms / 1e3)
+    log(f"{ms_per_step * 1e3:.2f} us/step, {value:.4g} tokens/s "
+        f"(eager {eager_ms / steps * 1e3:.2f} us/step)")
+
+    path = mla.mla_kv_prolog_selected_path(w.T, sets.dims)
+    step_s = ms_per_step / 1e3
+    if path == 0 or w.kind == "fp" and alg_flops / alg_bytes < 312:
+        roof = {"bound": "hbm", "achieved": alg_bytes / step_s / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    else:
+        dt = "i8" if w.kind == "w8a8" else w.dtype
+        roof = {"bound": "mfma", "achieved": alg_flops / step_s / 1e12,
+                "peak": MFMA_PEAK_TFLOPS[dt], "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = load_traffic(cfg["name"])
+    roof["kernel"] = "whole prolog step (all launches of one call)"
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        log(f"oracle: {cpu['value']:.4g} tokens/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": "MLA KV prolog tokens/s + % HBM (decode) / % MFMA (prefill) roofline",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"fp": w.dtype, "w8a8": "i8"}[w.kind],
+        "data": "synthetic (seeded; no public dataset exists for this path)",
+        "config": {"workload": cfg["name"], "T": w.T, "H": d.H, "kv_lora_rank": d.r,
+                   "rope_dim": d.dr, "heads": d.nh, "dn": d.dn, "dv": d.dv,
+                   "kernel_family": ["decode", "prefill"][path],
+                   "timing": "eager calls" if args.eager else "HIP graph replays",
+                   "rotated_sets": n_sets, "eager_us_per_step": eager_ms / steps * 1e3,
+                   "algorithmic_bytes_per_step": alg_bytes,
+                   "algorithmic_flops_per_step": alg_flops},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -33,6 +33,21 @@ int kslabs_a(int H, bool int8) { return int8 ? H / 128 : H * 2 / 128; }
 Plan make_plan(int64_t T, int H, bool int8, int path) {
     Plan p;
     p.path = path;
+    p.stream = (!int8 && path == 0 && T <= kDecodeMaxT) ? 1 : 0;
+    p.kw = 0;
+    if (p.stream) {
+        // weight-streaming kv_a_proj: 9 slabs x S splits of kw rows each;
+        // wider splits when the split-K partials (S * T rows of 576 floats)
+        // would grow large
+        const int64_t tt = T < 16 ? 16 : T;
+        int kw = H <= 64 ? 64 : 128;
+        while (kw < 512 && ((H + kw - 1) / kw) * tt > 1024) kw *= 2;
+        p.kw = kw;
+        p.s1 = (H + kw - 1) / kw;
+        p.bm1 = p.bm2 = 16;
+        p.bn2 = 64;
+        return p;
+    }
     const int ks = kslabs_a(H, int8);
     if (path == 0) {
         p.bm1 = T <= 16 ? 16 : (T <= 32 ? 32 : 64);
@@ -54,6 +69,13 @@ Plan make_plan(int64_t T, int H, bool int8, int path) {
     const int per = (int)((ks + s - 1) / s);
     p.s1 = (ks + per - 1) / per;
     return p;
+}
+
+RopeTab rope_table(float theta) {
+    RopeTab rt;
+    for (int i = 0; i < kDR / 2; ++i)
+        rt.f[i] = std::pow((double)theta, -2.0 * (double)i / (double)kDR);
+    return rt;
 }
 
 bool dims_supported(const mla_dims_t& d) {
@@ -136,8 +158,8 @@ mla_status_t mla_kv_prolog(const void* hidden, const void* W_kv_a, const void* g
     const Plan plan = make_plan(T, d.H, false, select_path(T));
     if (workspace_bytes < ws_fp(T, plan).total) return MLA_ERR_WORKSPACE;
     hipError_t e = launch_fp((int)dt, hidden, W_kv_a, gamma, W_kv_b, positions, T, d.H, d.nh,
-                             eps, theta, k_nope, value, k_pe, compressed_kv, workspace, plan,
-                             (hipStream_t)stream);
+                             eps, rope_table(theta), k_nope, value, k_pe, compressed_kv,
+                             workspace, plan, (hipStream_t)stream);
     return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -174,7 +196,7 @@ mla_status_t mla_kv_prolog_w8a8(const void* hidden_bf16, const int8_t* Wq_kv_a,
     const Plan plan = make_plan(T, d.H, true, select_path(T));
     if (workspace_bytes < ws_w8(T, d.H, plan).total) return MLA_ERR_WORKSPACE;
     hipError_t e = launch_w8a8(hidden_bf16, Wq_kv_a, s_kv_a, gamma_bf16, Wq_kv_b, s_kv_b,
-                               positions, T, d.H, d.nh, eps, theta, k_nope, value, k_pe,
+                               positions, T, d.H, d.nh, eps, rope_table(theta), k_nope, value, k_pe,
                                compressed_kv, dbg_acc1, dbg_acc2, dbg_row_begin, dbg_rows,
                                workspace, plan, (hipStream_t)stream);
     return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;

@@ -75,12 +75,38 @@ __device__ __forceinline__ float wave_max(float v) {
 // launch plan and workspace layout (host)
 // ---------------------------------------------------------------------------
 struct Plan {
-    int path;       // 0 decode, 1 prefill
-    int bm1, s1;    // kv_a_proj: rows per tile, split-K count (BN = 64)
-    int bm2, bn2;   // kv_b_proj tile
+    int path;       // 0 decode, 1 prefill (what mla_kv_prolog_selected_path reports)
+    int stream;     // 1: weight-streaming decode kernels, 0: tiled MFMA kernels
+    int bm1, s1;    // kv_a_proj: rows per tile (tiled), split-K count
+    int kw;         // streaming kv_a_proj: K rows per producer workgroup
+    int bm2, bn2;   // kv_b_proj tile (tiled)
 };
 
+// RoPE inverse frequencies theta^(-2i/dr), i < dr/2, evaluated once per call
+// on the host in double (they depend on theta only).
+struct RopeTab {
+    double f[kDR / 2];
+};
+
+// cos / sin of the rope angle pos * f: the angle is formed and reduced modulo
+// 2 pi in double (Cody-Waite, 2 pi split into two doubles), then the reduced
+// angle (|r| <= pi) goes through fp32 sincos.
+__device__ __forceinline__ void rope_cos_sin(int32_t pos, double f, float& cs, float& sn) {
+    const double a = (double)pos * f;
+    const double k = rint(a * 0.15915494309189535);
+    double r = fma(-k, 6.283185307179586, a);
+    r = fma(-k, 2.4492935982947064e-16, r);
+    sincosf((float)r, &sn, &cs);
+}
+
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Every workspace layout starts with 4 KiB of grid-synchronisation words
+// (zero between calls; the decode kernel resets them before it exits).
+constexpr size_t kSyncBytes = 4096;
+// most consumer workgroups of the fused decode kernel (each loops over its
+// (token tile, W_kv_b slab) items); a multiple of 8
+constexpr int kDecodeConsumers = 1024;
 
 // fp path: [s1][T][576] fp32 split-K partial sums of kv_a_proj
 struct WsFp {
@@ -88,8 +114,8 @@ struct WsFp {
 };
 inline WsFp ws_fp(int64_t T, const Plan& p) {
     WsFp w;
-    w.p1 = 0;
-    w.total = align256((size_t)p.s1 * (size_t)T * kN1 * 4);
+    w.p1 = kSyncBytes;
+    w.total = kSyncBytes + align256((size_t)p.s1 * (size_t)T * kN1 * 4);
     return w;
 }
 
@@ -100,7 +126,7 @@ struct WsW8 {
 };
 inline WsW8 ws_w8(int64_t T, int H, const Plan& p) {
     WsW8 w;
-    size_t o = 0;
+    size_t o = kSyncBytes;
     w.qx = o; o += align256((size_t)T * H);
     w.sx = o; o += align256((size_t)T * 4);
     w.p1 = o; o += align256((size_t)p.s1 * (size_t)T * kN1 * 4);
@@ -117,13 +143,23 @@ inline WsW8 ws_w8(int64_t T, int H, const Plan& p) {
 
 hipError_t launch_fp(int dt, const void* X, const void* Wa, const void* gamma,
                      const void* Wb, const int32_t* pos, int64_t T, int H, int nh,
-                     float eps, float theta, void* k_nope, void* value, void* k_pe,
+                     float eps, const RopeTab& rt, void* k_nope, void* value, void* k_pe,
                      void* ckv, void* ws, const Plan& plan, hipStream_t st);
+
+hipError_t launch_fp_decode(int dt, const void* X, const void* Wa, const void* gamma,
+                            const void* Wb, const int32_t* pos, int64_t T, int H, int nh,
+                            float eps, const RopeTab& rt, void* k_nope, void* value,
+                            void* k_pe, void* ckv, void* ws, const Plan& plan, hipStream_t st);
+
+// per-token finish of kv_a_proj (split, RMSNorm, RoPE) from split-K partials
+void launch_finish_fp(int dt, const float* P, int S, int64_t T, const void* gamma,
+                      const int32_t* pos, float eps, const RopeTab& rt, void* ckv, void* kpe,
+                      hipStream_t st);
 
 hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa,
                        const void* gamma, const int8_t* Wqb, const float* swb,
                        const int32_t* pos, int64_t T, int H, int nh, float eps,
-                       float theta, void* k_nope, void* value, void* k_pe, void* ckv,
+                       const RopeTab& rt, void* k_nope, void* value, void* k_pe, void* ckv,
                        int32_t* dbg1, int32_t* dbg2, int64_t dbg_begin, int64_t dbg_rows,
                        void* ws, const Plan& plan, hipStream_t st);
 

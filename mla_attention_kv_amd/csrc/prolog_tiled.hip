@@ -242,13 +242,13 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
 //   c, p  = sum of the split-K partials (split order ascending)
 //   y     = c / sqrt(sum(c^2)/512 + eps) * gamma      -> compressed_kv
 //   k_pe  = rotate-half RoPE of p at the token's position
-// The rope angle pos * theta^(-2i/64) and its sine / cosine are evaluated in
-// double, then rounded to fp32 for the rotation.
+// The rope angle pos * theta^(-2i/64) is formed and reduced modulo 2 pi in
+// double; sine / cosine of the reduced angle and the rotation run in fp32.
 // ---------------------------------------------------------------------------
 template <int E>
 __global__ __launch_bounds__(64) void finish_a_fp_kernel(
     const float* __restrict__ P, int S, int64_t T, const uint16_t* __restrict__ gamma,
-    const int32_t* __restrict__ pos, float eps, float theta, uint16_t* __restrict__ ckv,
+    const int32_t* __restrict__ pos, float eps, RopeTab rt, uint16_t* __restrict__ ckv,
     uint16_t* __restrict__ kpe) {
     const int64_t t = blockIdx.x;
     const int lane = threadIdx.x;
@@ -283,10 +283,8 @@ __global__ __launch_bounds__(64) void finish_a_fp_kernel(
     *(u4_t*)(ckv + t * kR + 8 * lane) = o;
 
     const float partner = __shfl_xor(p, 32, 64);
-    const int i = lane & 31;
-    const double f = pow((double)theta, -2.0 * (double)i / (double)kDR);
-    const double ang = (double)pos[t] * f;
-    const float cs = (float)cos(ang), sn = (float)sin(ang);
+    float cs, sn;
+    rope_cos_sin(pos[t], rt.f[lane & 31], cs, sn);
     const float out = (lane < 32) ? (p * cs - partner * sn) : (p * cs + partner * sn);
     kpe[t * kDR + lane] = f32_to_st<E>(out);
 }
@@ -349,7 +347,7 @@ __global__ __launch_bounds__(256) void quant_rows_bf16_kernel(const uint16_t* __
 __global__ __launch_bounds__(64) void finish_a_w8_kernel(
     const int32_t* __restrict__ P, int S, int64_t T, const float* __restrict__ sx,
     const float* __restrict__ swa, const uint16_t* __restrict__ gamma,
-    const int32_t* __restrict__ pos, float eps, float theta, int8_t* __restrict__ QZ,
+    const int32_t* __restrict__ pos, float eps, RopeTab rt, int8_t* __restrict__ QZ,
     float* __restrict__ sz, float* __restrict__ inv_out, uint16_t* __restrict__ ckv,
     uint16_t* __restrict__ kpe, int32_t* __restrict__ dbg, int64_t dbg_begin, int64_t dbg_rows) {
     const int64_t t = blockIdx.x;
@@ -413,10 +411,8 @@ __global__ __launch_bounds__(64) void finish_a_w8_kernel(
         inv_out[t] = inv_t;
     }
     const float partner = __shfl_xor(p, 32, 64);
-    const int i = lane & 31;
-    const double f = pow((double)theta, -2.0 * (double)i / (double)kDR);
-    const double ang = (double)pos[t] * f;
-    const float cs = (float)cos(ang), sn = (float)sin(ang);
+    float cs, sn;
+    rope_cos_sin(pos[t], rt.f[lane & 31], cs, sn);
     const float out = (lane < 32) ? (p * cs - partner * sn) : (p * cs + partner * sn);
     kpe[t * kDR + lane] = f32_to_bf16(out);
 }
@@ -464,18 +460,29 @@ static void gemm2_dispatch(int bm, int bn, const void* A, int64_t lda, const voi
     }
 }
 
+void launch_finish_fp(int dt, const float* P, int S, int64_t T, const void* gamma,
+                      const int32_t* pos, float eps, const RopeTab& rt, void* ckv, void* kpe,
+                      hipStream_t st) {
+    if (dt == kF16)
+        hipLaunchKernelGGL(finish_a_fp_kernel<kF16>, dim3((unsigned)T), dim3(64), 0, st, P, S, T,
+                           (const uint16_t*)gamma, pos, eps, rt, (uint16_t*)ckv, (uint16_t*)kpe);
+    else
+        hipLaunchKernelGGL(finish_a_fp_kernel<kBF16>, dim3((unsigned)T), dim3(64), 0, st, P, S,
+                           T, (const uint16_t*)gamma, pos, eps, rt, (uint16_t*)ckv,
+                           (uint16_t*)kpe);
+}
+
 template <int E>
 static hipError_t launch_fp_t(const void* X, const void* Wa, const void* gamma, const void* Wb,
                               const int32_t* pos, int64_t T, int H, int nh, float eps,
-                              float theta, void* k_nope, void* value, void* k_pe, void* ckv,
+                              const RopeTab& rt, void* k_nope, void* value, void* k_pe, void* ckv,
                               void* ws, const Plan& plan, hipStream_t st) {
     const WsFp w = ws_fp(T, plan);
     float* P1 = (float*)((uint8_t*)ws + w.p1);
     const int kslabs1 = H * 2 / 128;
     gemm1_dispatch<E>(plan.bm1, X, (int64_t)H * 2, Wa, T, kslabs1, plan.s1,
                       EpiPartialF32{P1, T}, st);
-    hipLaunchKernelGGL(finish_a_fp_kernel<E>, dim3((unsigned)T), dim3(64), 0, st, P1, plan.s1, T,
-                       (const uint16_t*)gamma, pos, eps, theta, (uint16_t*)ckv, (uint16_t*)k_pe);
+    launch_finish_fp(E, P1, plan.s1, T, gamma, pos, eps, rt, ckv, k_pe, st);
     const int N2 = nh * kHeadW;
     gemm2_dispatch<E>(plan.bm2, plan.bn2, ckv, (int64_t)kR * 2, Wb, T, N2,
                       EpiKvFp<E>{(uint16_t*)k_nope, (uint16_t*)value, nh}, st);
@@ -483,19 +490,22 @@ static hipError_t launch_fp_t(const void* X, const void* Wa, const void* gamma, 
 }
 
 hipError_t launch_fp(int dt, const void* X, const void* Wa, const void* gamma, const void* Wb,
-                     const int32_t* pos, int64_t T, int H, int nh, float eps, float theta,
+                     const int32_t* pos, int64_t T, int H, int nh, float eps, const RopeTab& rt,
                      void* k_nope, void* value, void* k_pe, void* ckv, void* ws,
                      const Plan& plan, hipStream_t st) {
+    if (plan.stream)
+        return launch_fp_decode(dt, X, Wa, gamma, Wb, pos, T, H, nh, eps, rt, k_nope, value,
+                                k_pe, ckv, ws, plan, st);
     if (dt == kF16)
-        return launch_fp_t<kF16>(X, Wa, gamma, Wb, pos, T, H, nh, eps, theta, k_nope, value,
+        return launch_fp_t<kF16>(X, Wa, gamma, Wb, pos, T, H, nh, eps, rt, k_nope, value,
                                  k_pe, ckv, ws, plan, st);
-    return launch_fp_t<kBF16>(X, Wa, gamma, Wb, pos, T, H, nh, eps, theta, k_nope, value, k_pe,
+    return launch_fp_t<kBF16>(X, Wa, gamma, Wb, pos, T, H, nh, eps, rt, k_nope, value, k_pe,
                               ckv, ws, plan, st);
 }
 
 hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa, const void* gamma,
                        const int8_t* Wqb, const float* swb, const int32_t* pos, int64_t T, int H,
-                       int nh, float eps, float theta, void* k_nope, void* value, void* k_pe,
+                       int nh, float eps, const RopeTab& rt, void* k_nope, void* value, void* k_pe,
                        void* ckv, int32_t* dbg1, int32_t* dbg2, int64_t dbg_begin,
                        int64_t dbg_rows, void* ws, const Plan& plan, hipStream_t st) {
     const WsW8 w = ws_w8(T, H, plan);
@@ -511,7 +521,7 @@ hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa, const
     gemm1_dispatch<kI8>(plan.bm1, QX, (int64_t)H, Wqa, T, H / 128, plan.s1,
                         EpiPartialI32{P1, T}, st);
     hipLaunchKernelGGL(finish_a_w8_kernel, dim3((unsigned)T), dim3(64), 0, st, P1, plan.s1, T, sx,
-                       swa, (const uint16_t*)gamma, pos, eps, theta, QZ, sz, inv,
+                       swa, (const uint16_t*)gamma, pos, eps, rt, QZ, sz, inv,
                        (uint16_t*)ckv, (uint16_t*)k_pe, dbg1, dbg_begin, dbg_rows);
     const int N2 = nh * kHeadW;
     gemm2_dispatch<kI8>(plan.bm2, plan.bn2, QZ, (int64_t)kR, Wqb, T, N2,

@@ -178,7 +178,7 @@ def test_nondefault_stream_and_reused_workspace(dev):
 
     w = workloads.make_config(1)
     t = upload(w, dev)
-    ws = torch.empty(mla.mla_kv_prolog_workspace_size(w.T, mla.Dims(H=2048, nh=16)),
+    ws = torch.zeros(mla.mla_kv_prolog_workspace_size(w.T, mla.Dims(H=2048, nh=16)),
                      dtype=torch.uint8, device=dev)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
@@ -188,3 +188,27 @@ def test_nondefault_stream_and_reused_workspace(dev):
     for x, y in zip(outs1, outs2):
         assert torch.equal(x, y)
     compare(gpu_rows(outs2), run_oracle(w), "stream")
+
+
+@pytest.mark.parametrize("T", [1, 64])
+def test_decode_many_calls_one_workspace(dev, T):
+    """The fused decode kernel's grid counters are reset by the kernel itself:
+    many back-to-back calls on one workspace (inputs changing between calls)
+    all give the oracle's result."""
+    import mla_attention_kv_amd as mla
+
+    ws = torch.zeros(mla.mla_kv_prolog_workspace_size(T, mla.Dims(H=2048, nh=16)),
+                     dtype=torch.uint8, device=dev)
+    cases = [workloads.make_custom(V2LITE, T, dtype="f16", seed=500 + T + i) for i in range(3)]
+    ups = [upload(w, dev) for w in cases]
+    refs = [run_oracle(w) for w in cases]
+    outs = None
+    for it in range(60):
+        i = it % 3
+        t = ups[i]
+        outs = mla.mla_kv_prolog(t["X"], t["Wa"], t["gamma"], t["Wb"], t["pos"], workspace=ws)
+        if it >= 57:
+            torch.cuda.synchronize()
+            compare(gpu_rows(outs), refs[i], f"repeat{it}")
+    torch.cuda.synchronize()
+    assert int(ws[:4096].view(torch.int32).abs().sum().item()) == 0  # sync words back at zero
