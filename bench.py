@@ -187,7 +187,7 @@ def cpu_baseline(w, seconds):
     t0 = time.perf_counter()
     run_oracle(w, rows)
     one = time.perf_counter() - t0
-    reps = max(1, min(200, int(seconds / max(one, 1e-6))))
+    reps = max(1, min(100000, int(seconds / max(one, 1e-6))))
     t0 = time.perf_counter()
     for _ in range(reps):
         run_oracle(w, rows)
@@ -272,7 +272,10 @@ def main():
                 "peak": MFMA_PEAK_TFLOPS[dt], "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = load_traffic(cfg["name"])
-    roof["kernel"] = "whole prolog step (all launches of one call)"
+    roof["kernel"] = ("one library call = every launch of the step: " +
+                      ("dec_kv_a + dec_finish + dec_kv_b" if (path == 0 and w.kind == "fp" and w.T <= 64)
+                       else "tiled kv_a_proj + finish + tiled kv_b_proj" +
+                       (" (+ activation quantiser)" if w.kind == "w8a8" else "")))
 
     cpu = None
     if not args.no_cpu_baseline:
