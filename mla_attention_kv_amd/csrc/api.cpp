@@ -55,7 +55,8 @@ Plan make_plan(int64_t T, int H, bool int8, int path) {
         p.bn2 = 64;
     } else {
         p.bm1 = 128;
-        p.bm2 = 128;
+        // kv_b_proj: 256 x 128 tiles once there are enough of them to fill the chip
+        p.bm2 = (!int8 && T >= 2048) ? 256 : 128;
         p.bn2 = 128;
     }
     // split kv_a_proj's K so that at least ~256 workgroups stream W_kv_a,

@@ -69,67 +69,118 @@ __device__ __forceinline__ void transpose16x16_b8(const u4_t in[16], u4_t out[16
 }
 
 // ---------------------------------------------------------------------------
-// Epilogues: called once per accumulator element.
+// Epilogues.  row_scale(row) / col_scale(col) are fetched once per row and
+// column a lane owns; value() turns one accumulator into the stored element.
+// The kernel gathers a whole output tile in LDS and then writes it with
+// 16-byte stores along rows, each to ptr(row, col) (col is a multiple of the
+// 16-byte chunk, and a tile never straddles a k_nope / value boundary).
 // ---------------------------------------------------------------------------
+struct NoScale {};
 struct EpiPartialF32 {  // kv_a_proj split-K partial, fp32 [s][T][576]
+    typedef float out_t;
+    typedef NoScale row_t;
     float* out;
     int64_t T;
-    __device__ __forceinline__ void operator()(int row, int col, int s, float v) const {
-        out[((int64_t)s * T + row) * kN1 + col] = v;
+    __device__ __forceinline__ row_t row_scale(int) const { return {}; }
+    __device__ __forceinline__ float col_scale(int) const { return 1.f; }
+    __device__ __forceinline__ float value(int, int, float v, row_t, float) const { return v; }
+    __device__ __forceinline__ void* ptr(int row, int col, int s) const {
+        return out + ((int64_t)s * T + row) * kN1 + col;
     }
 };
 struct EpiPartialI32 {  // kv_a_proj split-K partial, int32 [s][T][576]
+    typedef int32_t out_t;
+    typedef NoScale row_t;
     int32_t* out;
     int64_t T;
-    __device__ __forceinline__ void operator()(int row, int col, int s, int v) const {
-        out[((int64_t)s * T + row) * kN1 + col] = v;
+    __device__ __forceinline__ row_t row_scale(int) const { return {}; }
+    __device__ __forceinline__ float col_scale(int) const { return 1.f; }
+    __device__ __forceinline__ int32_t value(int, int, int v, row_t, float) const { return v; }
+    __device__ __forceinline__ void* ptr(int row, int col, int s) const {
+        return out + ((int64_t)s * T + row) * kN1 + col;
     }
 };
 // kv_b_proj result column `col` = head col/256, slot col%256: slots [0,128)
 // are k_nope, [128,256) are value.
+__device__ __forceinline__ uint16_t* kv_dst(uint16_t* k_nope, uint16_t* value, int nh, int row,
+                                            int col) {
+    const int h = col >> 8, sl = col & 255;
+    return ((sl < kDN) ? k_nope : value) + ((int64_t)row * nh + h) * kDN + (sl & 127);
+}
 template <int E>
 struct EpiKvFp {
+    typedef uint16_t out_t;
+    typedef NoScale row_t;
     uint16_t* k_nope;
-    uint16_t* value;
+    uint16_t* value_out;
     int nh;
-    __device__ __forceinline__ void operator()(int row, int col, int, float v) const {
-        const int h = col >> 8, s = col & 255;
-        uint16_t* dst = (s < kDN) ? k_nope : value;
-        dst[((int64_t)row * nh + h) * kDN + (s & 127)] = f32_to_st<E>(v);
+    __device__ __forceinline__ row_t row_scale(int) const { return {}; }
+    __device__ __forceinline__ float col_scale(int) const { return 1.f; }
+    __device__ __forceinline__ uint16_t value(int, int, float v, row_t, float) const {
+        return f32_to_st<E>(v);
+    }
+    __device__ __forceinline__ void* ptr(int row, int col, int) const {
+        return kv_dst(k_nope, value_out, nh, row, col);
     }
 };
 struct EpiKvW8 {
+    typedef uint16_t out_t;
+    struct row_t {
+        float sz, inv;
+    };
     uint16_t* k_nope;
-    uint16_t* value;
+    uint16_t* value_out;
     int nh;
     const float* sz;
     const float* inv_t;
     const float* swb;
     int32_t* dbg;
     int64_t dbg_begin, dbg_rows;
-    __device__ __forceinline__ void operator()(int row, int col, int, int acc) const {
-        float v = (((float)acc * sz[row]) * inv_t[row]) * swb[col];
-        const int h = col >> 8, s = col & 255;
-        uint16_t* dst = (s < kDN) ? k_nope : value;
-        dst[((int64_t)row * nh + h) * kDN + (s & 127)] = f32_to_bf16(v);
+    __device__ __forceinline__ row_t row_scale(int row) const { return {sz[row], inv_t[row]}; }
+    __device__ __forceinline__ float col_scale(int col) const { return swb[col]; }
+    __device__ __forceinline__ uint16_t value(int row, int col, int acc, row_t rs, float cs) const {
         if (dbg != nullptr && row >= dbg_begin && row < dbg_begin + dbg_rows)
             dbg[(row - dbg_begin) * (int64_t)nh * kHeadW + col] = acc;
+        return f32_to_bf16((((float)acc * rs.sz) * rs.inv) * cs);
+    }
+    __device__ __forceinline__ void* ptr(int row, int col, int) const {
+        return kv_dst(k_nope, value_out, nh, row, col);
     }
 };
+
+// Store `n` bytes (4, 8 or 16) of v to LDS.
+template <int NB>
+__device__ __forceinline__ void lds_store(uint8_t* p, const uint32_t* v) {
+    if constexpr (NB == 16) *(u4_t*)p = u4_t{v[0], v[1], v[2], v[3]};
+    else if constexpr (NB == 8) *(u2_t*)p = u2_t{v[0], v[1]};
+    else *(uint32_t*)p = v[0];
+}
 
 // ---------------------------------------------------------------------------
 // C[M, N] = A[M, K] . B[K, N]; A and B row-major, K consumed in 128-byte
 // slabs (64 fp16/bf16 or 128 int8 elements = two MFMA K steps).
-// Grid: x = M tiles, y = N tiles, z = split-K index.  256 threads, 4 waves
+//
+// Grid: one workgroup per (split, M tile, N tile), 256 threads = 4 waves
 // laid out (BM/WM) x (BN/WN), each wave owning a WM x WN block of 16x16
-// MFMA tiles.  The B slab is transposed into LDS as [n][k] so that both
-// operands are read as 16-byte K slices.  While one slab is multiplied, the
-// next is already being fetched into registers.
+// MFMA tiles.  Tile order is XCD-aware: workgroup b runs on XCD b % 8
+// (round-robin dispatch), each XCD takes a contiguous chunk of the tile
+// list, and the list walks groups of GM M tiles N-major, so an XCD's L2
+// keeps a group's A rows while the B tiles stream past them.
+//
+// Per slab: every thread fetches its share of the A slab (16-byte chunks)
+// and of the B slab (a block of BR rows x 16 bytes, transposed in registers
+// so that LDS holds B as [n][k]); both MFMA operands are then 16-byte K
+// slices.  The B rows' 16-byte K units are XOR-swizzled by (n / 8) % 8, so
+// the transposed stores of neighbouring column blocks land on different
+// banks.  LDS holds two slabs: while one is multiplied the next is stored,
+// and the one after that is already being fetched into registers; one
+// barrier per slab.  The output tile is gathered in LDS and written with
+// 16-byte row stores.
 // ---------------------------------------------------------------------------
-template <int E, int BM, int BN, int WM, int WN, class Epi>
+template <int E, int BM, int BN, int WM, int WN, int GM, class Epi>
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
-    int M, int kslabs_per_split, int kslabs_total, Epi epi) {
+    int M, int Nt, int S, int kslabs_per_split, int kslabs_total, Epi epi) {
     constexpr int KB = 128;           // bytes of K per slab
     constexpr int ST = KB + 16;       // LDS row stride in bytes (padding vs bank conflicts)
     constexpr int ES = (E == kI8) ? 1 : 2;
@@ -137,19 +188,37 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
     constexpr int WAVES_N = BN / WN;
     static_assert((BM / WM) * WAVES_N == 4, "4 waves");
     constexpr int TM = WM / 16, TN = WN / 16;
-    constexpr int A_CHUNKS = BM * (KB / 16);           // 16-byte chunks in an A slab
+    constexpr int A_CHUNKS = BM * (KB / 16);            // 16-byte chunks in an A slab
     constexpr int A_PER_T = (A_CHUNKS + 255) / 256;
-    constexpr int BR = (E == kI8) ? 16 : 8;             // rows per B block
-    constexpr int BC = 16 / ES;                         // columns per B block
+    constexpr int BC = 16 / ES;                         // columns per B block (16 bytes)
+    constexpr int BR0 = (KE * BN) / (BC * 256);          // rows per block for one per thread
+    constexpr int BR = BR0 * ES >= 4 ? BR0 : 4 / ES;      // at least 4 bytes per column
     constexpr int B_BLOCKS = (KE / BR) * (BN / BC);
-    static_assert(B_BLOCKS <= 256, "one B block per thread at most");
+    constexpr int BW = BR * ES;                         // bytes per column after transposing
+    static_assert(B_BLOCKS <= 256 && BW >= 4 && BW <= 16, "B block shape");
 
-    __shared__ __align__(16) uint8_t As[BM * ST];
-    __shared__ __align__(16) uint8_t Bs[BN * ST];
+    typedef typename Epi::out_t out_t;
+    constexpr int CST = BN + 16 / (int)sizeof(out_t);   // C tile row pitch (elements)
+    constexpr int STAGE = (BM + BN) * ST;
+    constexpr int AB_BYTES = 2 * STAGE;
+    constexpr int C_BYTES = BM * CST * (int)sizeof(out_t);
+    __shared__ __align__(16) uint8_t smem[AB_BYTES > C_BYTES ? AB_BYTES : C_BYTES];
+
+    // ---- tile of this workgroup
+    const int Mt = (M + BM - 1) / BM;
+    const int tiles = Mt * Nt * S;
+    const int per = (tiles + 7) / 8;
+    const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (t >= tiles) return;
+    const int s = t / (Mt * Nt);
+    const int rr = t - s * Mt * Nt;
+    const int grp = rr / (GM * Nt);
+    const int gm = min(GM, Mt - grp * GM);
+    const int q = rr - grp * GM * Nt;
+    const int m0 = (grp * GM + q % gm) * BM, n0 = (q / gm) * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm0 = (wave / WAVES_N) * WM, wn0 = (wave % WAVES_N) * WN;
-    const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN, s = blockIdx.z;
     const int kc0 = s * kslabs_per_split;
     const int kc1 = min(kc0 + kslabs_per_split, kslabs_total);
 
@@ -182,7 +251,9 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
             for (int i = 0; i < BR; ++i) rb[i] = *(const u4_t*)(src + (int64_t)i * ldb);
         }
     };
-    auto lstore = [&]() {
+    auto lstore = [&](uint8_t* stage) {
+        uint8_t* As = stage;
+        uint8_t* Bs = stage + BM * ST;
 #pragma unroll
         for (int i = 0; i < A_PER_T; ++i) {
             const int c = tid + i * 256;
@@ -192,20 +263,26 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
             }
         }
         if (tid < B_BLOCKS) {
-            u4_t t[BR];
-            if constexpr (E == kI8) transpose16x16_b8(rb, t);
-            else transpose8x8_b16(rb, t);
+            // column j of the block: its BR elements, packed along K
 #pragma unroll
-            for (int j = 0; j < BC; ++j)
-                *(u4_t*)(Bs + (b_cb * BC + j) * ST + b_rb * 16) = t[j];
+            for (int j = 0; j < BC; ++j) {
+                uint32_t col[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int i = 0; i < BR; ++i) {
+                    uint32_t e;
+                    if constexpr (ES == 2) e = (rb[i][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+                    else e = (rb[i][j >> 2] >> (8 * (j & 3))) & 0xFFu;
+                    const int bit = i * ES * 8;
+                    col[bit >> 5] |= e << (bit & 31);
+                }
+                const int n = b_cb * BC + j;
+                lds_store<BW>(Bs + n * ST + ((b_rb * BW) ^ (((n >> 3) & 7) << 4)), col);
+            }
         }
     };
-
-    if (kc0 < kc1) gload(kc0);
-    for (int kc = kc0; kc < kc1; ++kc) {
-        lstore();
-        __syncthreads();
-        if (kc + 1 < kc1) gload(kc + 1);
+    auto compute = [&](const uint8_t* stage) {
+        const uint8_t* As = stage;
+        const uint8_t* Bs = stage + BM * ST;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             u4_t a[TM], b[TN];
@@ -214,26 +291,73 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
             for (int i = 0; i < TM; ++i)
                 a[i] = *(const u4_t*)(As + (wm0 + i * 16 + (lane & 15)) * ST + kofs);
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                b[j] = *(const u4_t*)(Bs + (wn0 + j * 16 + (lane & 15)) * ST + kofs);
+            for (int j = 0; j < TN; ++j) {
+                const int n = wn0 + j * 16 + (lane & 15);
+                b[j] = *(const u4_t*)(Bs + n * ST + (kofs ^ (((n >> 3) & 7) << 4)));
+            }
+            // operands swapped (C^T = B^T A^T): lane l then holds output row
+            // (l % 16) and the 4 consecutive output columns 4 (l / 16) + v
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j] = mfma16<E>(a[i], b[j], acc[i][j]);
+                for (int j = 0; j < TN; ++j) acc[i][j] = mfma16<E>(b[j], a[i], acc[i][j]);
         }
+    };
+
+    if (kc0 < kc1) {
+        gload(kc0);
+        lstore(smem);
         __syncthreads();
+        if (kc0 + 1 < kc1) gload(kc0 + 1);
+        for (int kc = kc0; kc < kc1; ++kc) {
+            const int cur = (kc - kc0) & 1;
+            compute(smem + cur * STAGE);
+            if (kc + 1 < kc1) {
+                lstore(smem + (cur ^ 1) * STAGE);
+                if (kc + 2 < kc1) gload(kc + 2);
+            }
+            __syncthreads();
+        }
     }
 
+    // epilogue: gather the tile in LDS (the K loop ended with a barrier, so
+    // the staging area is free), then store 16-byte row chunks
+    out_t* Ct = (out_t*)smem;
+    float cs[TN][4];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+        for (int v = 0; v < 4; ++v) cs[j][v] = epi.col_scale(n0 + wn0 + j * 16 + (lane >> 4) * 4 + v);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int row = m0 + wm0 + i * 16 + (lane >> 4) * 4 + v;
-                const int col = n0 + wn0 + j * 16 + (lane & 15);
-                if (row < M) epi(row, col, s, acc[i][j][v]);
-            }
+    for (int i = 0; i < TM; ++i) {
+        const int r = wm0 + i * 16 + (lane & 15);
+        // rows past M are padding: never handed to the epilogue
+        const bool live = m0 + r < M;
+        const typename Epi::row_t rs = epi.row_scale(live ? m0 + r : 0);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int cl = wn0 + j * 16 + (lane >> 4) * 4;
+            out_t o[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                o[v] = live ? epi.value(m0 + r, n0 + cl + v, acc[i][j][v], rs, cs[j][v]) : out_t(0);
+            if constexpr (sizeof(out_t) == 2)
+                *(u2_t*)&Ct[r * CST + cl] = u2_t{(uint32_t)o[0] | ((uint32_t)o[1] << 16),
+                                                 (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
+            else
+                *(u4_t*)&Ct[r * CST + cl] = u4_t{__builtin_bit_cast(uint32_t, o[0]),
+                                                 __builtin_bit_cast(uint32_t, o[1]),
+                                                 __builtin_bit_cast(uint32_t, o[2]),
+                                                 __builtin_bit_cast(uint32_t, o[3])};
+        }
+    }
+    __syncthreads();
+    constexpr int EPC = 16 / (int)sizeof(out_t);
+    constexpr int CPR = BN / EPC;
+    for (int c = tid; c < BM * CPR; c += 256) {
+        const int r = c / CPR, cc = c % CPR;
+        if (m0 + r < M) *(u4_t*)epi.ptr(m0 + r, n0 + cc * EPC, s) = *(const u4_t*)&Ct[r * CST + cc * EPC];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -423,10 +547,13 @@ __global__ __launch_bounds__(64) void finish_a_w8_kernel(
 template <int E, int BM, int BN, int WM, int WN, class Epi>
 static void gemm_launch(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M,
                         int N, int kslabs, int S, Epi epi, hipStream_t st) {
+    constexpr int GM = 4;  // M tiles per group of the XCD-aware tile order
     const int per = (kslabs + S - 1) / S;
-    dim3 grid((unsigned)((M + BM - 1) / BM), (unsigned)(N / BN), (unsigned)S);
-    hipLaunchKernelGGL((gemm_tiled_kernel<E, BM, BN, WM, WN, Epi>), grid, dim3(256), 0, st,
-                       (const uint8_t*)A, lda, (const uint8_t*)B, ldb, (int)M, per, kslabs, epi);
+    const int64_t tiles = ((M + BM - 1) / BM) * (N / BN) * (int64_t)S;
+    const int64_t grid = ((tiles + 7) / 8) * 8;
+    hipLaunchKernelGGL((gemm_tiled_kernel<E, BM, BN, WM, WN, GM, Epi>), dim3((unsigned)grid),
+                       dim3(256), 0, st, (const uint8_t*)A, lda, (const uint8_t*)B, ldb, (int)M,
+                       N / BN, S, per, kslabs, epi);
 }
 
 // kv_a_proj tiles: BN = 64 always (576 = 9 x 64)
@@ -448,6 +575,10 @@ static void gemm2_dispatch(int bm, int bn, const void* A, int64_t lda, const voi
                            int N2, Epi epi, hipStream_t st) {
     const int64_t ldb = (int64_t)N2 * ((E == kI8) ? 1 : 2);
     const int kslabs = (E == kI8) ? kR / 128 : kR * 2 / 128;
+    if (bm == 256) {
+        gemm_launch<E, 256, 128, 128, 64>(A, lda, B, ldb, M, N2, kslabs, 1, epi, st);
+        return;
+    }
     if (bn == 128) {
         gemm_launch<E, 128, 128, 64, 64>(A, lda, B, ldb, M, N2, kslabs, 1, epi, st);
         return;
