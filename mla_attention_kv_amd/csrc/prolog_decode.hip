@@ -69,15 +69,22 @@ __device__ __forceinline__ void stage_store(const u4_t (&v)[NR], uint16_t* lds) 
 #pragma unroll
     for (int r = 0; r < NR; ++r) *(u4_t*)(lds + (r0 + 32 * r) * kPitch + 8 * q) = v[r];
 }
-// MFMA B operand from a staged slab: column col, rows kb + 8g .. kb + 8g + 7.
-__device__ __forceinline__ u4_t lds_col8(const uint16_t* lds, int kb, int col) {
-    const int g = (threadIdx.x & 63) >> 4;
-    const uint16_t* p = lds + (kb + 8 * g) * kPitch + col;
-    u4_t b;
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-        b[v] = (uint32_t)p[(2 * v) * kPitch] | ((uint32_t)p[(2 * v + 1) * kPitch] << 16);
-    return b;
+// MFMA B operand from a staged slab: lane (16 g + c) gets column c0 + c,
+// rows kb + 8g .. kb + 8g + 7.  Two transposing LDS reads
+// (ds_read_b64_tr_b16): in each 16-lane group, lane s points at row
+// k + s/4, columns c0 + 4 (s % 4) .. +3, and lane j receives rows k .. k+3
+// of column c0 + j.
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+    const v4s_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s_t*)(p));
+    return __builtin_bit_cast(uint2, r);
+}
+__device__ __forceinline__ u4_t lds_col8(const uint16_t* lds, int kb, int c0) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, sl = lane & 15;
+    const uint16_t* p = lds + (kb + 8 * g + (sl >> 2)) * kPitch + c0 + 4 * (sl & 3);
+    const uint2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * kPitch);
+    return u4_t{lo.x, lo.y, hi.x, hi.y};
 }
 
 // ---------------------------------------------------------------------------
@@ -116,7 +123,7 @@ __global__ __launch_bounds__(256) void dec_kv_a_kernel(const uint16_t* __restric
 #pragma unroll
     for (int ch = 0; ch < KW / 32; ++ch) {
         if (k0 + ch * 32 >= H) break;
-        const u4_t bw = lds_col8(lds, ch * 32, col);
+        const u4_t bw = lds_col8(lds, ch * 32, wave * 16);
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) acc[tt] = mfma_f<E>(x[ch][tt], bw, acc[tt]);
     }
@@ -240,7 +247,7 @@ __global__ __launch_bounds__(256) void dec_kv_b_kernel(const uint16_t* __restric
     const int col = wave * 16 + c;
     f4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ch = 0; ch < kR / 32; ++ch) acc = mfma_f<E>(y[ch], lds_col8(lds, ch * 32, col), acc);
+    for (int ch = 0; ch < kR / 32; ++ch) acc = mfma_f<E>(y[ch], lds_col8(lds, ch * 32, wave * 16), acc);
     // lane holds tokens tt*16 + 4g + i of slab column col
     const int n = slab * kSlabW + col;
     const int h = n >> 8, sl = n & 255;
