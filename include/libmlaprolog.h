@@ -28,10 +28,10 @@
  * - Every tensor pointer is a DEVICE pointer, allocated and owned by the
  *   caller; the library never allocates, frees or keeps a pointer past the
  *   call.  Scratch memory is the caller's `workspace` (size from the
- *   matching *_workspace_size query).  A workspace must be zero-filled once,
- *   before its first use; its first 4096 bytes hold grid-synchronisation
- *   counters that every call leaves at zero again, so it can be reused by
- *   any later call (of either entry point) without clearing.
+ *   matching *_workspace_size query).  A workspace needs no initialisation:
+ *   every call writes whatever it later reads, including the
+ *   synchronisation counters in its first 4096 bytes, so one workspace can
+ *   serve any sequence of ordered calls (of either entry point).
  * - Tensors are contiguous, row-major, in exactly the shapes given.  W_kv_b's
  *   columns come in per-head blocks [k_nope_h (dn) | value_h (dv)].
  *   Outputs are token-major: k_nope [T,nh,dn], value [T,nh,dv],

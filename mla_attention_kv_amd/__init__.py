@@ -177,8 +177,8 @@ def _outputs(T, d, dtype, device, k_nope, value, k_pe, compressed_kv):
 def _workspace(nbytes, device, workspace):
     torch = _torch()
     if workspace is None:
-        # zero-filled once (the synchronisation counters must start at zero)
-        workspace = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        # the library writes everything it reads from its workspace
+        workspace = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
     if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise ValueError("workspace: contiguous uint8 tensor expected")
     if workspace.numel() < nbytes:

@@ -58,17 +58,32 @@ __device__ __forceinline__ uint16_t f32_to_st(float f) {
 }
 
 // ---------------------------------------------------------------------------
-// wave reductions (64 lanes)
+// wave reductions (64 lanes): DPP steps inside each row of 16 lanes (swap
+// neighbours, swap pairs, mirror half-rows, mirror rows), then the four row
+// results read out of lanes 0, 16, 32, 48 and combined in a fixed order.
+// The result is the same in every lane.
 // ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_f<0x141>(v);  // row_half_mirror
+    v += dpp_f<0x140>(v);  // row_mirror
+    return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x141>(v));
+    v = fmaxf(v, dpp_f<0x140>(v));
+    return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
 // ---------------------------------------------------------------------------
@@ -88,15 +103,29 @@ struct RopeTab {
     double f[kDR / 2];
 };
 
-// cos / sin of the rope angle pos * f: the angle is formed and reduced modulo
-// 2 pi in double (Cody-Waite, 2 pi split into two doubles), then the reduced
-// angle (|r| <= pi) goes through fp32 sincos.
+// cos / sin of the rope angle a = pos * f.  The angle is formed in double
+// and reduced by quarter turns there (k = nearest integer to a / (pi/2), pi/2
+// split into two doubles, Cody-Waite), leaving |x| <= pi/4; sin x and cos x
+// then come from their Taylor series in fp32 (terms through x^9 and x^10:
+// truncation below 2e-9 on that interval), and k mod 4 rotates them into
+// place.  Straight-line code: no table lookups, no branches.
 __device__ __forceinline__ void rope_cos_sin(int32_t pos, double f, float& cs, float& sn) {
     const double a = (double)pos * f;
-    const double k = rint(a * 0.15915494309189535);
-    double r = fma(-k, 6.283185307179586, a);
-    r = fma(-k, 2.4492935982947064e-16, r);
-    sincosf((float)r, &sn, &cs);
+    const double k = rint(a * 0.6366197723675814);
+    double r = fma(-k, 1.5707963267948966, a);
+    r = fma(-k, 6.123233995736766e-17, r);
+    const float x = (float)r, x2 = x * x;
+    const float s =
+        x + x * x2 * (-1.0f / 6.0f +
+                      x2 * (1.0f / 120.0f + x2 * (-1.0f / 5040.0f + x2 * (1.0f / 362880.0f))));
+    const float c =
+        1.0f + x2 * (-0.5f + x2 * (1.0f / 24.0f +
+                                   x2 * (-1.0f / 720.0f +
+                                         x2 * (1.0f / 40320.0f + x2 * (-1.0f / 3628800.0f)))));
+    const int q = (int)((long long)k & 3);
+    const float cq = (q & 1) ? s : c, sq = (q & 1) ? c : s;
+    cs = ((q + 1) & 2) ? -cq : cq;  // quarter turns 1, 2 negate cos
+    sn = (q & 2) ? -sq : sq;        // quarter turns 2, 3 negate sin
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }

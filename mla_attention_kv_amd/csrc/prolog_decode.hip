@@ -53,14 +53,17 @@ constexpr int kPitch = kSlabW + 8;         // LDS row pitch of a staged slab (ha
 // columns) of rows i/8 + 32 r, r < NR; rows at or past kmax load zeros.
 // stage_store writes them to LDS as [row][kPitch].
 // ---------------------------------------------------------------------------
-template <int NR>
+template <int NR, bool CHECK = true>
 __device__ __forceinline__ void stage_load(u4_t (&v)[NR], const uint16_t* W, int64_t ld, int k0,
                                            int kmax, int n0) {
     const int q = threadIdx.x & 7, r0 = threadIdx.x >> 3;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
         const int k = k0 + r0 + 32 * r;
-        v[r] = (k < kmax) ? *(const u4_t*)(W + (int64_t)k * ld + n0 + 8 * q) : u4_t{0u, 0u, 0u, 0u};
+        if (!CHECK || k < kmax)
+            v[r] = *(const u4_t*)(W + (int64_t)k * ld + n0 + 8 * q);
+        else
+            v[r] = u4_t{0u, 0u, 0u, 0u};
     }
 }
 template <int NR>
@@ -88,49 +91,114 @@ __device__ __forceinline__ u4_t lds_col8(const uint16_t* lds, int kb, int c0) {
 }
 
 // ---------------------------------------------------------------------------
-// kv_a_proj partial of (slab, split) over K rows [s*KW, s*KW + KW).
-// grid = 9 slabs x S splits (slab fastest), 256 threads.
+// Activation rows: rows [0, 16 NT) x columns [k0, k0 + KA) of a row-major
+// [rows][ld] matrix, loaded 16 bytes per chunk by the whole workgroup and
+// kept in LDS as [row][KA + 8]; rows >= nrows and columns >= kmax are zero.
+// The +8 pitch puts the 16 rows an MFMA operand read touches on distinct
+// banks.  Each wave then reads its A operands (lane 16g + c: row c, 8
+// consecutive K at 8g) with one 16-byte LDS read.
 // ---------------------------------------------------------------------------
-template <int E, int NTT, int KW>
-__global__ __launch_bounds__(256) void dec_kv_a_kernel(const uint16_t* __restrict__ X,
-                                                       const uint16_t* __restrict__ Wa, int T,
-                                                       int H, float* __restrict__ P) {
-    __shared__ __align__(16) uint16_t lds[KW * kPitch];
-    const int slab = blockIdx.x % kSlabsA, s = blockIdx.x / kSlabsA;
+template <int NT, int KA>
+struct ARows {
+    static constexpr int kChunks = NT * 16 * KA / 8;
+    static constexpr int kPer = (kChunks + 255) / 256;
+    static constexpr int kPitchA = KA + 8;
+};
+template <int NT, int KA, int NP>
+__device__ __forceinline__ void arows_load(u4_t (&v)[NP], const uint16_t* A, int64_t ld, int nrows,
+                                           int k0, int kmax) {
+    static_assert(NP == ARows<NT, KA>::kPer, "chunks per thread");
+    constexpr int CPR = KA / 8;
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+        const int q = threadIdx.x + 256 * u;
+        const int row = q / CPR, k = k0 + 8 * (q % CPR);
+        v[u] = (q < ARows<NT, KA>::kChunks && row < nrows && k < kmax)
+                   ? *(const u4_t*)(A + (int64_t)row * ld + k)
+                   : u4_t{0u, 0u, 0u, 0u};
+    }
+}
+template <int NT, int KA, int NP>
+__device__ __forceinline__ void arows_store(const u4_t (&v)[NP], uint16_t* lds) {
+    static_assert(NP == ARows<NT, KA>::kPer, "chunks per thread");
+    constexpr int CPR = KA / 8;
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+        const int q = threadIdx.x + 256 * u;
+        if (q < ARows<NT, KA>::kChunks)
+            *(u4_t*)(lds + (q / CPR) * ARows<NT, KA>::kPitchA + 8 * (q % CPR)) = v[u];
+    }
+}
+
+// acc[tt] += A rows 16 tt .. 16 tt + 15 (LDS, pitch AP) x slab columns
+// 16 w .. 16 w + 15 (w = this wave) over the first kv rows (kv a multiple
+// of 32).  The weight operand is read once per 32-row chunk and reused by
+// every token tile.
+template <int E, int NT, int KA>
+__device__ __forceinline__ void slab_mma(const uint16_t* ldsW, const uint16_t* ldsA, int kv,
+                                         f4_t (&acc)[NT]) {
+    constexpr int AP = ARows<NT, KA>::kPitchA;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int c = lane & 15, g = lane >> 4;
-    const int k0 = s * KW;
-    u4_t v[KW / 32];
-    stage_load<KW / 32>(v, Wa, kN1, k0, H, slab * kSlabW);
-    // activation operands of all chunks, fetched with the weights
-    u4_t x[KW / 32][NTT];
 #pragma unroll
-    for (int ch = 0; ch < KW / 32; ++ch) {
-        const int kb = k0 + ch * 32;
+    for (int ch = 0; ch < KA / 32; ++ch) {
+        if (ch * 32 >= kv) break;
+        const u4_t bw = lds_col8(ldsW, ch * 32, wave * 16);
 #pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) {
-            const int t = tt * 16 + c;
-            x[ch][tt] = (t < T && kb < H) ? *(const u4_t*)(X + (int64_t)t * H + kb + 8 * g)
-                                          : u4_t{0u, 0u, 0u, 0u};
+        for (int tt = 0; tt < NT; ++tt) {
+            const u4_t a = *(const u4_t*)(ldsA + (tt * 16 + c) * AP + ch * 32 + 8 * g);
+            acc[tt] = mfma_f<E>(a, bw, acc[tt]);
         }
     }
-    stage_store<KW / 32>(v, lds);
+}
+
+// Work item of a workgroup: workgroup b runs on XCD b % 8, and XCD x takes
+// the contiguous item range [x per, (x + 1) per), so items with neighbouring
+// indices share an XCD and its L2.  Returns -1 for the padding workgroups.
+__device__ __forceinline__ int xcd_item(int nitems) {
+    const int per = (nitems + 7) / 8;
+    const int it = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+    return it < nitems ? it : -1;
+}
+
+// ---------------------------------------------------------------------------
+// kv_a_proj partial of (split s, slab) over K rows [s KW, s KW + KW) for all
+// T <= 16 NT tokens; item = 9 s + slab, so each XCD reads a contiguous
+// range of X's columns.  grid = 8 ceil(9 S / 8), 256 threads.
+// ---------------------------------------------------------------------------
+template <int E, int NT, int KW>
+__global__ __launch_bounds__(256) void dec_kv_a_kernel(const uint16_t* __restrict__ X,
+                                                       const uint16_t* __restrict__ Wa, int T,
+                                                       int H, int S, float* __restrict__ P,
+                                                       uint16_t* __restrict__ ckv) {
+    __shared__ __align__(16) uint16_t ldsW[KW * kPitch];
+    __shared__ __align__(16) uint16_t ldsA[NT * 16 * ARows<NT, KW>::kPitchA];
+    // compressed_kv rows start out as the "not written yet" pattern that the
+    // fused finish + kv_b_proj launch which follows waits on
+    for (int row = blockIdx.x; row < T; row += gridDim.x)
+        if (threadIdx.x < kR / 8)
+            *(u4_t*)(ckv + (int64_t)row * kR + 8 * threadIdx.x) = u4_t{~0u, ~0u, ~0u, ~0u};
+    const int item = xcd_item(kSlabsA * S);
+    if (item < 0) return;
+    const int s = item / kSlabsA, slab = item % kSlabsA;
+    const int k0 = s * KW;
+    u4_t v[KW / 32];
+    u4_t a[ARows<NT, KW>::kPer];
+    stage_load<KW / 32>(v, Wa, kN1, k0, H, slab * kSlabW);
+    arows_load<NT, KW>(a, X, H, T, k0, H);
+    stage_store<KW / 32>(v, ldsW);
+    arows_store<NT, KW>(a, ldsA);
     __syncthreads();
-    f4_t acc[NTT];
+    f4_t acc[NT];
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) acc[tt] = f4_t{0.f, 0.f, 0.f, 0.f};
-    const int col = wave * 16 + c;
+    for (int tt = 0; tt < NT; ++tt) acc[tt] = f4_t{0.f, 0.f, 0.f, 0.f};
+    slab_mma<E, NT, KW>(ldsW, ldsA, H - k0, acc);
+    // lane 16g + c holds tokens 16 tt + 4g + i of slab column 16 wave + c
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int c = lane & 15, g = lane >> 4;
+    float* Ps = P + (int64_t)s * T * kN1 + slab * kSlabW + wave * 16 + c;
 #pragma unroll
-    for (int ch = 0; ch < KW / 32; ++ch) {
-        if (k0 + ch * 32 >= H) break;
-        const u4_t bw = lds_col8(lds, ch * 32, wave * 16);
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) acc[tt] = mfma_f<E>(x[ch][tt], bw, acc[tt]);
-    }
-    // lane holds tokens tt*16 + 4g + i, slab column wave*16 + c
-    float* Ps = P + (int64_t)s * T * kN1 + slab * kSlabW + col;
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt)
+    for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = tt * 16 + 4 * g + i;
@@ -139,12 +207,143 @@ __global__ __launch_bounds__(256) void dec_kv_a_kernel(const uint16_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Finish of kv_a_proj, one workgroup per token t.  Wave w sums splits w,
-// w+4, ... of the partials; wave 0 adds the four wave sums (fixed order),
+// Finish of kv_a_proj for token t, by one workgroup.  Wave w sums splits
+// w, w+4, ... of the partials; wave 0 adds the four wave sums (fixed order),
 // then lane l owns latent columns 8l..8l+7 and rope column l:
 //   y     = c / sqrt(sum(c^2)/512 + eps) * gamma      -> compressed_kv
 //   k_pe  = rotate-half RoPE of p at the token's position
+// With COH the compressed_kv row is written with device-coherent stores
+// (through to memory), for workgroups on other XCDs that read it in the same
+// launch.  fred: 4 x (576 + 4) floats of LDS.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void store_coherent64(void* p, uint64_t v) {
+    __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load_coherent64(const void* p) {
+    return __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr int kFredPitch = kN1 + 4;
+
+// Partial sums of token t held by one wave: splits s0, s0 + 4, s0 + 8,
+// s0 + 12; those at or past S are loaded from split S - 1 (so that every
+// load is unconditional and all four are in flight together) and dropped
+// when added.
+struct FinPart {
+    f4_t v0[4], v1[4];
+    float vp[4];
+    int s0;
+    u4_t gm;      // gamma[8 lane .. 8 lane + 7]
+    int32_t pos;  // the token's position
+    double freq;  // RoPE frequency of rope column lane
+};
+__device__ __forceinline__ void fin_load(FinPart& r, const float* __restrict__ P, int S, int T,
+                                         int t, int s0) {
+    const int lane = threadIdx.x & 63;
+    r.s0 = s0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int sp = s0 + 4 * u < S ? s0 + 4 * u : S - 1;
+        const float* row = P + ((int64_t)sp * T + t) * kN1;
+        r.v0[u] = *(const f4_t*)(row + 8 * lane);
+        r.v1[u] = *(const f4_t*)(row + 8 * lane + 4);
+        r.vp[u] = row[kR + lane];
+    }
+}
+__device__ __forceinline__ void fin_load_aux(FinPart& r, const uint16_t* __restrict__ gamma,
+                                             const int32_t* __restrict__ pos, const RopeTab& rt,
+                                             int t) {
+    const int lane = threadIdx.x & 63;
+    r.gm = *(const u4_t*)(gamma + 8 * lane);
+    r.pos = pos[t];
+    r.freq = rt.f[lane & 31];
+}
+__device__ __forceinline__ void fin_add(const FinPart& r, int S, f4_t& c0, f4_t& c1, float& p) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        if (r.s0 + 4 * u < S) {
+            c0 += r.v0[u];
+            c1 += r.v1[u];
+            p += r.vp[u];
+        }
+    }
+}
+
+// Finish of token t given the wave's partials of its first 16 splits, gamma,
+// the position and the RoPE frequency in r.  After the partials are summed,
+// wave 0 normalises the latent and wave 1 rotates the rope part.
+template <int E, bool COH>
+__device__ __forceinline__ void finish_token_from(FinPart& r, const float* __restrict__ P, int S,
+                                                  int T, int t, float eps,
+                                                  uint16_t* __restrict__ ckv,
+                                                  uint16_t* __restrict__ kpe, float* fred) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    f4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+    float p = 0.f;
+    fin_add(r, S, c0, c1, p);
+    for (int s0 = wave + 16; s0 < S; s0 += 16) {
+        fin_load(r, P, S, T, t, s0);
+        fin_add(r, S, c0, c1, p);
+    }
+    float* fw = fred + wave * kFredPitch;
+    *(f4_t*)&fw[8 * lane] = c0;
+    *(f4_t*)&fw[8 * lane + 4] = c1;
+    fw[kR + lane] = p;
+    __syncthreads();
+    const float* f0 = fred;
+    const float* f1 = fred + kFredPitch;
+    const float* f2 = fred + 2 * kFredPitch;
+    const float* f3 = fred + 3 * kFredPitch;
+    if (wave == 0) {
+        const u4_t gm = r.gm;
+        float c[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            c[i] = (f0[8 * lane + i] + f1[8 * lane + i]) + (f2[8 * lane + i] + f3[8 * lane + i]);
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss += c[i] * c[i];
+        ss = wave_sum(ss);
+        const float inv = 1.0f / sqrtf(ss / (float)kR + eps);
+        u4_t o;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float g0 = ld_to_f32<E>((uint16_t)(gm[w] & 0xFFFFu));
+            const float g1 = ld_to_f32<E>((uint16_t)(gm[w] >> 16));
+            const uint32_t y0 = f32_to_st<E>((c[2 * w] * inv) * g0);
+            const uint32_t y1 = f32_to_st<E>((c[2 * w + 1] * inv) * g1);
+            o[w] = y0 | (y1 << 16);
+        }
+        uint16_t* dst = ckv + (int64_t)t * kR + 8 * lane;
+        if constexpr (COH) {
+            store_coherent64(dst, (uint64_t)o[0] | ((uint64_t)o[1] << 32));
+            store_coherent64(dst + 4, (uint64_t)o[2] | ((uint64_t)o[3] << 32));
+        } else {
+            *(u4_t*)dst = o;
+        }
+    } else if (wave == 1) {
+        float cs, sn;
+        rope_cos_sin(r.pos, r.freq, cs, sn);
+        const float q = (f0[kR + lane] + f1[kR + lane]) + (f2[kR + lane] + f3[kR + lane]);
+        const float partner = __shfl_xor(q, 32, 64);
+        const float out = (lane < 32) ? (q * cs - partner * sn) : (q * cs + partner * sn);
+        kpe[(int64_t)t * kDR + lane] = f32_to_st<E>(out);
+    }
+}
+
+template <int E, bool COH>
+__device__ __forceinline__ void finish_token(const float* __restrict__ P, int S, int T, int t,
+                                             const uint16_t* __restrict__ gamma,
+                                             const int32_t* __restrict__ pos, float eps,
+                                             const RopeTab& rt, uint16_t* __restrict__ ckv,
+                                             uint16_t* __restrict__ kpe, float* fred) {
+    FinPart r;
+    fin_load(r, P, S, T, t, threadIdx.x >> 6);
+    fin_load_aux(r, gamma, pos, rt, t);
+    finish_token_from<E, COH>(r, P, S, T, t, eps, ckv, kpe, fred);
+}
+
+// one workgroup per token
 template <int E>
 __global__ __launch_bounds__(256) void dec_finish_kernel(const float* __restrict__ P, int S, int T,
                                                          const uint16_t* __restrict__ gamma,
@@ -152,136 +351,201 @@ __global__ __launch_bounds__(256) void dec_finish_kernel(const float* __restrict
                                                          float eps, RopeTab rt,
                                                          uint16_t* __restrict__ ckv,
                                                          uint16_t* __restrict__ kpe) {
-    __shared__ __align__(16) float fred[4][kN1 + 4];
-    const int t = blockIdx.x;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const u4_t gm = *(const u4_t*)(gamma + 8 * lane);
-    const int32_t pos_t = pos[t];
-    const double freq = rt.f[lane & 31];
-    f4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
-    float p = 0.f;
-    for (int s0 = wave; s0 < S; s0 += 16) {
-        f4_t v0[4], v1[4];
-        float vp[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int sp = s0 + 4 * u;
-            if (sp < S) {
-                const float* row = P + ((int64_t)sp * T + t) * kN1;
-                v0[u] = *(const f4_t*)(row + 8 * lane);
-                v1[u] = *(const f4_t*)(row + 8 * lane + 4);
-                vp[u] = row[kR + lane];
-            } else {
-                v0[u] = v1[u] = f4_t{0.f, 0.f, 0.f, 0.f};
-                vp[u] = 0.f;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            c0 += v0[u];
-            c1 += v1[u];
-            p += vp[u];
-        }
-    }
-    *(f4_t*)&fred[wave][8 * lane] = c0;
-    *(f4_t*)&fred[wave][8 * lane + 4] = c1;
-    fred[wave][kR + lane] = p;
-    __syncthreads();
-    if (wave != 0) return;
-    float c[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        c[i] = (fred[0][8 * lane + i] + fred[1][8 * lane + i]) +
-               (fred[2][8 * lane + i] + fred[3][8 * lane + i]);
-    p = (fred[0][kR + lane] + fred[1][kR + lane]) + (fred[2][kR + lane] + fred[3][kR + lane]);
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ss += c[i] * c[i];
-    ss = wave_sum(ss);
-    const float inv = 1.0f / sqrtf(ss / (float)kR + eps);
-    u4_t o;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const float g0 = ld_to_f32<E>((uint16_t)(gm[w] & 0xFFFFu));
-        const float g1 = ld_to_f32<E>((uint16_t)(gm[w] >> 16));
-        const uint32_t y0 = f32_to_st<E>((c[2 * w] * inv) * g0);
-        const uint32_t y1 = f32_to_st<E>((c[2 * w + 1] * inv) * g1);
-        o[w] = y0 | (y1 << 16);
-    }
-    *(u4_t*)(ckv + (int64_t)t * kR + 8 * lane) = o;
-    const float partner = __shfl_xor(p, 32, 64);
-    float cs, sn;
-    rope_cos_sin(pos_t, freq, cs, sn);
-    const float out = (lane < 32) ? (p * cs - partner * sn) : (p * cs + partner * sn);
-    kpe[(int64_t)t * kDR + lane] = f32_to_st<E>(out);
+    __shared__ __align__(16) float fred[4 * kFredPitch];
+    finish_token<E, false>(P, S, T, blockIdx.x, gamma, pos, eps, rt, ckv, kpe, fred);
 }
 
 // ---------------------------------------------------------------------------
-// kv_b_proj.  One workgroup per item of (16-token tile, 64-column slab);
-// a slab of 64 columns is 64 consecutive entries of k_nope or of value of
-// one head.  Item i = 8 j + x (x = i % 8, the XCD it lands on) covers slab
-// 8 (j / ntile) + x and token tile j % ntile.
+// kv_b_proj.  Work item = (64-column slab of W_kv_b over the full K = 512,
+// group of NT token tiles); a slab is 64 consecutive entries of k_nope or of
+// value of one head.  Items of one slab are adjacent (group fastest), so
+// they share an XCD and read the slab through its L2.
 // ---------------------------------------------------------------------------
-template <int E>
+template <int E, int NT>
 __global__ __launch_bounds__(256) void dec_kv_b_kernel(const uint16_t* __restrict__ Y,
                                                        const uint16_t* __restrict__ Wb, int T,
                                                        int N2, uint16_t* __restrict__ k_nope,
                                                        uint16_t* __restrict__ value) {
-    __shared__ __align__(16) uint16_t lds[kR * kPitch];
+    __shared__ __align__(16) uint16_t ldsW[kR * kPitch];
+    __shared__ __align__(16) uint16_t ldsA[NT * 16 * ARows<NT, kR>::kPitchA];
+    const int nh = N2 / kHeadW;
+    const int ngrp = (T + 16 * NT - 1) / (16 * NT);
+    const int item = xcd_item((N2 / kSlabW) * ngrp);
+    if (item < 0) return;
+    const int slab = item / ngrp, t0 = (item % ngrp) * 16 * NT;
+    u4_t v[kR / 32];
+    u4_t a[ARows<NT, kR>::kPer];
+    stage_load<kR / 32, false>(v, Wb, N2, 0, kR, slab * kSlabW);
+    arows_load<NT, kR>(a, Y + (int64_t)t0 * kR, kR, T - t0, 0, kR);
+    stage_store<kR / 32>(v, ldsW);
+    arows_store<NT, kR>(a, ldsA);
+    __syncthreads();
+    f4_t acc[NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) acc[tt] = f4_t{0.f, 0.f, 0.f, 0.f};
+    slab_mma<E, NT, kR>(ldsW, ldsA, kR, acc);
+    // lane 16g + c holds tokens t0 + 16 tt + 4g + i of slab column 16 wave + c
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int c = lane & 15, g = lane >> 4;
+    const int n = slab * kSlabW + wave * 16 + c;
+    const int h = n >> 8, sl = n & 255;
+    uint16_t* dst = ((sl < kDN) ? k_nope : value) + (int64_t)h * kDN + (sl & 127);
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tok = t0 + tt * 16 + 4 * g + i;
+            if (tok < T) dst[(int64_t)tok * nh * kDN] = f32_to_st<E>(acc[tt][i]);
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Finish and kv_b_proj in one launch, for at most kFusedItems 16-token items
+// (all resident at once, one per CU).  Every workgroup first issues the loads
+// of its W_kv_b slab; workgroup b then finishes tokens b, b + G, ... (G =
+// grid size), writing each compressed_kv row with device-coherent 8-byte
+// stores.  The kv_a launch before it filled those rows with all-ones
+// halves, a NaN pattern that the finish of finite inputs never produces, so
+// a row chunk is known to be final once it holds no all-ones half (8-byte
+// coherent stores and loads are single-copy atomic).  Each workgroup stages
+// its slab, then reads its tile's rows with coherent loads, re-reading the
+// chunks that still hold the pattern, and runs the slab product.  No
+// workgroup waits before its own finish work is done, so every wait is on
+// work that is already running or done; the spin is bounded.
+// ---------------------------------------------------------------------------
+constexpr int kFusedItems = 256;
+constexpr uint32_t kSpinLimit = 1u << 20;
+
+__device__ __forceinline__ bool has_unset_half(uint64_t x) {
+    return ((x & 0xFFFFull) == 0xFFFFull) || (((x >> 16) & 0xFFFFull) == 0xFFFFull) ||
+           (((x >> 32) & 0xFFFFull) == 0xFFFFull) || ((x >> 48) == 0xFFFFull);
+}
+
+template <int E>
+__global__ __launch_bounds__(256) void dec_fin_kv_b_kernel(
+    const float* __restrict__ P, int S, int T, const uint16_t* __restrict__ gamma,
+    const int32_t* __restrict__ pos, float eps, RopeTab rt, const uint16_t* __restrict__ Wb,
+    int N2, uint16_t* ckv, uint16_t* __restrict__ kpe, uint16_t* __restrict__ k_nope,
+    uint16_t* __restrict__ value) {
+    constexpr int AP = ARows<1, kR>::kPitchA;
+    __shared__ __align__(16) uint16_t ldsW[kR * kPitch];
+    __shared__ __align__(16) uint16_t ldsA[16 * AP];  // also the finish's reduction buffer
+    static_assert(sizeof(ldsA) >= 4 * kFredPitch * sizeof(float), "reduction buffer fits");
     const int nh = N2 / kHeadW;
     const int ntile = (T + 15) / 16;
-    const int item = blockIdx.x;
-    const int x = item & 7, j = item >> 3;
-    const int slab = (j / ntile) * 8 + x, tt = j % ntile;
+    const int item = xcd_item((N2 / kSlabW) * ntile);
+    // the first token to finish: its partials are requested before the slab,
+    // so that the finish does not wait for the slab's loads (the slab loads
+    // are unconditional for the same reason: padding workgroups read slab 0)
+    const int t1 = blockIdx.x;
+    const int n0 = (item >= 0 ? item / ntile : 0) * kSlabW;
     u4_t v[kR / 32];
-    stage_load<kR / 32>(v, Wb, N2, 0, kR, slab * kSlabW);
-    const int t = tt * 16 + c;
-    u4_t y[kR / 32];
+    if (t1 < T) {
+        FinPart r;
+        fin_load(r, P, S, T, t1, threadIdx.x >> 6);
+        fin_load_aux(r, gamma, pos, rt, t1);
+        stage_load<kR / 32, false>(v, Wb, N2, 0, kR, n0);
+        finish_token_from<E, true>(r, P, S, T, t1, eps, ckv, kpe, (float*)ldsA);
+    } else {
+        stage_load<kR / 32, false>(v, Wb, N2, 0, kR, n0);
+    }
+    for (int t = t1 + (int)gridDim.x; t < T; t += gridDim.x) {
+        __syncthreads();  // the reduction buffer is free again
+        finish_token<E, true>(P, S, T, t, gamma, pos, eps, rt, ckv, kpe, (float*)ldsA);
+    }
+    if (item < 0) return;
+    const int slab = item / ntile, t0 = (item % ntile) * 16;
+    const int nrows = T - t0 < 16 ? T - t0 : 16;
+    stage_store<kR / 32>(v, ldsW);
+    // the tile's compressed_kv rows: 16 rows x 128 eight-byte chunks
+    uint64_t y[8];
+    uint32_t pend = 0;
 #pragma unroll
-    for (int ch = 0; ch < kR / 32; ++ch)
-        y[ch] = (t < T) ? *(const u4_t*)(Y + (int64_t)t * kR + ch * 32 + 8 * g) : u4_t{0u, 0u, 0u, 0u};
-    stage_store<kR / 32>(v, lds);
+    for (int u = 0; u < 8; ++u) {
+        const int row = (threadIdx.x + 256 * u) >> 7;
+        y[u] = 0ull;
+        if (row < nrows) pend |= 1u << u;
+    }
+    for (uint32_t it = 0; pend != 0u && it < kSpinLimit; ++it) {
+        if (it != 0) __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int q = threadIdx.x + 256 * u, row = q >> 7, col = (q & 127) * 4;
+            if (pend & (1u << u)) y[u] = load_coherent64(ckv + (int64_t)(t0 + row) * kR + col);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if ((pend & (1u << u)) && !has_unset_half(y[u])) pend &= ~(1u << u);
+    }
+    __syncthreads();  // every wave is past the finish's use of ldsA
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int q = threadIdx.x + 256 * u, row = q >> 7, col = (q & 127) * 4;
+        *(uint64_t*)(ldsA + row * AP + col) = y[u];
+    }
     __syncthreads();
-    const int col = wave * 16 + c;
-    f4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ch = 0; ch < kR / 32; ++ch) acc = mfma_f<E>(y[ch], lds_col8(lds, ch * 32, wave * 16), acc);
-    // lane holds tokens tt*16 + 4g + i of slab column col
-    const int n = slab * kSlabW + col;
+    f4_t acc[1] = {f4_t{0.f, 0.f, 0.f, 0.f}};
+    slab_mma<E, 1, kR>(ldsW, ldsA, kR, acc);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int c = lane & 15, g = lane >> 4;
+    const int n = slab * kSlabW + wave * 16 + c;
     const int h = n >> 8, sl = n & 255;
     uint16_t* dst = ((sl < kDN) ? k_nope : value) + (int64_t)h * kDN + (sl & 127);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int tok = tt * 16 + 4 * g + i;
-        if (tok < T) dst[(int64_t)tok * nh * kDN] = f32_to_st<E>(acc[i]);
+        const int tok = t0 + 4 * g + i;
+        if (tok < T) dst[(int64_t)tok * nh * kDN] = f32_to_st<E>(acc[0][i]);
     }
 }
 
 // ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
-template <int E, int NTT>
+static inline int grid8(int nitems) { return 8 * ((nitems + 7) / 8); }
+
+template <int E, int NA>
+static void dec_kv_a_launch(const void* X, const void* Wa, int T, int H, float* P, int kw, int S,
+                            uint16_t* ckv, hipStream_t st) {
+    const dim3 ga(grid8(kSlabsA * S)), blk(256);
+    const uint16_t* x = (const uint16_t*)X;
+    const uint16_t* wa = (const uint16_t*)Wa;
+#define MLA_KVA(KW) \
+    hipLaunchKernelGGL((dec_kv_a_kernel<E, NA, KW>), ga, blk, 0, st, x, wa, T, H, S, P, ckv)
+    switch (kw) {
+        case 64: MLA_KVA(64); break;
+        case 128: MLA_KVA(128); break;
+        case 256: MLA_KVA(256); break;
+        default: MLA_KVA(512); break;
+    }
+#undef MLA_KVA
+}
+
+template <int E>
 static void dec_launch_t(const void* X, const void* Wa, const void* gamma, const void* Wb,
                          const int32_t* pos, int T, int H, int nh, float eps, const RopeTab& rt,
                          void* k_nope, void* value, void* k_pe, void* ckv, float* P,
                          const Plan& plan, hipStream_t st) {
-    const dim3 ga(kSlabsA * plan.s1), blk(256);
-    const uint16_t* x = (const uint16_t*)X;
-    const uint16_t* wa = (const uint16_t*)Wa;
-    switch (plan.kw) {
-        case 64: hipLaunchKernelGGL((dec_kv_a_kernel<E, NTT, 64>), ga, blk, 0, st, x, wa, T, H, P); break;
-        case 128: hipLaunchKernelGGL((dec_kv_a_kernel<E, NTT, 128>), ga, blk, 0, st, x, wa, T, H, P); break;
-        case 256: hipLaunchKernelGGL((dec_kv_a_kernel<E, NTT, 256>), ga, blk, 0, st, x, wa, T, H, P); break;
-        default: hipLaunchKernelGGL((dec_kv_a_kernel<E, NTT, 512>), ga, blk, 0, st, x, wa, T, H, P); break;
+    const int ntile = (T + 15) / 16;
+    switch (ntile) {
+        case 1: dec_kv_a_launch<E, 1>(X, Wa, T, H, P, plan.kw, plan.s1, (uint16_t*)ckv, st); break;
+        case 2: dec_kv_a_launch<E, 2>(X, Wa, T, H, P, plan.kw, plan.s1, (uint16_t*)ckv, st); break;
+        case 3: dec_kv_a_launch<E, 3>(X, Wa, T, H, P, plan.kw, plan.s1, (uint16_t*)ckv, st); break;
+        default: dec_kv_a_launch<E, 4>(X, Wa, T, H, P, plan.kw, plan.s1, (uint16_t*)ckv, st); break;
     }
-    hipLaunchKernelGGL(dec_finish_kernel<E>, dim3(T), blk, 0, st, (const float*)P, plan.s1, T,
-                       (const uint16_t*)gamma, pos, eps, rt, (uint16_t*)ckv, (uint16_t*)k_pe);
     const int N2 = nh * kHeadW;
-    const int nitems = (N2 / kSlabW) * ((T + 15) / 16);
-    hipLaunchKernelGGL(dec_kv_b_kernel<E>, dim3(nitems), blk, 0, st, (const uint16_t*)ckv,
-                       (const uint16_t*)Wb, T, N2, (uint16_t*)k_nope, (uint16_t*)value);
+    const int nitems = (N2 / kSlabW) * ntile;
+    if (nitems <= kFusedItems) {
+        hipLaunchKernelGGL(dec_fin_kv_b_kernel<E>, dim3(grid8(nitems)), dim3(256), 0, st,
+                           (const float*)P, plan.s1, T, (const uint16_t*)gamma, pos, eps, rt,
+                           (const uint16_t*)Wb, N2, (uint16_t*)ckv, (uint16_t*)k_pe,
+                           (uint16_t*)k_nope, (uint16_t*)value);
+        return;
+    }
+    hipLaunchKernelGGL(dec_finish_kernel<E>, dim3(T), dim3(256), 0, st, (const float*)P, plan.s1,
+                       T, (const uint16_t*)gamma, pos, eps, rt, (uint16_t*)ckv, (uint16_t*)k_pe);
+    hipLaunchKernelGGL((dec_kv_b_kernel<E, 1>), dim3(grid8(nitems)), dim3(256), 0, st,
+                       (const uint16_t*)ckv, (const uint16_t*)Wb, T, N2, (uint16_t*)k_nope,
+                       (uint16_t*)value);
 }
 
 hipError_t launch_fp_decode(int dt, const void* X, const void* Wa, const void* gamma,
@@ -289,21 +553,12 @@ hipError_t launch_fp_decode(int dt, const void* X, const void* Wa, const void* g
                             float eps, const RopeTab& rt, void* k_nope, void* value, void* k_pe,
                             void* ckv, void* ws, const Plan& plan, hipStream_t st) {
     float* P = (float*)((uint8_t*)ws + ws_fp(T, plan).p1);
-    const int t = (int)T;
-#define MLA_DEC(NT)                                                                          \
-    if (dt == kF16)                                                                          \
-        dec_launch_t<kF16, NT>(X, Wa, gamma, Wb, pos, t, H, nh, eps, rt, k_nope, value, k_pe, \
-                               ckv, P, plan, st);                                            \
-    else                                                                                     \
-        dec_launch_t<kBF16, NT>(X, Wa, gamma, Wb, pos, t, H, nh, eps, rt, k_nope, value,     \
-                                k_pe, ckv, P, plan, st);
-    switch ((t + 15) / 16) {
-        case 1: MLA_DEC(1) break;
-        case 2: MLA_DEC(2) break;
-        case 3: MLA_DEC(3) break;
-        default: MLA_DEC(4) break;
-    }
-#undef MLA_DEC
+    if (dt == kF16)
+        dec_launch_t<kF16>(X, Wa, gamma, Wb, pos, (int)T, H, nh, eps, rt, k_nope, value, k_pe, ckv,
+                           P, plan, st);
+    else
+        dec_launch_t<kBF16>(X, Wa, gamma, Wb, pos, (int)T, H, nh, eps, rt, k_nope, value, k_pe,
+                            ckv, P, plan, st);
     return hipGetLastError();
 }
 
