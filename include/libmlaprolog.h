@@ -29,9 +29,8 @@
  *   caller; the library never allocates, frees or keeps a pointer past the
  *   call.  Scratch memory is the caller's `workspace` (size from the
  *   matching *_workspace_size query).  A workspace needs no initialisation:
- *   every call writes whatever it later reads, including the
- *   synchronisation counters in its first 4096 bytes, so one workspace can
- *   serve any sequence of ordered calls (of either entry point).
+ *   every call writes whatever it later reads, so one workspace can serve
+ *   any sequence of ordered calls (of either entry point).
  * - Tensors are contiguous, row-major, in exactly the shapes given.  W_kv_b's
  *   columns come in per-head blocks [k_nope_h (dn) | value_h (dv)].
  *   Outputs are token-major: k_nope [T,nh,dn], value [T,nh,dv],

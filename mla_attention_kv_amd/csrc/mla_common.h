@@ -130,21 +130,14 @@ __device__ __forceinline__ void rope_cos_sin(int32_t pos, double f, float& cs, f
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Every workspace layout starts with 4 KiB of grid-synchronisation words
-// (zero between calls; the decode kernel resets them before it exits).
-constexpr size_t kSyncBytes = 4096;
-// most consumer workgroups of the fused decode kernel (each loops over its
-// (token tile, W_kv_b slab) items); a multiple of 8
-constexpr int kDecodeConsumers = 1024;
-
 // fp path: [s1][T][576] fp32 split-K partial sums of kv_a_proj
 struct WsFp {
     size_t p1, total;
 };
 inline WsFp ws_fp(int64_t T, const Plan& p) {
     WsFp w;
-    w.p1 = kSyncBytes;
-    w.total = kSyncBytes + align256((size_t)p.s1 * (size_t)T * kN1 * 4);
+    w.p1 = 0;
+    w.total = align256((size_t)p.s1 * (size_t)T * kN1 * 4);
     return w;
 }
 
@@ -155,7 +148,7 @@ struct WsW8 {
 };
 inline WsW8 ws_w8(int64_t T, int H, const Plan& p) {
     WsW8 w;
-    size_t o = kSyncBytes;
+    size_t o = 0;
     w.qx = o; o += align256((size_t)T * H);
     w.sx = o; o += align256((size_t)T * 4);
     w.p1 = o; o += align256((size_t)p.s1 * (size_t)T * kN1 * 4);

@@ -50,8 +50,10 @@ constexpr int kPitch = kSlabW + 8;         // LDS row pitch of a staged slab (ha
 // ---------------------------------------------------------------------------
 // Slab staging.  Rows [k0, k0 + 32*NR) of a 64-column slab starting at
 // column n0 of a row-major [K][ld] matrix: thread i loads 16 bytes (8
-// columns) of rows i/8 + 32 r, r < NR; rows at or past kmax load zeros.
-// stage_store writes them to LDS as [row][kPitch].
+// columns) of rows i/8 + 32 r, r < NR.  With CHECK, rows at or past kmax are
+// loaded from row kmax - 1 and zeroed when stored (no branch around a load,
+// so every load is in flight before the first wait).  stage_store writes
+// them to LDS as [row][kPitch].
 // ---------------------------------------------------------------------------
 template <int NR, bool CHECK = true>
 __device__ __forceinline__ void stage_load(u4_t (&v)[NR], const uint16_t* W, int64_t ld, int k0,
@@ -59,18 +61,20 @@ __device__ __forceinline__ void stage_load(u4_t (&v)[NR], const uint16_t* W, int
     const int q = threadIdx.x & 7, r0 = threadIdx.x >> 3;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-        const int k = k0 + r0 + 32 * r;
-        if (!CHECK || k < kmax)
-            v[r] = *(const u4_t*)(W + (int64_t)k * ld + n0 + 8 * q);
-        else
-            v[r] = u4_t{0u, 0u, 0u, 0u};
+        int k = k0 + r0 + 32 * r;
+        if (CHECK) k = k < kmax ? k : kmax - 1;
+        v[r] = *(const u4_t*)(W + (int64_t)k * ld + n0 + 8 * q);
     }
 }
-template <int NR>
-__device__ __forceinline__ void stage_store(const u4_t (&v)[NR], uint16_t* lds) {
+template <int NR, bool CHECK = true>
+__device__ __forceinline__ void stage_store(const u4_t (&v)[NR], uint16_t* lds, int k0 = 0,
+                                            int kmax = 0) {
     const int q = threadIdx.x & 7, r0 = threadIdx.x >> 3;
 #pragma unroll
-    for (int r = 0; r < NR; ++r) *(u4_t*)(lds + (r0 + 32 * r) * kPitch + 8 * q) = v[r];
+    for (int r = 0; r < NR; ++r) {
+        const bool ok = !CHECK || k0 + r0 + 32 * r < kmax;
+        *(u4_t*)(lds + (r0 + 32 * r) * kPitch + 8 * q) = ok ? v[r] : u4_t{0u, 0u, 0u, 0u};
+    }
 }
 // MFMA B operand from a staged slab: lane (16 g + c) gets column c0 + c,
 // rows kb + 8g .. kb + 8g + 7.  Two transposing LDS reads
@@ -93,7 +97,9 @@ __device__ __forceinline__ u4_t lds_col8(const uint16_t* lds, int kb, int c0) {
 // ---------------------------------------------------------------------------
 // Activation rows: rows [0, 16 NT) x columns [k0, k0 + KA) of a row-major
 // [rows][ld] matrix, loaded 16 bytes per chunk by the whole workgroup and
-// kept in LDS as [row][KA + 8]; rows >= nrows and columns >= kmax are zero.
+// kept in LDS as [row][KA + 8]; rows >= nrows and columns >= kmax are stored
+// as zeros (their loads read a valid chunk instead: nrows >= 1, kmax a
+// multiple of 8).
 // The +8 pitch puts the 16 rows an MFMA operand read touches on distinct
 // banks.  Each wave then reads its A operands (lane 16g + c: row c, 8
 // consecutive K at 8g) with one 16-byte LDS read.
@@ -112,21 +118,24 @@ __device__ __forceinline__ void arows_load(u4_t (&v)[NP], const uint16_t* A, int
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
         const int q = threadIdx.x + 256 * u;
-        const int row = q / CPR, k = k0 + 8 * (q % CPR);
-        v[u] = (q < ARows<NT, KA>::kChunks && row < nrows && k < kmax)
-                   ? *(const u4_t*)(A + (int64_t)row * ld + k)
-                   : u4_t{0u, 0u, 0u, 0u};
+        int row = q / CPR, k = k0 + 8 * (q % CPR);
+        row = row < nrows ? row : nrows - 1;
+        k = k < kmax ? k : kmax - 8;
+        v[u] = *(const u4_t*)(A + (int64_t)row * ld + k);
     }
 }
 template <int NT, int KA, int NP>
-__device__ __forceinline__ void arows_store(const u4_t (&v)[NP], uint16_t* lds) {
+__device__ __forceinline__ void arows_store(const u4_t (&v)[NP], uint16_t* lds, int nrows, int k0,
+                                            int kmax) {
     static_assert(NP == ARows<NT, KA>::kPer, "chunks per thread");
     constexpr int CPR = KA / 8;
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
         const int q = threadIdx.x + 256 * u;
+        const int row = q / CPR, k = k0 + 8 * (q % CPR);
         if (q < ARows<NT, KA>::kChunks)
-            *(u4_t*)(lds + (q / CPR) * ARows<NT, KA>::kPitchA + 8 * (q % CPR)) = v[u];
+            *(u4_t*)(lds + row * ARows<NT, KA>::kPitchA + 8 * (q % CPR)) =
+                (row < nrows && k < kmax) ? v[u] : u4_t{0u, 0u, 0u, 0u};
     }
 }
 
@@ -170,7 +179,9 @@ template <int E, int NT, int KW>
 __global__ __launch_bounds__(256) void dec_kv_a_kernel(const uint16_t* __restrict__ X,
                                                        const uint16_t* __restrict__ Wa, int T,
                                                        int H, int S, float* __restrict__ P,
-                                                       uint16_t* __restrict__ ckv) {
+                                                       uint16_t* __restrict__ ckv,
+                                                       const uint16_t* __restrict__ Wb, int N2,
+                                                       int ntile) {
     __shared__ __align__(16) uint16_t ldsW[KW * kPitch];
     __shared__ __align__(16) uint16_t ldsA[NT * 16 * ARows<NT, KW>::kPitchA];
     // compressed_kv rows start out as the "not written yet" pattern that the
@@ -186,8 +197,30 @@ __global__ __launch_bounds__(256) void dec_kv_a_kernel(const uint16_t* __restric
     u4_t a[ARows<NT, KW>::kPer];
     stage_load<KW / 32>(v, Wa, kN1, k0, H, slab * kSlabW);
     arows_load<NT, KW>(a, X, H, T, k0, H);
-    stage_store<KW / 32>(v, ldsW);
-    arows_store<NT, KW>(a, ldsA);
+    // Touch the 128-byte lines of the W_kv_b slabs that the fused
+    // finish + kv_b_proj launch streams on this XCD (up to four per thread),
+    // so that its slab loads
+    // find them in this XCD's L2 or in the memory-side cache instead of
+    // competing for HBM with its partial-sum loads.  The value is consumed
+    // only by a store that no valid call makes.
+    uint32_t touch[4];
+    {
+        const int nitems = (N2 / kSlabW) * ntile;
+        const int per = (nitems + 7) / 8, x = blockIdx.x & 7;
+        const int i0 = x * per, i1 = min(nitems, i0 + per);
+        const bool on = Wb != nullptr && i0 < i1;
+        const int s0 = on ? i0 / ntile : 0, nlines = on ? ((i1 - 1) / ntile - s0 + 1) * kR : 1;
+        const int stride = (gridDim.x >> 3) * 256;
+        int l = (blockIdx.x >> 3) * 256 + threadIdx.x;
+#pragma unroll
+        for (int u = 0; u < 4; ++u, l += stride) {
+            const int lc = l < nlines ? l : nlines - 1;
+            const uint16_t* tp = on ? Wb + (int64_t)(lc % kR) * N2 + (s0 + lc / kR) * kSlabW : X;
+            touch[u] = *(const uint32_t*)tp;
+        }
+    }
+    stage_store<KW / 32>(v, ldsW, k0, H);
+    arows_store<NT, KW>(a, ldsA, T, k0, H);
     __syncthreads();
     f4_t acc[NT];
 #pragma unroll
@@ -204,6 +237,7 @@ __global__ __launch_bounds__(256) void dec_kv_a_kernel(const uint16_t* __restric
             const int t = tt * 16 + 4 * g + i;
             if (t < T) Ps[(int64_t)t * kN1] = acc[tt][i];
         }
+    if (((touch[0] ^ touch[1]) ^ (touch[2] ^ touch[3])) == 0x9E3779B9u && T < 0) P[0] = 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -377,8 +411,8 @@ __global__ __launch_bounds__(256) void dec_kv_b_kernel(const uint16_t* __restric
     u4_t a[ARows<NT, kR>::kPer];
     stage_load<kR / 32, false>(v, Wb, N2, 0, kR, slab * kSlabW);
     arows_load<NT, kR>(a, Y + (int64_t)t0 * kR, kR, T - t0, 0, kR);
-    stage_store<kR / 32>(v, ldsW);
-    arows_store<NT, kR>(a, ldsA);
+    stage_store<kR / 32, false>(v, ldsW);
+    arows_store<NT, kR>(a, ldsA, T - t0, 0, kR);
     __syncthreads();
     f4_t acc[NT];
 #pragma unroll
@@ -456,7 +490,7 @@ __global__ __launch_bounds__(256) void dec_fin_kv_b_kernel(
     if (item < 0) return;
     const int slab = item / ntile, t0 = (item % ntile) * 16;
     const int nrows = T - t0 < 16 ? T - t0 : 16;
-    stage_store<kR / 32>(v, ldsW);
+    stage_store<kR / 32, false>(v, ldsW);
     // the tile's compressed_kv rows: 16 rows x 128 eight-byte chunks
     uint64_t y[8];
     uint32_t pend = 0;
@@ -505,12 +539,14 @@ static inline int grid8(int nitems) { return 8 * ((nitems + 7) / 8); }
 
 template <int E, int NA>
 static void dec_kv_a_launch(const void* X, const void* Wa, int T, int H, float* P, int kw, int S,
-                            uint16_t* ckv, hipStream_t st) {
+                            uint16_t* ckv, const uint16_t* wb, int N2, hipStream_t st) {
+    const int ntile = (T + 15) / 16;
     const dim3 ga(grid8(kSlabsA * S)), blk(256);
     const uint16_t* x = (const uint16_t*)X;
     const uint16_t* wa = (const uint16_t*)Wa;
 #define MLA_KVA(KW) \
-    hipLaunchKernelGGL((dec_kv_a_kernel<E, NA, KW>), ga, blk, 0, st, x, wa, T, H, S, P, ckv)
+    hipLaunchKernelGGL((dec_kv_a_kernel<E, NA, KW>), ga, blk, 0, st, x, wa, T, H, S, P, ckv, wb, N2, \
+                       ntile)
     switch (kw) {
         case 64: MLA_KVA(64); break;
         case 128: MLA_KVA(128); break;
@@ -526,15 +562,19 @@ static void dec_launch_t(const void* X, const void* Wa, const void* gamma, const
                          void* k_nope, void* value, void* k_pe, void* ckv, float* P,
                          const Plan& plan, hipStream_t st) {
     const int ntile = (T + 15) / 16;
-    switch (ntile) {
-        case 1: dec_kv_a_launch<E, 1>(X, Wa, T, H, P, plan.kw, plan.s1, (uint16_t*)ckv, st); break;
-        case 2: dec_kv_a_launch<E, 2>(X, Wa, T, H, P, plan.kw, plan.s1, (uint16_t*)ckv, st); break;
-        case 3: dec_kv_a_launch<E, 3>(X, Wa, T, H, P, plan.kw, plan.s1, (uint16_t*)ckv, st); break;
-        default: dec_kv_a_launch<E, 4>(X, Wa, T, H, P, plan.kw, plan.s1, (uint16_t*)ckv, st); break;
-    }
     const int N2 = nh * kHeadW;
     const int nitems = (N2 / kSlabW) * ntile;
-    if (nitems <= kFusedItems) {
+    const bool fused = nitems <= kFusedItems;
+    // W_kv_b lines are touched ahead only for the fused launch
+    const uint16_t* wb = fused ? (const uint16_t*)Wb : nullptr;
+    uint16_t* y = (uint16_t*)ckv;
+    switch (ntile) {
+        case 1: dec_kv_a_launch<E, 1>(X, Wa, T, H, P, plan.kw, plan.s1, y, wb, N2, st); break;
+        case 2: dec_kv_a_launch<E, 2>(X, Wa, T, H, P, plan.kw, plan.s1, y, wb, N2, st); break;
+        case 3: dec_kv_a_launch<E, 3>(X, Wa, T, H, P, plan.kw, plan.s1, y, wb, N2, st); break;
+        default: dec_kv_a_launch<E, 4>(X, Wa, T, H, P, plan.kw, plan.s1, y, wb, N2, st); break;
+    }
+    if (fused) {
         hipLaunchKernelGGL(dec_fin_kv_b_kernel<E>, dim3(grid8(nitems)), dim3(256), 0, st,
                            (const float*)P, plan.s1, T, (const uint16_t*)gamma, pos, eps, rt,
                            (const uint16_t*)Wb, N2, (uint16_t*)ckv, (uint16_t*)k_pe,

@@ -230,9 +230,9 @@ def test_garbage_workspace(dev, path, kind):
 
 @pytest.mark.parametrize("T", [1, 64])
 def test_decode_many_calls_one_workspace(dev, T):
-    """The decode launches clear their own synchronisation counters: many
-    back-to-back calls on one workspace that starts out filled with garbage
-    (inputs changing between calls) all give the oracle's result."""
+    """Many back-to-back decode calls on one workspace that starts out filled
+    with garbage (inputs changing between calls) all give the oracle's
+    result."""
     import mla_attention_kv_amd as mla
 
     ws = torch.full((mla.mla_kv_prolog_workspace_size(T, mla.Dims(H=2048, nh=16)),), 0xA5,
