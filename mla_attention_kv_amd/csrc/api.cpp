@@ -35,6 +35,7 @@ Plan make_plan(int64_t T, int H, bool int8, int path) {
     p.path = path;
     p.stream = (!int8 && path == 0 && T <= kDecodeMaxT) ? 1 : 0;
     p.kw = 0;
+    p.dma1 = 0;
     if (p.stream) {
         // weight-streaming kv_a_proj: 9 slabs x S splits of kw rows each;
         // wider splits when the split-K partials (S * T rows of 576 floats)
@@ -55,9 +56,17 @@ Plan make_plan(int64_t T, int H, bool int8, int path) {
         p.bn2 = 64;
     } else {
         p.bm1 = 128;
-        // kv_b_proj: 256 x 128 tiles once there are enough of them to fill the chip
-        p.bm2 = (!int8 && T >= 2048) ? 256 : 128;
+        // kv_b_proj: the pipelined 256 x 128 kernel for fp16 / bf16, 128 x 128
+        // tiles for int8
+        p.bm2 = 128;
         p.bn2 = 128;
+    }
+    if (!int8 && path == 1 && T >= 4096) {
+        // enough 64 x 192 tiles (3 per 64 tokens) to occupy the chip without
+        // splitting K
+        p.dma1 = 1;
+        p.s1 = 1;
+        return p;
     }
     // split kv_a_proj's K so that at least ~256 workgroups stream W_kv_a,
     // keeping at least two K slabs per split

@@ -95,6 +95,7 @@ struct Plan {
     int bm1, s1;    // kv_a_proj: rows per tile (tiled), split-K count
     int kw;         // streaming kv_a_proj: K rows per producer workgroup
     int bm2, bn2;   // kv_b_proj tile (tiled)
+    int dma1;       // kv_a_proj by the direct-to-LDS pipelined GEMM (no split-K)
 };
 
 // RoPE inverse frequencies theta^(-2i/dr), i < dr/2, evaluated once per call

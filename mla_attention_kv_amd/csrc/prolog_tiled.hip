@@ -361,6 +361,272 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Pipelined fp16 / bf16 GEMM with direct-to-LDS loads.
+// C[M, N] = A[M, K] . B[K, N]; A, B row-major; K a multiple of 64 (one slab =
+// 64 K elements), N a multiple of BN.
+//
+// Each slab of A (BM rows x 128 bytes) and of B (64 rows x BN columns) goes
+// from global memory straight into LDS (global_load_lds_dwordx4: one wave
+// instruction fills 1 KB of LDS, lane l the 16 bytes at l * 16), so the
+// prefetch depth costs no registers: STAGES slabs live in STAGES separate
+// LDS arrays, up to STAGES - 1 of them in flight while one is multiplied.
+// A wave waits for its own copies of the next slab (s_waitcnt vmcnt), then a
+// barrier makes every wave's copies visible; the barrier also frees the
+// stage multiplied last, which then receives the slab STAGES - 1 ahead.  The
+// K loop is unrolled by STAGES so that every LDS array is named statically.
+//
+// LDS layouts (bank-conflict swizzles, done by choosing which global chunk
+// each lane copies, since a copy's LDS destination is fixed):
+//   A stage: [BM rows][8 chunks of 16 bytes]; chunk c of row r sits at
+//            position c ^ ((r >> 1) & 7).  An MFMA A operand (16 rows, one
+//            chunk each) then touches 16 distinct 16-byte bank groups.
+//   B stage: [64 k rows][BN columns]; 16-byte chunk c of row k sits at
+//            c ^ (2 (k & 3) + 8 ((k >> 3) & 1)) (c ^ 2 (k & 3) when a row is
+//            not a multiple of 16 chunks).  The B operand (column n,
+//            8 consecutive k) comes from two transposing reads
+//            (ds_read_b64_tr_b16) of 4 rows x 4 columns per 16-lane group.
+// Waves are laid out WAVES_M x WAVES_N, each owning a (BM / WAVES_M) x
+// (BN / WAVES_N) block of 16 x 16 MFMA tiles.  Tile order is the same
+// XCD-aware grouped order as gemm_tiled_kernel.  Results go from the
+// accumulators straight to global memory (lane: one row, four consecutive
+// columns).
+// ---------------------------------------------------------------------------
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_tr16(const uint8_t* p) {
+    const v4s_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s_t*)(p));
+    return __builtin_bit_cast(uint2, r);
+}
+// One 16-byte-per-lane copy from global memory into LDS (the wave's 64
+// lanes fill lds .. lds + 1023; lds is wave-uniform).  Issued from inline
+// assembly so that the compiler, which cannot tell the LDS stages apart,
+// does not wait for these copies before unrelated LDS reads; M0 (the LDS
+// base the instruction reads at issue) is saved and restored around it.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "s"(lds), "v"(g)
+        : "memory");
+}
+// Wait until at most N of this wave's copies are outstanding, then
+// barrier; a compiler memory barrier as well.
+template <int N>
+__device__ __forceinline__ void wait_copies_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(size_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+// B-row chunk swizzle: rows of 16 chunks or more (BN >= 128) use
+// 2 (k & 3) + 8 ((k >> 3) & 1); other rows (BN = 64 or 192) stay inside
+// aligned groups of 8 chunks with 2 (k & 3).
+template <int BRB>
+__device__ __forceinline__ int bswz(int k) {
+    if constexpr (BRB % 256 == 0) return 2 * (k & 3) + 8 * ((k >> 3) & 1);
+    else return 2 * (k & 3);
+}
+
+template <int E, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int GM, class Epi>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_lds_kernel(
+    const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
+    int M, int Nt, int nk, Epi epi) {
+    static_assert(E == kF16 || E == kBF16, "16-bit operands");
+    constexpr int NW = WAVES_M * WAVES_N;
+    constexpr int A_ST = BM * 128;            // A bytes per stage
+    constexpr int BRB = BN * 2;               // bytes per B row
+    constexpr int B_ST = 64 * BRB;            // B bytes per stage
+    constexpr int STAGE = A_ST + B_ST;
+    constexpr int A_PW = A_ST / 1024 / NW, B_PW = B_ST / 1024 / NW;
+    static_assert(A_PW * NW * 1024 == A_ST && B_PW * NW * 1024 == B_ST, "even copy split");
+    static_assert(BRB % 128 == 0, "whole groups of 8 chunks per B row");
+    constexpr int PW = A_PW + B_PW;           // copy instructions per wave per slab
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, TM = WM / 16, TN = WN / 16;
+    static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+    __shared__ __align__(1024) uint8_t st0[STAGE];
+    __shared__ __align__(1024) uint8_t st1[STAGE];
+    __shared__ __align__(1024) uint8_t st2[STAGES > 2 ? STAGE : 16];
+    __shared__ __align__(1024) uint8_t st3[STAGES > 3 ? STAGE : 16];
+
+    // ---- tiles of this workgroup: workgroup b runs on XCD b % 8; XCD x
+    // owns the contiguous tile range [x per, (x + 1) per) of the grouped
+    // order and its workgroups walk it in steps of (grid / 8), so that the
+    // output stores of one tile drain while the next tile is loaded and
+    // multiplied
+    const int Mt = (M + BM - 1) / BM;
+    const int tiles = Mt * Nt;
+    const int per = (tiles + 7) / 8;
+    const int x = blockIdx.x & 7, nwx = gridDim.x >> 3;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int tl = blockIdx.x >> 3; tl < per; tl += nwx) {
+    const int t = x * per + tl;
+    if (t >= tiles) break;
+    const int grp = t / (GM * Nt);
+    const int gm = min(GM, Mt - grp * GM);
+    const int q = t - grp * GM * Nt;
+    const int m0 = (grp * GM + q % gm) * BM, n0 = (q / gm) * BN;
+    // every wave has its last reads of the previous tile back before any
+    // copy of this tile lands in the stages
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    // ---- copy sources: instruction u of this wave covers LDS bytes
+    // [(wave + NW u) KB, +1 KB) of the A (resp. B) part of a stage
+    const uint8_t* asrc[A_PW];
+#pragma unroll
+    for (int u = 0; u < A_PW; ++u) {
+        const int row = (wave + NW * u) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ ((row >> 1) & 7);
+        const int grow = min(m0 + row, M - 1);
+        asrc[u] = A + (int64_t)grow * lda + c * 16;
+    }
+    const uint8_t* bsrc[B_PW];
+#pragma unroll
+    for (int u = 0; u < B_PW; ++u) {
+        const int byte = (wave + NW * u) * 1024 + lane * 16;
+        const int k = byte / BRB, pos = (byte % BRB) / 16;
+        const int c = pos ^ bswz<BRB>(k);
+        bsrc[u] = B + (int64_t)k * ldb + (int64_t)n0 * 2 + c * 16;
+    }
+    const int64_t bstep = 64 * ldb;           // bytes of B per slab
+
+    // wave-uniform LDS offset of this wave's first 1 KB block in a stage
+    const uint32_t wofs = (uint32_t)__builtin_amdgcn_readfirstlane(wave * 1024);
+    auto issue = [&](int kc, const uint8_t* stg) {
+        const uint32_t base = lds_addr(stg) + wofs;
+#pragma unroll
+        for (int u = 0; u < A_PW; ++u)
+            dma16(asrc[u] + (int64_t)kc * 128, base + u * NW * 1024);
+#pragma unroll
+        for (int u = 0; u < B_PW; ++u)
+            dma16(bsrc[u] + kc * bstep, base + A_ST + u * NW * 1024);
+    };
+
+    const int wm0 = (wave / WAVES_N) * WM, wn0 = (wave % WAVES_N) * WN;
+    f4_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int l16 = lane & 15, g = lane >> 4;
+    // operand fragments of one K step (32 K elements) in two register sets
+    u4_t fa[2][TM], fb[2][TN];
+    auto rd = [&](const uint8_t* stg, int ks, int buf) {
+        const uint8_t* As = stg;
+        const uint8_t* Bs = stg + A_ST;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int row = wm0 + i * 16 + l16;
+            const int c = (ks * 4 + g) ^ ((row >> 1) & 7);
+            fa[buf][i] = *(const u4_t*)(As + row * 128 + c * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            // lane (16 g + s): rows 32 ks + 8 g + s / 4 (+ 4), columns
+            // wn0 + 16 j + 4 (s % 4) .. + 3
+            const int k = ks * 32 + g * 8 + (l16 >> 2);
+            const int colb = (wn0 + j * 16 + 4 * (l16 & 3)) * 2;
+            const int c = colb >> 4, off = colb & 15;
+            const uint2 lo = lds_tr16(Bs + k * BRB + ((c ^ bswz<BRB>(k)) << 4) + off);
+            const uint2 hi = lds_tr16(Bs + (k + 4) * BRB + ((c ^ bswz<BRB>(k + 4)) << 4) + off);
+            fb[buf][j] = u4_t{lo.x, lo.y, hi.x, hi.y};
+        }
+    };
+    auto mma = [&](int buf) {
+        // operands swapped (C^T = B^T A^T): lane l then holds output row
+        // (l % 16) and the 4 consecutive output columns 4 (l / 16) + v
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = mfma16<E>(fb[buf][j], fa[buf][i], acc[i][j]);
+    };
+
+    // Software pipeline over (slab, K step): the reads of the next K step are
+    // in flight while the MFMAs of the current one run, and the barrier that
+    // hands over the next slab sits between the two K steps of a slab:
+    //   rd(k,1)  mma(k,0)  [wait slab k+1, barrier, copy slab k+S]  rd(k+1,0)  mma(k,1)
+    // Before the barrier a wave has all of its reads of slab k back in
+    // registers (lgkmcnt 0), so the copy into slab k's stage that follows
+    // the barrier overwrites nothing still being read.
+    auto step = [&](int kc, const uint8_t* cur, const uint8_t* nxt) {
+        rd(cur, 1, 1);
+        mma(0);
+        if (kc + 1 < nk) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (kc + STAGES - 1 < nk) wait_copies_barrier<(STAGES - 2) * PW>();
+            else wait_copies_barrier<0>();
+            if (kc + STAGES < nk) issue(kc + STAGES, cur);
+            rd(nxt, 0, 0);
+        }
+        mma(1);
+    };
+
+#pragma unroll
+    for (int p = 0; p < STAGES - 1; ++p)
+        if (p < nk) issue(p, p == 0 ? st0 : (p == 1 ? st1 : st2));
+    // slab 0 in place (slabs 1 .. STAGES - 2 may still be on their way), slab
+    // STAGES - 1 requested, first K step read
+    if (STAGES - 2 < nk) wait_copies_barrier<(STAGES - 2) * PW>();
+    else wait_copies_barrier<0>();
+    if (STAGES - 1 < nk) issue(STAGES - 1, STAGES == 2 ? st1 : (STAGES == 3 ? st2 : st3));
+    rd(st0, 0, 0);
+    // slab kc lives in stage kc % STAGES; step(kc, its stage, the stage of
+    // slab kc + 1); the stage of kc then receives slab kc + STAGES
+    for (int kc = 0; kc < nk; kc += STAGES) {
+        if constexpr (STAGES == 2) {
+            step(kc, st0, st1);
+            if (kc + 1 < nk) step(kc + 1, st1, st0);
+        } else if constexpr (STAGES == 3) {
+            step(kc, st0, st1);
+            if (kc + 1 < nk) step(kc + 1, st1, st2);
+            if (kc + 2 < nk) step(kc + 2, st2, st0);
+        } else {
+            step(kc, st0, st1);
+            if (kc + 1 < nk) step(kc + 1, st1, st2);
+            if (kc + 2 < nk) step(kc + 2, st2, st3);
+            if (kc + 3 < nk) step(kc + 3, st3, st0);
+        }
+    }
+
+    // ---- epilogue: lane holds output row (l16) and columns 4 g .. 4 g + 3 of
+    // each 16 x 16 tile
+    typedef typename Epi::out_t out_t;
+    float cs[TN][4];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) cs[j][v] = epi.col_scale(n0 + wn0 + j * 16 + g * 4 + v);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int row = m0 + wm0 + i * 16 + l16;
+        if (row >= M) continue;
+        const typename Epi::row_t rs = epi.row_scale(row);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int col = n0 + wn0 + j * 16 + g * 4;
+            out_t o[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) o[v] = epi.value(row, col + v, acc[i][j][v], rs, cs[j][v]);
+            if constexpr (sizeof(out_t) == 2)
+                *(u2_t*)epi.ptr(row, col, 0) = u2_t{(uint32_t)o[0] | ((uint32_t)o[1] << 16),
+                                                    (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
+            else
+                *(u4_t*)epi.ptr(row, col, 0) = u4_t{__builtin_bit_cast(uint32_t, o[0]),
+                                                    __builtin_bit_cast(uint32_t, o[1]),
+                                                    __builtin_bit_cast(uint32_t, o[2]),
+                                                    __builtin_bit_cast(uint32_t, o[3])};
+        }
+    }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Per-token finish of kv_a_proj, fp16/bf16 path.  One wave per token: lane l
 // owns latent columns 8l..8l+7 and rope column l.
 //   c, p  = sum of the split-K partials (split order ascending)
@@ -556,6 +822,22 @@ static void gemm_launch(const void* A, int64_t lda, const void* B, int64_t ldb, 
                        N / BN, S, per, kslabs, epi);
 }
 
+constexpr int64_t kPersistentGrid = 256;  // MI355X compute units
+
+template <int E, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, class Epi>
+static void gemm_lds_launch(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M,
+                            int N, int K, Epi epi, hipStream_t st) {
+    constexpr int GM = 4;
+    const int64_t tiles = ((M + BM - 1) / BM) * (N / BN);
+    // one workgroup per CU (the stages fill most of the LDS); each walks
+    // its XCD's tiles
+    const int64_t grid = std::min<int64_t>(((tiles + 7) / 8) * 8, kPersistentGrid);
+    hipLaunchKernelGGL((gemm_lds_kernel<E, BM, BN, WAVES_M, WAVES_N, STAGES, GM, Epi>),
+                       dim3((unsigned)grid), dim3(64 * WAVES_M * WAVES_N), 0, st,
+                       (const uint8_t*)A, lda, (const uint8_t*)B, ldb, (int)M, N / BN, K / 64,
+                       epi);
+}
+
 // kv_a_proj tiles: BN = 64 always (576 = 9 x 64)
 template <int E, class Epi>
 static void gemm1_dispatch(int bm, const void* A, int64_t lda, const void* B, int64_t M,
@@ -575,9 +857,11 @@ static void gemm2_dispatch(int bm, int bn, const void* A, int64_t lda, const voi
                            int N2, Epi epi, hipStream_t st) {
     const int64_t ldb = (int64_t)N2 * ((E == kI8) ? 1 : 2);
     const int kslabs = (E == kI8) ? kR / 128 : kR * 2 / 128;
-    if (bm == 256) {
-        gemm_launch<E, 256, 128, 128, 64>(A, lda, B, ldb, M, N2, kslabs, 1, epi, st);
-        return;
+    if constexpr (E != kI8) {
+        if (bm >= 128) {
+            gemm_lds_launch<E, 256, 128, 4, 2, 3>(A, lda, B, ldb, M, N2, kR, epi, st);
+            return;
+        }
     }
     if (bn == 128) {
         gemm_launch<E, 128, 128, 64, 64>(A, lda, B, ldb, M, N2, kslabs, 1, epi, st);
@@ -611,8 +895,12 @@ static hipError_t launch_fp_t(const void* X, const void* Wa, const void* gamma, 
     const WsFp w = ws_fp(T, plan);
     float* P1 = (float*)((uint8_t*)ws + w.p1);
     const int kslabs1 = H * 2 / 128;
-    gemm1_dispatch<E>(plan.bm1, X, (int64_t)H * 2, Wa, T, kslabs1, plan.s1,
-                      EpiPartialF32{P1, T}, st);
+    if (plan.dma1)
+        gemm_lds_launch<E, 64, 192, 1, 4, 4>(X, (int64_t)H * 2, Wa, (int64_t)kN1 * 2, T, kN1, H,
+                                             EpiPartialF32{P1, T}, st);
+    else
+        gemm1_dispatch<E>(plan.bm1, X, (int64_t)H * 2, Wa, T, kslabs1, plan.s1,
+                          EpiPartialF32{P1, T}, st);
     launch_finish_fp(E, P1, plan.s1, T, gamma, pos, eps, rt, ckv, k_pe, st);
     const int N2 = nh * kHeadW;
     gemm2_dispatch<E>(plan.bm2, plan.bn2, ckv, (int64_t)kR * 2, Wb, T, N2,

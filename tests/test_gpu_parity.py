@@ -133,6 +133,14 @@ def test_minimal_hidden_single_head(dev):
     check_full(w, dev, "H64_nh1")
 
 
+def test_long_prefill_ragged_tail(dev):
+    # long prefill (kv_a_proj without split-K, pipelined kv_b_proj) with a
+    # token count that leaves partial tiles; every row checked
+    d = Dims(H=512, nh=2)
+    w = workloads.make_custom(d, 4100, dtype="f16", seed=430, wstd=0.03, max_pos=8192)
+    check_full(w, dev, "prefill_T4100", path=1)
+
+
 @pytest.mark.parametrize("T", [17, 40, 64])
 def test_odd_head_count_multi_tile(dev, T):
     # kv_b_proj work items over an odd number of 64-column slab pairs with
