@@ -179,9 +179,7 @@ template <int E, int NT, int KW>
 __global__ __launch_bounds__(256) void dec_kv_a_kernel(const uint16_t* __restrict__ X,
                                                        const uint16_t* __restrict__ Wa, int T,
                                                        int H, int S, float* __restrict__ P,
-                                                       uint16_t* __restrict__ ckv,
-                                                       const uint16_t* __restrict__ Wb, int N2,
-                                                       int ntile) {
+                                                       uint16_t* __restrict__ ckv) {
     __shared__ __align__(16) uint16_t ldsW[KW * kPitch];
     __shared__ __align__(16) uint16_t ldsA[NT * 16 * ARows<NT, KW>::kPitchA];
     // compressed_kv rows start out as the "not written yet" pattern that the
@@ -197,28 +195,6 @@ __global__ __launch_bounds__(256) void dec_kv_a_kernel(const uint16_t* __restric
     u4_t a[ARows<NT, KW>::kPer];
     stage_load<KW / 32>(v, Wa, kN1, k0, H, slab * kSlabW);
     arows_load<NT, KW>(a, X, H, T, k0, H);
-    // Touch the 128-byte lines of the W_kv_b slabs that the fused
-    // finish + kv_b_proj launch streams on this XCD (up to four per thread),
-    // so that its slab loads
-    // find them in this XCD's L2 or in the memory-side cache instead of
-    // competing for HBM with its partial-sum loads.  The value is consumed
-    // only by a store that no valid call makes.
-    uint32_t touch[4];
-    {
-        const int nitems = (N2 / kSlabW) * ntile;
-        const int per = (nitems + 7) / 8, x = blockIdx.x & 7;
-        const int i0 = x * per, i1 = min(nitems, i0 + per);
-        const bool on = Wb != nullptr && i0 < i1;
-        const int s0 = on ? i0 / ntile : 0, nlines = on ? ((i1 - 1) / ntile - s0 + 1) * kR : 1;
-        const int stride = (gridDim.x >> 3) * 256;
-        int l = (blockIdx.x >> 3) * 256 + threadIdx.x;
-#pragma unroll
-        for (int u = 0; u < 4; ++u, l += stride) {
-            const int lc = l < nlines ? l : nlines - 1;
-            const uint16_t* tp = on ? Wb + (int64_t)(lc % kR) * N2 + (s0 + lc / kR) * kSlabW : X;
-            touch[u] = *(const uint32_t*)tp;
-        }
-    }
     stage_store<KW / 32>(v, ldsW, k0, H);
     arows_store<NT, KW>(a, ldsA, T, k0, H);
     __syncthreads();
@@ -237,7 +213,6 @@ __global__ __launch_bounds__(256) void dec_kv_a_kernel(const uint16_t* __restric
             const int t = tt * 16 + 4 * g + i;
             if (t < T) Ps[(int64_t)t * kN1] = acc[tt][i];
         }
-    if (((touch[0] ^ touch[1]) ^ (touch[2] ^ touch[3])) == 0x9E3779B9u && T < 0) P[0] = 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -539,14 +514,12 @@ static inline int grid8(int nitems) { return 8 * ((nitems + 7) / 8); }
 
 template <int E, int NA>
 static void dec_kv_a_launch(const void* X, const void* Wa, int T, int H, float* P, int kw, int S,
-                            uint16_t* ckv, const uint16_t* wb, int N2, hipStream_t st) {
-    const int ntile = (T + 15) / 16;
+                            uint16_t* ckv, hipStream_t st) {
     const dim3 ga(grid8(kSlabsA * S)), blk(256);
     const uint16_t* x = (const uint16_t*)X;
     const uint16_t* wa = (const uint16_t*)Wa;
 #define MLA_KVA(KW) \
-    hipLaunchKernelGGL((dec_kv_a_kernel<E, NA, KW>), ga, blk, 0, st, x, wa, T, H, S, P, ckv, wb, N2, \
-                       ntile)
+    hipLaunchKernelGGL((dec_kv_a_kernel<E, NA, KW>), ga, blk, 0, st, x, wa, T, H, S, P, ckv)
     switch (kw) {
         case 64: MLA_KVA(64); break;
         case 128: MLA_KVA(128); break;
@@ -565,14 +538,12 @@ static void dec_launch_t(const void* X, const void* Wa, const void* gamma, const
     const int N2 = nh * kHeadW;
     const int nitems = (N2 / kSlabW) * ntile;
     const bool fused = nitems <= kFusedItems;
-    // W_kv_b lines are touched ahead only for the fused launch
-    const uint16_t* wb = fused ? (const uint16_t*)Wb : nullptr;
     uint16_t* y = (uint16_t*)ckv;
     switch (ntile) {
-        case 1: dec_kv_a_launch<E, 1>(X, Wa, T, H, P, plan.kw, plan.s1, y, wb, N2, st); break;
-        case 2: dec_kv_a_launch<E, 2>(X, Wa, T, H, P, plan.kw, plan.s1, y, wb, N2, st); break;
-        case 3: dec_kv_a_launch<E, 3>(X, Wa, T, H, P, plan.kw, plan.s1, y, wb, N2, st); break;
-        default: dec_kv_a_launch<E, 4>(X, Wa, T, H, P, plan.kw, plan.s1, y, wb, N2, st); break;
+        case 1: dec_kv_a_launch<E, 1>(X, Wa, T, H, P, plan.kw, plan.s1, y, st); break;
+        case 2: dec_kv_a_launch<E, 2>(X, Wa, T, H, P, plan.kw, plan.s1, y, st); break;
+        case 3: dec_kv_a_launch<E, 3>(X, Wa, T, H, P, plan.kw, plan.s1, y, st); break;
+        default: dec_kv_a_launch<E, 4>(X, Wa, T, H, P, plan.kw, plan.s1, y, st); break;
     }
     if (fused) {
         hipLaunchKernelGGL(dec_fin_kv_b_kernel<E>, dim3(grid8(nitems)), dim3(256), 0, st,
