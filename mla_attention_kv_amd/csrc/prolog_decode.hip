@@ -2,29 +2,26 @@
 // batches (decode: a few sequences x one or two query tokens).
 //
 // At decode sizes the prolog is bound by reading the two weight matrices
-// once from HBM, so the kernels are shaped around the weight stream:
-//   dec_kv_a     kv_a_proj: W_kv_a cut into 64-column slabs x K ranges of
-//                KW rows, one workgroup each, writing split-K partial sums
-//                P[s][t][576]
-//   dec_finish   one workgroup per token: sum the partials, RMSNorm the
-//                latent (-> compressed_kv), rotate the rope part (-> k_pe)
-//   dec_kv_b     kv_b_proj: items of (16-token tile, 64-column slab of
-//                W_kv_b over the full K = 512), one workgroup each, writing
-//                its tile of k_nope / value
-// Each workgroup issues all of its weight loads first (16 bytes per lane,
-// 128 contiguous bytes per row) and stages the slab in LDS, where the MFMA
-// operand (8 consecutive K of one column per lane) is read back
-// column-wise; wave w owns slab columns 16w..16w+15 over the whole K range,
-// so no cross-wave reduction is needed.  The kv_b items sharing a slab sit
-// on one XCD (workgroups go to the 8 XCDs round-robin), so that XCD's L2
-// serves the repeated slab reads, and all items of a slab read the latent
-// through the same L2.
-//
-// The three launches are stream-ordered: a kernel boundary publishes the
-// previous kernel's results to the whole device at once, which on this
-// part is cheaper than any in-kernel grid hand-off for data that many
-// workgroups must read (each in-kernel reader would have to drop its XCD's
-// cache lines or bypass them).
+// once from HBM and by the latency of doing so, so the kernels are shaped
+// around the weight stream:
+//   dec_kv_a       kv_a_proj: W_kv_a cut into 64-column slabs x K ranges of
+//                  KW rows, one workgroup each, writing split-K partial sums
+//                  P[s][t][576]
+//   dec_fin_kv_b   the finish (sum of the partials, RMSNorm -> compressed_kv,
+//                  RoPE -> k_pe) fused into kv_b_proj: items of (16-token
+//                  tile, 64-column slab of W_kv_b over the full K = 512), one
+//                  workgroup each; the first workgroups also finish one token
+//                  each and hand the latent rows to the others (see the
+//                  kernel)
+//   dec_finish, dec_kv_b   the same two steps as separate launches, for
+//                  shapes with more kv_b_proj items than fit on the chip at
+//                  once
+// Each workgroup issues all of its global loads before its first wait (16
+// bytes per lane, 128 contiguous bytes per weight row; out-of-range rows are
+// clamped and zeroed when stored, never branched around), stages the weight
+// slab and the activation rows in LDS once, and multiplies with
+// v_mfma_f32_16x16x32 (tokens as M); wave w owns slab columns 16w..16w+15
+// over the whole K range, so no cross-wave reduction is needed.
 //
 // Steps as in the DeepSeek-V2-Lite-Chat MLA KV Prolog migration guide
 // (dpshk.com), sections "Background" and "Source-level principle"; RoPE in

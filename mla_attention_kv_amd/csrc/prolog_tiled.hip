@@ -1,7 +1,8 @@
 // Tiled gfx950 kernels of the MLA KV prolog: both projections as MFMA GEMMs
-// (LDS-staged tiles, register prefetch of the next K slab, optional split-K),
-// plus the per-token kernels that finish kv_a_proj (split, RMSNorm, RoPE) and,
-// on the W8A8 path, quantise the activations.
+// (gemm_lds_kernel: persistent, slabs copied straight into a ring of LDS
+// stages, fp16 / bf16; gemm_tiled_kernel: register-staged slabs, int8 and
+// split-K), plus the per-token kernels that finish kv_a_proj (split, RMSNorm,
+// RoPE) and, on the W8A8 path, quantise the activations.
 //
 // Steps follow the DeepSeek-V2-Lite-Chat MLA KV Prolog migration guide
 // (dpshk.com), sections "Background" and "Source-level principle"; RoPE is
@@ -632,8 +633,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_lds_kernel(
 //   c, p  = sum of the split-K partials (split order ascending)
 //   y     = c / sqrt(sum(c^2)/512 + eps) * gamma      -> compressed_kv
 //   k_pe  = rotate-half RoPE of p at the token's position
-// The rope angle pos * theta^(-2i/64) is formed and reduced modulo 2 pi in
-// double; sine / cosine of the reduced angle and the rotation run in fp32.
+// The rope angle pos * theta^(-2i/64) is formed and reduced by quarter turns
+// in double; sine / cosine of the reduced angle and the rotation run in fp32
+// (rope_cos_sin).
 // ---------------------------------------------------------------------------
 template <int E>
 __global__ __launch_bounds__(64) void finish_a_fp_kernel(
