@@ -362,11 +362,13 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined fp16 / bf16 GEMM with direct-to-LDS loads.
-// C[M, N] = A[M, K] . B[K, N]; A, B row-major; K a multiple of 64 (one slab =
-// 64 K elements), N a multiple of BN.
+// Pipelined GEMM with direct-to-LDS loads (fp16 / bf16 / int8).
+// C[M, N] = A[M, K] . B[K, N]; A, B row-major; one slab = 128 bytes of an A
+// row (64 fp16 / bf16 or 128 int8 K elements), K a multiple of a slab, N a
+// multiple of BN.
 //
-// Each slab of A (BM rows x 128 bytes) and of B (64 rows x BN columns) goes
+// Each slab of A (BM rows x 128 bytes) and of B (one row per K element of
+// the slab, BN columns) goes
 // from global memory straight into LDS (global_load_lds_dwordx4: one wave
 // instruction fills 1 KB of LDS, lane l the 16 bytes at l * 16), so the
 // prefetch depth costs no registers: STAGES slabs live in STAGES separate
@@ -383,9 +385,10 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
 //            chunk each) then touches 16 distinct 16-byte bank groups.
 //   B stage: [64 k rows][BN columns]; 16-byte chunk c of row k sits at
 //            c ^ (2 (k & 3) + 8 ((k >> 3) & 1)) (c ^ 2 (k & 3) when a row is
-//            not a multiple of 16 chunks).  The B operand (column n,
-//            8 consecutive k) comes from two transposing reads
-//            (ds_read_b64_tr_b16) of 4 rows x 4 columns per 16-lane group.
+//            not a multiple of 16 chunks; c ^ (k & 7) for int8).  The B
+//            operand (column n, 8 or 16 consecutive k) comes from two
+//            transposing reads: ds_read_b64_tr_b16 (4 rows x 4 columns per
+//            16-lane group) or ds_read_b64_tr_b8 (8 rows x 8 columns).
 // Waves are laid out WAVES_M x WAVES_N, each owning a (BM / WAVES_M) x
 // (BN / WAVES_N) block of 16 x 16 MFMA tiles.  Tile order is the same
 // XCD-aware grouped order as gemm_tiled_kernel.  Results go from the
@@ -425,24 +428,34 @@ __device__ __forceinline__ void wait_copies_barrier() {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(size_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
-// B-row chunk swizzle: rows of 16 chunks or more (BN >= 128) use
-// 2 (k & 3) + 8 ((k >> 3) & 1); other rows (BN = 64 or 192) stay inside
-// aligned groups of 8 chunks with 2 (k & 3).
-template <int BRB>
+// B-row chunk swizzle (16-byte chunk c of row k is stored at c ^ bswz(k)):
+// 16-bit rows of 16 chunks or more (BN >= 128) use 2 (k & 3) + 8 ((k >> 3) & 1);
+// other 16-bit rows (BN = 64 or 192) stay inside aligned groups of 8 chunks
+// with 2 (k & 3); int8 rows use k & 7 (a transposing 8-bit read touches one
+// chunk in each of 8 consecutive rows).
+template <int E, int BRB>
 __device__ __forceinline__ int bswz(int k) {
-    if constexpr (BRB % 256 == 0) return 2 * (k & 3) + 8 * ((k >> 3) & 1);
+    if constexpr (E == kI8) return k & 7;
+    else if constexpr (BRB % 256 == 0) return 2 * (k & 3) + 8 * ((k >> 3) & 1);
     else return 2 * (k & 3);
+}
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 lds_tr8(const uint8_t* p) {
+    const v2i_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) v2i_t*)(p));
+    return __builtin_bit_cast(uint2, r);
 }
 
 template <int E, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int GM, class Epi>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_lds_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     int M, int Nt, int nk, Epi epi) {
-    static_assert(E == kF16 || E == kBF16, "16-bit operands");
+    constexpr int ES = (E == kI8) ? 1 : 2;    // bytes per element
+    constexpr int KE = 128 / ES;              // K elements per slab (128 bytes of an A row)
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int A_ST = BM * 128;            // A bytes per stage
-    constexpr int BRB = BN * 2;               // bytes per B row
-    constexpr int B_ST = 64 * BRB;            // B bytes per stage
+    constexpr int BRB = BN * ES;              // bytes per B row
+    constexpr int B_ST = KE * BRB;            // B bytes per stage (KE rows)
     constexpr int STAGE = A_ST + B_ST;
     constexpr int A_PW = A_ST / 1024 / NW, B_PW = B_ST / 1024 / NW;
     static_assert(A_PW * NW * 1024 == A_ST && B_PW * NW * 1024 == B_ST, "even copy split");
@@ -491,10 +504,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_lds_kernel(
     for (int u = 0; u < B_PW; ++u) {
         const int byte = (wave + NW * u) * 1024 + lane * 16;
         const int k = byte / BRB, pos = (byte % BRB) / 16;
-        const int c = pos ^ bswz<BRB>(k);
-        bsrc[u] = B + (int64_t)k * ldb + (int64_t)n0 * 2 + c * 16;
+        const int c = pos ^ bswz<E, BRB>(k);
+        bsrc[u] = B + (int64_t)k * ldb + (int64_t)n0 * ES + c * 16;
     }
-    const int64_t bstep = 64 * ldb;           // bytes of B per slab
+    const int64_t bstep = KE * ldb;           // bytes of B per slab
 
     // wave-uniform LDS offset of this wave's first 1 KB block in a stage
     const uint32_t wofs = (uint32_t)__builtin_amdgcn_readfirstlane(wave * 1024);
@@ -509,11 +522,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_lds_kernel(
     };
 
     const int wm0 = (wave / WAVES_N) * WM, wn0 = (wave % WAVES_N) * WN;
-    f4_t acc[TM][TN];
+    typedef typename Acc<E>::type acc_t;
+    acc_t acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = f4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < TN; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
 
     const int l16 = lane & 15, g = lane >> 4;
     // operand fragments of one K step (32 K elements) in two register sets
@@ -529,14 +543,29 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_lds_kernel(
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            // lane (16 g + s): rows 32 ks + 8 g + s / 4 (+ 4), columns
-            // wn0 + 16 j + 4 (s % 4) .. + 3
-            const int k = ks * 32 + g * 8 + (l16 >> 2);
-            const int colb = (wn0 + j * 16 + 4 * (l16 & 3)) * 2;
-            const int c = colb >> 4, off = colb & 15;
-            const uint2 lo = lds_tr16(Bs + k * BRB + ((c ^ bswz<BRB>(k)) << 4) + off);
-            const uint2 hi = lds_tr16(Bs + (k + 4) * BRB + ((c ^ bswz<BRB>(k + 4)) << 4) + off);
-            fb[buf][j] = u4_t{lo.x, lo.y, hi.x, hi.y};
+            if constexpr (ES == 2) {
+                // lane (16 g + s): rows 32 ks + 8 g + s / 4 (+ 4), columns
+                // wn0 + 16 j + 4 (s % 4) .. + 3; lane s receives 4 rows of
+                // column wn0 + 16 j + s per read
+                const int k = ks * 32 + g * 8 + (l16 >> 2);
+                const int colb = (wn0 + j * 16 + 4 * (l16 & 3)) * 2;
+                const int c = colb >> 4, off = colb & 15;
+                const uint2 lo = lds_tr16(Bs + k * BRB + ((c ^ bswz<E, BRB>(k)) << 4) + off);
+                const uint2 hi =
+                    lds_tr16(Bs + (k + 4) * BRB + ((c ^ bswz<E, BRB>(k + 4)) << 4) + off);
+                fb[buf][j] = u4_t{lo.x, lo.y, hi.x, hi.y};
+            } else {
+                // lane (16 g + s): rows 64 ks + 16 g + s / 2 (+ 8), columns
+                // wn0 + 16 j + 8 (s % 2) .. + 7; lane s receives 8 rows of
+                // column wn0 + 16 j + s per read
+                const int k = ks * 64 + g * 16 + (l16 >> 1);
+                const int colb = wn0 + j * 16 + 8 * (l16 & 1);
+                const int c = colb >> 4, off = colb & 15;
+                const uint2 lo = lds_tr8(Bs + k * BRB + ((c ^ bswz<E, BRB>(k)) << 4) + off);
+                const uint2 hi =
+                    lds_tr8(Bs + (k + 8) * BRB + ((c ^ bswz<E, BRB>(k + 8)) << 4) + off);
+                fb[buf][j] = u4_t{lo.x, lo.y, hi.x, hi.y};
+            }
         }
     };
     auto mma = [&](int buf) {
@@ -836,8 +865,8 @@ static void gemm_lds_launch(const void* A, int64_t lda, const void* B, int64_t l
     const int64_t grid = std::min<int64_t>(((tiles + 7) / 8) * 8, kPersistentGrid);
     hipLaunchKernelGGL((gemm_lds_kernel<E, BM, BN, WAVES_M, WAVES_N, STAGES, GM, Epi>),
                        dim3((unsigned)grid), dim3(64 * WAVES_M * WAVES_N), 0, st,
-                       (const uint8_t*)A, lda, (const uint8_t*)B, ldb, (int)M, N / BN, K / 64,
-                       epi);
+                       (const uint8_t*)A, lda, (const uint8_t*)B, ldb, (int)M, N / BN,
+                       K * (E == kI8 ? 1 : 2) / 128, epi);
 }
 
 // kv_a_proj tiles: BN = 64 always (576 = 9 x 64)
@@ -859,11 +888,9 @@ static void gemm2_dispatch(int bm, int bn, const void* A, int64_t lda, const voi
                            int N2, Epi epi, hipStream_t st) {
     const int64_t ldb = (int64_t)N2 * ((E == kI8) ? 1 : 2);
     const int kslabs = (E == kI8) ? kR / 128 : kR * 2 / 128;
-    if constexpr (E != kI8) {
-        if (bm >= 128) {
-            gemm_lds_launch<E, 256, 128, 4, 2, 3>(A, lda, B, ldb, M, N2, kR, epi, st);
-            return;
-        }
+    if (bm >= 128) {
+        gemm_lds_launch<E, 256, 128, 4, 2, 3>(A, lda, B, ldb, M, N2, kR, epi, st);
+        return;
     }
     if (bn == 128) {
         gemm_launch<E, 128, 128, 64, 64>(A, lda, B, ldb, M, N2, kslabs, 1, epi, st);
