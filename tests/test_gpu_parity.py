@@ -133,6 +133,15 @@ def test_minimal_hidden_single_head(dev):
     check_full(w, dev, "H64_nh1")
 
 
+@pytest.mark.parametrize("T", [9, 40])
+def test_decode_many_k_splits(dev, T):
+    # more than 16 kv_a_proj K splits: the finish reads its later splits in
+    # a second round of partial loads
+    d = Dims(H=4096, nh=2)
+    w = workloads.make_custom(d, T, dtype="f16", seed=440 + T, wstd=0.02)
+    check_full(w, dev, f"H4096_T{T}", path=0)
+
+
 def test_long_prefill_ragged_tail(dev):
     # long prefill (kv_a_proj without split-K, pipelined kv_b_proj) with a
     # token count that leaves partial tiles; every row checked
