@@ -61,7 +61,7 @@ Plan make_plan(int64_t T, int H, bool int8, int path) {
         p.bm2 = 128;
         p.bn2 = 128;
     }
-    if (!int8 && path == 1 && T >= 4096) {
+    if (path == 1 && T >= 4096) {
         // enough 64 x 192 tiles (3 per 64 tokens) to occupy the chip without
         // splitting K
         p.dma1 = 1;

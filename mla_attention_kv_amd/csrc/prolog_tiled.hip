@@ -431,11 +431,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // B-row chunk swizzle (16-byte chunk c of row k is stored at c ^ bswz(k)):
 // 16-bit rows of 16 chunks or more (BN >= 128) use 2 (k & 3) + 8 ((k >> 3) & 1);
 // other 16-bit rows (BN = 64 or 192) stay inside aligned groups of 8 chunks
-// with 2 (k & 3); int8 rows use k & 7 (a transposing 8-bit read touches one
-// chunk in each of 8 consecutive rows).
+// with 2 (k & 3); int8 rows use k & 7, or (k >> 1) & 3 for 12-chunk rows (a
+// transposing 8-bit read touches one chunk in each of 8 consecutive rows).
 template <int E, int BRB>
 __device__ __forceinline__ int bswz(int k) {
-    if constexpr (E == kI8) return k & 7;
+    if constexpr (E == kI8 && BRB % 128 == 0) return k & 7;
+    else if constexpr (E == kI8) return (k >> 1) & 3;  // 12-chunk rows (BN = 192)
     else if constexpr (BRB % 256 == 0) return 2 * (k & 3) + 8 * ((k >> 3) & 1);
     else return 2 * (k & 3);
 }
@@ -459,7 +460,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_lds_kernel(
     constexpr int STAGE = A_ST + B_ST;
     constexpr int A_PW = A_ST / 1024 / NW, B_PW = B_ST / 1024 / NW;
     static_assert(A_PW * NW * 1024 == A_ST && B_PW * NW * 1024 == B_ST, "even copy split");
-    static_assert(BRB % 128 == 0, "whole groups of 8 chunks per B row");
+    static_assert(BRB % 128 == 0 || (E == kI8 && BRB == 192), "B row swizzle groups");
     constexpr int PW = A_PW + B_PW;           // copy instructions per wave per slab
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, TM = WM / 16, TN = WN / 16;
     static_assert(STAGES >= 2 && STAGES <= 4, "stages");
@@ -470,67 +471,71 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_lds_kernel(
 
     // ---- tiles of this workgroup: workgroup b runs on XCD b % 8; XCD x
     // owns the contiguous tile range [x per, (x + 1) per) of the grouped
-    // order and its workgroups walk it in steps of (grid / 8), so that the
-    // output stores of one tile drain while the next tile is loaded and
-    // multiplied
+    // order and its workgroups walk it in steps of (grid / 8).  The slabs of
+    // all of a workgroup's tiles form one pipeline: the first slabs of the
+    // next tile are copied while the last ones of the current tile are
+    // multiplied, and a tile's output stores drain while the next is
+    // multiplied.
     const int Mt = (M + BM - 1) / BM;
     const int tiles = Mt * Nt;
     const int per = (tiles + 7) / 8;
     const int x = blockIdx.x & 7, nwx = gridDim.x >> 3;
+    const int first = x * per + (blockIdx.x >> 3);
+    const int lim = min(tiles, (x + 1) * per);
+    const int ntl = first < lim ? (lim - first + nwx - 1) / nwx : 0;
+    if (ntl == 0) return;
+    const int total = ntl * nk;  // slabs of all tiles, in order
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int tl = blockIdx.x >> 3; tl < per; tl += nwx) {
-    const int t = x * per + tl;
-    if (t >= tiles) break;
-    const int grp = t / (GM * Nt);
-    const int gm = min(GM, Mt - grp * GM);
-    const int q = t - grp * GM * Nt;
-    const int m0 = (grp * GM + q % gm) * BM, n0 = (q / gm) * BN;
-    // every wave has its last reads of the previous tile back before any
-    // copy of this tile lands in the stages
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    auto tile_origin = [&](int i, int& m0, int& n0) {
+        const int t = first + i * nwx;
+        const int grp = t / (GM * Nt);
+        const int gm = min(GM, Mt - grp * GM);
+        const int q = t - grp * GM * Nt;
+        m0 = (grp * GM + q % gm) * BM;
+        n0 = (q / gm) * BN;
+    };
 
     // ---- copy sources: instruction u of this wave covers LDS bytes
     // [(wave + NW u) KB, +1 KB) of the A (resp. B) part of a stage
-    const uint8_t* asrc[A_PW];
+    int arow[A_PW], acol[A_PW];
 #pragma unroll
     for (int u = 0; u < A_PW; ++u) {
-        const int row = (wave + NW * u) * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ ((row >> 1) & 7);
-        const int grow = min(m0 + row, M - 1);
-        asrc[u] = A + (int64_t)grow * lda + c * 16;
+        arow[u] = (wave + NW * u) * 8 + (lane >> 3);
+        acol[u] = ((lane & 7) ^ ((arow[u] >> 1) & 7)) * 16;
     }
-    const uint8_t* bsrc[B_PW];
+    int64_t boff[B_PW];
 #pragma unroll
     for (int u = 0; u < B_PW; ++u) {
         const int byte = (wave + NW * u) * 1024 + lane * 16;
         const int k = byte / BRB, pos = (byte % BRB) / 16;
-        const int c = pos ^ bswz<E, BRB>(k);
-        bsrc[u] = B + (int64_t)k * ldb + (int64_t)n0 * ES + c * 16;
+        boff[u] = (int64_t)k * ldb + (pos ^ bswz<E, BRB>(k)) * 16;
     }
     const int64_t bstep = KE * ldb;           // bytes of B per slab
 
     // wave-uniform LDS offset of this wave's first 1 KB block in a stage
     const uint32_t wofs = (uint32_t)__builtin_amdgcn_readfirstlane(wave * 1024);
-    auto issue = [&](int kc, const uint8_t* stg) {
+    // copy slab gs of the pipeline (slab gs % nk of tile gs / nk)
+    auto issue = [&](int gs, const uint8_t* stg) {
+        const int i = gs / nk, kc = gs - i * nk;
+        int m0, n0;
+        tile_origin(i, m0, n0);
         const uint32_t base = lds_addr(stg) + wofs;
 #pragma unroll
-        for (int u = 0; u < A_PW; ++u)
-            dma16(asrc[u] + (int64_t)kc * 128, base + u * NW * 1024);
+        for (int u = 0; u < A_PW; ++u) {
+            const int grow = min(m0 + arow[u], M - 1);
+            dma16(A + (int64_t)grow * lda + (int64_t)kc * 128 + acol[u], base + u * NW * 1024);
+        }
 #pragma unroll
         for (int u = 0; u < B_PW; ++u)
-            dma16(bsrc[u] + kc * bstep, base + A_ST + u * NW * 1024);
+            dma16(B + kc * bstep + (int64_t)n0 * ES + boff[u], base + A_ST + u * NW * 1024);
     };
 
     const int wm0 = (wave / WAVES_N) * WM, wn0 = (wave % WAVES_N) * WN;
     typedef typename Acc<E>::type acc_t;
     acc_t acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
 
     const int l16 = lane & 15, g = lane >> 4;
-    // operand fragments of one K step (32 K elements) in two register sets
+    // operand fragments of one K step in two register sets
     u4_t fa[2][TM], fb[2][TN];
     auto rd = [&](const uint8_t* stg, int ks, int buf) {
         const uint8_t* As = stg;
@@ -577,6 +582,40 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_lds_kernel(
             for (int j = 0; j < TN; ++j) acc[i][j] = mfma16<E>(fb[buf][j], fa[buf][i], acc[i][j]);
     };
 
+    // ---- epilogue of tile ti: lane holds output row (l16) and columns
+    // 4 g .. 4 g + 3 of each 16 x 16 MFMA tile
+    auto epilogue = [&](int ti) {
+        int m0, n0;
+        tile_origin(ti, m0, n0);
+        typedef typename Epi::out_t out_t;
+        float cs[TN][4];
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) cs[j][v] = epi.col_scale(n0 + wn0 + j * 16 + g * 4 + v);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int row = m0 + wm0 + i * 16 + l16;
+            if (row >= M) continue;
+            const typename Epi::row_t rs = epi.row_scale(row);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int col = n0 + wn0 + j * 16 + g * 4;
+                out_t o[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) o[v] = epi.value(row, col + v, acc[i][j][v], rs, cs[j][v]);
+                if constexpr (sizeof(out_t) == 2)
+                    *(u2_t*)epi.ptr(row, col, 0) = u2_t{(uint32_t)o[0] | ((uint32_t)o[1] << 16),
+                                                        (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
+                else
+                    *(u4_t*)epi.ptr(row, col, 0) = u4_t{__builtin_bit_cast(uint32_t, o[0]),
+                                                        __builtin_bit_cast(uint32_t, o[1]),
+                                                        __builtin_bit_cast(uint32_t, o[2]),
+                                                        __builtin_bit_cast(uint32_t, o[3])};
+            }
+        }
+    };
+
     // Software pipeline over (slab, K step): the reads of the next K step are
     // in flight while the MFMAs of the current one run, and the barrier that
     // hands over the next slab sits between the two K steps of a slab:
@@ -584,75 +623,52 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_lds_kernel(
     // Before the barrier a wave has all of its reads of slab k back in
     // registers (lgkmcnt 0), so the copy into slab k's stage that follows
     // the barrier overwrites nothing still being read.
-    auto step = [&](int kc, const uint8_t* cur, const uint8_t* nxt) {
+    auto step = [&](int gs, const uint8_t* cur, const uint8_t* nxt) {
+        const int kc = gs % nk;
+        if (kc == 0) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
+        }
         rd(cur, 1, 1);
         mma(0);
-        if (kc + 1 < nk) {
+        if (gs + 1 < total) {
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            if (kc + STAGES - 1 < nk) wait_copies_barrier<(STAGES - 2) * PW>();
+            if (gs + STAGES - 1 < total) wait_copies_barrier<(STAGES - 2) * PW>();
             else wait_copies_barrier<0>();
-            if (kc + STAGES < nk) issue(kc + STAGES, cur);
+            if (gs + STAGES < total) issue(gs + STAGES, cur);
             rd(nxt, 0, 0);
         }
         mma(1);
+        if (kc == nk - 1) epilogue(gs / nk);
     };
 
 #pragma unroll
     for (int p = 0; p < STAGES - 1; ++p)
-        if (p < nk) issue(p, p == 0 ? st0 : (p == 1 ? st1 : st2));
+        if (p < total) issue(p, p == 0 ? st0 : (p == 1 ? st1 : st2));
     // slab 0 in place (slabs 1 .. STAGES - 2 may still be on their way), slab
     // STAGES - 1 requested, first K step read
-    if (STAGES - 2 < nk) wait_copies_barrier<(STAGES - 2) * PW>();
+    if (STAGES - 2 < total) wait_copies_barrier<(STAGES - 2) * PW>();
     else wait_copies_barrier<0>();
-    if (STAGES - 1 < nk) issue(STAGES - 1, STAGES == 2 ? st1 : (STAGES == 3 ? st2 : st3));
+    if (STAGES - 1 < total) issue(STAGES - 1, STAGES == 2 ? st1 : (STAGES == 3 ? st2 : st3));
     rd(st0, 0, 0);
-    // slab kc lives in stage kc % STAGES; step(kc, its stage, the stage of
-    // slab kc + 1); the stage of kc then receives slab kc + STAGES
-    for (int kc = 0; kc < nk; kc += STAGES) {
+    // slab gs lives in stage gs % STAGES; step(gs, its stage, the stage of
+    // slab gs + 1); the stage of gs then receives slab gs + STAGES
+    for (int gs = 0; gs < total; gs += STAGES) {
         if constexpr (STAGES == 2) {
-            step(kc, st0, st1);
-            if (kc + 1 < nk) step(kc + 1, st1, st0);
+            step(gs, st0, st1);
+            if (gs + 1 < total) step(gs + 1, st1, st0);
         } else if constexpr (STAGES == 3) {
-            step(kc, st0, st1);
-            if (kc + 1 < nk) step(kc + 1, st1, st2);
-            if (kc + 2 < nk) step(kc + 2, st2, st0);
+            step(gs, st0, st1);
+            if (gs + 1 < total) step(gs + 1, st1, st2);
+            if (gs + 2 < total) step(gs + 2, st2, st0);
         } else {
-            step(kc, st0, st1);
-            if (kc + 1 < nk) step(kc + 1, st1, st2);
-            if (kc + 2 < nk) step(kc + 2, st2, st3);
-            if (kc + 3 < nk) step(kc + 3, st3, st0);
+            step(gs, st0, st1);
+            if (gs + 1 < total) step(gs + 1, st1, st2);
+            if (gs + 2 < total) step(gs + 2, st2, st3);
+            if (gs + 3 < total) step(gs + 3, st3, st0);
         }
-    }
-
-    // ---- epilogue: lane holds output row (l16) and columns 4 g .. 4 g + 3 of
-    // each 16 x 16 tile
-    typedef typename Epi::out_t out_t;
-    float cs[TN][4];
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) cs[j][v] = epi.col_scale(n0 + wn0 + j * 16 + g * 4 + v);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int row = m0 + wm0 + i * 16 + l16;
-        if (row >= M) continue;
-        const typename Epi::row_t rs = epi.row_scale(row);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int col = n0 + wn0 + j * 16 + g * 4;
-            out_t o[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) o[v] = epi.value(row, col + v, acc[i][j][v], rs, cs[j][v]);
-            if constexpr (sizeof(out_t) == 2)
-                *(u2_t*)epi.ptr(row, col, 0) = u2_t{(uint32_t)o[0] | ((uint32_t)o[1] << 16),
-                                                    (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
-            else
-                *(u4_t*)epi.ptr(row, col, 0) = u4_t{__builtin_bit_cast(uint32_t, o[0]),
-                                                    __builtin_bit_cast(uint32_t, o[1]),
-                                                    __builtin_bit_cast(uint32_t, o[2]),
-                                                    __builtin_bit_cast(uint32_t, o[3])};
-        }
-    }
     }
 }
 
@@ -714,8 +730,38 @@ __global__ __launch_bounds__(64) void finish_a_fp_kernel(
 // W8A8: per-token activation quantisation (one 256-thread block per token).
 //   amax = max |x|;  q = clamp(rint(x * (127/amax)), -127, 127);
 //   scale = amax / 127;  amax == 0 -> q = 0, scale = 0.
-// fp32 with IEEE division and round-half-even rint.
+// fp32 with IEEE division and round-half-even rint.  With NC > 0 (rows of at
+// most NC * 2048 elements) every thread loads its NC 16-byte chunks once,
+// all before the first wait, and quantises them from registers; NC = 0 walks
+// the row twice.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ u2_t quant8(const u4_t v, float inv) {
+    u2_t q;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int e = w * 4 + b;
+            const uint32_t bits = (v[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+            float r = rintf(bf16_to_f32((uint16_t)bits) * inv);
+            r = fminf(fmaxf(r, -127.f), 127.f);
+            packed |= ((uint32_t)(uint8_t)(int8_t)(int)r) << (8 * b);
+        }
+        q[w] = packed;
+    }
+    return q;
+}
+__device__ __forceinline__ float absmax8(const u4_t v, float amax) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        amax = fmaxf(amax, fabsf(bf16_to_f32((uint16_t)(v[w] & 0xFFFFu))));
+        amax = fmaxf(amax, fabsf(bf16_to_f32((uint16_t)(v[w] >> 16))));
+    }
+    return amax;
+}
+
+template <int NC>
 __global__ __launch_bounds__(256) void quant_rows_bf16_kernel(const uint16_t* __restrict__ X,
                                                               int H, int8_t* __restrict__ Q,
                                                               float* __restrict__ scale) {
@@ -724,36 +770,33 @@ __global__ __launch_bounds__(256) void quant_rows_bf16_kernel(const uint16_t* __
     const int tid = threadIdx.x;
     const uint16_t* row = X + t * H;
     float amax = 0.f;
-    for (int k = tid * 8; k < H; k += 256 * 8) {
-        const u4_t v = *(const u4_t*)(row + k);
+    u4_t v[NC > 0 ? NC : 1];
+    if constexpr (NC > 0) {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            amax = fmaxf(amax, fabsf(bf16_to_f32((uint16_t)(v[w] & 0xFFFFu))));
-            amax = fmaxf(amax, fabsf(bf16_to_f32((uint16_t)(v[w] >> 16))));
+        for (int u = 0; u < NC; ++u) {
+            const int k = tid * 8 + u * 2048;
+            v[u] = *(const u4_t*)(row + (k < H ? k : 0));
         }
+#pragma unroll
+        for (int u = 0; u < NC; ++u)
+            if (tid * 8 + u * 2048 < H) amax = absmax8(v[u], amax);
+    } else {
+        for (int k = tid * 8; k < H; k += 256 * 8) amax = absmax8(*(const u4_t*)(row + k), amax);
     }
     amax = wave_max(amax);
     if ((tid & 63) == 0) red[tid >> 6] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const float inv = (amax > 0.f) ? (127.0f / amax) : 0.f;
-    for (int k = tid * 8; k < H; k += 256 * 8) {
-        const u4_t v = *(const u4_t*)(row + k);
-        u2_t q;
+    if constexpr (NC > 0) {
 #pragma unroll
-        for (int w = 0; w < 2; ++w) {
-            uint32_t packed = 0;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int e = w * 4 + b;
-                const uint32_t bits = (v[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-                float r = rintf(bf16_to_f32((uint16_t)bits) * inv);
-                r = fminf(fmaxf(r, -127.f), 127.f);
-                packed |= ((uint32_t)(uint8_t)(int8_t)(int)r) << (8 * b);
-            }
-            q[w] = packed;
+        for (int u = 0; u < NC; ++u) {
+            const int k = tid * 8 + u * 2048;
+            if (k < H) *(u2_t*)(Q + t * H + k) = quant8(v[u], inv);
         }
-        *(u2_t*)(Q + t * H + k) = q;
+    } else {
+        for (int k = tid * 8; k < H; k += 256 * 8)
+            *(u2_t*)(Q + t * H + k) = quant8(*(const u4_t*)(row + k), inv);
     }
     if (tid == 0) scale[t] = (amax > 0.f) ? (amax / 127.0f) : 0.f;
 }
@@ -964,10 +1007,23 @@ hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa, const
     int8_t* QZ = (int8_t*)(base + w.qz);
     float* sz = (float*)(base + w.sz);
     float* inv = (float*)(base + w.inv);
-    hipLaunchKernelGGL(quant_rows_bf16_kernel, dim3((unsigned)T), dim3(256), 0, st,
-                       (const uint16_t*)X, H, QX, sx);
-    gemm1_dispatch<kI8>(plan.bm1, QX, (int64_t)H, Wqa, T, H / 128, plan.s1,
-                        EpiPartialI32{P1, T}, st);
+    {
+        const dim3 grid((unsigned)T), blk(256);
+        const uint16_t* x = (const uint16_t*)X;
+        switch ((H + 2047) / 2048) {
+            case 1: hipLaunchKernelGGL(quant_rows_bf16_kernel<1>, grid, blk, 0, st, x, H, QX, sx); break;
+            case 2: hipLaunchKernelGGL(quant_rows_bf16_kernel<2>, grid, blk, 0, st, x, H, QX, sx); break;
+            case 3: hipLaunchKernelGGL(quant_rows_bf16_kernel<3>, grid, blk, 0, st, x, H, QX, sx); break;
+            case 4: hipLaunchKernelGGL(quant_rows_bf16_kernel<4>, grid, blk, 0, st, x, H, QX, sx); break;
+            default: hipLaunchKernelGGL(quant_rows_bf16_kernel<0>, grid, blk, 0, st, x, H, QX, sx); break;
+        }
+    }
+    if (plan.dma1)
+        gemm_lds_launch<kI8, 64, 192, 1, 4, 4>(QX, (int64_t)H, Wqa, (int64_t)kN1, T, kN1, H,
+                                               EpiPartialI32{P1, T}, st);
+    else
+        gemm1_dispatch<kI8>(plan.bm1, QX, (int64_t)H, Wqa, T, H / 128, plan.s1,
+                            EpiPartialI32{P1, T}, st);
     hipLaunchKernelGGL(finish_a_w8_kernel, dim3((unsigned)T), dim3(64), 0, st, P1, plan.s1, T, sx,
                        swa, (const uint16_t*)gamma, pos, eps, rt, QZ, sz, inv,
                        (uint16_t*)ckv, (uint16_t*)k_pe, dbg1, dbg_begin, dbg_rows);

@@ -133,6 +133,15 @@ def test_minimal_hidden_single_head(dev):
     check_full(w, dev, "H64_nh1")
 
 
+def test_w8a8_long_prefill_ragged_tail_exact(dev):
+    # W8A8 at a long token count: both projections on the pipelined kernel;
+    # int32 accumulators of every row bit-exact
+    d = Dims(H=512, nh=2)
+    w = workloads.make_custom(d, 4100, kind="w8a8", dtype="bf16", seed=450, wstd=0.02,
+                              max_pos=8192)
+    check_full(w, dev, "w8a8_T4100", path=1, dbg=True)
+
+
 @pytest.mark.parametrize("T", [9, 40])
 def test_decode_many_k_splits(dev, T):
     # more than 16 kv_a_proj K splits: the finish reads its later splits in
