@@ -274,7 +274,7 @@ def main():
     roof["traffic"] = load_traffic(cfg["name"])
     roof["kernel"] = ("one library call = every launch of the step: " +
                       ("dec_kv_a + dec_fin_kv_b (finish fused into kv_b_proj)"
-                       if (path == 0 and w.kind == "fp" and w.T <= 64 and w.dims.nh * (w.T + 15) // 16 <= 64)
+                       if (path == 0 and w.kind == "fp" and w.T <= 64 and w.dims.nh * ((w.T + 15) // 16) <= 64)
                        else "dec_kv_a + dec_finish + dec_kv_b" if (path == 0 and w.kind == "fp" and w.T <= 64)
                        else "kv_a_proj GEMM + finish + kv_b_proj GEMM" +
                        (" (+ activation quantiser)" if w.kind == "w8a8" else "")))

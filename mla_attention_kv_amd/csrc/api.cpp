@@ -38,11 +38,12 @@ Plan make_plan(int64_t T, int H, bool int8, int path) {
     p.dma1 = 0;
     if (p.stream) {
         // weight-streaming kv_a_proj: 9 slabs x S splits of kw rows each;
-        // wider splits when the split-K partials (S * T rows of 576 floats)
-        // would grow large
+        // wider splits once the split-K partials (S * T rows of 576 floats)
+        // outweigh the extra workgroups (measured: V2-Lite at T = 64 is
+        // faster with S = 8 than with 16, at T = 1 slower)
         const int64_t tt = T < 16 ? 16 : T;
         int kw = H <= 64 ? 64 : 128;
-        while (kw < 512 && ((H + kw - 1) / kw) * tt > 1024) kw *= 2;
+        while (kw < 512 && ((H + kw - 1) / kw) * tt > 512) kw *= 2;
         p.kw = kw;
         p.s1 = (H + kw - 1) / kw;
         p.bm1 = p.bm2 = 16;
