@@ -62,11 +62,17 @@ Plan make_plan(int64_t T, int H, bool int8, int path) {
         p.bm2 = 128;
         p.bn2 = 128;
     }
-    if (path == 1 && T >= 4096) {
-        // enough 64 x 192 tiles (3 per 64 tokens) to occupy the chip without
-        // splitting K
+    if (path == 1) {
+        // kv_a_proj on the pipelined kernel: 128 x 192 tiles from 2048
+        // tokens, 64 x 192 below; K split by the largest divisor of the slab
+        // count that keeps the (tile, split) items within one per CU and at
+        // least two slabs per split
         p.dma1 = 1;
+        p.bm1 = T >= 2048 ? 128 : 64;
+        const int64_t items = ((T + p.bm1 - 1) / p.bm1) * (kN1 / 192);
         p.s1 = 1;
+        for (int d = 2; d <= ks / 2; ++d)
+            if (ks % d == 0 && items * d <= 256) p.s1 = d;
         return p;
     }
     // split kv_a_proj's K so that at least ~256 workgroups stream W_kv_a,

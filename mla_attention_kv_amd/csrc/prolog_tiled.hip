@@ -362,21 +362,30 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined GEMM with direct-to-LDS loads (fp16 / bf16 / int8).
+// Pipelined GEMM with direct-to-LDS loads and copy waves (fp16 / bf16 / int8).
 // C[M, N] = A[M, K] . B[K, N]; A, B row-major; one slab = 128 bytes of an A
 // row (64 fp16 / bf16 or 128 int8 K elements), K a multiple of a slab, N a
 // multiple of BN.
 //
-// Each slab of A (BM rows x 128 bytes) and of B (one row per K element of
-// the slab, BN columns) goes
-// from global memory straight into LDS (global_load_lds_dwordx4: one wave
-// instruction fills 1 KB of LDS, lane l the 16 bytes at l * 16), so the
-// prefetch depth costs no registers: STAGES slabs live in STAGES separate
-// LDS arrays, up to STAGES - 1 of them in flight while one is multiplied.
-// A wave waits for its own copies of the next slab (s_waitcnt vmcnt), then a
-// barrier makes every wave's copies visible; the barrier also frees the
-// stage multiplied last, which then receives the slab STAGES - 1 ahead.  The
-// K loop is unrolled by STAGES so that every LDS array is named statically.
+// A workgroup has WAVES_M x WAVES_N MFMA waves and NP copy waves.  Each slab
+// of A (BM rows x 128 bytes) and of B (one row per K element of the slab, BN
+// columns) goes from global memory straight into one of STAGES LDS stages
+// (global_load_lds_dwordx4: one wave instruction fills 1 KB of LDS, lane l
+// the 16 bytes at l * 16), so the prefetch depth costs no registers.  Only
+// the copy waves issue copies and wait on the vector-memory counter; the
+// MFMA waves never wait for their output stores, which drain while the next
+// tile is multiplied.
+//
+// One barrier per slab g (B_g) orders the two roles:
+//   copy waves:  wait for their copies of slab g, B_g, copy slab
+//                g + STAGES - 1 into the stage that held slab g - 1
+//   MFMA waves:  MFMAs of slab g - 1's first K step, every LDS read of slab
+//                g - 1 back in registers (lgkmcnt 0), B_g, reads of slab g's
+//                first K step, MFMAs of slab g - 1's second K step
+// so a stage is read only after its copies have landed and overwritten only
+// after every MFMA wave has finished reading it.  The slabs of all of a
+// workgroup's tiles form one sequence (slab gs is tile gs / nk, slab
+// gs % nk, stage gs % STAGES); both roles step through it incrementally.
 //
 // LDS layouts (bank-conflict swizzles, done by choosing which global chunk
 // each lane copies, since a copy's LDS destination is fixed):
@@ -389,7 +398,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
 //            operand (column n, 8 or 16 consecutive k) comes from two
 //            transposing reads: ds_read_b64_tr_b16 (4 rows x 4 columns per
 //            16-lane group) or ds_read_b64_tr_b8 (8 rows x 8 columns).
-// Waves are laid out WAVES_M x WAVES_N, each owning a (BM / WAVES_M) x
+// MFMA waves are laid out WAVES_M x WAVES_N, each owning a (BM / WAVES_M) x
 // (BN / WAVES_N) block of 16 x 16 MFMA tiles.  Tile order is the same
 // XCD-aware grouped order as gemm_tiled_kernel.  Results go from the
 // accumulators straight to global memory (lane: one row, four consecutive
@@ -447,37 +456,37 @@ __device__ __forceinline__ uint2 lds_tr8(const uint8_t* p) {
     return __builtin_bit_cast(uint2, r);
 }
 
-template <int E, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int GM, class Epi>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_lds_kernel(
+template <int E, int BM, int BN, int WAVES_M, int WAVES_N, int NP, int STAGES, int GM, class Epi>
+__global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP)) void gemm_lds_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
-    int M, int Nt, int nk, Epi epi) {
+    int M, int Nt, int nk, int S, Epi epi) {
     constexpr int ES = (E == kI8) ? 1 : 2;    // bytes per element
     constexpr int KE = 128 / ES;              // K elements per slab (128 bytes of an A row)
-    constexpr int NW = WAVES_M * WAVES_N;
+    constexpr int NC = WAVES_M * WAVES_N;     // MFMA waves
     constexpr int A_ST = BM * 128;            // A bytes per stage
     constexpr int BRB = BN * ES;              // bytes per B row
     constexpr int B_ST = KE * BRB;            // B bytes per stage (KE rows)
     constexpr int STAGE = A_ST + B_ST;
-    constexpr int A_PW = A_ST / 1024 / NW, B_PW = B_ST / 1024 / NW;
-    static_assert(A_PW * NW * 1024 == A_ST && B_PW * NW * 1024 == B_ST, "even copy split");
+    constexpr int A_PW = A_ST / 1024 / NP, B_PW = B_ST / 1024 / NP;
+    static_assert(A_PW * NP * 1024 == A_ST && B_PW * NP * 1024 == B_ST, "even copy split");
     static_assert(BRB % 128 == 0 || (E == kI8 && BRB == 192), "B row swizzle groups");
-    constexpr int PW = A_PW + B_PW;           // copy instructions per wave per slab
+    constexpr int PW = A_PW + B_PW;           // copy instructions per copy wave per slab
+    static_assert(STAGES >= 2 && (STAGES - 2) * PW < 64, "stages / vmcnt range");
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, TM = WM / 16, TN = WN / 16;
-    static_assert(STAGES >= 2 && STAGES <= 4, "stages");
-    __shared__ __align__(1024) uint8_t st0[STAGE];
-    __shared__ __align__(1024) uint8_t st1[STAGE];
-    __shared__ __align__(1024) uint8_t st2[STAGES > 2 ? STAGE : 16];
-    __shared__ __align__(1024) uint8_t st3[STAGES > 3 ? STAGE : 16];
+    // 2-byte results are staged per wave (16 rows x 128 bytes) so that every
+    // store writes whole 128-byte lines
+    constexpr bool STAGE_OUT = sizeof(typename Epi::out_t) == 2;
+    static_assert(!STAGE_OUT || WN * 2 == 128, "one 128-byte row segment per wave");
+    constexpr int OUT_ST = STAGE_OUT ? NC * 2048 : 0;
+    __shared__ __align__(1024) uint8_t smem[STAGES * STAGE + OUT_ST];
 
-    // ---- tiles of this workgroup: workgroup b runs on XCD b % 8; XCD x
-    // owns the contiguous tile range [x per, (x + 1) per) of the grouped
-    // order and its workgroups walk it in steps of (grid / 8).  The slabs of
-    // all of a workgroup's tiles form one pipeline: the first slabs of the
-    // next tile are copied while the last ones of the current tile are
-    // multiplied, and a tile's output stores drain while the next is
-    // multiplied.
+    // ---- work items: (tile, K split) pairs, split-major, so that an XCD's
+    // range holds the tiles of one split.  Workgroup b runs on XCD b % 8;
+    // XCD x owns the contiguous item range [x per, (x + 1) per) of the
+    // grouped order and its workgroups walk it in steps of (grid / 8).  Item
+    // (t, s) covers slabs [s nk, (s + 1) nk) of K.
     const int Mt = (M + BM - 1) / BM;
-    const int tiles = Mt * Nt;
+    const int tiles = Mt * Nt * S;
     const int per = (tiles + 7) / 8;
     const int x = blockIdx.x & 7, nwx = gridDim.x >> 3;
     const int first = x * per + (blockIdx.x >> 3);
@@ -486,8 +495,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_lds_kernel(
     if (ntl == 0) return;
     const int total = ntl * nk;  // slabs of all tiles, in order
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    auto tile_origin = [&](int i, int& m0, int& n0) {
-        const int t = first + i * nwx;
+    auto tile_origin = [&](int i, int& m0, int& n0, int& sk) {
+        const int w = first + i * nwx;
+        sk = w / (Mt * Nt);
+        const int t = w - sk * (Mt * Nt);
         const int grp = t / (GM * Nt);
         const int gm = min(GM, Mt - grp * GM);
         const int q = t - grp * GM * Nt;
@@ -495,41 +506,68 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_lds_kernel(
         n0 = (q / gm) * BN;
     };
 
-    // ---- copy sources: instruction u of this wave covers LDS bytes
-    // [(wave + NW u) KB, +1 KB) of the A (resp. B) part of a stage
-    int arow[A_PW], acol[A_PW];
-#pragma unroll
-    for (int u = 0; u < A_PW; ++u) {
-        arow[u] = (wave + NW * u) * 8 + (lane >> 3);
-        acol[u] = ((lane & 7) ^ ((arow[u] >> 1) & 7)) * 16;
-    }
-    int64_t boff[B_PW];
-#pragma unroll
-    for (int u = 0; u < B_PW; ++u) {
-        const int byte = (wave + NW * u) * 1024 + lane * 16;
-        const int k = byte / BRB, pos = (byte % BRB) / 16;
-        boff[u] = (int64_t)k * ldb + (pos ^ bswz<E, BRB>(k)) * 16;
-    }
-    const int64_t bstep = KE * ldb;           // bytes of B per slab
-
-    // wave-uniform LDS offset of this wave's first 1 KB block in a stage
-    const uint32_t wofs = (uint32_t)__builtin_amdgcn_readfirstlane(wave * 1024);
-    // copy slab gs of the pipeline (slab gs % nk of tile gs / nk)
-    auto issue = [&](int gs, const uint8_t* stg) {
-        const int i = gs / nk, kc = gs - i * nk;
-        int m0, n0;
-        tile_origin(i, m0, n0);
-        const uint32_t base = lds_addr(stg) + wofs;
+    if (wave >= NC) {
+        // ================= copy wave p =================
+        // instruction u covers LDS bytes [(p + NP u) KB, +1 KB) of the A
+        // (resp. B) part of a stage
+        const int p = wave - NC;
+        int arow[A_PW], acol[A_PW];
 #pragma unroll
         for (int u = 0; u < A_PW; ++u) {
-            const int grow = min(m0 + arow[u], M - 1);
-            dma16(A + (int64_t)grow * lda + (int64_t)kc * 128 + acol[u], base + u * NW * 1024);
+            arow[u] = (p + NP * u) * 8 + (lane >> 3);
+            acol[u] = ((lane & 7) ^ ((arow[u] >> 1) & 7)) * 16;
         }
+        int64_t boff[B_PW];
 #pragma unroll
-        for (int u = 0; u < B_PW; ++u)
-            dma16(B + kc * bstep + (int64_t)n0 * ES + boff[u], base + A_ST + u * NW * 1024);
-    };
+        for (int u = 0; u < B_PW; ++u) {
+            const int byte = (p + NP * u) * 1024 + lane * 16;
+            const int k = byte / BRB, pos = (byte % BRB) / 16;
+            boff[u] = (int64_t)k * ldb + (pos ^ bswz<E, BRB>(k)) * 16;
+        }
+        const int64_t bstep = KE * ldb;  // bytes of B per slab
+        const uint32_t base0 =
+            lds_addr(smem) + (uint32_t)__builtin_amdgcn_readfirstlane(p * 1024);
+        const uint8_t* pa[A_PW];
+        const uint8_t* pb[B_PW];
+        // next slab to copy: slab kc of item ti, into the stage at byte sofs
+        int ti = 0, kc = 0;
+        uint32_t sofs = 0;
+        auto issue = [&]() {
+            if (kc == 0) {
+                int m0, n0, sk;
+                tile_origin(ti, m0, n0, sk);
+                const int64_t k0 = (int64_t)sk * nk;  // first slab of the item's split
+#pragma unroll
+                for (int u = 0; u < A_PW; ++u)
+                    pa[u] = A + (int64_t)min(m0 + arow[u], M - 1) * lda + k0 * 128 + acol[u];
+#pragma unroll
+                for (int u = 0; u < B_PW; ++u) pb[u] = B + k0 * bstep + (int64_t)n0 * ES + boff[u];
+            }
+            const uint32_t base = base0 + sofs;
+#pragma unroll
+            for (int u = 0; u < A_PW; ++u) dma16(pa[u] + kc * 128, base + u * NP * 1024);
+#pragma unroll
+            for (int u = 0; u < B_PW; ++u)
+                dma16(pb[u] + kc * bstep, base + A_ST + u * NP * 1024);
+            sofs = (sofs + STAGE == (uint32_t)(STAGES * STAGE)) ? 0u : sofs + STAGE;
+            if (++kc == nk) {
+                kc = 0;
+                ++ti;
+            }
+        };
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; ++s)
+            if (s < total) issue();
+        for (int g = 0; g < total; ++g) {
+            // slabs g + 1 .. g + STAGES - 2 may stay in flight
+            if (g + STAGES - 2 < total) wait_copies_barrier<(STAGES - 2) * PW>();
+            else wait_copies_barrier<0>();
+            if (g + STAGES - 1 < total) issue();
+        }
+        return;
+    }
 
+    // ================= MFMA waves =================
     const int wm0 = (wave / WAVES_N) * WM, wn0 = (wave % WAVES_N) * WN;
     typedef typename Acc<E>::type acc_t;
     acc_t acc[TM][TN];
@@ -582,49 +620,78 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_lds_kernel(
             for (int j = 0; j < TN; ++j) acc[i][j] = mfma16<E>(fb[buf][j], fa[buf][i], acc[i][j]);
     };
 
-    // ---- epilogue of tile ti: lane holds output row (l16) and columns
-    // 4 g .. 4 g + 3 of each 16 x 16 MFMA tile
-    auto epilogue = [&](int ti) {
-        int m0, n0;
-        tile_origin(ti, m0, n0);
+    // ---- epilogue of the tile at (m0, n0), split sk: lane holds output row
+    // (l16) and columns 4 g .. 4 g + 3 of each 16 x 16 MFMA tile
+    auto epilogue = [&](int m0, int n0, int sk) {
         typedef typename Epi::out_t out_t;
         float cs[TN][4];
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v) cs[j][v] = epi.col_scale(n0 + wn0 + j * 16 + g * 4 + v);
+        if constexpr (STAGE_OUT) {
+            // per row of MFMA tiles: the lanes' 8-byte pieces go to this
+            // wave's 16 x 128-byte LDS area (16-byte chunk c of row r at
+            // c ^ (r & 7)), then come back as whole rows: lane l reads chunk
+            // l % 8 of rows l / 8 and l / 8 + 8 and stores 16 bytes each, so
+            // one store covers 8 full 128-byte lines.  LDS accesses of one
+            // wave complete in order, so the area is reused without waits.
+            uint8_t* ep = smem + STAGES * STAGE + wave * 2048;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int row = m0 + wm0 + i * 16 + l16;
-            if (row >= M) continue;
-            const typename Epi::row_t rs = epi.row_scale(row);
+            for (int i = 0; i < TM; ++i) {
+                const int row = m0 + wm0 + i * 16 + l16;
+                const typename Epi::row_t rs = epi.row_scale(min(row, M - 1));
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int col = n0 + wn0 + j * 16 + g * 4;
-                out_t o[4];
+                for (int j = 0; j < TN; ++j) {
+                    const int col = n0 + wn0 + j * 16 + g * 4;
+                    out_t o[4];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) o[v] = epi.value(row, col + v, acc[i][j][v], rs, cs[j][v]);
-                if constexpr (sizeof(out_t) == 2)
-                    *(u2_t*)epi.ptr(row, col, 0) = u2_t{(uint32_t)o[0] | ((uint32_t)o[1] << 16),
-                                                        (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
-                else
-                    *(u4_t*)epi.ptr(row, col, 0) = u4_t{__builtin_bit_cast(uint32_t, o[0]),
-                                                        __builtin_bit_cast(uint32_t, o[1]),
-                                                        __builtin_bit_cast(uint32_t, o[2]),
-                                                        __builtin_bit_cast(uint32_t, o[3])};
+                    for (int v = 0; v < 4; ++v)
+                        o[v] = epi.value(row, col + v, acc[i][j][v], rs, cs[j][v]);
+                    const int ch = (2 * j + (g >> 1)) ^ (l16 & 7);
+                    *(u2_t*)(ep + l16 * 128 + ch * 16 + (g & 1) * 8) =
+                        u2_t{(uint32_t)o[0] | ((uint32_t)o[1] << 16),
+                             (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
+                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int r = (lane >> 3) + 8 * h;
+                    const u4_t v = *(const u4_t*)(ep + r * 128 + (((lane & 7) ^ (r & 7)) << 4));
+                    const int grow = m0 + wm0 + i * 16 + r;
+                    if (grow < M) *(u4_t*)epi.ptr(grow, n0 + wn0 + (lane & 7) * 8, sk) = v;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int row = m0 + wm0 + i * 16 + l16;
+                if (row >= M) continue;
+                const typename Epi::row_t rs = epi.row_scale(row);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int col = n0 + wn0 + j * 16 + g * 4;
+                    out_t o[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        o[v] = epi.value(row, col + v, acc[i][j][v], rs, cs[j][v]);
+                    *(u4_t*)epi.ptr(row, col, sk) = u4_t{__builtin_bit_cast(uint32_t, o[0]),
+                                                         __builtin_bit_cast(uint32_t, o[1]),
+                                                         __builtin_bit_cast(uint32_t, o[2]),
+                                                         __builtin_bit_cast(uint32_t, o[3])};
+                }
             }
         }
     };
 
     // Software pipeline over (slab, K step): the reads of the next K step are
-    // in flight while the MFMAs of the current one run, and the barrier that
-    // hands over the next slab sits between the two K steps of a slab:
-    //   rd(k,1)  mma(k,0)  [wait slab k+1, barrier, copy slab k+S]  rd(k+1,0)  mma(k,1)
-    // Before the barrier a wave has all of its reads of slab k back in
-    // registers (lgkmcnt 0), so the copy into slab k's stage that follows
-    // the barrier overwrites nothing still being read.
-    auto step = [&](int gs, const uint8_t* cur, const uint8_t* nxt) {
-        const int kc = gs % nk;
+    // in flight while the MFMAs of the current one run, and barrier B_(g+1)
+    // sits between the two K steps of slab g:
+    //   rd(g,1)  mma(g,0)  [lgkmcnt 0, B_(g+1)]  rd(g+1,0)  mma(g,1)
+    int ti = 0, kc = 0;
+    const uint8_t* cur = smem;
+    asm volatile("s_barrier" ::: "memory");  // B_0: slab 0 in place
+    rd(cur, 0, 0);
+    for (int gs = 0; gs < total; ++gs) {
         if (kc == 0) {
 #pragma unroll
             for (int i = 0; i < TM; ++i)
@@ -633,42 +700,20 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_lds_kernel(
         }
         rd(cur, 1, 1);
         mma(0);
+        const uint8_t* nxt = (cur + STAGE == smem + STAGES * STAGE) ? smem : cur + STAGE;
         if (gs + 1 < total) {
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            if (gs + STAGES - 1 < total) wait_copies_barrier<(STAGES - 2) * PW>();
-            else wait_copies_barrier<0>();
-            if (gs + STAGES < total) issue(gs + STAGES, cur);
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             rd(nxt, 0, 0);
         }
         mma(1);
-        if (kc == nk - 1) epilogue(gs / nk);
-    };
-
-#pragma unroll
-    for (int p = 0; p < STAGES - 1; ++p)
-        if (p < total) issue(p, p == 0 ? st0 : (p == 1 ? st1 : st2));
-    // slab 0 in place (slabs 1 .. STAGES - 2 may still be on their way), slab
-    // STAGES - 1 requested, first K step read
-    if (STAGES - 2 < total) wait_copies_barrier<(STAGES - 2) * PW>();
-    else wait_copies_barrier<0>();
-    if (STAGES - 1 < total) issue(STAGES - 1, STAGES == 2 ? st1 : (STAGES == 3 ? st2 : st3));
-    rd(st0, 0, 0);
-    // slab gs lives in stage gs % STAGES; step(gs, its stage, the stage of
-    // slab gs + 1); the stage of gs then receives slab gs + STAGES
-    for (int gs = 0; gs < total; gs += STAGES) {
-        if constexpr (STAGES == 2) {
-            step(gs, st0, st1);
-            if (gs + 1 < total) step(gs + 1, st1, st0);
-        } else if constexpr (STAGES == 3) {
-            step(gs, st0, st1);
-            if (gs + 1 < total) step(gs + 1, st1, st2);
-            if (gs + 2 < total) step(gs + 2, st2, st0);
-        } else {
-            step(gs, st0, st1);
-            if (gs + 1 < total) step(gs + 1, st1, st2);
-            if (gs + 2 < total) step(gs + 2, st2, st3);
-            if (gs + 3 < total) step(gs + 3, st3, st0);
+        if (++kc == nk) {
+            int m0, n0, sk;
+            tile_origin(ti, m0, n0, sk);
+            epilogue(m0, n0, sk);
+            kc = 0;
+            ++ti;
         }
+        cur = nxt;
     }
 }
 
@@ -898,18 +943,20 @@ static void gemm_launch(const void* A, int64_t lda, const void* B, int64_t ldb, 
 
 constexpr int64_t kPersistentGrid = 256;  // MI355X compute units
 
-template <int E, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, class Epi>
+// K is split S ways (S must divide K's slab count); split s writes its
+// partial through epi.ptr(row, col, s).
+template <int E, int BM, int BN, int WAVES_M, int WAVES_N, int NP, int STAGES, class Epi>
 static void gemm_lds_launch(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M,
-                            int N, int K, Epi epi, hipStream_t st) {
+                            int N, int K, int S, Epi epi, hipStream_t st) {
     constexpr int GM = 4;
-    const int64_t tiles = ((M + BM - 1) / BM) * (N / BN);
+    const int64_t tiles = ((M + BM - 1) / BM) * (N / BN) * S;
     // one workgroup per CU (the stages fill most of the LDS); each walks
     // its XCD's tiles
     const int64_t grid = std::min<int64_t>(((tiles + 7) / 8) * 8, kPersistentGrid);
-    hipLaunchKernelGGL((gemm_lds_kernel<E, BM, BN, WAVES_M, WAVES_N, STAGES, GM, Epi>),
-                       dim3((unsigned)grid), dim3(64 * WAVES_M * WAVES_N), 0, st,
+    hipLaunchKernelGGL((gemm_lds_kernel<E, BM, BN, WAVES_M, WAVES_N, NP, STAGES, GM, Epi>),
+                       dim3((unsigned)grid), dim3(64 * (WAVES_M * WAVES_N + NP)), 0, st,
                        (const uint8_t*)A, lda, (const uint8_t*)B, ldb, (int)M, N / BN,
-                       K * (E == kI8 ? 1 : 2) / 128, epi);
+                       K * (E == kI8 ? 1 : 2) / 128 / S, S, epi);
 }
 
 // kv_a_proj tiles: BN = 64 always (576 = 9 x 64)
@@ -932,7 +979,7 @@ static void gemm2_dispatch(int bm, int bn, const void* A, int64_t lda, const voi
     const int64_t ldb = (int64_t)N2 * ((E == kI8) ? 1 : 2);
     const int kslabs = (E == kI8) ? kR / 128 : kR * 2 / 128;
     if (bm >= 128) {
-        gemm_lds_launch<E, 256, 128, 4, 2, 3>(A, lda, B, ldb, M, N2, kR, epi, st);
+        gemm_lds_launch<E, 256, 128, 4, 2, 4, 3>(A, lda, B, ldb, M, N2, kR, 1, epi, st);
         return;
     }
     if (bn == 128) {
@@ -967,9 +1014,12 @@ static hipError_t launch_fp_t(const void* X, const void* Wa, const void* gamma, 
     const WsFp w = ws_fp(T, plan);
     float* P1 = (float*)((uint8_t*)ws + w.p1);
     const int kslabs1 = H * 2 / 128;
-    if (plan.dma1)
-        gemm_lds_launch<E, 64, 192, 1, 4, 4>(X, (int64_t)H * 2, Wa, (int64_t)kN1 * 2, T, kN1, H,
-                                             EpiPartialF32{P1, T}, st);
+    if (plan.dma1 && plan.bm1 == 128)
+        gemm_lds_launch<E, 128, 192, 2, 4, 4, 4>(X, (int64_t)H * 2, Wa, (int64_t)kN1 * 2, T, kN1,
+                                                 H, plan.s1, EpiPartialF32{P1, T}, st);
+    else if (plan.dma1)
+        gemm_lds_launch<E, 64, 192, 2, 4, 4, 4>(X, (int64_t)H * 2, Wa, (int64_t)kN1 * 2, T, kN1, H,
+                                                plan.s1, EpiPartialF32{P1, T}, st);
     else
         gemm1_dispatch<E>(plan.bm1, X, (int64_t)H * 2, Wa, T, kslabs1, plan.s1,
                           EpiPartialF32{P1, T}, st);
@@ -1018,9 +1068,12 @@ hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa, const
             default: hipLaunchKernelGGL(quant_rows_bf16_kernel<0>, grid, blk, 0, st, x, H, QX, sx); break;
         }
     }
-    if (plan.dma1)
-        gemm_lds_launch<kI8, 64, 192, 1, 4, 4>(QX, (int64_t)H, Wqa, (int64_t)kN1, T, kN1, H,
-                                               EpiPartialI32{P1, T}, st);
+    if (plan.dma1 && plan.bm1 == 128)
+        gemm_lds_launch<kI8, 128, 192, 2, 4, 4, 4>(QX, (int64_t)H, Wqa, (int64_t)kN1, T, kN1, H,
+                                                   plan.s1, EpiPartialI32{P1, T}, st);
+    else if (plan.dma1)
+        gemm_lds_launch<kI8, 64, 192, 2, 4, 4, 4>(QX, (int64_t)H, Wqa, (int64_t)kN1, T, kN1, H,
+                                                  plan.s1, EpiPartialI32{P1, T}, st);
     else
         gemm1_dispatch<kI8>(plan.bm1, QX, (int64_t)H, Wqa, T, H / 128, plan.s1,
                             EpiPartialI32{P1, T}, st);
