@@ -144,6 +144,8 @@ inline WsFp ws_fp(int64_t T, const Plan& p) {
 
 // W8A8 path: int8 codes of x [T][H], their scales [T], int32 split-K partials
 // [s1][T][576], int8 codes of z [T][512], their scales [T], RMS factors [T]
+// (the last two padded to a multiple of 256 tokens: the kv_b_proj epilogue
+// reads them in whole 256-row tiles)
 struct WsW8 {
     size_t qx, sx, p1, qz, sz, inv, total;
 };
@@ -154,8 +156,9 @@ inline WsW8 ws_w8(int64_t T, int H, const Plan& p) {
     w.sx = o; o += align256((size_t)T * 4);
     w.p1 = o; o += align256((size_t)p.s1 * (size_t)T * kN1 * 4);
     w.qz = o; o += align256((size_t)T * kR);
-    w.sz = o; o += align256((size_t)T * 4);
-    w.inv = o; o += align256((size_t)T * 4);
+    const size_t tpad = (size_t)((T + 255) / 256) * 256;
+    w.sz = o; o += tpad * 4;
+    w.inv = o; o += tpad * 4;
     w.total = o;
     return w;
 }

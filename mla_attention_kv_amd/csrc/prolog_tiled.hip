@@ -108,10 +108,26 @@ __device__ __forceinline__ uint16_t* kv_dst(uint16_t* k_nope, uint16_t* value, i
     const int h = col >> 8, sl = col & 255;
     return ((sl < kDN) ? k_nope : value) + ((int64_t)row * nh + h) * kDN + (sl & 127);
 }
+// Two results rounded to nearest even into one packed 2-byte pair
+// (v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32).
+typedef float f2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+template <int OE>
+__device__ __forceinline__ uint32_t cvt_pk(float a, float b) {
+    if constexpr (OE == kF16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, h2_t));
+    else return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, b2_t));
+}
+
+// Epilogues with 2-byte results also give valuef() (the result before
+// rounding; kOut names its storage type) and say whether they carry an
+// accumulator debug copy (kDbg, dbg_store()).
 template <int E>
 struct EpiKvFp {
     typedef uint16_t out_t;
     typedef NoScale row_t;
+    static constexpr int kOut = E;
+    static constexpr bool kDbg = false;
     uint16_t* k_nope;
     uint16_t* value_out;
     int nh;
@@ -120,15 +136,17 @@ struct EpiKvFp {
     __device__ __forceinline__ uint16_t value(int, int, float v, row_t, float) const {
         return f32_to_st<E>(v);
     }
+    __device__ __forceinline__ float valuef(float v, row_t, float) const { return v; }
+    __device__ __forceinline__ void dbg_store(int, int, float) const {}
     __device__ __forceinline__ void* ptr(int row, int col, int) const {
         return kv_dst(k_nope, value_out, nh, row, col);
     }
 };
 struct EpiKvW8 {
     typedef uint16_t out_t;
-    struct row_t {
-        float sz, inv;
-    };
+    typedef float row_t;  // the token's activation scale times its RMS factor
+    static constexpr int kOut = kBF16;
+    static constexpr bool kDbg = true;
     uint16_t* k_nope;
     uint16_t* value_out;
     int nh;
@@ -137,12 +155,20 @@ struct EpiKvW8 {
     const float* swb;
     int32_t* dbg;
     int64_t dbg_begin, dbg_rows;
-    __device__ __forceinline__ row_t row_scale(int row) const { return {sz[row], inv_t[row]}; }
+    __device__ __forceinline__ row_t row_scale(int row) const { return sz[row] * inv_t[row]; }
     __device__ __forceinline__ float col_scale(int col) const { return swb[col]; }
     __device__ __forceinline__ uint16_t value(int row, int col, int acc, row_t rs, float cs) const {
         if (dbg != nullptr && row >= dbg_begin && row < dbg_begin + dbg_rows)
             dbg[(row - dbg_begin) * (int64_t)nh * kHeadW + col] = acc;
-        return f32_to_bf16((((float)acc * rs.sz) * rs.inv) * cs);
+        return f32_to_bf16(((float)acc * rs) * cs);
+    }
+    __device__ __forceinline__ float valuef(int acc, row_t rs, float cs) const {
+        return ((float)acc * rs) * cs;
+    }
+    // the raw accumulator of (row, col), kept when row is in the debug range
+    __device__ __forceinline__ void dbg_store(int row, int col, int acc) const {
+        if (row >= dbg_begin && row < dbg_begin + dbg_rows)
+            dbg[(row - dbg_begin) * (int64_t)nh * kHeadW + col] = acc;
     }
     __device__ __forceinline__ void* ptr(int row, int col, int) const {
         return kv_dst(k_nope, value_out, nh, row, col);
@@ -456,8 +482,10 @@ __device__ __forceinline__ uint2 lds_tr8(const uint8_t* p) {
     return __builtin_bit_cast(uint2, r);
 }
 
-template <int E, int BM, int BN, int WAVES_M, int WAVES_N, int NP, int STAGES, int GM, class Epi>
-__global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP)) void gemm_lds_kernel(
+template <int E, int BM, int BN, int WAVES_M, int WAVES_N, int NP, int STAGES, int GM, int WGPC,
+          class Epi>
+__global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP),
+                             (WGPC * (WAVES_M * WAVES_N + NP) + 3) / 4) void gemm_lds_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     int M, int Nt, int nk, int S, Epi epi) {
     constexpr int ES = (E == kI8) ? 1 : 2;    // bytes per element
@@ -564,6 +592,8 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP)) void gemm_lds_kernel
             else wait_copies_barrier<0>();
             if (g + STAGES - 1 < total) issue();
         }
+        // the MFMA waves' last barrier (after their last slab's first K step)
+        asm volatile("s_barrier" ::: "memory");
         return;
     }
 
@@ -629,7 +659,24 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP)) void gemm_lds_kernel
         for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v) cs[j][v] = epi.col_scale(n0 + wn0 + j * 16 + g * 4 + v);
+        typename Epi::row_t rsv[TM];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) rsv[i] = epi.row_scale(min(m0 + wm0 + i * 16 + l16, M - 1));
         if constexpr (STAGE_OUT) {
+            if constexpr (Epi::kDbg) {
+                if (epi.dbg != nullptr) {
+#pragma unroll
+                    for (int i = 0; i < TM; ++i) {
+                        const int row = m0 + wm0 + i * 16 + l16;
+                        if (row >= M) continue;
+#pragma unroll
+                        for (int j = 0; j < TN; ++j)
+#pragma unroll
+                            for (int v = 0; v < 4; ++v)
+                                epi.dbg_store(row, n0 + wn0 + j * 16 + g * 4 + v, acc[i][j][v]);
+                    }
+                }
+            }
             // per row of MFMA tiles: the lanes' 8-byte pieces go to this
             // wave's 16 x 128-byte LDS area (16-byte chunk c of row r at
             // c ^ (r & 7)), then come back as whole rows: lane l reads chunk
@@ -639,19 +686,14 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP)) void gemm_lds_kernel
             uint8_t* ep = smem + STAGES * STAGE + wave * 2048;
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
-                const int row = m0 + wm0 + i * 16 + l16;
-                const typename Epi::row_t rs = epi.row_scale(min(row, M - 1));
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
-                    const int col = n0 + wn0 + j * 16 + g * 4;
-                    out_t o[4];
+                    float f[4];
 #pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        o[v] = epi.value(row, col + v, acc[i][j][v], rs, cs[j][v]);
+                    for (int v = 0; v < 4; ++v) f[v] = epi.valuef(acc[i][j][v], rsv[i], cs[j][v]);
                     const int ch = (2 * j + (g >> 1)) ^ (l16 & 7);
                     *(u2_t*)(ep + l16 * 128 + ch * 16 + (g & 1) * 8) =
-                        u2_t{(uint32_t)o[0] | ((uint32_t)o[1] << 16),
-                             (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
+                        u2_t{cvt_pk<Epi::kOut>(f[0], f[1]), cvt_pk<Epi::kOut>(f[2], f[3])};
                 }
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
@@ -666,14 +708,13 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP)) void gemm_lds_kernel
             for (int i = 0; i < TM; ++i) {
                 const int row = m0 + wm0 + i * 16 + l16;
                 if (row >= M) continue;
-                const typename Epi::row_t rs = epi.row_scale(row);
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     const int col = n0 + wn0 + j * 16 + g * 4;
                     out_t o[4];
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
-                        o[v] = epi.value(row, col + v, acc[i][j][v], rs, cs[j][v]);
+                        o[v] = epi.value(row, col + v, acc[i][j][v], rsv[i], cs[j][v]);
                     *(u4_t*)epi.ptr(row, col, sk) = u4_t{__builtin_bit_cast(uint32_t, o[0]),
                                                          __builtin_bit_cast(uint32_t, o[1]),
                                                          __builtin_bit_cast(uint32_t, o[2]),
@@ -683,11 +724,25 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP)) void gemm_lds_kernel
         }
     };
 
+    // every LDS read of this wave complete (lgkmcnt 0; a waitcnt the compiler
+    // sees, so it adds no wait of its own), then the workgroup barrier
+    auto reads_done_barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);  // keep the MFMAs above ahead of the wait
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
     // Software pipeline over (slab, K step): the reads of the next K step are
     // in flight while the MFMAs of the current one run, and barrier B_(g+1)
     // sits between the two K steps of slab g:
     //   rd(g,1)  mma(g,0)  [lgkmcnt 0, B_(g+1)]  rd(g+1,0)  mma(g,1)
-    int ti = 0, kc = 0;
+    // After the last slab the same steps run once more with nothing to
+    // multiply: its barrier meets the copy waves' final one and its reads of
+    // an idle stage are discarded, which keeps the loop free of branches
+    // around the MFMAs (the compiler then adds no waits inside them).
+    int ti = 0, kc = 0, m0 = 0, n0 = 0, sk = 0;
     const uint8_t* cur = smem;
     asm volatile("s_barrier" ::: "memory");  // B_0: slab 0 in place
     rd(cur, 0, 0);
@@ -697,18 +752,19 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP)) void gemm_lds_kernel
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
+            tile_origin(ti, m0, n0, sk);
         }
+        // the previous K step's reads (issued a whole K step of MFMAs ago)
+        // are complete: said explicitly, so that the compiler does not wait
+        // for the reads issued next before the first MFMA
+        __builtin_amdgcn_s_waitcnt(0xC07F);
         rd(cur, 1, 1);
         mma(0);
         const uint8_t* nxt = (cur + STAGE == smem + STAGES * STAGE) ? smem : cur + STAGE;
-        if (gs + 1 < total) {
-            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            rd(nxt, 0, 0);
-        }
+        reads_done_barrier();
+        rd(nxt, 0, 0);
         mma(1);
         if (++kc == nk) {
-            int m0, n0, sk;
-            tile_origin(ti, m0, n0, sk);
             epilogue(m0, n0, sk);
             kc = 0;
             ++ti;
@@ -944,16 +1000,16 @@ static void gemm_launch(const void* A, int64_t lda, const void* B, int64_t ldb, 
 constexpr int64_t kPersistentGrid = 256;  // MI355X compute units
 
 // K is split S ways (S must divide K's slab count); split s writes its
-// partial through epi.ptr(row, col, s).
-template <int E, int BM, int BN, int WAVES_M, int WAVES_N, int NP, int STAGES, class Epi>
+// partial through epi.ptr(row, col, s).  WGPC workgroups share a CU (their
+// stages must fit its LDS together); each walks its XCD's tiles.
+template <int E, int BM, int BN, int WAVES_M, int WAVES_N, int NP, int STAGES, class Epi,
+          int WGPC = 1>
 static void gemm_lds_launch(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M,
                             int N, int K, int S, Epi epi, hipStream_t st) {
     constexpr int GM = 4;
     const int64_t tiles = ((M + BM - 1) / BM) * (N / BN) * S;
-    // one workgroup per CU (the stages fill most of the LDS); each walks
-    // its XCD's tiles
-    const int64_t grid = std::min<int64_t>(((tiles + 7) / 8) * 8, kPersistentGrid);
-    hipLaunchKernelGGL((gemm_lds_kernel<E, BM, BN, WAVES_M, WAVES_N, NP, STAGES, GM, Epi>),
+    const int64_t grid = std::min<int64_t>(((tiles + 7) / 8) * 8, kPersistentGrid * WGPC);
+    hipLaunchKernelGGL((gemm_lds_kernel<E, BM, BN, WAVES_M, WAVES_N, NP, STAGES, GM, WGPC, Epi>),
                        dim3((unsigned)grid), dim3(64 * (WAVES_M * WAVES_N + NP)), 0, st,
                        (const uint8_t*)A, lda, (const uint8_t*)B, ldb, (int)M, N / BN,
                        K * (E == kI8 ? 1 : 2) / 128 / S, S, epi);
