@@ -774,8 +774,9 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP),
 }
 
 // ---------------------------------------------------------------------------
-// Per-token finish of kv_a_proj, fp16/bf16 path.  One wave per token: lane l
-// owns latent columns 8l..8l+7 and rope column l.
+// Per-token finish of kv_a_proj, fp16/bf16 path.  One wave per token, four
+// tokens per workgroup: lane l owns latent columns 8l..8l+7 and rope column
+// l.  Every load (position, gamma, partials) is issued before the first use.
 //   c, p  = sum of the split-K partials (split order ascending)
 //   y     = c / sqrt(sum(c^2)/512 + eps) * gamma      -> compressed_kv
 //   k_pe  = rotate-half RoPE of p at the token's position
@@ -784,14 +785,18 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP),
 // (rope_cos_sin).
 // ---------------------------------------------------------------------------
 template <int E>
-__global__ __launch_bounds__(64) void finish_a_fp_kernel(
+__global__ __launch_bounds__(256) void finish_a_fp_kernel(
     const float* __restrict__ P, int S, int64_t T, const uint16_t* __restrict__ gamma,
     const int32_t* __restrict__ pos, float eps, RopeTab rt, uint16_t* __restrict__ ckv,
     uint16_t* __restrict__ kpe) {
-    const int64_t t = blockIdx.x;
-    const int lane = threadIdx.x;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const int lane = threadIdx.x & 63;
+    const int pt = pos[t];
+    const u4_t g = *(const u4_t*)(gamma + 8 * lane);
     float c[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float p = 0.f;
+#pragma unroll 2
     for (int s = 0; s < S; ++s) {
         const float* row = P + ((int64_t)s * T + t) * kN1;
         const f4_t v0 = *(const f4_t*)(row + 8 * lane);
@@ -808,7 +813,6 @@ __global__ __launch_bounds__(64) void finish_a_fp_kernel(
     for (int i = 0; i < 8; ++i) ss += c[i] * c[i];
     ss = wave_sum(ss);
     const float inv = 1.0f / sqrtf(ss / (float)kR + eps);
-    const u4_t g = *(const u4_t*)(gamma + 8 * lane);
     u4_t o;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -822,7 +826,7 @@ __global__ __launch_bounds__(64) void finish_a_fp_kernel(
 
     const float partner = __shfl_xor(p, 32, 64);
     float cs, sn;
-    rope_cos_sin(pos[t], rt.f[lane & 31], cs, sn);
+    rope_cos_sin(pt, rt.f[lane & 31], cs, sn);
     const float out = (lane < 32) ? (p * cs - partner * sn) : (p * cs + partner * sn);
     kpe[t * kDR + lane] = f32_to_st<E>(out);
 }
@@ -860,6 +864,34 @@ __device__ __forceinline__ float absmax8(const u4_t v, float amax) {
         amax = fmaxf(amax, fabsf(bf16_to_f32((uint16_t)(v[w] >> 16))));
     }
     return amax;
+}
+
+// One wave per token row (four rows per workgroup), NCH 16-byte chunks per
+// lane (chunk lane + 64 u), all loaded before the first wait; the row maximum
+// is a wave reduction, so no LDS or barrier is involved.
+template <int NCH>
+__global__ __launch_bounds__(256) void quant_rows_wave_kernel(const uint16_t* __restrict__ X,
+                                                              int H, int64_t T,
+                                                              int8_t* __restrict__ Q,
+                                                              float* __restrict__ scale) {
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const int lane = threadIdx.x & 63;
+    const uint16_t* row = X + t * H;
+    const int nch = H >> 3;
+    u4_t v[NCH];
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) v[u] = *(const u4_t*)(row + 8 * min(lane + 64 * u, nch - 1));
+    float amax = 0.f;
+#pragma unroll
+    for (int u = 0; u < NCH; ++u)
+        if (lane + 64 * u < nch) amax = absmax8(v[u], amax);
+    amax = wave_max(amax);
+    const float inv = (amax > 0.f) ? (127.0f / amax) : 0.f;
+#pragma unroll
+    for (int u = 0; u < NCH; ++u)
+        if (lane + 64 * u < nch) *(u2_t*)(Q + t * H + 8 * (lane + 64 * u)) = quant8(v[u], inv);
+    if (lane == 0) scale[t] = (amax > 0.f) ? (amax / 127.0f) : 0.f;
 }
 
 template <int NC>
@@ -909,16 +941,24 @@ __global__ __launch_bounds__(256) void quant_rows_bf16_kernel(const uint16_t* __
 //   inv_t = 1/sqrt(sum(c^2)/512 + eps);  compressed_kv = bf16(z * inv_t)
 //   k_pe = RoPE(p)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void finish_a_w8_kernel(
+__global__ __launch_bounds__(256) void finish_a_w8_kernel(
     const int32_t* __restrict__ P, int S, int64_t T, const float* __restrict__ sx,
     const float* __restrict__ swa, const uint16_t* __restrict__ gamma,
     const int32_t* __restrict__ pos, float eps, RopeTab rt, int8_t* __restrict__ QZ,
     float* __restrict__ sz, float* __restrict__ inv_out, uint16_t* __restrict__ ckv,
     uint16_t* __restrict__ kpe, int32_t* __restrict__ dbg, int64_t dbg_begin, int64_t dbg_rows) {
-    const int64_t t = blockIdx.x;
-    const int lane = threadIdx.x;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const int lane = threadIdx.x & 63;
+    // every load before the first use
+    const int pt = pos[t];
+    const float sxt = sx[t];
+    const f4_t wa0 = *(const f4_t*)(swa + 8 * lane), wa1 = *(const f4_t*)(swa + 8 * lane + 4);
+    const float wap = swa[kR + lane];
+    const u4_t gm = *(const u4_t*)(gamma + 8 * lane);
     int a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     int ap = 0;
+#pragma unroll 2
     for (int s = 0; s < S; ++s) {
         const int32_t* row = P + ((int64_t)s * T + t) * kN1;
         const i4_t v0 = *(const i4_t*)(row + 8 * lane);
@@ -936,19 +976,18 @@ __global__ __launch_bounds__(64) void finish_a_w8_kernel(
         for (int i = 0; i < 8; ++i) d[8 * lane + i] = a[i];
         d[kR + lane] = ap;
     }
-    const float sxt = sx[t];
     float c[8], z[8];
     float ss = 0.f, az = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int col = 8 * lane + i;
-        c[i] = ((float)a[i] * sxt) * swa[col];
-        const uint16_t gb = gamma[col];
+        const float w = i < 4 ? wa0[i] : wa1[i - 4];
+        c[i] = ((float)a[i] * sxt) * w;
+        const uint16_t gb = (uint16_t)(gm[i >> 1] >> (16 * (i & 1)));
         z[i] = c[i] * bf16_to_f32(gb);
         ss += c[i] * c[i];
         az = fmaxf(az, fabsf(z[i]));
     }
-    const float p = ((float)ap * sxt) * swa[kR + lane];
+    const float p = ((float)ap * sxt) * wap;
     ss = wave_sum(ss);
     az = wave_max(az);
     const float inv_t = 1.0f / sqrtf(ss / (float)kR + eps);
@@ -977,7 +1016,7 @@ __global__ __launch_bounds__(64) void finish_a_w8_kernel(
     }
     const float partner = __shfl_xor(p, 32, 64);
     float cs, sn;
-    rope_cos_sin(pos[t], rt.f[lane & 31], cs, sn);
+    rope_cos_sin(pt, rt.f[lane & 31], cs, sn);
     const float out = (lane < 32) ? (p * cs - partner * sn) : (p * cs + partner * sn);
     kpe[t * kDR + lane] = f32_to_bf16(out);
 }
@@ -1053,13 +1092,13 @@ static void gemm2_dispatch(int bm, int bn, const void* A, int64_t lda, const voi
 void launch_finish_fp(int dt, const float* P, int S, int64_t T, const void* gamma,
                       const int32_t* pos, float eps, const RopeTab& rt, void* ckv, void* kpe,
                       hipStream_t st) {
+    const dim3 grid((unsigned)((T + 3) / 4)), blk(256);  // four tokens per workgroup
     if (dt == kF16)
-        hipLaunchKernelGGL(finish_a_fp_kernel<kF16>, dim3((unsigned)T), dim3(64), 0, st, P, S, T,
+        hipLaunchKernelGGL(finish_a_fp_kernel<kF16>, grid, blk, 0, st, P, S, T,
                            (const uint16_t*)gamma, pos, eps, rt, (uint16_t*)ckv, (uint16_t*)kpe);
     else
-        hipLaunchKernelGGL(finish_a_fp_kernel<kBF16>, dim3((unsigned)T), dim3(64), 0, st, P, S,
-                           T, (const uint16_t*)gamma, pos, eps, rt, (uint16_t*)ckv,
-                           (uint16_t*)kpe);
+        hipLaunchKernelGGL(finish_a_fp_kernel<kBF16>, grid, blk, 0, st, P, S, T,
+                           (const uint16_t*)gamma, pos, eps, rt, (uint16_t*)ckv, (uint16_t*)kpe);
 }
 
 template <int E>
@@ -1114,14 +1153,22 @@ hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa, const
     float* sz = (float*)(base + w.sz);
     float* inv = (float*)(base + w.inv);
     {
-        const dim3 grid((unsigned)T), blk(256);
+        // rows of up to 8192 elements: one wave per row; longer rows: one
+        // workgroup per row, walked twice
+        const dim3 g4((unsigned)((T + 3) / 4)), blk(256);
         const uint16_t* x = (const uint16_t*)X;
-        switch ((H + 2047) / 2048) {
-            case 1: hipLaunchKernelGGL(quant_rows_bf16_kernel<1>, grid, blk, 0, st, x, H, QX, sx); break;
-            case 2: hipLaunchKernelGGL(quant_rows_bf16_kernel<2>, grid, blk, 0, st, x, H, QX, sx); break;
-            case 3: hipLaunchKernelGGL(quant_rows_bf16_kernel<3>, grid, blk, 0, st, x, H, QX, sx); break;
-            case 4: hipLaunchKernelGGL(quant_rows_bf16_kernel<4>, grid, blk, 0, st, x, H, QX, sx); break;
-            default: hipLaunchKernelGGL(quant_rows_bf16_kernel<0>, grid, blk, 0, st, x, H, QX, sx); break;
+        switch ((H + 511) / 512) {
+#define MLA_QUANT_WAVE(n)                                                                     \
+    case n: hipLaunchKernelGGL(quant_rows_wave_kernel<n>, g4, blk, 0, st, x, H, T, QX, sx); break;
+            MLA_QUANT_WAVE(1) MLA_QUANT_WAVE(2) MLA_QUANT_WAVE(3) MLA_QUANT_WAVE(4)
+            MLA_QUANT_WAVE(5) MLA_QUANT_WAVE(6) MLA_QUANT_WAVE(7) MLA_QUANT_WAVE(8)
+            MLA_QUANT_WAVE(9) MLA_QUANT_WAVE(10) MLA_QUANT_WAVE(11) MLA_QUANT_WAVE(12)
+            MLA_QUANT_WAVE(13) MLA_QUANT_WAVE(14) MLA_QUANT_WAVE(15) MLA_QUANT_WAVE(16)
+#undef MLA_QUANT_WAVE
+            default:
+                hipLaunchKernelGGL(quant_rows_bf16_kernel<0>, dim3((unsigned)T), blk, 0, st, x, H,
+                                   QX, sx);
+                break;
         }
     }
     if (plan.dma1 && plan.bm1 == 128)
@@ -1133,7 +1180,8 @@ hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa, const
     else
         gemm1_dispatch<kI8>(plan.bm1, QX, (int64_t)H, Wqa, T, H / 128, plan.s1,
                             EpiPartialI32{P1, T}, st);
-    hipLaunchKernelGGL(finish_a_w8_kernel, dim3((unsigned)T), dim3(64), 0, st, P1, plan.s1, T, sx,
+    hipLaunchKernelGGL(finish_a_w8_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, P1,
+                       plan.s1, T, sx,
                        swa, (const uint16_t*)gamma, pos, eps, rt, QZ, sz, inv,
                        (uint16_t*)ckv, (uint16_t*)k_pe, dbg1, dbg_begin, dbg_rows);
     const int N2 = nh * kHeadW;
