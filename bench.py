@@ -40,9 +40,15 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(files=None) -> str:
+    """Hash of the kernel sources: the given repository-relative files, or
+    every file under the package's csrc/."""
+    if files is None:
+        paths = sorted(glob.glob(os.path.join(ROOT, "mla_attention_kv_amd", "csrc", "*")))
+    else:
+        paths = [os.path.join(ROOT, f) for f in sorted(files)]
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "mla_attention_kv_amd", "csrc", "*"))):
+    for p in paths:
         with open(p, "rb") as f:
             h.update(os.path.basename(p).encode())
             h.update(f.read())
@@ -51,13 +57,14 @@ def kernel_source_hash() -> str:
 
 def load_traffic(workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, or None
-    when they are absent or were taken on different kernel sources."""
+    when they are absent or any source file of the kernels they measured
+    (listed in the file as "sources") has changed since."""
     p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         t = json.load(f)
-    if t.get("src_hash") != kernel_source_hash():
+    if t.get("src_hash") != kernel_source_hash(t.get("sources")):
         return None
     return t.get("hbm_bytes_per_launch")
 

@@ -1,8 +1,9 @@
 // Tiled gfx950 kernels of the MLA KV prolog: both projections as MFMA GEMMs
-// (gemm_lds_kernel: persistent, slabs copied straight into a ring of LDS
-// stages, fp16 / bf16; gemm_tiled_kernel: register-staged slabs, int8 and
-// split-K), plus the per-token kernels that finish kv_a_proj (split, RMSNorm,
-// RoPE) and, on the W8A8 path, quantise the activations.
+// (gemm_lds_kernel: persistent, copy waves stream slabs straight into a ring
+// of LDS stages, fp16 / bf16 / int8, optional split-K; gemm_tiled_kernel:
+// register-staged slabs, for W8A8 calls of up to 64 tokens and the forced
+// small-tile path), plus the per-token kernels that finish kv_a_proj (split,
+// RMSNorm, RoPE) and, on the W8A8 path, quantise the activations.
 //
 // Steps follow the DeepSeek-V2-Lite-Chat MLA KV Prolog migration guide
 // (dpshk.com), sections "Background" and "Source-level principle"; RoPE is
@@ -832,13 +833,13 @@ __global__ __launch_bounds__(256) void finish_a_fp_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// W8A8: per-token activation quantisation (one 256-thread block per token).
+// W8A8: per-token activation quantisation.
 //   amax = max |x|;  q = clamp(rint(x * (127/amax)), -127, 127);
 //   scale = amax / 127;  amax == 0 -> q = 0, scale = 0.
-// fp32 with IEEE division and round-half-even rint.  With NC > 0 (rows of at
-// most NC * 2048 elements) every thread loads its NC 16-byte chunks once,
-// all before the first wait, and quantises them from registers; NC = 0 walks
-// the row twice.
+// fp32 with IEEE division and round-half-even rint.  Rows of up to 8192
+// elements: one wave per row, every chunk held in registers
+// (quant_rows_wave_kernel); longer rows: one 256-thread workgroup per row
+// that walks it twice (quant_rows_long_kernel).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ u2_t quant8(const u4_t v, float inv) {
     u2_t q;
@@ -894,8 +895,7 @@ __global__ __launch_bounds__(256) void quant_rows_wave_kernel(const uint16_t* __
     if (lane == 0) scale[t] = (amax > 0.f) ? (amax / 127.0f) : 0.f;
 }
 
-template <int NC>
-__global__ __launch_bounds__(256) void quant_rows_bf16_kernel(const uint16_t* __restrict__ X,
+__global__ __launch_bounds__(256) void quant_rows_long_kernel(const uint16_t* __restrict__ X,
                                                               int H, int8_t* __restrict__ Q,
                                                               float* __restrict__ scale) {
     __shared__ float red[4];
@@ -903,34 +903,14 @@ __global__ __launch_bounds__(256) void quant_rows_bf16_kernel(const uint16_t* __
     const int tid = threadIdx.x;
     const uint16_t* row = X + t * H;
     float amax = 0.f;
-    u4_t v[NC > 0 ? NC : 1];
-    if constexpr (NC > 0) {
-#pragma unroll
-        for (int u = 0; u < NC; ++u) {
-            const int k = tid * 8 + u * 2048;
-            v[u] = *(const u4_t*)(row + (k < H ? k : 0));
-        }
-#pragma unroll
-        for (int u = 0; u < NC; ++u)
-            if (tid * 8 + u * 2048 < H) amax = absmax8(v[u], amax);
-    } else {
-        for (int k = tid * 8; k < H; k += 256 * 8) amax = absmax8(*(const u4_t*)(row + k), amax);
-    }
+    for (int k = tid * 8; k < H; k += 256 * 8) amax = absmax8(*(const u4_t*)(row + k), amax);
     amax = wave_max(amax);
     if ((tid & 63) == 0) red[tid >> 6] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const float inv = (amax > 0.f) ? (127.0f / amax) : 0.f;
-    if constexpr (NC > 0) {
-#pragma unroll
-        for (int u = 0; u < NC; ++u) {
-            const int k = tid * 8 + u * 2048;
-            if (k < H) *(u2_t*)(Q + t * H + k) = quant8(v[u], inv);
-        }
-    } else {
-        for (int k = tid * 8; k < H; k += 256 * 8)
-            *(u2_t*)(Q + t * H + k) = quant8(*(const u4_t*)(row + k), inv);
-    }
+    for (int k = tid * 8; k < H; k += 256 * 8)
+        *(u2_t*)(Q + t * H + k) = quant8(*(const u4_t*)(row + k), inv);
     if (tid == 0) scale[t] = (amax > 0.f) ? (amax / 127.0f) : 0.f;
 }
 
@@ -1166,8 +1146,8 @@ hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa, const
             MLA_QUANT_WAVE(13) MLA_QUANT_WAVE(14) MLA_QUANT_WAVE(15) MLA_QUANT_WAVE(16)
 #undef MLA_QUANT_WAVE
             default:
-                hipLaunchKernelGGL(quant_rows_bf16_kernel<0>, dim3((unsigned)T), blk, 0, st, x, H,
-                                   QX, sx);
+                hipLaunchKernelGGL(quant_rows_long_kernel, dim3((unsigned)T), blk, 0, st, x, H, QX,
+                                   sx);
                 break;
         }
     }

@@ -142,6 +142,16 @@ def test_w8a8_long_prefill_ragged_tail_exact(dev):
     check_full(w, dev, "w8a8_T4100", path=1, dbg=True)
 
 
+@pytest.mark.parametrize("H,T", [(640, 7), (8320, 6)])
+def test_w8a8_hidden_sizes_exact(dev, H, T):
+    # the activation quantiser: H = 640 leaves lanes with a partial last chunk
+    # (one wave per row), H = 8320 takes the long-row workgroup kernel; token
+    # counts that are not a multiple of the four rows per workgroup
+    d = Dims(H=H, nh=2)
+    w = workloads.make_custom(d, T, kind="w8a8", dtype="bf16", seed=470 + T, wstd=0.02)
+    check_full(w, dev, f"w8a8_H{H}_T{T}", path=1, dbg=True)
+
+
 @pytest.mark.parametrize("T", [9, 40])
 def test_decode_many_k_splits(dev, T):
     # more than 16 kv_a_proj K splits: the finish reads its later splits in
