@@ -63,16 +63,32 @@ Plan make_plan(int64_t T, int H, bool int8, int path) {
         p.bn2 = 128;
     }
     if (path == 1) {
-        // kv_a_proj on the pipelined kernel: 128 x 192 tiles from 2048
-        // tokens, 64 x 192 below; K split by the largest divisor of the slab
-        // count that keeps the (tile, split) items within one per CU and at
-        // least two slabs per split
+        // kv_a_proj on the pipelined kernel, tiles of 64, 128 or 160 rows by
+        // 192 columns, K split S ways (S divides the slab count, at least two
+        // slabs per split).  Chosen by a cost model: rounds of one item per CU
+        // times the bytes each item copies into LDS, plus the split-K
+        // partials written and read back (fp32/int32; the whole chip moves
+        // them ~90x faster than one CU's copy stream: ~5.5 TB/s against
+        // ~60 GB/s)
         p.dma1 = 1;
-        p.bm1 = T >= 2048 ? 128 : 64;
-        const int64_t items = ((T + p.bm1 - 1) / p.bm1) * (kN1 / 192);
-        p.s1 = 1;
-        for (int d = 2; d <= ks / 2; ++d)
-            if (ks % d == 0 && items * d <= 256) p.s1 = d;
+        const int bms[3] = {64, 128, 160};
+        double best = 0.0;
+        for (int bm : bms) {
+            const int64_t tiles = ((T + bm - 1) / bm) * (kN1 / 192);
+            for (int d = 1; d <= ks; ++d) {
+                if (ks % d != 0 || (d > 1 && ks / d < 2)) continue;
+                const int64_t items = tiles * d;
+                const double rounds = (double)((items + 255) / 256);
+                const double copy = rounds * (double)(bm + 192) * (double)ks / (double)d;
+                const double partial = (double)d * (double)T * kN1 * 8.0 / 90.0 / 128.0;
+                const double cost = copy + partial;
+                if (best == 0.0 || cost < best) {
+                    best = cost;
+                    p.bm1 = bm;
+                    p.s1 = d;
+                }
+            }
+        }
         return p;
     }
     // split kv_a_proj's K so that at least ~256 workgroups stream W_kv_a,

@@ -1089,7 +1089,10 @@ static hipError_t launch_fp_t(const void* X, const void* Wa, const void* gamma, 
     const WsFp w = ws_fp(T, plan);
     float* P1 = (float*)((uint8_t*)ws + w.p1);
     const int kslabs1 = H * 2 / 128;
-    if (plan.dma1 && plan.bm1 == 128)
+    if (plan.dma1 && plan.bm1 == 160)
+        gemm_lds_launch<E, 160, 192, 2, 4, 4, 3>(X, (int64_t)H * 2, Wa, (int64_t)kN1 * 2, T, kN1,
+                                                 H, plan.s1, EpiPartialF32{P1, T}, st);
+    else if (plan.dma1 && plan.bm1 == 128)
         gemm_lds_launch<E, 128, 192, 2, 4, 4, 4>(X, (int64_t)H * 2, Wa, (int64_t)kN1 * 2, T, kN1,
                                                  H, plan.s1, EpiPartialF32{P1, T}, st);
     else if (plan.dma1)
@@ -1151,7 +1154,10 @@ hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa, const
                 break;
         }
     }
-    if (plan.dma1 && plan.bm1 == 128)
+    if (plan.dma1 && plan.bm1 == 160)
+        gemm_lds_launch<kI8, 160, 192, 2, 4, 4, 3>(QX, (int64_t)H, Wqa, (int64_t)kN1, T, kN1, H,
+                                                   plan.s1, EpiPartialI32{P1, T}, st);
+    else if (plan.dma1 && plan.bm1 == 128)
         gemm_lds_launch<kI8, 128, 192, 2, 4, 4, 4>(QX, (int64_t)H, Wqa, (int64_t)kN1, T, kN1, H,
                                                    plan.s1, EpiPartialI32{P1, T}, st);
     else if (plan.dma1)

@@ -142,6 +142,20 @@ def test_w8a8_long_prefill_ragged_tail_exact(dev):
     check_full(w, dev, "w8a8_T4100", path=1, dbg=True)
 
 
+@pytest.mark.parametrize("kind", ["fp16", "w8a8"])
+def test_tall_kv_a_tiles(dev, kind):
+    # 12000 tokens with a short K: the dispatcher takes 160-row kv_a_proj
+    # tiles (225 tiles, one round over the CUs) and a ragged last tile
+    d = Dims(H=256, nh=2)
+    if kind == "w8a8":
+        w = workloads.make_custom(d, 12000, kind="w8a8", dtype="bf16", seed=480, wstd=0.02,
+                                  max_pos=16384)
+        check_full(w, dev, "w8a8_T12000", path=1, dbg=True)
+    else:
+        w = workloads.make_custom(d, 12000, dtype="f16", seed=481, wstd=0.05, max_pos=16384)
+        check_full(w, dev, "f16_T12000", path=1)
+
+
 @pytest.mark.parametrize("H,T", [(640, 7), (8320, 6)])
 def test_w8a8_hidden_sizes_exact(dev, H, T):
     # the activation quantiser: H = 640 leaves lanes with a partial last chunk
