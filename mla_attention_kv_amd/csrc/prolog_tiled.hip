@@ -80,6 +80,7 @@ __device__ __forceinline__ void transpose16x16_b8(const u4_t in[16], u4_t out[16
 struct NoScale {};
 struct EpiPartialF32 {  // kv_a_proj split-K partial, fp32 [s][T][576]
     typedef float out_t;
+    static constexpr bool kScaleDma = false;
     typedef NoScale row_t;
     float* out;
     int64_t T;
@@ -92,6 +93,7 @@ struct EpiPartialF32 {  // kv_a_proj split-K partial, fp32 [s][T][576]
 };
 struct EpiPartialI32 {  // kv_a_proj split-K partial, int32 [s][T][576]
     typedef int32_t out_t;
+    static constexpr bool kScaleDma = false;
     typedef NoScale row_t;
     int32_t* out;
     int64_t T;
@@ -122,13 +124,16 @@ __device__ __forceinline__ uint32_t cvt_pk(float a, float b) {
 
 // Epilogues with 2-byte results also give valuef() (the result before
 // rounding; kOut names its storage type) and say whether they carry an
-// accumulator debug copy (kDbg, dbg_store()).
+// accumulator debug copy (kDbg, dbg_store()).  kScaleDma: the pipelined
+// kernel's copy waves bring each tile's scales into LDS (scale_src());
+// row_scale2() then combines the two row values read back from there.
 template <int E>
 struct EpiKvFp {
     typedef uint16_t out_t;
     typedef NoScale row_t;
     static constexpr int kOut = E;
     static constexpr bool kDbg = false;
+    static constexpr bool kScaleDma = false;
     uint16_t* k_nope;
     uint16_t* value_out;
     int nh;
@@ -148,6 +153,19 @@ struct EpiKvW8 {
     typedef float row_t;  // the token's activation scale times its RMS factor
     static constexpr int kOut = kBF16;
     static constexpr bool kDbg = true;
+    static constexpr bool kScaleDma = true;
+    // 16-byte source of lane group q (16 lanes, 64 values) for rows m.. and
+    // columns n..: column scales (q = 0, and 3 as filler), activation scales
+    // (q = 1), RMS factors (q = 2).  The two row arrays are padded to whole
+    // 256-row tiles.
+    __device__ __forceinline__ const void* scale_src(int q, int m, int n) const {
+        // three addresses first, then a per-lane choice of value (a choice of
+        // member would make the compiler load the pointer per lane)
+        const uintptr_t a = (uintptr_t)(sz + m), b = (uintptr_t)(inv_t + m), c = (uintptr_t)(swb + n);
+        const uintptr_t r = q == 1 ? a : c;
+        return (const void*)(q == 2 ? b : r);
+    }
+    __device__ __forceinline__ row_t row_scale2(float s, float i) const { return s * i; }
     uint16_t* k_nope;
     uint16_t* value_out;
     int nh;
@@ -558,13 +576,33 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP),
             lds_addr(smem) + (uint32_t)__builtin_amdgcn_readfirstlane(p * 1024);
         const uint8_t* pa[A_PW];
         const uint8_t* pb[B_PW];
-        // next slab to copy: slab kc of item ti, into the stage at byte sofs
-        int ti = 0, kc = 0;
+        // next slab to copy: slab kc of item ti (origin tm0, tn0), into the
+        // stage at byte sofs
+        int ti = 0, kc = 0, tm0 = 0, tn0 = 0;
         uint32_t sofs = 0;
         auto issue = [&]() {
+            if constexpr (STAGE_OUT && Epi::kScaleDma) {
+                // with slab STAGES of a tile (issued after the barrier that
+                // follows the MFMA waves' previous epilogue, landed before
+                // the barrier that ends the tile): the tile's scales into
+                // the staging areas of MFMA waves p, p + NP, ...; lane group
+                // q of the 1 KB copy fills bytes 256 q .. of an area
+                if (kc == STAGES) {
+#pragma unroll
+                    for (int w = p; w < NC; w += NP) {
+                        const int r4 = (lane & 15) * 4;
+                        dma16(epi.scale_src(lane >> 4, tm0 + (w / WAVES_N) * WM + r4,
+                                            tn0 + (w % WAVES_N) * WN + r4),
+                              lds_addr(smem + STAGES * STAGE) +
+                                  (uint32_t)__builtin_amdgcn_readfirstlane(w * 2048));
+                    }
+                }
+            }
             if (kc == 0) {
                 int m0, n0, sk;
                 tile_origin(ti, m0, n0, sk);
+                tm0 = m0;
+                tn0 = n0;
                 const int64_t k0 = (int64_t)sk * nk;  // first slab of the item's split
 #pragma unroll
                 for (int u = 0; u < A_PW; ++u)
@@ -604,17 +642,17 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP),
     acc_t acc[TM][TN];
 
     const int l16 = lane & 15, g = lane >> 4;
-    // operand fragments of one K step in two register sets
-    u4_t fa[2][TM], fb[2][TN];
-    auto rd = [&](const uint8_t* stg, int ks, int buf) {
-        const uint8_t* As = stg;
+    // operand fragments: A in one register set, each row of MFMA tiles
+    // re-read for the next K step as soon as its MFMAs are issued; B (two
+    // transposing reads per fragment) in two sets, read a whole K step ahead
+    u4_t fa[TM], fb[2][TN];
+    auto rd_a = [&](const uint8_t* stg, int ks, int i) {
+        const int row = wm0 + i * 16 + l16;
+        const int c = (ks * 4 + g) ^ ((row >> 1) & 7);
+        fa[i] = *(const u4_t*)(stg + row * 128 + c * 16);
+    };
+    auto rd_b = [&](const uint8_t* stg, int ks, int buf) {
         const uint8_t* Bs = stg + A_ST;
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int row = wm0 + i * 16 + l16;
-            const int c = (ks * 4 + g) ^ ((row >> 1) & 7);
-            fa[buf][i] = *(const u4_t*)(As + row * 128 + c * 16);
-        }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             if constexpr (ES == 2) {
@@ -642,27 +680,50 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP),
             }
         }
     };
-    auto mma = [&](int buf) {
+    // MFMAs of one K step with B set `buf`, refilling A row by row from
+    // K step ks of stage stg
+    auto mma = [&](int buf, const uint8_t* stg, int ks) {
         // operands swapped (C^T = B^T A^T): lane l then holds output row
         // (l % 16) and the 4 consecutive output columns 4 (l / 16) + v
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i) {
 #pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] = mfma16<E>(fb[buf][j], fa[buf][i], acc[i][j]);
+            for (int j = 0; j < TN; ++j) acc[i][j] = mfma16<E>(fb[buf][j], fa[i], acc[i][j]);
+            rd_a(stg, ks, i);
+        }
     };
 
     // ---- epilogue of the tile at (m0, n0), split sk: lane holds output row
-    // (l16) and columns 4 g .. 4 g + 3 of each 16 x 16 MFMA tile
+    // (l16) and columns 4 g .. 4 g + 3 of each 16 x 16 MFMA tile.  The MFMA
+    // waves issue no global loads: their vector-memory counter also counts
+    // their output stores, so a load waited for here would wait for the
+    // previous tile's stores as well.
     auto epilogue = [&](int m0, int n0, int sk) {
         typedef typename Epi::out_t out_t;
         float cs[TN][4];
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) cs[j][v] = epi.col_scale(n0 + wn0 + j * 16 + g * 4 + v);
         typename Epi::row_t rsv[TM];
+        if constexpr (STAGE_OUT && Epi::kScaleDma) {
+            // the copy waves brought this tile's scales into the staging
+            // area (landed before the barrier this epilogue follows)
+            const uint8_t* sa = smem + STAGES * STAGE + wave * 2048;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) rsv[i] = epi.row_scale(min(m0 + wm0 + i * 16 + l16, M - 1));
+            for (int j = 0; j < TN; ++j) {
+                const f4_t c = *(const f4_t*)(sa + 64 * j + 16 * g);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) cs[j][v] = c[v];
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                rsv[i] = epi.row_scale2(((const float*)(sa + 256))[i * 16 + l16],
+                                        ((const float*)(sa + 512))[i * 16 + l16]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) cs[j][v] = epi.col_scale(n0 + wn0 + j * 16 + g * 4 + v);
+#pragma unroll
+            for (int i = 0; i < TM; ++i) rsv[i] = epi.row_scale(min(m0 + wm0 + i * 16 + l16, M - 1));
+        }
         if constexpr (STAGE_OUT) {
             if constexpr (Epi::kDbg) {
                 if (epi.dbg != nullptr) {
@@ -746,7 +807,9 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP),
     int ti = 0, kc = 0, m0 = 0, n0 = 0, sk = 0;
     const uint8_t* cur = smem;
     asm volatile("s_barrier" ::: "memory");  // B_0: slab 0 in place
-    rd(cur, 0, 0);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) rd_a(cur, 0, i);
+    rd_b(cur, 0, 0);
     for (int gs = 0; gs < total; ++gs) {
         if (kc == 0) {
 #pragma unroll
@@ -755,16 +818,16 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP),
                 for (int j = 0; j < TN; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
             tile_origin(ti, m0, n0, sk);
         }
-        // the previous K step's reads (issued a whole K step of MFMAs ago)
-        // are complete: said explicitly, so that the compiler does not wait
-        // for the reads issued next before the first MFMA
+        // the previous K step's reads (issued during its MFMAs) are complete:
+        // said explicitly, so that the compiler does not wait for the reads
+        // issued next before the first MFMA
         __builtin_amdgcn_s_waitcnt(0xC07F);
-        rd(cur, 1, 1);
-        mma(0);
+        rd_b(cur, 1, 1);
+        mma(0, cur, 1);
         const uint8_t* nxt = (cur + STAGE == smem + STAGES * STAGE) ? smem : cur + STAGE;
         reads_done_barrier();
-        rd(nxt, 0, 0);
-        mma(1);
+        rd_b(nxt, 0, 0);
+        mma(1, nxt, 0);
         if (++kc == nk) {
             epilogue(m0, n0, sk);
             kc = 0;
@@ -1047,7 +1110,9 @@ static void gemm1_dispatch(int bm, const void* A, int64_t lda, const void* B, in
     }
 }
 
-// kv_b_proj tiles
+// kv_b_proj tiles.  The W8A8 epilogue's scales travel with slab STAGES of
+// each tile, so a tile needs more slabs than the kernel has stages.
+static_assert(kR / 128 > 3, "int8 kv_b_proj: slabs per tile > stages");
 template <int E, class Epi>
 static void gemm2_dispatch(int bm, int bn, const void* A, int64_t lda, const void* B, int64_t M,
                            int N2, Epi epi, hipStream_t st) {
