@@ -60,7 +60,8 @@ __device__ __forceinline__ void stage_load(u4_t (&v)[NR], const uint16_t* W, int
     for (int r = 0; r < NR; ++r) {
         int k = k0 + r0 + 32 * r;
         if (CHECK) k = k < kmax ? k : kmax - 1;
-        v[r] = *(const u4_t*)(W + (int64_t)k * ld + n0 + 8 * q);
+        // weights are read once per call: streaming (non-temporal) loads
+        v[r] = __builtin_nontemporal_load((const u4_t*)(W + (int64_t)k * ld + n0 + 8 * q));
     }
 }
 template <int NR, bool CHECK = true>
@@ -251,9 +252,10 @@ __device__ __forceinline__ void fin_load(FinPart& r, const float* __restrict__ P
     for (int u = 0; u < 4; ++u) {
         const int sp = s0 + 4 * u < S ? s0 + 4 * u : S - 1;
         const float* row = P + ((int64_t)sp * T + t) * kN1;
-        r.v0[u] = *(const f4_t*)(row + 8 * lane);
-        r.v1[u] = *(const f4_t*)(row + 8 * lane + 4);
-        r.vp[u] = row[kR + lane];
+        // partials are read once: streaming loads
+        r.v0[u] = __builtin_nontemporal_load((const f4_t*)(row + 8 * lane));
+        r.v1[u] = __builtin_nontemporal_load((const f4_t*)(row + 8 * lane + 4));
+        r.vp[u] = __builtin_nontemporal_load(row + kR + lane);
     }
 }
 __device__ __forceinline__ void fin_load_aux(FinPart& r, const uint16_t* __restrict__ gamma,

@@ -863,14 +863,15 @@ __global__ __launch_bounds__(256) void finish_a_fp_kernel(
 #pragma unroll 2
     for (int s = 0; s < S; ++s) {
         const float* row = P + ((int64_t)s * T + t) * kN1;
-        const f4_t v0 = *(const f4_t*)(row + 8 * lane);
-        const f4_t v1 = *(const f4_t*)(row + 8 * lane + 4);
+        // partials are read once: streaming (non-temporal) loads
+        const f4_t v0 = __builtin_nontemporal_load((const f4_t*)(row + 8 * lane));
+        const f4_t v1 = __builtin_nontemporal_load((const f4_t*)(row + 8 * lane + 4));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             c[i] += v0[i];
             c[4 + i] += v1[i];
         }
-        p += row[kR + lane];
+        p += __builtin_nontemporal_load(row + kR + lane);
     }
     float ss = 0.f;
 #pragma unroll
@@ -945,7 +946,8 @@ __global__ __launch_bounds__(256) void quant_rows_wave_kernel(const uint16_t* __
     const int nch = H >> 3;
     u4_t v[NCH];
 #pragma unroll
-    for (int u = 0; u < NCH; ++u) v[u] = *(const u4_t*)(row + 8 * min(lane + 64 * u, nch - 1));
+    for (int u = 0; u < NCH; ++u)  // read once: streaming (non-temporal) loads
+        v[u] = __builtin_nontemporal_load((const u4_t*)(row + 8 * min(lane + 64 * u, nch - 1)));
     float amax = 0.f;
 #pragma unroll
     for (int u = 0; u < NCH; ++u)
@@ -1004,14 +1006,15 @@ __global__ __launch_bounds__(256) void finish_a_w8_kernel(
 #pragma unroll 2
     for (int s = 0; s < S; ++s) {
         const int32_t* row = P + ((int64_t)s * T + t) * kN1;
-        const i4_t v0 = *(const i4_t*)(row + 8 * lane);
-        const i4_t v1 = *(const i4_t*)(row + 8 * lane + 4);
+        // partials are read once: streaming (non-temporal) loads
+        const i4_t v0 = __builtin_nontemporal_load((const i4_t*)(row + 8 * lane));
+        const i4_t v1 = __builtin_nontemporal_load((const i4_t*)(row + 8 * lane + 4));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             a[i] += v0[i];
             a[4 + i] += v1[i];
         }
-        ap += row[kR + lane];
+        ap += __builtin_nontemporal_load(row + kR + lane);
     }
     if (dbg != nullptr && t >= dbg_begin && t < dbg_begin + dbg_rows) {
         int32_t* d = dbg + (t - dbg_begin) * kN1;
