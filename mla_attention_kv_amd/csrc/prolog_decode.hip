@@ -403,7 +403,7 @@ __global__ __launch_bounds__(256) void dec_kv_b_kernel(const uint16_t* __restric
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int tok = t0 + tt * 16 + 4 * g + i;
-            if (tok < T) dst[(int64_t)tok * nh * kDN] = f32_to_st<E>(acc[tt][i]);
+            if (tok < T) __builtin_nontemporal_store(f32_to_st<E>(acc[tt][i]), dst + (int64_t)tok * nh * kDN);
         }
 }
 
@@ -502,7 +502,7 @@ __global__ __launch_bounds__(256) void dec_fin_kv_b_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int tok = t0 + 4 * g + i;
-        if (tok < T) dst[(int64_t)tok * nh * kDN] = f32_to_st<E>(acc[0][i]);
+        if (tok < T) __builtin_nontemporal_store(f32_to_st<E>(acc[0][i]), dst + (int64_t)tok * nh * kDN);
     }
 }
 

@@ -762,7 +762,9 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP),
                     const int r = (lane >> 3) + 8 * h;
                     const u4_t v = *(const u4_t*)(ep + r * 128 + (((lane & 7) ^ (r & 7)) << 4));
                     const int grow = m0 + wm0 + i * 16 + r;
-                    if (grow < M) *(u4_t*)epi.ptr(grow, n0 + wn0 + (lane & 7) * 8, sk) = v;
+                    // written once, never re-read here: streaming stores
+                    if (grow < M)
+                        __builtin_nontemporal_store(v, (u4_t*)epi.ptr(grow, n0 + wn0 + (lane & 7) * 8, sk));
                 }
             }
         } else {
