@@ -779,6 +779,7 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP),
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
                         o[v] = epi.value(row, col + v, acc[i][j][v], rsv[i], cs[j][v]);
+                    // split-K partials are read back right away: cached stores
                     *(u4_t*)epi.ptr(row, col, sk) = u4_t{__builtin_bit_cast(uint32_t, o[0]),
                                                          __builtin_bit_cast(uint32_t, o[1]),
                                                          __builtin_bit_cast(uint32_t, o[2]),
@@ -895,7 +896,7 @@ __global__ __launch_bounds__(256) void finish_a_fp_kernel(
     float cs, sn;
     rope_cos_sin(pt, rt.f[lane & 31], cs, sn);
     const float out = (lane < 32) ? (p * cs - partner * sn) : (p * cs + partner * sn);
-    kpe[t * kDR + lane] = f32_to_st<E>(out);
+    __builtin_nontemporal_store(f32_to_st<E>(out), kpe + t * kDR + lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1066,7 +1067,7 @@ __global__ __launch_bounds__(256) void finish_a_w8_kernel(
     float cs, sn;
     rope_cos_sin(pt, rt.f[lane & 31], cs, sn);
     const float out = (lane < 32) ? (p * cs - partner * sn) : (p * cs + partner * sn);
-    kpe[t * kDR + lane] = f32_to_bf16(out);
+    __builtin_nontemporal_store(f32_to_bf16(out), kpe + t * kDR + lane);
 }
 
 // ---------------------------------------------------------------------------
