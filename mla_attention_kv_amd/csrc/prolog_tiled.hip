@@ -437,17 +437,24 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
 //   A stage: [BM rows][8 chunks of 16 bytes]; chunk c of row r sits at
 //            position c ^ ((r >> 1) & 7).  An MFMA A operand (16 rows, one
 //            chunk each) then touches 16 distinct 16-byte bank groups.
-//   B stage: [64 k rows][BN columns]; 16-byte chunk c of row k sits at
+//   B stage: [KE k rows][BN columns] (64 rows of fp16 / bf16, 128 of
+//            int8); 16-byte chunk c of row k sits at
 //            c ^ (2 (k & 3) + 8 ((k >> 3) & 1)) (c ^ 2 (k & 3) when a row is
 //            not a multiple of 16 chunks; c ^ (k & 7) for int8).  The B
 //            operand (column n, 8 or 16 consecutive k) comes from two
 //            transposing reads: ds_read_b64_tr_b16 (4 rows x 4 columns per
 //            16-lane group) or ds_read_b64_tr_b8 (8 rows x 8 columns).
 // MFMA waves are laid out WAVES_M x WAVES_N, each owning a (BM / WAVES_M) x
-// (BN / WAVES_N) block of 16 x 16 MFMA tiles.  Tile order is the same
-// XCD-aware grouped order as gemm_tiled_kernel.  Results go from the
-// accumulators straight to global memory (lane: one row, four consecutive
-// columns).
+// (BN / WAVES_N) block of 16 x 16 MFMA tiles; A fragments are held once and
+// refilled row by row as their MFMAs issue, B fragments in two sets a K step
+// ahead.  Tile order is the same XCD-aware grouped order as
+// gemm_tiled_kernel.  Epilogue: 2-byte results are rounded in pairs, staged
+// in the wave's own 2 KB of LDS and stored as whole 128-byte lines with
+// streaming stores; fp32 / int32 split-K partials are stored from the
+// accumulators (lane: one row, four consecutive columns).  The MFMA waves
+// issue no global loads (their vector-memory counter also counts their
+// stores): epilogue scales, where there are any, arrive in the staging area
+// through the copy waves.
 // ---------------------------------------------------------------------------
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint2 lds_tr16(const uint8_t* p) {
