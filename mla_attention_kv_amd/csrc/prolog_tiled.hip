@@ -479,6 +479,20 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
         : "s"(lds), "v"(g)
         : "memory");
 }
+// The same copy with the non-temporal (streaming) hint, for data that no
+// other workgroup reads.
+__device__ __forceinline__ void dma16_nt(const void* g, uint32_t lds) {
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, off nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "s"(lds), "v"(g)
+        : "memory");
+}
 // Wait until at most N of this wave's copies are outstanding, then
 // barrier; a compiler memory barrier as well.
 template <int N>
@@ -620,9 +634,17 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP),
             const uint32_t base = base0 + sofs;
 #pragma unroll
             for (int u = 0; u < A_PW; ++u) dma16(pa[u] + kc * 128, base + u * NP * 1024);
+            if (Mt == 1) {
+                // a single row of tiles: each B slab is read by this
+                // workgroup only
 #pragma unroll
-            for (int u = 0; u < B_PW; ++u)
-                dma16(pb[u] + kc * bstep, base + A_ST + u * NP * 1024);
+                for (int u = 0; u < B_PW; ++u)
+                    dma16_nt(pb[u] + kc * bstep, base + A_ST + u * NP * 1024);
+            } else {
+#pragma unroll
+                for (int u = 0; u < B_PW; ++u)
+                    dma16(pb[u] + kc * bstep, base + A_ST + u * NP * 1024);
+            }
             sofs = (sofs + STAGE == (uint32_t)(STAGES * STAGE)) ? 0u : sofs + STAGE;
             if (++kc == nk) {
                 kc = 0;
