@@ -42,6 +42,10 @@ def _load():
         [i64] * 7 + [vp] * 7 + [dbl, dbl] + [vp] * 4 + [vp] * 6 + [i32]
     )
     lib.oracle_kv_prolog_w8a8.restype = i32
+    lib.oracle_kv_cache_append.argtypes = [i64, i64, i64, vp, vp, vp, i64, vp]
+    lib.oracle_kv_cache_append.restype = i32
+    lib.oracle_kv_cache_append_int8.argtypes = [i64, i64, i64, vp, vp, vp, i64, vp, vp]
+    lib.oracle_kv_cache_append_int8.restype = i32
     lib.oracle_num_threads.argtypes = [i32]
     lib.oracle_num_threads.restype = i32
     _lib = lib
@@ -144,3 +148,36 @@ def kv_prolog_w8a8(X, Wqa, swa, gamma, Wqb, swb, pos, *, r, dr, nh, dn, dv,
     if rc != 0:
         raise RuntimeError(f"oracle_kv_prolog_w8a8 failed: {rc}")
     return out
+
+
+def kv_cache_append(ckv, kpe, slots, cache) -> np.ndarray:
+    """Paged KV-cache append (fp): returns a copy of ``cache`` [num_slots,
+    r + dr] with token t's [ckv row | kpe row] in slot ``slots[t]`` (slots
+    outside [0, num_slots) skip the token)."""
+    ckv, kpe = _c(ckv, np.float64), _c(kpe, np.float64)
+    slots = _c(slots, np.int64)
+    out = _c(cache, np.float64).copy()
+    T, r = ckv.shape
+    dr = kpe.shape[1]
+    rc = _load().oracle_kv_cache_append(T, r, dr, _ptr(ckv), _ptr(kpe), _ptr(slots),
+                                        out.shape[0], _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_kv_cache_append failed: {rc}")
+    return out
+
+
+def kv_cache_append_int8(ckv, kpe, slots, cache_q, scale):
+    """Paged KV-cache append into an int8 cache with one fp32 scale per slot
+    (the W8A8 activation scheme over the slot's r + dr values); returns
+    copies of ``cache_q`` [num_slots, r + dr] and ``scale`` [num_slots]."""
+    ckv, kpe = _c(ckv, np.float32), _c(kpe, np.float32)
+    slots = _c(slots, np.int64)
+    q = _c(cache_q, np.int8).copy()
+    sc = _c(scale, np.float32).copy()
+    T, r = ckv.shape
+    dr = kpe.shape[1]
+    rc = _load().oracle_kv_cache_append_int8(T, r, dr, _ptr(ckv), _ptr(kpe), _ptr(slots),
+                                             q.shape[0], _ptr(q), _ptr(sc))
+    if rc != 0:
+        raise ValueError(f"oracle_kv_cache_append_int8 failed: {rc}")
+    return q, sc

@@ -395,6 +395,69 @@ int oracle_kv_prolog_w8a8(int64_t T, int64_t H, int64_t r, int64_t dr,
     return bad ? ORACLE_NOMEM : ORACLE_OK;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Paged KV-cache append (the step after "assemble").                         */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * MLA caches the normalised latent and the rotated rope key of every token
+ * (the smaller KV cache is the point of the method: migration guide,
+ * "Background"); the R1 recipe page names paged attention ("Benchmark") and
+ * an int8-cache mode W8A8C8 ("Weight conversion") without a layout or a
+ * formula.  The reading implemented here:
+ *   - the cache is num_slots slots of (r + dr) values, slot s holding
+ *     [compressed_kv row | k_pe row]; a paged cache of blocks of B slots is
+ *     the same array with slot = block * B + offset;
+ *   - token t goes to slot slots[t]; a slot outside [0, num_slots) means the
+ *     token is not cached (for example -1 for a padding token); slots of
+ *     different tokens are distinct; slots not mapped keep their contents.
+ * fp cache: the values themselves (the prolog's outputs, already in the model
+ * dtype), no arithmetic.
+ */
+int oracle_kv_cache_append(int64_t T, int64_t r, int64_t dr, const double* ckv,
+                           const double* kpe, const int64_t* slots, int64_t num_slots,
+                           double* cache)
+{
+    if (T < 0 || r < 0 || dr < 0 || num_slots < 0 || (T > 0 && (!ckv || !kpe || !slots)) ||
+        (num_slots > 0 && !cache))
+        return ORACLE_BAD_ARG;
+    const int64_t W = r + dr;
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t s = slots[t];
+        if (s < 0 || s >= num_slots) continue;
+        for (int64_t j = 0; j < r; ++j) cache[s * W + j] = ckv[t * r + j];
+        for (int64_t i = 0; i < dr; ++i) cache[s * W + r + i] = kpe[t * dr + i];
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * int8 ("C8") cache: each mapped slot's r + dr values (the model-dtype
+ * values, exact in fp32) quantised together by quantize_row above -- the
+ * same symmetric per-token scheme as the W8A8 activations -- giving codes
+ * [num_slots, r + dr] and one fp32 scale per slot (value ~ code * scale).
+ */
+int oracle_kv_cache_append_int8(int64_t T, int64_t r, int64_t dr, const float* ckv,
+                                const float* kpe, const int64_t* slots, int64_t num_slots,
+                                int8_t* cache_q, float* scale)
+{
+    if (T < 0 || r < 0 || dr < 0 || num_slots < 0 || (T > 0 && (!ckv || !kpe || !slots)) ||
+        (num_slots > 0 && (!cache_q || !scale)))
+        return ORACLE_BAD_ARG;
+    const int64_t W = r + dr;
+    float* row = (float*)malloc((size_t)(W > 0 ? W : 1) * sizeof(float));
+    if (!row) return ORACLE_NOMEM;
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t s = slots[t];
+        if (s < 0 || s >= num_slots) continue;
+        for (int64_t j = 0; j < r; ++j) row[j] = ckv[t * r + j];
+        for (int64_t i = 0; i < dr; ++i) row[r + i] = kpe[t * dr + i];
+        scale[s] = quantize_row(row, W, cache_q + s * W);
+    }
+    free(row);
+    return ORACLE_OK;
+}
+
 /* Number of threads an OpenMP parallel region of this library uses. */
 int oracle_num_threads(int nthreads)
 {
