@@ -142,6 +142,48 @@ mla_status_t mla_kv_prolog_w8a8(const void* hidden_bf16, const int8_t* Wq_kv_a,
                                 int32_t* dbg_acc2, int64_t dbg_row_begin, int64_t dbg_rows,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Paged KV-cache append: the step after "assemble".  MLA caches, per token,
+ * the normalised latent and the rotated rope key (the smaller KV cache is the
+ * point of the method: migration guide, section "Background"); the R1 recipe
+ * page names paged attention ("Benchmark") and an int8-cache mode W8A8C8
+ * ("Weight conversion") but fixes no layout or formula.  Layout used here:
+ * the cache is num_slots slots of r + dr values; slot s holds
+ * [compressed_kv row | k_pe row].  A paged cache of blocks of B slots is the
+ * same array with slot = block * B + offset.
+ *   compressed_kv [T, r]  dt, k_pe [T, dr] dt  (the prolog's outputs)
+ *   slot_mapping  [T]     int64: token t goes to slot slot_mapping[t]; a
+ *                         value outside [0, num_slots) (e.g. -1 for a
+ *                         padding token) skips the token.  The kernels test
+ *                         every value, so no mapping writes outside the
+ *                         cache.  Slots of different tokens must be distinct
+ *                         (precondition: otherwise the result is any one of
+ *                         the tokens).
+ *   kv_cache      [num_slots, r + dr]  dt (in/out; only mapped slots change)
+ * Supported: r = 512, dr = 64 (d's other fields are not used).
+ * compressed_kv, k_pe and the caches 16-byte aligned, slot_mapping 8-byte and
+ * kv_scale 4-byte aligned.  T == 0 or num_slots == 0 launches nothing.
+ * Errors as for the prolog (checked before any launch).
+ */
+mla_status_t mla_kv_cache_append(const void* compressed_kv, const void* k_pe,
+                                 const int64_t* slot_mapping, int64_t T, mla_dims_t d,
+                                 mla_dtype_t dt, void* kv_cache, int64_t num_slots,
+                                 void* stream);
+
+/*
+ * The same into an int8 ("C8") cache with one fp32 scale per slot: the
+ * slot's r + dr values are quantised together by the W8A8 activation scheme
+ * (fp32, round half to even): amax = max |v|, code = clamp(rint(v *
+ * (127/amax)), +-127), scale = amax / 127; a zero row gives codes 0, scale 0.
+ * Value ~ code * scale.
+ *   kv_cache_q [num_slots, r + dr] int8 (in/out), kv_scale [num_slots] fp32
+ *   (in/out; only mapped slots change)
+ */
+mla_status_t mla_kv_cache_append_int8(const void* compressed_kv, const void* k_pe,
+                                      const int64_t* slot_mapping, int64_t T, mla_dims_t d,
+                                      mla_dtype_t dt, int8_t* kv_cache_q, float* kv_scale,
+                                      int64_t num_slots, void* stream);
+
 /* The kernel family the dispatcher picks for T tokens: 0 = decode
  * (weight-streaming, small T), 1 = prefill (MFMA-tiled, large T). */
 int mla_kv_prolog_selected_path(int64_t T, mla_dims_t d);

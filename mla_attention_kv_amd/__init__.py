@@ -35,6 +35,8 @@ EXPORTS = (
     "mla_kv_prolog",
     "mla_kv_prolog_w8a8_workspace_size",
     "mla_kv_prolog_w8a8",
+    "mla_kv_cache_append",
+    "mla_kv_cache_append_int8",
     "mla_kv_prolog_selected_path",
     "mla_kv_prolog_force_path",
     "mla_status_string",
@@ -90,6 +92,10 @@ def lib() -> ctypes.CDLL:
     L.mla_kv_prolog_w8a8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, mla_dims_t, f32, f32,
                                      vp, vp, vp, vp, vp, vp, i64, i64, vp, sz, vp]
     L.mla_kv_prolog_w8a8.restype = i32
+    L.mla_kv_cache_append.argtypes = [vp, vp, vp, i64, mla_dims_t, i32, vp, i64, vp]
+    L.mla_kv_cache_append.restype = i32
+    L.mla_kv_cache_append_int8.argtypes = [vp, vp, vp, i64, mla_dims_t, i32, vp, vp, i64, vp]
+    L.mla_kv_cache_append_int8.restype = i32
     L.mla_kv_prolog_selected_path.argtypes = [i64, mla_dims_t]
     L.mla_kv_prolog_selected_path.restype = i32
     L.mla_kv_prolog_force_path.argtypes = [i32]
@@ -267,3 +273,55 @@ def mla_kv_prolog_w8a8(hidden, Wq_kv_a, s_kv_a, gamma, Wq_kv_b, s_kv_b, position
     if st != MLA_OK:
         raise MlaError(st, "mla_kv_prolog_w8a8")
     return outs
+
+
+def _cache_inputs(compressed_kv, k_pe, slot_mapping, r=512, dr=64):
+    torch = _torch()
+    code = {torch.float16: MLA_F16, torch.bfloat16: MLA_BF16}.get(compressed_kv.dtype)
+    if code is None:
+        raise ValueError(f"compressed_kv: dtype {compressed_kv.dtype}, expected float16/bfloat16")
+    T = compressed_kv.shape[0]
+    dev = compressed_kv.device
+    _check(compressed_kv, "compressed_kv", compressed_kv.dtype, (T, r), dev)
+    _check(k_pe, "k_pe", compressed_kv.dtype, (T, dr), dev)
+    _check(slot_mapping, "slot_mapping", torch.int64, (T,), dev)
+    return code, T, dev
+
+
+def mla_kv_cache_append(compressed_kv, k_pe, slot_mapping, kv_cache, *, stream=None):
+    """Write each token's [compressed_kv row | k_pe row] into slot
+    slot_mapping[t] of kv_cache ([num_slots, 576] or [blocks, block_size,
+    576], same dtype, contiguous); slots outside [0, num_slots) skip the
+    token.  Returns kv_cache."""
+    code, T, dev = _cache_inputs(compressed_kv, k_pe, slot_mapping)
+    W = compressed_kv.shape[1] + k_pe.shape[1]
+    if kv_cache.dtype != compressed_kv.dtype or kv_cache.device != dev or kv_cache.shape[-1] != W \
+            or not kv_cache.is_contiguous():
+        raise ValueError(f"kv_cache: contiguous {compressed_kv.dtype} [..., {W}] on {dev} expected")
+    rc = lib().mla_kv_cache_append(compressed_kv.data_ptr(), k_pe.data_ptr(), slot_mapping.data_ptr(),
+                                   T, Dims(H=64, nh=1).c(), code, kv_cache.data_ptr(),
+                                   kv_cache.numel() // W, _stream_ptr(dev, stream))
+    if rc != MLA_OK:
+        raise MlaError(rc, "mla_kv_cache_append")
+    return kv_cache
+
+
+def mla_kv_cache_append_int8(compressed_kv, k_pe, slot_mapping, kv_cache_q, kv_scale, *,
+                             stream=None):
+    """The same into an int8 cache (kv_cache_q [..., 576] int8) with one fp32
+    scale per slot (kv_scale [num_slots]).  Returns (kv_cache_q, kv_scale)."""
+    torch = _torch()
+    code, T, dev = _cache_inputs(compressed_kv, k_pe, slot_mapping)
+    W = compressed_kv.shape[1] + k_pe.shape[1]
+    if kv_cache_q.dtype != torch.int8 or kv_cache_q.device != dev or kv_cache_q.shape[-1] != W \
+            or not kv_cache_q.is_contiguous():
+        raise ValueError(f"kv_cache_q: contiguous int8 [..., {W}] on {dev} expected")
+    S = kv_cache_q.numel() // W
+    _check(kv_scale, "kv_scale", torch.float32, (S,), dev)
+    rc = lib().mla_kv_cache_append_int8(compressed_kv.data_ptr(), k_pe.data_ptr(),
+                                        slot_mapping.data_ptr(), T, Dims(H=64, nh=1).c(), code,
+                                        kv_cache_q.data_ptr(), kv_scale.data_ptr(), S,
+                                        _stream_ptr(dev, stream))
+    if rc != MLA_OK:
+        raise MlaError(rc, "mla_kv_cache_append_int8")
+    return kv_cache_q, kv_scale

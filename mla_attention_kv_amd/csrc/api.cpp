@@ -235,4 +235,46 @@ mla_status_t mla_kv_prolog_w8a8(const void* hidden_bf16, const int8_t* Wq_kv_a,
     return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+static mla_status_t kv_cache_args(const void* compressed_kv, const void* k_pe,
+                                  const int64_t* slot_mapping, int64_t T, mla_dims_t d,
+                                  mla_dtype_t dt, int64_t num_slots) {
+    if (T < 0 || T > MLA_MAX_TOKENS || num_slots < 0) return MLA_ERR_INVALID_ARG;
+    if (dt != MLA_F16 && dt != MLA_BF16) return MLA_ERR_INVALID_ARG;
+    if (d.r != kR || d.dr != kDR) return MLA_ERR_UNSUPPORTED;
+    if (T == 0) return MLA_OK;
+    if (compressed_kv == nullptr || k_pe == nullptr || slot_mapping == nullptr)
+        return MLA_ERR_INVALID_ARG;
+    if (!aligned16(compressed_kv) || !aligned16(k_pe) || ((uintptr_t)slot_mapping & 7u) != 0)
+        return MLA_ERR_MISALIGNED;
+    return MLA_OK;
+}
+
+mla_status_t mla_kv_cache_append(const void* compressed_kv, const void* k_pe,
+                                 const int64_t* slot_mapping, int64_t T, mla_dims_t d,
+                                 mla_dtype_t dt, void* kv_cache, int64_t num_slots,
+                                 void* stream) {
+    const mla_status_t st = kv_cache_args(compressed_kv, k_pe, slot_mapping, T, d, dt, num_slots);
+    if (st != MLA_OK || T == 0 || num_slots == 0) return st;
+    if (kv_cache == nullptr) return MLA_ERR_INVALID_ARG;
+    if (!aligned16(kv_cache)) return MLA_ERR_MISALIGNED;
+    const hipError_t e = launch_kv_cache_append(dt, compressed_kv, k_pe, slot_mapping, T,
+                                                num_slots, kv_cache, nullptr, nullptr,
+                                                (hipStream_t)stream);
+    return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_kv_cache_append_int8(const void* compressed_kv, const void* k_pe,
+                                      const int64_t* slot_mapping, int64_t T, mla_dims_t d,
+                                      mla_dtype_t dt, int8_t* kv_cache_q, float* kv_scale,
+                                      int64_t num_slots, void* stream) {
+    const mla_status_t st = kv_cache_args(compressed_kv, k_pe, slot_mapping, T, d, dt, num_slots);
+    if (st != MLA_OK || T == 0 || num_slots == 0) return st;
+    if (kv_cache_q == nullptr || kv_scale == nullptr) return MLA_ERR_INVALID_ARG;
+    if (!aligned16(kv_cache_q) || ((uintptr_t)kv_scale & 3u) != 0) return MLA_ERR_MISALIGNED;
+    const hipError_t e = launch_kv_cache_append(dt, compressed_kv, k_pe, slot_mapping, T,
+                                                num_slots, nullptr, kv_cache_q, kv_scale,
+                                                (hipStream_t)stream);
+    return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 }  // extern "C"

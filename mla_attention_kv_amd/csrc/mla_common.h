@@ -182,6 +182,11 @@ void launch_finish_fp(int dt, const float* P, int S, int64_t T, const void* gamm
                       const int32_t* pos, float eps, const RopeTab& rt, void* ckv, void* kpe,
                       hipStream_t st);
 
+// paged KV-cache append: fp cache (cache_q == nullptr) or int8 codes + scales
+hipError_t launch_kv_cache_append(int dt, const void* ckv, const void* kpe, const int64_t* slots,
+                                  int64_t T, int64_t num_slots, void* cache, int8_t* cache_q,
+                                  float* scale, hipStream_t st);
+
 hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa,
                        const void* gamma, const int8_t* Wqb, const float* swb,
                        const int32_t* pos, int64_t T, int H, int nh, float eps,

@@ -145,3 +145,39 @@ def test_python_binding_checks_tensors():
     X = torch.zeros(2, 64, dtype=torch.float32)
     with pytest.raises(ValueError):
         mla.mla_kv_prolog(X, X, X, X, X)
+
+
+def call_cache(T=4, d=V2, dt=1, ptrs=None, slots=1024, q8=False):
+    p = [FAKE] * 5 if ptrs is None else ptrs
+    if q8:
+        return mla.lib().mla_kv_cache_append_int8(p[0], p[1], p[2], T, d.c(), dt, p[3], p[4],
+                                                  slots, None)
+    return mla.lib().mla_kv_cache_append(p[0], p[1], p[2], T, d.c(), dt, p[3], slots, None)
+
+
+@pytest.mark.parametrize("q8", [False, True])
+def test_cache_append_argument_errors(q8):
+    n = 5 if q8 else 4
+    for i in range(n):
+        p = [FAKE] * 5
+        p[i] = None
+        assert call_cache(ptrs=p, q8=q8) == mla.MLA_ERR_INVALID_ARG, i
+    # 16-byte rows and caches, 8-byte slot mapping, 4-byte scales (only
+    # misalignments: a valid call would launch)
+    for i, off in ((0, 8), (1, 8), (2, 4), (3, 8)):
+        p = [FAKE] * 5
+        p[i] = FAKE + off
+        assert call_cache(ptrs=p, q8=q8) == mla.MLA_ERR_MISALIGNED, (i, off)
+    if q8:
+        p = [FAKE] * 5
+        p[4] = FAKE + 2
+        assert call_cache(ptrs=p, q8=True) == mla.MLA_ERR_MISALIGNED
+    assert call_cache(T=-1, q8=q8) == mla.MLA_ERR_INVALID_ARG
+    assert call_cache(T=(1 << 22) + 1, q8=q8) == mla.MLA_ERR_INVALID_ARG
+    assert call_cache(slots=-1, q8=q8) == mla.MLA_ERR_INVALID_ARG
+    assert call_cache(dt=0, q8=q8) == mla.MLA_ERR_INVALID_ARG
+    assert call_cache(d=Dims(H=2048, nh=16, r=256), q8=q8) == mla.MLA_ERR_UNSUPPORTED
+    assert call_cache(d=Dims(H=2048, nh=16, dr=32), q8=q8) == mla.MLA_ERR_UNSUPPORTED
+    # nothing to do: no pointer is needed and nothing is launched
+    assert call_cache(T=0, ptrs=[None] * 5, q8=q8) == mla.MLA_OK
+    assert call_cache(slots=0, ptrs=[FAKE, FAKE, FAKE, None, None], q8=q8) == mla.MLA_OK
