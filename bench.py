@@ -14,6 +14,12 @@ a serving loop would) on one stream and bracketed by synchronisation and
 HIP events on that stream.  value = T * K / elapsed (tokens/s).
 
 Prints ONE JSON line on stdout.
+
+--op cache_append / cache_append_int8 times the paged KV-cache append
+instead (the step after "assemble"): the workload's T rows of
+compressed_kv and k_pe (seeded, model dtype) written into a cache by a slot
+mapping, rotating over input sets that map to disjoint slot ranges of one
+cache.
 """
 from __future__ import annotations
 
@@ -205,6 +211,117 @@ def cpu_baseline(w, seconds):
             "sample": sample}
 
 
+class CacheSets:
+    """Rotated inputs of the paged KV-cache append: n_sets of (compressed_kv,
+    k_pe, slot mapping) over disjoint slot ranges of one shared cache, with
+    the same call interface as Sets."""
+
+    def __init__(self, T, dtype, int8, n_sets, dev, seed):
+        import numpy as np
+        import torch
+
+        import mla_attention_kv_amd as mla
+
+        self.mla = mla
+        tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+        code = mla.MLA_F16 if dtype == "f16" else mla.MLA_BF16
+        rng = np.random.default_rng(seed)
+        S = T * n_sets
+        if int8:
+            self.cache = (torch.zeros((S, 576), dtype=torch.int8, device=dev),
+                          torch.zeros(S, dtype=torch.float32, device=dev))
+        else:
+            self.cache = (torch.zeros((S, 576), dtype=tdt, device=dev),)
+        self.keep, self.args = [], []
+        d = mla.Dims(H=64, nh=1).c()
+        for i in range(n_sets):
+            ckv = torch.from_numpy(rng.standard_normal((T, 512)).astype(np.float32)).to(tdt).to(dev)
+            kpe = torch.from_numpy(rng.standard_normal((T, 64)).astype(np.float32)).to(tdt).to(dev)
+            slots = torch.from_numpy(i * T + rng.permutation(T).astype(np.int64)).to(dev)
+            self.keep.append((ckv, kpe, slots))
+            if int8:
+                a = (ckv.data_ptr(), kpe.data_ptr(), slots.data_ptr(), T, d, code,
+                     self.cache[0].data_ptr(), self.cache[1].data_ptr(), S)
+            else:
+                a = (ckv.data_ptr(), kpe.data_ptr(), slots.data_ptr(), T, d, code,
+                     self.cache[0].data_ptr(), S)
+            self.args.append(a)
+        self.fn = mla.lib().mla_kv_cache_append_int8 if int8 else mla.lib().mla_kv_cache_append
+
+    def call(self, i, stream_ptr):
+        st = self.fn(*self.args[i % len(self.args)], ctypes.c_void_p(stream_ptr))
+        if st != 0:
+            raise RuntimeError(f"library call failed: {self.mla.mla_status_string(st)}")
+
+
+def cache_cpu_baseline(T, dtype, int8, seconds, seed):
+    """The CPU oracle of the append on the same shapes, repeated for about
+    `seconds`."""
+    import numpy as np
+
+    import oracle
+
+    rng = np.random.default_rng(seed)
+    ckv = oracle.round_to_dtype(rng.standard_normal((T, 512)), dtype)
+    kpe = oracle.round_to_dtype(rng.standard_normal((T, 64)), dtype)
+    slots = rng.permutation(T).astype(np.int64)
+    if int8:
+        q, sc = np.zeros((T, 576), np.int8), np.zeros(T, np.float32)
+        f = lambda: oracle.kv_cache_append_int8(ckv, kpe, slots, q, sc)  # noqa: E731
+    else:
+        cache = np.zeros((T, 576))
+        f = lambda: oracle.kv_cache_append(ckv, kpe, slots, cache)  # noqa: E731
+    t0 = time.perf_counter()
+    f()
+    one = time.perf_counter() - t0
+    reps = max(1, min(100000, int(seconds / max(one, 1e-6))))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        f()
+    dt = time.perf_counter() - t0
+    return {"value": T * reps / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} x all {T} token rows ({dt:.1f} s; the append is single-threaded)"}
+
+
+def main_cache(args, cfg, w, dev):
+    import torch
+
+    int8 = args.op == "cache_append_int8"
+    es = 2
+    per_tok = 576 * es + 8 + (576 + 4 if int8 else 576 * es)  # read rows + slot, write slot
+    alg_bytes = w.T * per_tok
+    n_sets = max(2, math.ceil(ROTATE_BYTES / alg_bytes))
+    log(f"cache append{' int8' if int8 else ''}: T={w.T} bytes/step={alg_bytes} sets={n_sets}")
+    sets = CacheSets(w.T, w.dtype, int8, n_sets, dev, seed=1000 + args.config)
+    torch.cuda.synchronize()
+    steps, warmup = args.steps, args.warmup
+    ms = time_graph(sets, steps, warmup, dev)
+    ms_per_step = ms / steps
+    step_s = ms_per_step / 1e3
+    value = w.T * steps / (ms / 1e3)
+    log(f"{ms_per_step * 1e3:.2f} us/step, {value:.4g} tokens/s")
+    roof = {"bound": "hbm", "achieved": alg_bytes / step_s / 1e9, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "traffic": None,
+            "kernel": "kv_cache_append_kernel (one launch per call)"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cache_cpu_baseline(w.T, w.dtype, int8, args.cpu_seconds, 1000 + args.config)
+    out = {
+        "metric": "MLA KV cache append tokens/s + % HBM roofline",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "i8" if int8 else w.dtype,
+        "data": "synthetic (seeded; no public dataset exists for this path)",
+        "config": {"workload": f"{cfg['name']}_{args.op}", "T": w.T, "slot_width": 576,
+                   "cache_slots": w.T * n_sets, "timing": "HIP graph replays",
+                   "rotated_sets": n_sets, "algorithmic_bytes_per_step": alg_bytes},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -213,6 +330,9 @@ def main():
     ap.add_argument("--config", type=int, default=1, help="workload index (default 1)")
     ap.add_argument("--eager", action="store_true", help="time direct calls, not graph replays")
     ap.add_argument("--path", type=int, default=-1, help="force kernel family 0/1 (A/B runs)")
+    ap.add_argument("--op", default="prolog",
+                    choices=["prolog", "cache_append", "cache_append_int8"],
+                    help="what one step is (default: the prolog)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -238,6 +358,13 @@ def main():
         mla.mla_kv_prolog_force_path(args.path)
 
     cfg = workloads.CONFIGS[args.config]
+    if args.op != "prolog":
+        if cfg["kind"] != "fp":
+            print("--op cache_append needs an fp16 / bf16 workload", file=sys.stderr)
+            sys.exit(2)
+        w = workloads.make_config(args.config)
+        main_cache(args, cfg, w, dev)
+        return
     log(f"generating workload {cfg['name']}")
     w = workloads.make_config(args.config)
     d = w.dims
