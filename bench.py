@@ -15,6 +15,12 @@ HIP events on that stream.  value = T * K / elapsed (tokens/s).
 
 Prints ONE JSON line on stdout.
 
+--op prolog_cached times the prolog with the paged KV-cache append fused
+into its finish (each token's compressed_kv and k_pe rows also land in its
+slot of a paged cache; the rotated input sets map to disjoint blocks of one
+cache); --op prolog_then_append times the same work as two calls (the
+prolog, then mla_kv_cache_append), for comparison.
+
 --op cache_append / cache_append_int8 times the paged KV-cache append
 instead (the step after "assemble"): the workload's T rows of
 compressed_kv and k_pe (seeded, model dtype) written into a cache by a slot
@@ -79,7 +85,7 @@ class Sets:
     """n_sets device copies of one workload's tensors plus output buffers and
     workspace, with ready-made C argument tuples."""
 
-    def __init__(self, w, n_sets, dev):
+    def __init__(self, w, n_sets, dev, cache_mode=None):
         import torch
 
         import mla_attention_kv_amd as mla
@@ -99,6 +105,14 @@ class Sets:
             nbytes = mla.mla_kv_prolog_w8a8_workspace_size(w.T, self.dims)
         self.keep = []
         self.args = []
+        self.cache_mode = cache_mode
+        self.append_args = []
+        if cache_mode is not None:
+            import workloads
+
+            slots, nsl = workloads.paged_slot_mapping(w, seed=7)
+            self.cache = torch.zeros((nsl * n_sets, d.r + d.dr), dtype=odt, device=dev)
+            self.slot_sets = [torch.from_numpy(slots + i * nsl).to(dev) for i in range(n_sets)]
         for i in range(n_sets):
             t = {k: v.clone() for k, v in base.items()}
             outs = (torch.empty((w.T, d.nh, d.dn), dtype=odt, device=dev),
@@ -112,6 +126,13 @@ class Sets:
                      t["Wb"].data_ptr(), t["pos"].data_ptr(), w.T, self.dims.c(), code,
                      w.eps, w.theta, outs[0].data_ptr(), outs[1].data_ptr(),
                      outs[2].data_ptr(), outs[3].data_ptr(), ws.data_ptr(), ws.numel())
+                if cache_mode == "fused":
+                    a = a[:14] + (self.slot_sets[i].data_ptr(), self.cache.data_ptr(),
+                                  self.cache.shape[0]) + a[14:]
+                elif cache_mode == "separate":
+                    self.append_args.append(
+                        (outs[3].data_ptr(), outs[2].data_ptr(), self.slot_sets[i].data_ptr(),
+                         w.T, self.dims.c(), code, self.cache.data_ptr(), self.cache.shape[0]))
             else:
                 a = (t["X"].data_ptr(), t["Wqa"].data_ptr(), t["swa"].data_ptr(),
                      t["gamma"].data_ptr(), t["Wqb"].data_ptr(), t["swb"].data_ptr(),
@@ -120,9 +141,14 @@ class Sets:
                      outs[3].data_ptr(), None, None, 0, 0, ws.data_ptr(), ws.numel())
             self.args.append(a)
         self.fn = mla.lib().mla_kv_prolog if w.kind == "fp" else mla.lib().mla_kv_prolog_w8a8
+        if cache_mode == "fused":
+            self.fn = mla.lib().mla_kv_prolog_cached
 
     def call(self, i, stream_ptr):
         st = self.fn(*self.args[i % len(self.args)], ctypes.c_void_p(stream_ptr))
+        if st == 0 and self.cache_mode == "separate":
+            st = self.mla.lib().mla_kv_cache_append(*self.append_args[i % len(self.args)],
+                                                    ctypes.c_void_p(stream_ptr))
         if st != 0:
             raise RuntimeError(f"library call failed: {self.mla.mla_status_string(st)}")
 
@@ -331,7 +357,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time direct calls, not graph replays")
     ap.add_argument("--path", type=int, default=-1, help="force kernel family 0/1 (A/B runs)")
     ap.add_argument("--op", default="prolog",
-                    choices=["prolog", "cache_append", "cache_append_int8"],
+                    choices=["prolog", "prolog_cached", "prolog_then_append", "cache_append",
+                             "cache_append_int8"],
                     help="what one step is (default: the prolog)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -358,10 +385,10 @@ def main():
         mla.mla_kv_prolog_force_path(args.path)
 
     cfg = workloads.CONFIGS[args.config]
-    if args.op != "prolog":
-        if cfg["kind"] != "fp":
-            print("--op cache_append needs an fp16 / bf16 workload", file=sys.stderr)
-            sys.exit(2)
+    if args.op != "prolog" and cfg["kind"] != "fp":
+        print(f"--op {args.op} needs an fp16 / bf16 workload", file=sys.stderr)
+        sys.exit(2)
+    if args.op.startswith("cache_append"):
         w = workloads.make_config(args.config)
         main_cache(args, cfg, w, dev)
         return
@@ -369,10 +396,13 @@ def main():
     w = workloads.make_config(args.config)
     d = w.dims
     alg_bytes = workloads.algorithmic_bytes(d, w.T, w.kind, w.dtype)
+    cache_mode = {"prolog_cached": "fused", "prolog_then_append": "separate"}.get(args.op)
+    if cache_mode is not None:
+        alg_bytes += w.T * ((d.r + d.dr) * 2 + 8)  # each token's cache slot and its slot index
     alg_flops = workloads.algorithmic_flops(d, w.T)
     n_sets = max(1, math.ceil(ROTATE_BYTES / alg_bytes))
     log(f"T={w.T} algorithmic bytes/step={alg_bytes} flops/step={alg_flops} sets={n_sets}")
-    sets = Sets(w, n_sets, dev)
+    sets = Sets(w, n_sets, dev, cache_mode)
     torch.cuda.synchronize()
 
     if args.copy_calibration:
@@ -405,13 +435,15 @@ def main():
         roof = {"bound": "mfma", "achieved": alg_flops / step_s / 1e12,
                 "peak": MFMA_PEAK_TFLOPS[dt], "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = load_traffic(cfg["name"])
+    roof["traffic"] = load_traffic(cfg["name"]) if cache_mode is None else None
     roof["kernel"] = ("one library call = every launch of the step: " +
                       ("dec_kv_a + dec_fin_kv_b (finish fused into kv_b_proj)"
                        if (path == 0 and w.kind == "fp" and w.T <= 64 and w.dims.nh * ((w.T + 15) // 16) <= 64)
                        else "dec_kv_a + dec_finish + dec_kv_b" if (path == 0 and w.kind == "fp" and w.T <= 64)
                        else "kv_a_proj GEMM + finish + kv_b_proj GEMM" +
-                       (" (+ activation quantiser)" if w.kind == "w8a8" else "")))
+                       (" (+ activation quantiser)" if w.kind == "w8a8" else "")) +
+                      {None: "", "fused": "; paged-cache write fused into the finish",
+                       "separate": "; then kv_cache_append"}[cache_mode])
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -432,7 +464,8 @@ def main():
         "vs_baseline": None,
         "dtype": {"fp": w.dtype, "w8a8": "i8"}[w.kind],
         "data": "synthetic (seeded; no public dataset exists for this path)",
-        "config": {"workload": cfg["name"], "T": w.T, "H": d.H, "kv_lora_rank": d.r,
+        "config": {"workload": cfg["name"] + ("" if cache_mode is None else "_" + args.op),
+                   "T": w.T, "H": d.H, "kv_lora_rank": d.r,
                    "rope_dim": d.dr, "heads": d.nh, "dn": d.dn, "dv": d.dv,
                    "kernel_family": ["decode", "prefill"][path],
                    "timing": "eager calls" if args.eager else "HIP graph replays",

@@ -184,6 +184,24 @@ mla_status_t mla_kv_cache_append_int8(const void* compressed_kv, const void* k_p
                                       mla_dtype_t dt, int8_t* kv_cache_q, float* kv_scale,
                                       int64_t num_slots, void* stream);
 
+/*
+ * The prolog (mla_kv_prolog, same arguments and outputs) with the paged
+ * KV-cache append fused into its finish: the kernel that writes a token's
+ * compressed_kv and k_pe rows also writes them into kv_cache slot
+ * slot_mapping[t] (layout, slot rules and alignment as for
+ * mla_kv_cache_append), so the cache holds exactly the bits of the returned
+ * rows and the rows are not read back from HBM.  num_slots == 0 writes no
+ * cache (slot_mapping and kv_cache may then be NULL).  Errors as for the
+ * prolog and the append; nothing launches when any check fails.
+ */
+mla_status_t mla_kv_prolog_cached(const void* hidden, const void* W_kv_a, const void* gamma,
+                                  const void* W_kv_b, const int32_t* positions, int64_t T,
+                                  mla_dims_t d, mla_dtype_t dt, float eps, float theta,
+                                  void* k_nope, void* value, void* k_pe, void* compressed_kv,
+                                  const int64_t* slot_mapping, void* kv_cache,
+                                  int64_t num_slots, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
 /* The kernel family the dispatcher picks for T tokens: 0 = decode
  * (weight-streaming, small T), 1 = prefill (MFMA-tiled, large T). */
 int mla_kv_prolog_selected_path(int64_t T, mla_dims_t d);

@@ -37,6 +37,7 @@ EXPORTS = (
     "mla_kv_prolog_w8a8",
     "mla_kv_cache_append",
     "mla_kv_cache_append_int8",
+    "mla_kv_prolog_cached",
     "mla_kv_prolog_selected_path",
     "mla_kv_prolog_force_path",
     "mla_status_string",
@@ -96,6 +97,9 @@ def lib() -> ctypes.CDLL:
     L.mla_kv_cache_append.restype = i32
     L.mla_kv_cache_append_int8.argtypes = [vp, vp, vp, i64, mla_dims_t, i32, vp, vp, i64, vp]
     L.mla_kv_cache_append_int8.restype = i32
+    L.mla_kv_prolog_cached.argtypes = [vp, vp, vp, vp, vp, i64, mla_dims_t, i32, f32, f32,
+                                       vp, vp, vp, vp, vp, vp, i64, vp, sz, vp]
+    L.mla_kv_prolog_cached.restype = i32
     L.mla_kv_prolog_selected_path.argtypes = [i64, mla_dims_t]
     L.mla_kv_prolog_selected_path.restype = i32
     L.mla_kv_prolog_force_path.argtypes = [i32]
@@ -201,6 +205,24 @@ def mla_kv_prolog(hidden, W_kv_a, gamma, W_kv_b, positions, eps: float = 1e-6,
     hidden [T,H], W_kv_a [H,r+dr], gamma [r], W_kv_b [r,nh*(dn+dv)] of one
     dtype (float16 or bfloat16); positions [T] int32.  Returns
     (k_nope [T,nh,dn], value [T,nh,dv], k_pe [T,dr], compressed_kv [T,r])."""
+    return _prolog_fp(hidden, W_kv_a, gamma, W_kv_b, positions, eps, theta, k_nope, value,
+                      k_pe, compressed_kv, workspace, stream, dn, dv, None, None)
+
+
+def mla_kv_prolog_cached(hidden, W_kv_a, gamma, W_kv_b, positions, slot_mapping, kv_cache,
+                         eps: float = 1e-6, theta: float = 10000.0, *, k_nope=None,
+                         value=None, k_pe=None, compressed_kv=None, workspace=None,
+                         stream=None, dn: int = 128, dv: int = 128):
+    """mla_kv_prolog that also writes each token's [compressed_kv | k_pe] row
+    into slot slot_mapping[t] ([T] int64) of kv_cache ([num_slots, r+dr] or
+    [blocks, block_size, r+dr], the hidden dtype, contiguous); slots outside
+    [0, num_slots) skip the token.  Returns the prolog's four outputs."""
+    return _prolog_fp(hidden, W_kv_a, gamma, W_kv_b, positions, eps, theta, k_nope, value,
+                      k_pe, compressed_kv, workspace, stream, dn, dv, slot_mapping, kv_cache)
+
+
+def _prolog_fp(hidden, W_kv_a, gamma, W_kv_b, positions, eps, theta, k_nope, value, k_pe,
+               compressed_kv, workspace, stream, dn, dv, slot_mapping, kv_cache):
     torch = _torch()
     dtype = hidden.dtype
     code = {torch.float16: MLA_F16, torch.bfloat16: MLA_BF16}.get(dtype)
@@ -221,13 +243,28 @@ def mla_kv_prolog(hidden, W_kv_a, gamma, W_kv_b, positions, eps: float = 1e-6,
     if T > 0 and nbytes == 0:
         raise MlaError(MLA_ERR_UNSUPPORTED, "mla_kv_prolog_workspace_size")
     ws = _workspace(nbytes, dev, workspace)
-    st = lib().mla_kv_prolog(
+    if kv_cache is None:
+        st = lib().mla_kv_prolog(
+            hidden.data_ptr(), W_kv_a.data_ptr(), gamma.data_ptr(), W_kv_b.data_ptr(),
+            positions.data_ptr(), T, d.c(), code, float(eps), float(theta),
+            outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(), outs[3].data_ptr(),
+            ws.data_ptr(), ws.numel(), _stream_ptr(dev, stream))
+        if st != MLA_OK:
+            raise MlaError(st, "mla_kv_prolog")
+        return outs
+    W = d.r + d.dr
+    _check(slot_mapping, "slot_mapping", torch.int64, (T,), dev)
+    if kv_cache.dtype != dtype or kv_cache.device != dev or kv_cache.shape[-1] != W \
+            or not kv_cache.is_contiguous():
+        raise ValueError(f"kv_cache: contiguous {dtype} [..., {W}] on {dev} expected")
+    st = lib().mla_kv_prolog_cached(
         hidden.data_ptr(), W_kv_a.data_ptr(), gamma.data_ptr(), W_kv_b.data_ptr(),
         positions.data_ptr(), T, d.c(), code, float(eps), float(theta),
         outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(), outs[3].data_ptr(),
+        slot_mapping.data_ptr(), kv_cache.data_ptr(), kv_cache.numel() // W,
         ws.data_ptr(), ws.numel(), _stream_ptr(dev, stream))
     if st != MLA_OK:
-        raise MlaError(st, "mla_kv_prolog")
+        raise MlaError(st, "mla_kv_prolog_cached")
     return outs
 
 

@@ -169,11 +169,15 @@ const char* mla_status_string(mla_status_t s) {
     return "unknown mla_status_t";
 }
 
-mla_status_t mla_kv_prolog(const void* hidden, const void* W_kv_a, const void* gamma,
-                           const void* W_kv_b, const int32_t* positions, int64_t T,
-                           mla_dims_t d, mla_dtype_t dt, float eps, float theta,
-                           void* k_nope, void* value, void* k_pe, void* compressed_kv,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// The fp16/bf16 prolog, with or without the paged-cache write in its finish.
+mla_status_t prolog_fp(const void* hidden, const void* W_kv_a, const void* gamma,
+                       const void* W_kv_b, const int32_t* positions, int64_t T, mla_dims_t d,
+                       mla_dtype_t dt, float eps, float theta, void* k_nope, void* value,
+                       void* k_pe, void* compressed_kv, const CacheOut& co, void* workspace,
+                       size_t workspace_bytes, void* stream) {
     if (T < 0 || T > MLA_MAX_TOKENS) return MLA_ERR_INVALID_ARG;
     if (dt != MLA_F16 && dt != MLA_BF16) return MLA_ERR_INVALID_ARG;
     if (!std::isfinite(eps) || eps < 0.f || !std::isfinite(theta) || theta <= 0.f)
@@ -192,8 +196,21 @@ mla_status_t mla_kv_prolog(const void* hidden, const void* W_kv_a, const void* g
     if (workspace_bytes < ws_fp(T, plan).total) return MLA_ERR_WORKSPACE;
     hipError_t e = launch_fp((int)dt, hidden, W_kv_a, gamma, W_kv_b, positions, T, d.H, d.nh,
                              eps, rope_table(theta), k_nope, value, k_pe, compressed_kv,
-                             workspace, plan, (hipStream_t)stream);
+                             workspace, plan, co, (hipStream_t)stream);
     return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+}  // namespace
+
+extern "C" {
+
+mla_status_t mla_kv_prolog(const void* hidden, const void* W_kv_a, const void* gamma,
+                           const void* W_kv_b, const int32_t* positions, int64_t T,
+                           mla_dims_t d, mla_dtype_t dt, float eps, float theta,
+                           void* k_nope, void* value, void* k_pe, void* compressed_kv,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    return prolog_fp(hidden, W_kv_a, gamma, W_kv_b, positions, T, d, dt, eps, theta, k_nope,
+                     value, k_pe, compressed_kv, CacheOut{nullptr, nullptr, 0}, workspace,
+                     workspace_bytes, stream);
 }
 
 mla_status_t mla_kv_prolog_w8a8(const void* hidden_bf16, const int8_t* Wq_kv_a,
@@ -275,6 +292,24 @@ mla_status_t mla_kv_cache_append_int8(const void* compressed_kv, const void* k_p
                                                 num_slots, nullptr, kv_cache_q, kv_scale,
                                                 (hipStream_t)stream);
     return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_kv_prolog_cached(const void* hidden, const void* W_kv_a, const void* gamma,
+                                  const void* W_kv_b, const int32_t* positions, int64_t T,
+                                  mla_dims_t d, mla_dtype_t dt, float eps, float theta,
+                                  void* k_nope, void* value, void* k_pe, void* compressed_kv,
+                                  const int64_t* slot_mapping, void* kv_cache,
+                                  int64_t num_slots, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+    if (num_slots < 0) return MLA_ERR_INVALID_ARG;
+    if (T > 0 && num_slots > 0) {
+        if (slot_mapping == nullptr || kv_cache == nullptr) return MLA_ERR_INVALID_ARG;
+        if (((uintptr_t)slot_mapping & 7u) != 0 || !aligned16(kv_cache)) return MLA_ERR_MISALIGNED;
+    }
+    const CacheOut co{num_slots > 0 ? slot_mapping : nullptr,
+                      num_slots > 0 ? (uint16_t*)kv_cache : nullptr, num_slots};
+    return prolog_fp(hidden, W_kv_a, gamma, W_kv_b, positions, T, d, dt, eps, theta, k_nope,
+                     value, k_pe, compressed_kv, co, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -163,6 +163,19 @@ inline WsW8 ws_w8(int64_t T, int H, const Plan& p) {
     return w;
 }
 
+// Optional paged KV-cache output of the prolog: the finish step also writes
+// each token's [compressed_kv row | k_pe row] into slot slots[t] of cache
+// ([num_slots, 576], model dtype) when cache != nullptr; a slot outside
+// [0, num_slots) skips the token.
+struct CacheOut {
+    const int64_t* slots;
+    uint16_t* cache;
+    int64_t num_slots;
+};
+__device__ __forceinline__ bool cache_slot_ok(const CacheOut& co, int64_t s) {
+    return co.cache != nullptr && s >= 0 && s < co.num_slots;
+}
+
 // ---------------------------------------------------------------------------
 // host-side launchers (defined in the .hip files)
 // ---------------------------------------------------------------------------
@@ -170,17 +183,18 @@ inline WsW8 ws_w8(int64_t T, int H, const Plan& p) {
 hipError_t launch_fp(int dt, const void* X, const void* Wa, const void* gamma,
                      const void* Wb, const int32_t* pos, int64_t T, int H, int nh,
                      float eps, const RopeTab& rt, void* k_nope, void* value, void* k_pe,
-                     void* ckv, void* ws, const Plan& plan, hipStream_t st);
+                     void* ckv, void* ws, const Plan& plan, const CacheOut& co, hipStream_t st);
 
 hipError_t launch_fp_decode(int dt, const void* X, const void* Wa, const void* gamma,
                             const void* Wb, const int32_t* pos, int64_t T, int H, int nh,
                             float eps, const RopeTab& rt, void* k_nope, void* value,
-                            void* k_pe, void* ckv, void* ws, const Plan& plan, hipStream_t st);
+                            void* k_pe, void* ckv, void* ws, const Plan& plan, const CacheOut& co,
+                            hipStream_t st);
 
 // per-token finish of kv_a_proj (split, RMSNorm, RoPE) from split-K partials
 void launch_finish_fp(int dt, const float* P, int S, int64_t T, const void* gamma,
                       const int32_t* pos, float eps, const RopeTab& rt, void* ckv, void* kpe,
-                      hipStream_t st);
+                      const CacheOut& co, hipStream_t st);
 
 // paged KV-cache append: fp cache (cache_q == nullptr) or int8 codes + scales
 hipError_t launch_kv_cache_append(int dt, const void* ckv, const void* kpe, const int64_t* slots,

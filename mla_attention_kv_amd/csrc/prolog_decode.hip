@@ -243,6 +243,7 @@ struct FinPart {
     u4_t gm;      // gamma[8 lane .. 8 lane + 7]
     int32_t pos;  // the token's position
     double freq;  // RoPE frequency of rope column lane
+    int64_t slot; // the token's paged-cache slot (-1 without a cache)
 };
 __device__ __forceinline__ void fin_load(FinPart& r, const float* __restrict__ P, int S, int T,
                                          int t, int s0) {
@@ -260,11 +261,12 @@ __device__ __forceinline__ void fin_load(FinPart& r, const float* __restrict__ P
 }
 __device__ __forceinline__ void fin_load_aux(FinPart& r, const uint16_t* __restrict__ gamma,
                                              const int32_t* __restrict__ pos, const RopeTab& rt,
-                                             int t) {
+                                             const CacheOut& co, int t) {
     const int lane = threadIdx.x & 63;
     r.gm = *(const u4_t*)(gamma + 8 * lane);
     r.pos = pos[t];
     r.freq = rt.f[lane & 31];
+    r.slot = co.cache != nullptr ? co.slots[t] : -1;
 }
 __device__ __forceinline__ void fin_add(const FinPart& r, int S, f4_t& c0, f4_t& c1, float& p) {
 #pragma unroll
@@ -284,7 +286,8 @@ template <int E, bool COH>
 __device__ __forceinline__ void finish_token_from(FinPart& r, const float* __restrict__ P, int S,
                                                   int T, int t, float eps,
                                                   uint16_t* __restrict__ ckv,
-                                                  uint16_t* __restrict__ kpe, float* fred) {
+                                                  uint16_t* __restrict__ kpe, const CacheOut& co,
+                                                  float* fred) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     f4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
     float p = 0.f;
@@ -329,13 +332,18 @@ __device__ __forceinline__ void finish_token_from(FinPart& r, const float* __res
         } else {
             *(u4_t*)dst = o;
         }
+        if (cache_slot_ok(co, r.slot))  // the paged cache: [latent | rope key] in the slot
+            __builtin_nontemporal_store(o, (u4_t*)(co.cache + r.slot * (kR + kDR) + 8 * lane));
     } else if (wave == 1) {
         float cs, sn;
         rope_cos_sin(r.pos, r.freq, cs, sn);
         const float q = (f0[kR + lane] + f1[kR + lane]) + (f2[kR + lane] + f3[kR + lane]);
         const float partner = __shfl_xor(q, 32, 64);
         const float out = (lane < 32) ? (q * cs - partner * sn) : (q * cs + partner * sn);
-        kpe[(int64_t)t * kDR + lane] = f32_to_st<E>(out);
+        const uint16_t ko = f32_to_st<E>(out);
+        kpe[(int64_t)t * kDR + lane] = ko;
+        if (cache_slot_ok(co, r.slot))
+            __builtin_nontemporal_store(ko, co.cache + r.slot * (kR + kDR) + kR + lane);
     }
 }
 
@@ -344,11 +352,12 @@ __device__ __forceinline__ void finish_token(const float* __restrict__ P, int S,
                                              const uint16_t* __restrict__ gamma,
                                              const int32_t* __restrict__ pos, float eps,
                                              const RopeTab& rt, uint16_t* __restrict__ ckv,
-                                             uint16_t* __restrict__ kpe, float* fred) {
+                                             uint16_t* __restrict__ kpe, const CacheOut& co,
+                                             float* fred) {
     FinPart r;
     fin_load(r, P, S, T, t, threadIdx.x >> 6);
-    fin_load_aux(r, gamma, pos, rt, t);
-    finish_token_from<E, COH>(r, P, S, T, t, eps, ckv, kpe, fred);
+    fin_load_aux(r, gamma, pos, rt, co, t);
+    finish_token_from<E, COH>(r, P, S, T, t, eps, ckv, kpe, co, fred);
 }
 
 // one workgroup per token
@@ -358,9 +367,10 @@ __global__ __launch_bounds__(256) void dec_finish_kernel(const float* __restrict
                                                          const int32_t* __restrict__ pos,
                                                          float eps, RopeTab rt,
                                                          uint16_t* __restrict__ ckv,
-                                                         uint16_t* __restrict__ kpe) {
+                                                         uint16_t* __restrict__ kpe,
+                                                         CacheOut co) {
     __shared__ __align__(16) float fred[4 * kFredPitch];
-    finish_token<E, false>(P, S, T, blockIdx.x, gamma, pos, eps, rt, ckv, kpe, fred);
+    finish_token<E, false>(P, S, T, blockIdx.x, gamma, pos, eps, rt, ckv, kpe, co, fred);
 }
 
 // ---------------------------------------------------------------------------
@@ -434,7 +444,7 @@ __global__ __launch_bounds__(256) void dec_fin_kv_b_kernel(
     const float* __restrict__ P, int S, int T, const uint16_t* __restrict__ gamma,
     const int32_t* __restrict__ pos, float eps, RopeTab rt, const uint16_t* __restrict__ Wb,
     int N2, uint16_t* ckv, uint16_t* __restrict__ kpe, uint16_t* __restrict__ k_nope,
-    uint16_t* __restrict__ value) {
+    uint16_t* __restrict__ value, CacheOut co) {
     constexpr int AP = ARows<1, kR>::kPitchA;
     __shared__ __align__(16) uint16_t ldsW[kR * kPitch];
     __shared__ __align__(16) uint16_t ldsA[16 * AP];  // also the finish's reduction buffer
@@ -451,15 +461,15 @@ __global__ __launch_bounds__(256) void dec_fin_kv_b_kernel(
     if (t1 < T) {
         FinPart r;
         fin_load(r, P, S, T, t1, threadIdx.x >> 6);
-        fin_load_aux(r, gamma, pos, rt, t1);
+        fin_load_aux(r, gamma, pos, rt, co, t1);
         stage_load<kR / 32, false>(v, Wb, N2, 0, kR, n0);
-        finish_token_from<E, true>(r, P, S, T, t1, eps, ckv, kpe, (float*)ldsA);
+        finish_token_from<E, true>(r, P, S, T, t1, eps, ckv, kpe, co, (float*)ldsA);
     } else {
         stage_load<kR / 32, false>(v, Wb, N2, 0, kR, n0);
     }
     for (int t = t1 + (int)gridDim.x; t < T; t += gridDim.x) {
         __syncthreads();  // the reduction buffer is free again
-        finish_token<E, true>(P, S, T, t, gamma, pos, eps, rt, ckv, kpe, (float*)ldsA);
+        finish_token<E, true>(P, S, T, t, gamma, pos, eps, rt, ckv, kpe, co, (float*)ldsA);
     }
     if (item < 0) return;
     const int slab = item / ntile, t0 = (item % ntile) * 16;
@@ -532,7 +542,7 @@ template <int E>
 static void dec_launch_t(const void* X, const void* Wa, const void* gamma, const void* Wb,
                          const int32_t* pos, int T, int H, int nh, float eps, const RopeTab& rt,
                          void* k_nope, void* value, void* k_pe, void* ckv, float* P,
-                         const Plan& plan, hipStream_t st) {
+                         const Plan& plan, const CacheOut& co, hipStream_t st) {
     const int ntile = (T + 15) / 16;
     const int N2 = nh * kHeadW;
     const int nitems = (N2 / kSlabW) * ntile;
@@ -548,11 +558,11 @@ static void dec_launch_t(const void* X, const void* Wa, const void* gamma, const
         hipLaunchKernelGGL(dec_fin_kv_b_kernel<E>, dim3(grid8(nitems)), dim3(256), 0, st,
                            (const float*)P, plan.s1, T, (const uint16_t*)gamma, pos, eps, rt,
                            (const uint16_t*)Wb, N2, (uint16_t*)ckv, (uint16_t*)k_pe,
-                           (uint16_t*)k_nope, (uint16_t*)value);
+                           (uint16_t*)k_nope, (uint16_t*)value, co);
         return;
     }
     hipLaunchKernelGGL(dec_finish_kernel<E>, dim3(T), dim3(256), 0, st, (const float*)P, plan.s1,
-                       T, (const uint16_t*)gamma, pos, eps, rt, (uint16_t*)ckv, (uint16_t*)k_pe);
+                       T, (const uint16_t*)gamma, pos, eps, rt, (uint16_t*)ckv, (uint16_t*)k_pe, co);
     hipLaunchKernelGGL((dec_kv_b_kernel<E, 1>), dim3(grid8(nitems)), dim3(256), 0, st,
                        (const uint16_t*)ckv, (const uint16_t*)Wb, T, N2, (uint16_t*)k_nope,
                        (uint16_t*)value);
@@ -561,14 +571,15 @@ static void dec_launch_t(const void* X, const void* Wa, const void* gamma, const
 hipError_t launch_fp_decode(int dt, const void* X, const void* Wa, const void* gamma,
                             const void* Wb, const int32_t* pos, int64_t T, int H, int nh,
                             float eps, const RopeTab& rt, void* k_nope, void* value, void* k_pe,
-                            void* ckv, void* ws, const Plan& plan, hipStream_t st) {
+                            void* ckv, void* ws, const Plan& plan, const CacheOut& co,
+                            hipStream_t st) {
     float* P = (float*)((uint8_t*)ws + ws_fp(T, plan).p1);
     if (dt == kF16)
         dec_launch_t<kF16>(X, Wa, gamma, Wb, pos, (int)T, H, nh, eps, rt, k_nope, value, k_pe, ckv,
-                           P, plan, st);
+                           P, plan, co, st);
     else
         dec_launch_t<kBF16>(X, Wa, gamma, Wb, pos, (int)T, H, nh, eps, rt, k_nope, value, k_pe,
-                            ckv, P, plan, st);
+                            ckv, P, plan, co, st);
     return hipGetLastError();
 }
 

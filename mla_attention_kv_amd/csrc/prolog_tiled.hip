@@ -884,11 +884,12 @@ template <int E>
 __global__ __launch_bounds__(256) void finish_a_fp_kernel(
     const float* __restrict__ P, int S, int64_t T, const uint16_t* __restrict__ gamma,
     const int32_t* __restrict__ pos, float eps, RopeTab rt, uint16_t* __restrict__ ckv,
-    uint16_t* __restrict__ kpe) {
+    uint16_t* __restrict__ kpe, CacheOut co) {
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     const int lane = threadIdx.x & 63;
     const int pt = pos[t];
+    const int64_t slot = co.cache != nullptr ? co.slots[t] : -1;
     const u4_t g = *(const u4_t*)(gamma + 8 * lane);
     float c[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float p = 0.f;
@@ -925,7 +926,13 @@ __global__ __launch_bounds__(256) void finish_a_fp_kernel(
     float cs, sn;
     rope_cos_sin(pt, rt.f[lane & 31], cs, sn);
     const float out = (lane < 32) ? (p * cs - partner * sn) : (p * cs + partner * sn);
-    __builtin_nontemporal_store(f32_to_st<E>(out), kpe + t * kDR + lane);
+    const uint16_t ko = f32_to_st<E>(out);
+    __builtin_nontemporal_store(ko, kpe + t * kDR + lane);
+    if (cache_slot_ok(co, slot)) {  // the paged cache: [latent | rope key] in the token's slot
+        uint16_t* row = co.cache + slot * (kR + kDR);
+        __builtin_nontemporal_store(o, (u4_t*)(row + 8 * lane));
+        __builtin_nontemporal_store(ko, row + kR + lane);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1171,21 +1178,23 @@ static void gemm2_dispatch(int bm, int bn, const void* A, int64_t lda, const voi
 
 void launch_finish_fp(int dt, const float* P, int S, int64_t T, const void* gamma,
                       const int32_t* pos, float eps, const RopeTab& rt, void* ckv, void* kpe,
-                      hipStream_t st) {
+                      const CacheOut& co, hipStream_t st) {
     const dim3 grid((unsigned)((T + 3) / 4)), blk(256);  // four tokens per workgroup
     if (dt == kF16)
         hipLaunchKernelGGL(finish_a_fp_kernel<kF16>, grid, blk, 0, st, P, S, T,
-                           (const uint16_t*)gamma, pos, eps, rt, (uint16_t*)ckv, (uint16_t*)kpe);
+                           (const uint16_t*)gamma, pos, eps, rt, (uint16_t*)ckv, (uint16_t*)kpe,
+                           co);
     else
         hipLaunchKernelGGL(finish_a_fp_kernel<kBF16>, grid, blk, 0, st, P, S, T,
-                           (const uint16_t*)gamma, pos, eps, rt, (uint16_t*)ckv, (uint16_t*)kpe);
+                           (const uint16_t*)gamma, pos, eps, rt, (uint16_t*)ckv, (uint16_t*)kpe,
+                           co);
 }
 
 template <int E>
 static hipError_t launch_fp_t(const void* X, const void* Wa, const void* gamma, const void* Wb,
                               const int32_t* pos, int64_t T, int H, int nh, float eps,
                               const RopeTab& rt, void* k_nope, void* value, void* k_pe, void* ckv,
-                              void* ws, const Plan& plan, hipStream_t st) {
+                              void* ws, const Plan& plan, const CacheOut& co, hipStream_t st) {
     const WsFp w = ws_fp(T, plan);
     float* P1 = (float*)((uint8_t*)ws + w.p1);
     const int kslabs1 = H * 2 / 128;
@@ -1201,7 +1210,7 @@ static hipError_t launch_fp_t(const void* X, const void* Wa, const void* gamma, 
     else
         gemm1_dispatch<E>(plan.bm1, X, (int64_t)H * 2, Wa, T, kslabs1, plan.s1,
                           EpiPartialF32{P1, T}, st);
-    launch_finish_fp(E, P1, plan.s1, T, gamma, pos, eps, rt, ckv, k_pe, st);
+    launch_finish_fp(E, P1, plan.s1, T, gamma, pos, eps, rt, ckv, k_pe, co, st);
     const int N2 = nh * kHeadW;
     gemm2_dispatch<E>(plan.bm2, plan.bn2, ckv, (int64_t)kR * 2, Wb, T, N2,
                       EpiKvFp<E>{(uint16_t*)k_nope, (uint16_t*)value, nh}, st);
@@ -1211,15 +1220,15 @@ static hipError_t launch_fp_t(const void* X, const void* Wa, const void* gamma, 
 hipError_t launch_fp(int dt, const void* X, const void* Wa, const void* gamma, const void* Wb,
                      const int32_t* pos, int64_t T, int H, int nh, float eps, const RopeTab& rt,
                      void* k_nope, void* value, void* k_pe, void* ckv, void* ws,
-                     const Plan& plan, hipStream_t st) {
+                     const Plan& plan, const CacheOut& co, hipStream_t st) {
     if (plan.stream)
         return launch_fp_decode(dt, X, Wa, gamma, Wb, pos, T, H, nh, eps, rt, k_nope, value,
-                                k_pe, ckv, ws, plan, st);
+                                k_pe, ckv, ws, plan, co, st);
     if (dt == kF16)
         return launch_fp_t<kF16>(X, Wa, gamma, Wb, pos, T, H, nh, eps, rt, k_nope, value,
-                                 k_pe, ckv, ws, plan, st);
+                                 k_pe, ckv, ws, plan, co, st);
     return launch_fp_t<kBF16>(X, Wa, gamma, Wb, pos, T, H, nh, eps, rt, k_nope, value, k_pe,
-                              ckv, ws, plan, st);
+                              ckv, ws, plan, co, st);
 }
 
 hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa, const void* gamma,

@@ -181,3 +181,49 @@ def test_cache_append_argument_errors(q8):
     # nothing to do: no pointer is needed and nothing is launched
     assert call_cache(T=0, ptrs=[None] * 5, q8=q8) == mla.MLA_OK
     assert call_cache(slots=0, ptrs=[FAKE, FAKE, FAKE, None, None], q8=q8) == mla.MLA_OK
+
+
+def call_fp_cached(T=4, ptrs=None, slots_ptr=FAKE, cache=FAKE, slots=1024, ws=FAKE,
+                   wsb=1 << 40):
+    p = [FAKE] * 9 if ptrs is None else ptrs
+    return mla.lib().mla_kv_prolog_cached(p[0], p[1], p[2], p[3], p[4], T, V2.c(), 1, 1e-6,
+                                          1e4, p[5], p[6], p[7], p[8], slots_ptr, cache, slots,
+                                          ws, wsb, None)
+
+
+def test_prolog_cached_argument_errors():
+    # the prolog's own checks still apply
+    for i in range(9):
+        p = [FAKE] * 9
+        p[i] = None
+        assert call_fp_cached(ptrs=p) == mla.MLA_ERR_INVALID_ARG, i
+        p[i] = FAKE + 2
+        assert call_fp_cached(ptrs=p) == mla.MLA_ERR_MISALIGNED, i
+    assert call_fp_cached(wsb=0) == mla.MLA_ERR_WORKSPACE
+    # and the cache's
+    assert call_fp_cached(slots=-1) == mla.MLA_ERR_INVALID_ARG
+    assert call_fp_cached(slots_ptr=None) == mla.MLA_ERR_INVALID_ARG
+    assert call_fp_cached(cache=None) == mla.MLA_ERR_INVALID_ARG
+    assert call_fp_cached(slots_ptr=FAKE + 4) == mla.MLA_ERR_MISALIGNED
+    assert call_fp_cached(cache=FAKE + 8) == mla.MLA_ERR_MISALIGNED
+    # without slots the cache pointers are not needed (the call then fails
+    # only on the prolog's workspace check, so nothing launches)
+    assert call_fp_cached(slots=0, slots_ptr=None, cache=None, wsb=0) == mla.MLA_ERR_WORKSPACE
+    assert call_fp_cached(T=0, ptrs=[None] * 9, slots_ptr=None, cache=None, ws=None,
+                          wsb=0) == mla.MLA_OK
+
+
+def test_python_prolog_cached_checks_tensors():
+    torch = pytest.importorskip("torch")
+    T, H = 3, 64
+    X = torch.zeros(T, H, dtype=torch.float16)
+    Wa = torch.zeros(H, 576, dtype=torch.float16)
+    g = torch.zeros(512, dtype=torch.float16)
+    Wb = torch.zeros(512, 256, dtype=torch.float16)
+    pos = torch.zeros(T, dtype=torch.int32)
+    with pytest.raises(ValueError):  # int32 slot mapping
+        mla.mla_kv_prolog_cached(X, Wa, g, Wb, pos, torch.zeros(T, dtype=torch.int32),
+                                 torch.zeros(8, 576, dtype=torch.float16))
+    with pytest.raises(ValueError):  # cache of another dtype
+        mla.mla_kv_prolog_cached(X, Wa, g, Wb, pos, torch.zeros(T, dtype=torch.int64),
+                                 torch.zeros(8, 576, dtype=torch.bfloat16))

@@ -150,17 +150,17 @@ CONFIGS = [
 def _positions_for(idx: int, rng: np.random.Generator):
     """Token count, positions and sequence lengths of a configuration."""
     if idx == 0:
-        return np.array([rng.integers(0, 4096)], np.int32), None
+        return np.array([rng.integers(0, 4096)], np.int32), np.array([1], np.int64)
     if idx == 1:
         lens = rng.integers(16, 4096, 32)
         pos = np.stack([lens, lens + 1], axis=1).reshape(-1)
-        return pos.astype(np.int32), None
+        return pos.astype(np.int32), np.full(32, 2, np.int64)
     if idx == 2:
-        return np.arange(4096, dtype=np.int32), None
+        return np.arange(4096, dtype=np.int32), np.array([4096], np.int64)
     if idx == 3:
         base = rng.integers(0, 32767, 128)
         pos = np.stack([base, base + 1], axis=1).reshape(-1)
-        return pos.astype(np.int32), None
+        return pos.astype(np.int32), np.full(128, 2, np.int64)
     if idx == 4:
         lens = rng.integers(512, 4097, 8)
         pos = np.concatenate([np.arange(L) for L in lens])
@@ -208,6 +208,28 @@ def make_custom(dims: Dims, T: int, *, kind: str = "fp", dtype: str = "f16",
     tens = _draw_tensors(rng, dims, T, kind, dtype, wstd)
     return Workload(name=f"custom_T{T}_H{dims.H}_nh{dims.nh}_{kind}_{dtype}", dims=dims,
                     kind=kind, dtype=dtype, T=T, positions=positions, **tens)
+
+
+def paged_slot_mapping(w: Workload, block_size: int = 64, seed: int = 0,
+                       spare_blocks: float = 1.0):
+    """A paged-cache slot mapping for the workload's tokens: every sequence
+    owns blocks of ``block_size`` slots drawn at random (without replacement)
+    from one pool, one block per ``block_size`` positions it touches, and
+    token t of sequence q goes to slot block(q, pos // B) * B + pos % B.
+    Returns (int64 slots [T], number of slots in the pool); the pool holds
+    ``1 + spare_blocks`` times the blocks in use, so most slots stay empty.
+    In a workload without sequence lengths every token is a sequence of its
+    own (its positions are independent draws)."""
+    rng = np.random.default_rng(seed)
+    lens = w.seq_lens if w.seq_lens is not None else np.ones(w.T, np.int64)
+    seq = np.repeat(np.arange(len(lens)), lens)
+    assert len(seq) == w.T
+    keys = seq.astype(np.int64) * (1 << 32) + (w.positions.astype(np.int64) // block_size)
+    uniq, inv = np.unique(keys, return_inverse=True)
+    nblocks = int(np.ceil(len(uniq) * (1.0 + spare_blocks)))
+    blocks = rng.permutation(nblocks)[:len(uniq)].astype(np.int64)
+    slots = blocks[inv] * block_size + w.positions.astype(np.int64) % block_size
+    return slots, nblocks * block_size
 
 
 def algorithmic_bytes(dims: Dims, T: int, kind: str, dtype: str = "f16") -> int:
