@@ -18,8 +18,9 @@ Prints ONE JSON line on stdout.
 --op prolog_cached times the prolog with the paged KV-cache append fused
 into its finish (each token's compressed_kv and k_pe rows also land in its
 slot of a paged cache; the rotated input sets map to disjoint blocks of one
-cache); --op prolog_then_append times the same work as two calls (the
-prolog, then mla_kv_cache_append), for comparison.
+cache; for the W8A8 workload the int8 cache with one scale per slot);
+--op prolog_then_append times the same work as two calls (the prolog, then
+the append), for comparison.
 
 --op cache_append / cache_append_int8 times the paged KV-cache append
 instead (the step after "assemble"): the workload's T rows of
@@ -111,7 +112,11 @@ class Sets:
             import workloads
 
             slots, nsl = workloads.paged_slot_mapping(w, seed=7)
-            self.cache = torch.zeros((nsl * n_sets, d.r + d.dr), dtype=odt, device=dev)
+            # fp16 / bf16 prolog: a cache of the model dtype; W8A8: the int8
+            # cache with one scale per slot
+            cdt = odt if w.kind == "fp" else torch.int8
+            self.cache = torch.zeros((nsl * n_sets, d.r + d.dr), dtype=cdt, device=dev)
+            self.scale = torch.zeros(nsl * n_sets, dtype=torch.float32, device=dev)
             self.slot_sets = [torch.from_numpy(slots + i * nsl).to(dev) for i in range(n_sets)]
         for i in range(n_sets):
             t = {k: v.clone() for k, v in base.items()}
@@ -139,16 +144,27 @@ class Sets:
                      t["pos"].data_ptr(), w.T, self.dims.c(), w.eps, w.theta,
                      outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
                      outs[3].data_ptr(), None, None, 0, 0, ws.data_ptr(), ws.numel())
+                if cache_mode == "fused":
+                    a = a[:15] + (self.slot_sets[i].data_ptr(), None, self.cache.data_ptr(),
+                                  self.scale.data_ptr(), self.cache.shape[0]) + a[19:]
+                elif cache_mode == "separate":
+                    self.append_args.append(
+                        (outs[3].data_ptr(), outs[2].data_ptr(), self.slot_sets[i].data_ptr(),
+                         w.T, self.dims.c(), mla.MLA_BF16, self.cache.data_ptr(),
+                         self.scale.data_ptr(), self.cache.shape[0]))
             self.args.append(a)
         self.fn = mla.lib().mla_kv_prolog if w.kind == "fp" else mla.lib().mla_kv_prolog_w8a8
         if cache_mode == "fused":
-            self.fn = mla.lib().mla_kv_prolog_cached
+            self.fn = (mla.lib().mla_kv_prolog_cached if w.kind == "fp"
+                       else mla.lib().mla_kv_prolog_w8a8_cached)
+        self.append_fn = (mla.lib().mla_kv_cache_append if w.kind == "fp"
+                          else mla.lib().mla_kv_cache_append_int8)
 
     def call(self, i, stream_ptr):
         st = self.fn(*self.args[i % len(self.args)], ctypes.c_void_p(stream_ptr))
         if st == 0 and self.cache_mode == "separate":
-            st = self.mla.lib().mla_kv_cache_append(*self.append_args[i % len(self.args)],
-                                                    ctypes.c_void_p(stream_ptr))
+            st = self.append_fn(*self.append_args[i % len(self.args)],
+                                ctypes.c_void_p(stream_ptr))
         if st != 0:
             raise RuntimeError(f"library call failed: {self.mla.mla_status_string(st)}")
 
@@ -385,7 +401,7 @@ def main():
         mla.mla_kv_prolog_force_path(args.path)
 
     cfg = workloads.CONFIGS[args.config]
-    if args.op != "prolog" and cfg["kind"] != "fp":
+    if args.op.startswith("cache_append") and cfg["kind"] != "fp":
         print(f"--op {args.op} needs an fp16 / bf16 workload", file=sys.stderr)
         sys.exit(2)
     if args.op.startswith("cache_append"):
@@ -398,7 +414,9 @@ def main():
     alg_bytes = workloads.algorithmic_bytes(d, w.T, w.kind, w.dtype)
     cache_mode = {"prolog_cached": "fused", "prolog_then_append": "separate"}.get(args.op)
     if cache_mode is not None:
-        alg_bytes += w.T * ((d.r + d.dr) * 2 + 8)  # each token's cache slot and its slot index
+        # each token's cache slot (int8 codes + scale for W8A8) and its slot index
+        alg_bytes += w.T * ((d.r + d.dr) * (2 if w.kind == "fp" else 1) +
+                            (0 if w.kind == "fp" else 4) + 8)
     alg_flops = workloads.algorithmic_flops(d, w.T)
     n_sets = max(1, math.ceil(ROTATE_BYTES / alg_bytes))
     log(f"T={w.T} algorithmic bytes/step={alg_bytes} flops/step={alg_flops} sets={n_sets}")
@@ -443,7 +461,8 @@ def main():
                        else "kv_a_proj GEMM + finish + kv_b_proj GEMM" +
                        (" (+ activation quantiser)" if w.kind == "w8a8" else "")) +
                       {None: "", "fused": "; paged-cache write fused into the finish",
-                       "separate": "; then kv_cache_append"}[cache_mode])
+                       "separate": "; then kv_cache_append"}[cache_mode] +
+                      ("" if cache_mode is None or w.kind == "fp" else " (int8 cache)"))
 
     cpu = None
     if not args.no_cpu_baseline:

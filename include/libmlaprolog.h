@@ -202,6 +202,29 @@ mla_status_t mla_kv_prolog_cached(const void* hidden, const void* W_kv_a, const 
                                   int64_t num_slots, void* workspace, size_t workspace_bytes,
                                   void* stream);
 
+/*
+ * The W8A8 prolog (mla_kv_prolog_w8a8, same arguments and outputs, without
+ * the debug export) with the paged-cache append fused into its finish, into
+ * exactly one cache:
+ *   kv_cache   [num_slots, r + dr] bf16: the returned rows' bits; or
+ *   kv_cache_q [num_slots, r + dr] int8 + kv_scale [num_slots] fp32: the
+ *              returned bf16 rows quantised per slot as mla_kv_cache_append_int8
+ *              does (the int8-cache "C8" of the R1 recipe's W8A8C8 mode,
+ *              section "Weight conversion"); bit-identical to that call on the
+ *              returned rows.
+ * The other cache pointer(s) must be NULL.  Slot rules, alignment and
+ * num_slots == 0 as for mla_kv_prolog_cached.
+ */
+mla_status_t mla_kv_prolog_w8a8_cached(const void* hidden_bf16, const int8_t* Wq_kv_a,
+                                       const float* s_kv_a, const void* gamma_bf16,
+                                       const int8_t* Wq_kv_b, const float* s_kv_b,
+                                       const int32_t* positions, int64_t T, mla_dims_t d,
+                                       float eps, float theta, void* k_nope, void* value,
+                                       void* k_pe, void* compressed_kv,
+                                       const int64_t* slot_mapping, void* kv_cache,
+                                       int8_t* kv_cache_q, float* kv_scale, int64_t num_slots,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* The kernel family the dispatcher picks for T tokens: 0 = decode
  * (weight-streaming, small T), 1 = prefill (MFMA-tiled, large T). */
 int mla_kv_prolog_selected_path(int64_t T, mla_dims_t d);

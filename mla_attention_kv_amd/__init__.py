@@ -38,6 +38,7 @@ EXPORTS = (
     "mla_kv_cache_append",
     "mla_kv_cache_append_int8",
     "mla_kv_prolog_cached",
+    "mla_kv_prolog_w8a8_cached",
     "mla_kv_prolog_selected_path",
     "mla_kv_prolog_force_path",
     "mla_status_string",
@@ -100,6 +101,10 @@ def lib() -> ctypes.CDLL:
     L.mla_kv_prolog_cached.argtypes = [vp, vp, vp, vp, vp, i64, mla_dims_t, i32, f32, f32,
                                        vp, vp, vp, vp, vp, vp, i64, vp, sz, vp]
     L.mla_kv_prolog_cached.restype = i32
+    L.mla_kv_prolog_w8a8_cached.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, mla_dims_t, f32,
+                                            f32, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, sz,
+                                            vp]
+    L.mla_kv_prolog_w8a8_cached.restype = i32
     L.mla_kv_prolog_selected_path.argtypes = [i64, mla_dims_t]
     L.mla_kv_prolog_selected_path.restype = i32
     L.mla_kv_prolog_force_path.argtypes = [i32]
@@ -277,6 +282,29 @@ def mla_kv_prolog_w8a8(hidden, Wq_kv_a, s_kv_a, gamma, Wq_kv_b, s_kv_b, position
     with float32 per-output-column scales, bfloat16 outputs.  dbg_acc1
     [dbg_rows, r+dr] / dbg_acc2 [dbg_rows, nh*(dn+dv)] int32 (optional)
     receive the exact accumulators of rows [dbg_row_begin, +dbg_rows)."""
+    return _prolog_w8(hidden, Wq_kv_a, s_kv_a, gamma, Wq_kv_b, s_kv_b, positions, eps, theta,
+                      k_nope, value, k_pe, compressed_kv, dbg_acc1, dbg_acc2, dbg_row_begin,
+                      dbg_rows, workspace, stream, dn, dv, None)
+
+
+def mla_kv_prolog_w8a8_cached(hidden, Wq_kv_a, s_kv_a, gamma, Wq_kv_b, s_kv_b, positions,
+                              slot_mapping, eps: float = 1e-6, theta: float = 10000.0, *,
+                              kv_cache=None, kv_cache_q=None, kv_scale=None, k_nope=None,
+                              value=None, k_pe=None, compressed_kv=None, workspace=None,
+                              stream=None, dn: int = 128, dv: int = 128):
+    """mla_kv_prolog_w8a8 that also writes each token's [compressed_kv |
+    k_pe] row into slot slot_mapping[t] ([T] int64) of exactly one cache:
+    kv_cache ([..., r+dr] bfloat16) or the int8 cache kv_cache_q ([...,
+    r+dr] int8) with kv_scale ([num_slots] float32).  Returns the four
+    outputs."""
+    return _prolog_w8(hidden, Wq_kv_a, s_kv_a, gamma, Wq_kv_b, s_kv_b, positions, eps, theta,
+                      k_nope, value, k_pe, compressed_kv, None, None, 0, 0, workspace, stream,
+                      dn, dv, (slot_mapping, kv_cache, kv_cache_q, kv_scale))
+
+
+def _prolog_w8(hidden, Wq_kv_a, s_kv_a, gamma, Wq_kv_b, s_kv_b, positions, eps, theta, k_nope,
+               value, k_pe, compressed_kv, dbg_acc1, dbg_acc2, dbg_row_begin, dbg_rows,
+               workspace, stream, dn, dv, cache):
     torch = _torch()
     dev = hidden.device
     if hidden.dim() != 2:
@@ -300,6 +328,36 @@ def mla_kv_prolog_w8a8(hidden, Wq_kv_a, s_kv_a, gamma, Wq_kv_b, s_kv_b, position
     if T > 0 and nbytes == 0:
         raise MlaError(MLA_ERR_UNSUPPORTED, "mla_kv_prolog_w8a8_workspace_size")
     ws = _workspace(nbytes, dev, workspace)
+    if cache is not None:
+        slot_mapping, kv_cache, kv_cache_q, kv_scale = cache
+        W = d.r + d.dr
+        _check(slot_mapping, "slot_mapping", torch.int64, (T,), dev)
+        if (kv_cache is None) == (kv_cache_q is None):
+            raise ValueError("give exactly one of kv_cache (bfloat16) and kv_cache_q (int8)")
+        if kv_cache is not None:
+            if kv_cache.dtype != torch.bfloat16 or kv_cache.device != dev \
+                    or kv_cache.shape[-1] != W or not kv_cache.is_contiguous():
+                raise ValueError(f"kv_cache: contiguous bfloat16 [..., {W}] on {dev} expected")
+            ptrs = (kv_cache.data_ptr(), None, None)
+            nslots = kv_cache.numel() // W
+        else:
+            if kv_cache_q.dtype != torch.int8 or kv_cache_q.device != dev \
+                    or kv_cache_q.shape[-1] != W or not kv_cache_q.is_contiguous():
+                raise ValueError(f"kv_cache_q: contiguous int8 [..., {W}] on {dev} expected")
+            nslots = kv_cache_q.numel() // W
+            if kv_scale is None:
+                raise ValueError("kv_scale is needed with kv_cache_q")
+            _check(kv_scale, "kv_scale", torch.float32, (nslots,), dev)
+            ptrs = (None, kv_cache_q.data_ptr(), kv_scale.data_ptr())
+        st = lib().mla_kv_prolog_w8a8_cached(
+            hidden.data_ptr(), Wq_kv_a.data_ptr(), s_kv_a.data_ptr(), gamma.data_ptr(),
+            Wq_kv_b.data_ptr(), s_kv_b.data_ptr(), positions.data_ptr(), T, d.c(), float(eps),
+            float(theta), outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
+            outs[3].data_ptr(), slot_mapping.data_ptr(), ptrs[0], ptrs[1], ptrs[2], nslots,
+            ws.data_ptr(), ws.numel(), _stream_ptr(dev, stream))
+        if st != MLA_OK:
+            raise MlaError(st, "mla_kv_prolog_w8a8_cached")
+        return outs
     st = lib().mla_kv_prolog_w8a8(
         hidden.data_ptr(), Wq_kv_a.data_ptr(), s_kv_a.data_ptr(), gamma.data_ptr(),
         Wq_kv_b.data_ptr(), s_kv_b.data_ptr(), positions.data_ptr(), T, d.c(), float(eps),

@@ -213,14 +213,17 @@ mla_status_t mla_kv_prolog(const void* hidden, const void* W_kv_a, const void* g
                      workspace_bytes, stream);
 }
 
-mla_status_t mla_kv_prolog_w8a8(const void* hidden_bf16, const int8_t* Wq_kv_a,
+}  // extern "C"
+
+namespace {
+mla_status_t prolog_w8(const void* hidden_bf16, const int8_t* Wq_kv_a,
                                 const float* s_kv_a, const void* gamma_bf16,
                                 const int8_t* Wq_kv_b, const float* s_kv_b,
                                 const int32_t* positions, int64_t T, mla_dims_t d, float eps,
                                 float theta, void* k_nope, void* value, void* k_pe,
                                 void* compressed_kv, int32_t* dbg_acc1, int32_t* dbg_acc2,
-                                int64_t dbg_row_begin, int64_t dbg_rows, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+                                int64_t dbg_row_begin, int64_t dbg_rows, const CacheOut& co,
+                                void* workspace, size_t workspace_bytes, void* stream) {
     if (T < 0 || T > MLA_MAX_TOKENS) return MLA_ERR_INVALID_ARG;
     if (!std::isfinite(eps) || eps < 0.f || !std::isfinite(theta) || theta <= 0.f)
         return MLA_ERR_INVALID_ARG;
@@ -248,8 +251,25 @@ mla_status_t mla_kv_prolog_w8a8(const void* hidden_bf16, const int8_t* Wq_kv_a,
     hipError_t e = launch_w8a8(hidden_bf16, Wq_kv_a, s_kv_a, gamma_bf16, Wq_kv_b, s_kv_b,
                                positions, T, d.H, d.nh, eps, rope_table(theta), k_nope, value, k_pe,
                                compressed_kv, dbg_acc1, dbg_acc2, dbg_row_begin, dbg_rows,
-                               workspace, plan, (hipStream_t)stream);
+                               workspace, plan, co, (hipStream_t)stream);
     return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+}  // namespace
+
+extern "C" {
+
+mla_status_t mla_kv_prolog_w8a8(const void* hidden_bf16, const int8_t* Wq_kv_a,
+                                const float* s_kv_a, const void* gamma_bf16,
+                                const int8_t* Wq_kv_b, const float* s_kv_b,
+                                const int32_t* positions, int64_t T, mla_dims_t d, float eps,
+                                float theta, void* k_nope, void* value, void* k_pe,
+                                void* compressed_kv, int32_t* dbg_acc1, int32_t* dbg_acc2,
+                                int64_t dbg_row_begin, int64_t dbg_rows, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    return prolog_w8(hidden_bf16, Wq_kv_a, s_kv_a, gamma_bf16, Wq_kv_b, s_kv_b, positions, T, d,
+                     eps, theta, k_nope, value, k_pe, compressed_kv, dbg_acc1, dbg_acc2,
+                     dbg_row_begin, dbg_rows, CacheOut{nullptr, nullptr, 0}, workspace,
+                     workspace_bytes, stream);
 }
 
 static mla_status_t kv_cache_args(const void* compressed_kv, const void* k_pe,
@@ -310,6 +330,44 @@ mla_status_t mla_kv_prolog_cached(const void* hidden, const void* W_kv_a, const 
                       num_slots > 0 ? (uint16_t*)kv_cache : nullptr, num_slots};
     return prolog_fp(hidden, W_kv_a, gamma, W_kv_b, positions, T, d, dt, eps, theta, k_nope,
                      value, k_pe, compressed_kv, co, workspace, workspace_bytes, stream);
+}
+
+mla_status_t mla_kv_prolog_w8a8_cached(const void* hidden_bf16, const int8_t* Wq_kv_a,
+                                       const float* s_kv_a, const void* gamma_bf16,
+                                       const int8_t* Wq_kv_b, const float* s_kv_b,
+                                       const int32_t* positions, int64_t T, mla_dims_t d,
+                                       float eps, float theta, void* k_nope, void* value,
+                                       void* k_pe, void* compressed_kv,
+                                       const int64_t* slot_mapping, void* kv_cache,
+                                       int8_t* kv_cache_q, float* kv_scale, int64_t num_slots,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+    if (num_slots < 0) return MLA_ERR_INVALID_ARG;
+    const bool q8 = kv_cache_q != nullptr || kv_scale != nullptr;
+    if (T > 0 && num_slots > 0) {
+        // exactly one cache: bf16 (kv_cache) or int8 codes + scales
+        if (slot_mapping == nullptr) return MLA_ERR_INVALID_ARG;
+        if (q8 ? (kv_cache != nullptr || kv_cache_q == nullptr || kv_scale == nullptr)
+               : kv_cache == nullptr)
+            return MLA_ERR_INVALID_ARG;
+        if (((uintptr_t)slot_mapping & 7u) != 0) return MLA_ERR_MISALIGNED;
+        if (q8 ? (!aligned16(kv_cache_q) || ((uintptr_t)kv_scale & 3u) != 0)
+               : !aligned16(kv_cache))
+            return MLA_ERR_MISALIGNED;
+    }
+    CacheOut co{nullptr, nullptr, 0};
+    if (num_slots > 0) {
+        co.slots = slot_mapping;
+        co.num_slots = num_slots;
+        if (q8) {
+            co.cache_q = kv_cache_q;
+            co.scale = kv_scale;
+        } else {
+            co.cache = (uint16_t*)kv_cache;
+        }
+    }
+    return prolog_w8(hidden_bf16, Wq_kv_a, s_kv_a, gamma_bf16, Wq_kv_b, s_kv_b, positions, T, d,
+                     eps, theta, k_nope, value, k_pe, compressed_kv, nullptr, nullptr, 0, 0, co,
+                     workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -15,36 +15,6 @@
 
 namespace mla {
 
-// 8 values of dtype E (in v) to 8 int8 codes: clamp(rint(x * inv), +-127),
-// fp32 with round-half-even (the W8A8 activation scheme)
-template <int E>
-__device__ __forceinline__ u2_t codes8(const u4_t v, float inv) {
-    u2_t q;
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-        uint32_t packed = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const uint32_t word = v[2 * w + (b >> 1)];
-            const uint16_t bits = (uint16_t)((b & 1) ? (word >> 16) : (word & 0xFFFFu));
-            float r = rintf(ld_to_f32<E>(bits) * inv);
-            r = fminf(fmaxf(r, -127.f), 127.f);
-            packed |= ((uint32_t)(uint8_t)(int8_t)(int)r) << (8 * b);
-        }
-        q[w] = packed;
-    }
-    return q;
-}
-template <int E>
-__device__ __forceinline__ float absmax8_e(const u4_t v, float a) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        a = fmaxf(a, fabsf(ld_to_f32<E>((uint16_t)(v[w] & 0xFFFFu))));
-        a = fmaxf(a, fabsf(ld_to_f32<E>((uint16_t)(v[w] >> 16))));
-    }
-    return a;
-}
-
 // One wave per token, four tokens per workgroup.  Lane l carries latent
 // values 8l .. 8l + 7; lanes 0-7 also carry rope values 8l .. 8l + 7.  Both
 // rows are loaded (streaming) before the slot test, so every load is in

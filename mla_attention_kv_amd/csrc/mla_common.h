@@ -163,17 +163,52 @@ inline WsW8 ws_w8(int64_t T, int H, const Plan& p) {
     return w;
 }
 
-// Optional paged KV-cache output of the prolog: the finish step also writes
-// each token's [compressed_kv row | k_pe row] into slot slots[t] of cache
-// ([num_slots, 576], model dtype) when cache != nullptr; a slot outside
-// [0, num_slots) skips the token.
+// Optional paged KV-cache output of the prolog: when slots != nullptr the
+// finish step also writes each token's [compressed_kv row | k_pe row] into
+// slot slots[t], either as the model dtype (cache, [num_slots, 576]) or as
+// int8 codes with one fp32 scale per slot (cache_q [num_slots, 576], scale
+// [num_slots]; W8A8 prolog only); a slot outside [0, num_slots) skips the
+// token.
 struct CacheOut {
     const int64_t* slots;
     uint16_t* cache;
     int64_t num_slots;
+    int8_t* cache_q = nullptr;
+    float* scale = nullptr;
 };
 __device__ __forceinline__ bool cache_slot_ok(const CacheOut& co, int64_t s) {
-    return co.cache != nullptr && s >= 0 && s < co.num_slots;
+    return co.slots != nullptr && s >= 0 && s < co.num_slots;
+}
+
+// The int8 cache scheme (the W8A8 activation one, over a slot's 576
+// values): 8 values of dtype E (in v) to 8 codes clamp(rint(x * inv), +-127)
+// in fp32 with round-half-even, inv = 127 / max|value| (0 for a zero slot).
+template <int E>
+__device__ __forceinline__ u2_t codes8(const u4_t v, float inv) {
+    u2_t q;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const uint32_t word = v[2 * w + (b >> 1)];
+            const uint16_t bits = (uint16_t)((b & 1) ? (word >> 16) : (word & 0xFFFFu));
+            float r = rintf(ld_to_f32<E>(bits) * inv);
+            r = fminf(fmaxf(r, -127.f), 127.f);
+            packed |= ((uint32_t)(uint8_t)(int8_t)(int)r) << (8 * b);
+        }
+        q[w] = packed;
+    }
+    return q;
+}
+template <int E>
+__device__ __forceinline__ float absmax8_e(const u4_t v, float a) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        a = fmaxf(a, fabsf(ld_to_f32<E>((uint16_t)(v[w] & 0xFFFFu))));
+        a = fmaxf(a, fabsf(ld_to_f32<E>((uint16_t)(v[w] >> 16))));
+    }
+    return a;
 }
 
 // ---------------------------------------------------------------------------
@@ -206,6 +241,6 @@ hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa,
                        const int32_t* pos, int64_t T, int H, int nh, float eps,
                        const RopeTab& rt, void* k_nope, void* value, void* k_pe, void* ckv,
                        int32_t* dbg1, int32_t* dbg2, int64_t dbg_begin, int64_t dbg_rows,
-                       void* ws, const Plan& plan, hipStream_t st);
+                       void* ws, const Plan& plan, const CacheOut& co, hipStream_t st);
 
 }  // namespace mla

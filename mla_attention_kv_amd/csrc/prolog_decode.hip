@@ -266,7 +266,7 @@ __device__ __forceinline__ void fin_load_aux(FinPart& r, const uint16_t* __restr
     r.gm = *(const u4_t*)(gamma + 8 * lane);
     r.pos = pos[t];
     r.freq = rt.f[lane & 31];
-    r.slot = co.cache != nullptr ? co.slots[t] : -1;
+    r.slot = co.slots != nullptr ? co.slots[t] : -1;
 }
 __device__ __forceinline__ void fin_add(const FinPart& r, int S, f4_t& c0, f4_t& c1, float& p) {
 #pragma unroll

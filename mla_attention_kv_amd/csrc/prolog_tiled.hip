@@ -889,7 +889,7 @@ __global__ __launch_bounds__(256) void finish_a_fp_kernel(
     if (t >= T) return;
     const int lane = threadIdx.x & 63;
     const int pt = pos[t];
-    const int64_t slot = co.cache != nullptr ? co.slots[t] : -1;
+    const int64_t slot = co.slots != nullptr ? co.slots[t] : -1;
     const u4_t g = *(const u4_t*)(gamma + 8 * lane);
     float c[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float p = 0.f;
@@ -1030,12 +1030,14 @@ __global__ __launch_bounds__(256) void finish_a_w8_kernel(
     const float* __restrict__ swa, const uint16_t* __restrict__ gamma,
     const int32_t* __restrict__ pos, float eps, RopeTab rt, int8_t* __restrict__ QZ,
     float* __restrict__ sz, float* __restrict__ inv_out, uint16_t* __restrict__ ckv,
-    uint16_t* __restrict__ kpe, int32_t* __restrict__ dbg, int64_t dbg_begin, int64_t dbg_rows) {
+    uint16_t* __restrict__ kpe, int32_t* __restrict__ dbg, int64_t dbg_begin, int64_t dbg_rows,
+    CacheOut co) {
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     const int lane = threadIdx.x & 63;
     // every load before the first use
     const int pt = pos[t];
+    const int64_t slot = co.slots != nullptr ? co.slots[t] : -1;
     const float sxt = sx[t];
     const f4_t wa0 = *(const f4_t*)(swa + 8 * lane), wa1 = *(const f4_t*)(swa + 8 * lane + 4);
     const float wap = swa[kR + lane];
@@ -1103,7 +1105,27 @@ __global__ __launch_bounds__(256) void finish_a_w8_kernel(
     float cs, sn;
     rope_cos_sin(pt, rt.f[lane & 31], cs, sn);
     const float out = (lane < 32) ? (p * cs - partner * sn) : (p * cs + partner * sn);
-    __builtin_nontemporal_store(f32_to_bf16(out), kpe + t * kDR + lane);
+    const uint16_t ko = f32_to_bf16(out);
+    __builtin_nontemporal_store(ko, kpe + t * kDR + lane);
+    if (cache_slot_ok(co, slot)) {
+        // the paged cache, [latent | rope key] in the token's slot: the
+        // returned bf16 rows, or their int8 codes and the slot's scale
+        constexpr int W = kR + kDR;
+        if (co.cache_q == nullptr) {
+            uint16_t* row = co.cache + slot * W;
+            __builtin_nontemporal_store(o, (u4_t*)(row + 8 * lane));
+            __builtin_nontemporal_store(ko, row + kR + lane);
+        } else {
+            const float am = wave_max(fmaxf(absmax8_e<kBF16>(o, 0.f), fabsf(bf16_to_f32(ko))));
+            const float qi = (am > 0.f) ? (127.0f / am) : 0.f;
+            int8_t* row = co.cache_q + slot * W;
+            __builtin_nontemporal_store(codes8<kBF16>(o, qi), (u2_t*)(row + 8 * lane));
+            float rk = rintf(bf16_to_f32(ko) * qi);
+            rk = fminf(fmaxf(rk, -127.f), 127.f);
+            __builtin_nontemporal_store((int8_t)(int)rk, row + kR + lane);
+            if (lane == 0) co.scale[slot] = (am > 0.f) ? (am / 127.0f) : 0.f;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1235,7 +1257,8 @@ hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa, const
                        const int8_t* Wqb, const float* swb, const int32_t* pos, int64_t T, int H,
                        int nh, float eps, const RopeTab& rt, void* k_nope, void* value, void* k_pe,
                        void* ckv, int32_t* dbg1, int32_t* dbg2, int64_t dbg_begin,
-                       int64_t dbg_rows, void* ws, const Plan& plan, hipStream_t st) {
+                       int64_t dbg_rows, void* ws, const Plan& plan, const CacheOut& co,
+                       hipStream_t st) {
     const WsW8 w = ws_w8(T, H, plan);
     uint8_t* base = (uint8_t*)ws;
     int8_t* QX = (int8_t*)(base + w.qx);
@@ -1278,7 +1301,7 @@ hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa, const
     hipLaunchKernelGGL(finish_a_w8_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, P1,
                        plan.s1, T, sx,
                        swa, (const uint16_t*)gamma, pos, eps, rt, QZ, sz, inv,
-                       (uint16_t*)ckv, (uint16_t*)k_pe, dbg1, dbg_begin, dbg_rows);
+                       (uint16_t*)ckv, (uint16_t*)k_pe, dbg1, dbg_begin, dbg_rows, co);
     const int N2 = nh * kHeadW;
     gemm2_dispatch<kI8>(plan.bm2, plan.bn2, QZ, (int64_t)kR, Wqb, T, N2,
                         EpiKvW8{(uint16_t*)k_nope, (uint16_t*)value, nh, sz, inv, swb, dbg2,

@@ -227,3 +227,29 @@ def test_python_prolog_cached_checks_tensors():
     with pytest.raises(ValueError):  # cache of another dtype
         mla.mla_kv_prolog_cached(X, Wa, g, Wb, pos, torch.zeros(T, dtype=torch.int64),
                                  torch.zeros(8, 576, dtype=torch.bfloat16))
+
+
+def call_w8_cached(T=4, slots_ptr=FAKE, cache=None, q=FAKE, sc=FAKE, slots=1024, wsb=1 << 40):
+    p = [FAKE] * 11
+    return mla.lib().mla_kv_prolog_w8a8_cached(p[0], p[1], p[2], p[3], p[4], p[5], p[6], T,
+                                               R1.c(), 1e-6, 1e4, p[7], p[8], p[9], p[10],
+                                               slots_ptr, cache, q, sc, slots, FAKE, wsb, None)
+
+
+def test_prolog_w8a8_cached_argument_errors():
+    assert call_w8_cached(slots=-1) == mla.MLA_ERR_INVALID_ARG
+    assert call_w8_cached(slots_ptr=None) == mla.MLA_ERR_INVALID_ARG
+    # exactly one cache
+    assert call_w8_cached(cache=FAKE) == mla.MLA_ERR_INVALID_ARG
+    assert call_w8_cached(q=None, sc=None) == mla.MLA_ERR_INVALID_ARG
+    assert call_w8_cached(sc=None) == mla.MLA_ERR_INVALID_ARG
+    assert call_w8_cached(q=None) == mla.MLA_ERR_INVALID_ARG
+    assert call_w8_cached(slots_ptr=FAKE + 4) == mla.MLA_ERR_MISALIGNED
+    assert call_w8_cached(q=FAKE + 8) == mla.MLA_ERR_MISALIGNED
+    assert call_w8_cached(sc=FAKE + 2) == mla.MLA_ERR_MISALIGNED
+    assert call_w8_cached(cache=FAKE + 8, q=None, sc=None) == mla.MLA_ERR_MISALIGNED
+    # valid cache arguments: the prolog's own checks still apply
+    assert call_w8_cached(wsb=16) == mla.MLA_ERR_WORKSPACE
+    assert call_w8_cached(cache=FAKE, q=None, sc=None, wsb=16) == mla.MLA_ERR_WORKSPACE
+    assert call_w8_cached(slots=0, slots_ptr=None, q=None, sc=None, wsb=16) == \
+        mla.MLA_ERR_WORKSPACE

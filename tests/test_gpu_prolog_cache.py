@@ -1,5 +1,5 @@
 """GPU parity of the prolog with the paged KV-cache append fused into its
-finish (mla_kv_prolog_cached).
+finish (mla_kv_prolog_cached, mla_kv_prolog_w8a8_cached).
 
 Each case checks, on seeded synthetic inputs and a paged slot mapping:
   * the four returned outputs against the CPU oracle's prolog (the
@@ -10,6 +10,9 @@ Each case checks, on seeded synthetic inputs and a paged slot mapping:
   * that every written slot holds exactly the bits of the returned rows, and
     that the returned outputs equal those of the plain prolog bit for bit
     (the fused write changes no arithmetic).
+The int8 cache of the W8A8 prolog is checked bit for bit against the
+standalone int8 append of the returned rows, and dequantised against the
+oracle's values.
 """
 import numpy as np
 import pytest
@@ -179,3 +182,99 @@ def test_prolog_cached_without_slots(dev):
                                     w.eps, w.theta)
     torch.cuda.synchronize()
     compare(gpu_rows(outs), run_oracle(w), "cached no slots")
+
+
+# ---------------------------------------------------------------------------
+# W8A8 prolog with a bf16 cache or the int8 ("C8") cache
+# ---------------------------------------------------------------------------
+
+def run_w8_cached(w, dev, slots, num_slots, q8):
+    import mla_attention_kv_amd as mla
+
+    t = upload(w, dev)
+    W = w.dims.r + w.dims.dr
+    sl = torch.from_numpy(slots).to(dev)
+    args = (t["X"], t["Wqa"], t["swa"], t["gamma"], t["Wqb"], t["swb"], t["pos"])
+    if q8:
+        cq = torch.full((num_slots, W), 99, dtype=torch.int8, device=dev)
+        cs = torch.full((num_slots,), -2.0, dtype=torch.float32, device=dev)
+        outs = mla.mla_kv_prolog_w8a8_cached(*args, sl, w.eps, w.theta, kv_cache_q=cq,
+                                             kv_scale=cs)
+        cache = (cq, cs)
+    else:
+        cb = torch.full((num_slots, W), FILL, dtype=torch.bfloat16, device=dev)
+        outs = mla.mla_kv_prolog_w8a8_cached(*args, sl, w.eps, w.theta, kv_cache=cb)
+        cache = cb
+    plain = mla.mla_kv_prolog_w8a8(*args, w.eps, w.theta)
+    torch.cuda.synchronize()
+    for a, b, n in zip(outs, plain, ("k_nope", "value", "k_pe", "ckv")):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{n}: fused != plain"
+    return outs, cache
+
+
+def check_c8(outs, cq, cs, slots, num_slots, ref, rows):
+    """The int8 cache: bit for bit what the standalone int8 append makes of
+    the returned rows (that kernel is pinned bit-exact to the oracle), and,
+    dequantised, within half a quantisation step of the oracle's values plus
+    the output tolerance.  Untouched slots keep their fill."""
+    import mla_attention_kv_amd as mla
+
+    dev = cq.device
+    W = cq.shape[1]
+    q2 = torch.full_like(cq, 99)
+    s2 = torch.full_like(cs, -2.0)
+    mla.mla_kv_cache_append_int8(outs[3], outs[2], torch.from_numpy(slots).to(dev), q2, s2)
+    torch.cuda.synchronize()
+    assert torch.equal(cq, q2), "int8 codes differ from the standalone append"
+    assert torch.equal(cs.view(torch.int32), s2.view(torch.int32)), "scales differ"
+    rows = np.asarray(rows)
+    ok = (slots[rows] >= 0) & (slots[rows] < num_slots)
+    sidx = torch.from_numpy(slots[rows][ok]).to(dev)
+    codes = cq[sidx].cpu().numpy().astype(np.float64)
+    scale = cs[sidx].cpu().numpy().astype(np.float64)
+    deq = codes * scale[:, None]
+    refv = np.concatenate([ref["ckv"][ok], ref["k_pe"][ok]], axis=1)
+    bound = 0.5 * scale[:, None] * (1 + 1e-6) + ATOL + RTOL * np.abs(refv)
+    bad = ~(np.abs(deq - refv) <= bound)
+    assert not bad.any(), f"{int(bad.sum())} dequantised cache values out of bound"
+    assert np.all(np.abs(codes).max(axis=1) == 127), "each slot's largest code is 127"
+    mapped = slots[(slots >= 0) & (slots < num_slots)]
+    untouched = np.setdiff1d(np.arange(num_slots), mapped)
+    if untouched.size:
+        u = torch.from_numpy(untouched).to(dev)
+        assert bool((cq[u] == 99).all()) and bool((cs[u] == -2.0).all())
+
+
+@pytest.mark.parametrize("q8", [False, True])
+@pytest.mark.parametrize("T", [5, 131])
+def test_prolog_w8a8_cached_small(dev, T, q8):
+    w = workloads.make_custom(Dims(H=1024, nh=8), T, kind="w8a8", dtype="bf16", seed=950 + T,
+                              wstd=0.03)
+    slots, n = workloads.paged_slot_mapping(w, block_size=16, seed=T)
+    slots = skip_some(slots, n)
+    print(f"[prolog-cache] w8a8 T={T} q8={q8} slots={n}", flush=True)
+    outs, cache = run_w8_cached(w, dev, slots, n, q8)
+    ref = run_oracle(w)
+    compare(gpu_rows(outs), ref, f"w8a8 cached T{T}")
+    if q8:
+        check_c8(outs, cache[0], cache[1], slots, n, ref, np.arange(T))
+    else:
+        check_cache_rows(outs, cache, slots, n, ref, np.arange(T))
+        check_untouched(cache, slots, n)
+
+
+@pytest.mark.parametrize("q8", [False, True])
+def test_prolog_w8a8_cached_config4_sampled(dev, q8):
+    w = workloads.make_config(4)
+    slots, n = workloads.paged_slot_mapping(w, seed=4)
+    slots = skip_some(slots, n)
+    print(f"[prolog-cache] config4 T={w.T} q8={q8} slots={n}", flush=True)
+    outs, cache = run_w8_cached(w, dev, slots, n, q8)
+    rows = np.unique(np.concatenate([sample_rows(w.T, 12, seed=44), [0, 1, 4, 6]]))
+    ref = run_oracle(w, rows)
+    compare(gpu_rows(outs, rows), ref, "w8a8 cached config4")
+    if q8:
+        check_c8(outs, cache[0], cache[1], slots, n, ref, rows)
+    else:
+        check_cache_rows(outs, cache, slots, n, ref, rows)
+        check_untouched(cache, slots, n)
