@@ -225,6 +225,38 @@ mla_status_t mla_kv_prolog_w8a8_cached(const void* hidden_bf16, const int8_t* Wq
                                        int8_t* kv_cache_q, float* kv_scale, int64_t num_slots,
                                        void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Standalone RMSNorm: the prolog's step 3 as an operator of its own (the
+ * migration guide ships it as a separate kernel next to the fused prolog:
+ * section "Directory layout", and a switch of its own in its usage section).
+ * Per row of n values, in fp32:
+ *   y[j] = round_dt((x[j] * inv) * gamma[j]),  inv = 1 / sqrt(sum_j x[j]^2 / n + eps)
+ * (eps inside the root, gamma after the normalisation: section "Precision
+ * verification"; the same arithmetic as the prolog's compressed_kv).
+ *   x [rows, n] dt (input), gamma [n] dt (input), y [rows, n] dt (output;
+ *   may be x: in place)
+ * Supported: n a multiple of 8, 8 <= n <= 8192; rows <= 2^32.  Pointers
+ * 16-byte aligned.  rows == 0 launches nothing.  Errors as for the prolog
+ * (checked before any launch).
+ */
+mla_status_t mla_rms_norm(const void* x, const void* gamma, int64_t rows, int64_t n,
+                          mla_dtype_t dt, float eps, void* y, void* stream);
+
+/*
+ * Standalone RoPE: the prolog's step 6 as an operator of its own (same
+ * sections as mla_rms_norm), rotate-half form on rows of dr values; every
+ * head of token t is rotated by positions[t]:
+ *   f_i = theta^(-2i/dr), a = positions[t] * f_i, for i < dr/2:
+ *   y[i] = x[i] cos a - x[i + dr/2] sin a;  y[i + dr/2] = x[i + dr/2] cos a + x[i] sin a
+ * (cos and sin as in the prolog: the angle formed and reduced in double).
+ *   x [T, heads, dr] dt (input), positions [T] int32 (input),
+ *   y [T, heads, dr] dt (output; may be x: in place)
+ * Supported: dr = 64, 1 <= heads <= 1024.  x and y 16-byte aligned,
+ * positions 4-byte aligned.  T == 0 launches nothing.
+ */
+mla_status_t mla_rope(const void* x, const int32_t* positions, int64_t T, int64_t heads,
+                      int64_t dr, mla_dtype_t dt, float theta, void* y, void* stream);
+
 /* The kernel family the dispatcher picks for T tokens: 0 = decode
  * (weight-streaming, small T), 1 = prefill (MFMA-tiled, large T). */
 int mla_kv_prolog_selected_path(int64_t T, mla_dims_t d);

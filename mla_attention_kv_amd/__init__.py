@@ -39,6 +39,8 @@ EXPORTS = (
     "mla_kv_cache_append_int8",
     "mla_kv_prolog_cached",
     "mla_kv_prolog_w8a8_cached",
+    "mla_rms_norm",
+    "mla_rope",
     "mla_kv_prolog_selected_path",
     "mla_kv_prolog_force_path",
     "mla_status_string",
@@ -105,6 +107,10 @@ def lib() -> ctypes.CDLL:
                                             f32, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, sz,
                                             vp]
     L.mla_kv_prolog_w8a8_cached.restype = i32
+    L.mla_rms_norm.argtypes = [vp, vp, i64, i64, i32, f32, vp, vp]
+    L.mla_rms_norm.restype = i32
+    L.mla_rope.argtypes = [vp, vp, i64, i64, i64, i32, f32, vp, vp]
+    L.mla_rope.restype = i32
     L.mla_kv_prolog_selected_path.argtypes = [i64, mla_dims_t]
     L.mla_kv_prolog_selected_path.restype = i32
     L.mla_kv_prolog_force_path.argtypes = [i32]
@@ -420,3 +426,55 @@ def mla_kv_cache_append_int8(compressed_kv, k_pe, slot_mapping, kv_cache_q, kv_s
     if rc != MLA_OK:
         raise MlaError(rc, "mla_kv_cache_append_int8")
     return kv_cache_q, kv_scale
+
+
+def _dt_code(t, name):
+    torch = _torch()
+    code = {torch.float16: MLA_F16, torch.bfloat16: MLA_BF16}.get(t.dtype)
+    if code is None:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected float16 or bfloat16")
+    return code
+
+
+def mla_rms_norm(x, gamma, eps: float = 1e-6, *, out=None, stream=None):
+    """RMSNorm over the last dimension of x ([..., n], float16 / bfloat16,
+    contiguous) with weight gamma [n]; out may be x (in place).  Returns out."""
+    code = _dt_code(x, "x")
+    n = x.shape[-1]
+    rows = x.numel() // n if n else 0
+    dev = x.device
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    _check(gamma, "gamma", x.dtype, (n,), dev)
+    if out is None:
+        out = _torch().empty_like(x)
+    _check(out, "out", x.dtype, tuple(x.shape), dev)
+    st = lib().mla_rms_norm(x.data_ptr(), gamma.data_ptr(), rows, n, code, float(eps),
+                            out.data_ptr(), _stream_ptr(dev, stream))
+    if st != MLA_OK:
+        raise MlaError(st, "mla_rms_norm")
+    return out
+
+
+def mla_rope(x, positions, theta: float = 10000.0, *, out=None, stream=None):
+    """Rotate-half RoPE of x ([T, heads, dr] or [T, dr], float16 / bfloat16,
+    contiguous), every head of token t rotated by positions[t] ([T] int32);
+    out may be x (in place).  Returns out."""
+    torch = _torch()
+    code = _dt_code(x, "x")
+    if x.dim() not in (2, 3):
+        raise ValueError("x must be [T, dr] or [T, heads, dr]")
+    T, dr = x.shape[0], x.shape[-1]
+    heads = x.shape[1] if x.dim() == 3 else 1
+    dev = x.device
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    _check(positions, "positions", torch.int32, (T,), dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", x.dtype, tuple(x.shape), dev)
+    st = lib().mla_rope(x.data_ptr(), positions.data_ptr(), T, heads, dr, code, float(theta),
+                        out.data_ptr(), _stream_ptr(dev, stream))
+    if st != MLA_OK:
+        raise MlaError(st, "mla_rope")
+    return out

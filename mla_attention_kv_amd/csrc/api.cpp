@@ -332,6 +332,34 @@ mla_status_t mla_kv_prolog_cached(const void* hidden, const void* W_kv_a, const 
                      value, k_pe, compressed_kv, co, workspace, workspace_bytes, stream);
 }
 
+mla_status_t mla_rms_norm(const void* x, const void* gamma, int64_t rows, int64_t n,
+                          mla_dtype_t dt, float eps, void* y, void* stream) {
+    if (rows < 0 || rows > (int64_t)MLA_MAX_TOKENS * 1024) return MLA_ERR_INVALID_ARG;
+    if (dt != MLA_F16 && dt != MLA_BF16) return MLA_ERR_INVALID_ARG;
+    if (!std::isfinite(eps) || eps < 0.f) return MLA_ERR_INVALID_ARG;
+    if (n < 8 || n > 8192 || (n % 8) != 0) return MLA_ERR_UNSUPPORTED;
+    if (rows == 0) return MLA_OK;
+    if (x == nullptr || gamma == nullptr || y == nullptr) return MLA_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(gamma) || !aligned16(y)) return MLA_ERR_MISALIGNED;
+    const hipError_t e = launch_rms_norm(dt, x, gamma, rows, (int)n, eps, y, (hipStream_t)stream);
+    return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_rope(const void* x, const int32_t* positions, int64_t T, int64_t heads,
+                      int64_t dr, mla_dtype_t dt, float theta, void* y, void* stream) {
+    if (T < 0 || T > MLA_MAX_TOKENS || heads < 1 || heads > 1024) return MLA_ERR_INVALID_ARG;
+    if (dt != MLA_F16 && dt != MLA_BF16) return MLA_ERR_INVALID_ARG;
+    if (!std::isfinite(theta) || theta <= 0.f) return MLA_ERR_INVALID_ARG;
+    if (dr != kDR) return MLA_ERR_UNSUPPORTED;
+    if (T == 0) return MLA_OK;
+    if (x == nullptr || positions == nullptr || y == nullptr) return MLA_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(y) || ((uintptr_t)positions & 3u) != 0)
+        return MLA_ERR_MISALIGNED;
+    const hipError_t e = launch_rope(dt, x, positions, T, (int)heads, rope_table(theta), y,
+                                     (hipStream_t)stream);
+    return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 mla_status_t mla_kv_prolog_w8a8_cached(const void* hidden_bf16, const int8_t* Wq_kv_a,
                                        const float* s_kv_a, const void* gamma_bf16,
                                        const int8_t* Wq_kv_b, const float* s_kv_b,

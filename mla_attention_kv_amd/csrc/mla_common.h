@@ -163,6 +163,32 @@ inline WsW8 ws_w8(int64_t T, int H, const Plan& p) {
     return w;
 }
 
+// RMSNorm's last step on 8 consecutive values c (fp32): times the row's
+// inverse RMS, then times gamma (8 values of dtype E packed in g), rounded to
+// E and packed.  The prolog's finish kernels and the standalone RMSNorm share
+// it.
+template <int E>
+__device__ __forceinline__ u4_t rms_scale8(const float (&c)[8], float inv, const u4_t g) {
+    u4_t o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const float g0 = ld_to_f32<E>((uint16_t)(g[w] & 0xFFFFu));
+        const float g1 = ld_to_f32<E>((uint16_t)(g[w] >> 16));
+        const uint32_t y0 = f32_to_st<E>((c[2 * w] * inv) * g0);
+        const uint32_t y1 = f32_to_st<E>((c[2 * w + 1] * inv) * g1);
+        o[w] = y0 | (y1 << 16);
+    }
+    return o;
+}
+
+// Rotate-half RoPE of one value v with its partner in the other half of the
+// rope row (v's index +- dr/2): the first half takes v cos - partner sin, the
+// second v cos + partner sin.
+__device__ __forceinline__ float rope_rotate(float v, float partner, float cs, float sn,
+                                             bool first_half) {
+    return first_half ? (v * cs - partner * sn) : (v * cs + partner * sn);
+}
+
 // Optional paged KV-cache output of the prolog: when slots != nullptr the
 // finish step also writes each token's [compressed_kv row | k_pe row] into
 // slot slots[t], either as the model dtype (cache, [num_slots, 576]) or as
@@ -230,6 +256,13 @@ hipError_t launch_fp_decode(int dt, const void* X, const void* Wa, const void* g
 void launch_finish_fp(int dt, const float* P, int S, int64_t T, const void* gamma,
                       const int32_t* pos, float eps, const RopeTab& rt, void* ckv, void* kpe,
                       const CacheOut& co, hipStream_t st);
+
+// standalone RMSNorm over rows of n values (n % 8 == 0, 8 <= n <= 8192) and
+// RoPE over x [T, heads, 64]; rows / T > 0
+hipError_t launch_rms_norm(int dt, const void* x, const void* gamma, int64_t rows, int n,
+                           float eps, void* y, hipStream_t st);
+hipError_t launch_rope(int dt, const void* x, const int32_t* pos, int64_t T, int heads,
+                       const RopeTab& rt, void* y, hipStream_t st);
 
 // paged KV-cache append: fp cache (cache_q == nullptr) or int8 codes + scales
 hipError_t launch_kv_cache_append(int dt, const void* ckv, const void* kpe, const int64_t* slots,

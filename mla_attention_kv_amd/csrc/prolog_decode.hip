@@ -316,15 +316,7 @@ __device__ __forceinline__ void finish_token_from(FinPart& r, const float* __res
         for (int i = 0; i < 8; ++i) ss += c[i] * c[i];
         ss = wave_sum(ss);
         const float inv = 1.0f / sqrtf(ss / (float)kR + eps);
-        u4_t o;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float g0 = ld_to_f32<E>((uint16_t)(gm[w] & 0xFFFFu));
-            const float g1 = ld_to_f32<E>((uint16_t)(gm[w] >> 16));
-            const uint32_t y0 = f32_to_st<E>((c[2 * w] * inv) * g0);
-            const uint32_t y1 = f32_to_st<E>((c[2 * w + 1] * inv) * g1);
-            o[w] = y0 | (y1 << 16);
-        }
+        const u4_t o = rms_scale8<E>(c, inv, gm);
         uint16_t* dst = ckv + (int64_t)t * kR + 8 * lane;
         if constexpr (COH) {
             store_coherent64(dst, (uint64_t)o[0] | ((uint64_t)o[1] << 32));
@@ -339,8 +331,7 @@ __device__ __forceinline__ void finish_token_from(FinPart& r, const float* __res
         rope_cos_sin(r.pos, r.freq, cs, sn);
         const float q = (f0[kR + lane] + f1[kR + lane]) + (f2[kR + lane] + f3[kR + lane]);
         const float partner = __shfl_xor(q, 32, 64);
-        const float out = (lane < 32) ? (q * cs - partner * sn) : (q * cs + partner * sn);
-        const uint16_t ko = f32_to_st<E>(out);
+        const uint16_t ko = f32_to_st<E>(rope_rotate(q, partner, cs, sn, lane < 32));
         kpe[(int64_t)t * kDR + lane] = ko;
         if (cache_slot_ok(co, r.slot))
             __builtin_nontemporal_store(ko, co.cache + r.slot * (kR + kDR) + kR + lane);

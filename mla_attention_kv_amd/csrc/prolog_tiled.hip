@@ -911,22 +911,13 @@ __global__ __launch_bounds__(256) void finish_a_fp_kernel(
     for (int i = 0; i < 8; ++i) ss += c[i] * c[i];
     ss = wave_sum(ss);
     const float inv = 1.0f / sqrtf(ss / (float)kR + eps);
-    u4_t o;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const float g0 = ld_to_f32<E>((uint16_t)(g[w] & 0xFFFFu));
-        const float g1 = ld_to_f32<E>((uint16_t)(g[w] >> 16));
-        const uint32_t y0 = f32_to_st<E>((c[2 * w] * inv) * g0);
-        const uint32_t y1 = f32_to_st<E>((c[2 * w + 1] * inv) * g1);
-        o[w] = y0 | (y1 << 16);
-    }
+    const u4_t o = rms_scale8<E>(c, inv, g);
     *(u4_t*)(ckv + t * kR + 8 * lane) = o;
 
     const float partner = __shfl_xor(p, 32, 64);
     float cs, sn;
     rope_cos_sin(pt, rt.f[lane & 31], cs, sn);
-    const float out = (lane < 32) ? (p * cs - partner * sn) : (p * cs + partner * sn);
-    const uint16_t ko = f32_to_st<E>(out);
+    const uint16_t ko = f32_to_st<E>(rope_rotate(p, partner, cs, sn, lane < 32));
     __builtin_nontemporal_store(ko, kpe + t * kDR + lane);
     if (cache_slot_ok(co, slot)) {  // the paged cache: [latent | rope key] in the token's slot
         uint16_t* row = co.cache + slot * (kR + kDR);
@@ -1104,7 +1095,7 @@ __global__ __launch_bounds__(256) void finish_a_w8_kernel(
     const float partner = __shfl_xor(p, 32, 64);
     float cs, sn;
     rope_cos_sin(pt, rt.f[lane & 31], cs, sn);
-    const float out = (lane < 32) ? (p * cs - partner * sn) : (p * cs + partner * sn);
+    const float out = rope_rotate(p, partner, cs, sn, lane < 32);
     const uint16_t ko = f32_to_bf16(out);
     __builtin_nontemporal_store(ko, kpe + t * kDR + lane);
     if (cache_slot_ok(co, slot)) {

@@ -46,6 +46,10 @@ def _load():
     lib.oracle_kv_cache_append.restype = i32
     lib.oracle_kv_cache_append_int8.argtypes = [i64, i64, i64, vp, vp, vp, i64, vp, vp]
     lib.oracle_kv_cache_append_int8.restype = i32
+    lib.oracle_rms_norm.argtypes = [i64, i64, vp, vp, dbl, vp]
+    lib.oracle_rms_norm.restype = i32
+    lib.oracle_rope.argtypes = [i64, i64, i64, vp, vp, dbl, vp]
+    lib.oracle_rope.restype = i32
     lib.oracle_num_threads.argtypes = [i32]
     lib.oracle_num_threads.restype = i32
     _lib = lib
@@ -181,3 +185,31 @@ def kv_cache_append_int8(ckv, kpe, slots, cache_q, scale):
     if rc != 0:
         raise ValueError(f"oracle_kv_cache_append_int8 failed: {rc}")
     return q, sc
+
+
+def rms_norm(x, gamma, eps: float) -> np.ndarray:
+    """Standalone RMSNorm over the last axis of ``x`` (fp64, before the final
+    rounding)."""
+    x = _c(x, np.float64)
+    gamma = _c(gamma, np.float64)
+    n = x.shape[-1]
+    rows = x.size // n if n else 0
+    y = np.empty_like(x)
+    rc = _load().oracle_rms_norm(rows, n, _ptr(x), _ptr(gamma), float(eps), _ptr(y))
+    if rc != 0:
+        raise ValueError(f"oracle_rms_norm failed: {rc}")
+    return y
+
+
+def rope(x, pos, theta: float) -> np.ndarray:
+    """Standalone rotate-half RoPE of ``x`` [T, dr] or [T, heads, dr], every
+    head of token t rotated by ``pos[t]`` (fp64, before the final rounding)."""
+    x = _c(x, np.float64)
+    pos = _c(pos, np.int32)
+    T, dr = x.shape[0], x.shape[-1]
+    heads = x.shape[1] if x.ndim == 3 else 1
+    y = np.empty_like(x)
+    rc = _load().oracle_rope(T, heads, dr, _ptr(x), _ptr(pos), float(theta), _ptr(y))
+    if rc != 0:
+        raise ValueError(f"oracle_rope failed: {rc}")
+    return y

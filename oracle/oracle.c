@@ -458,6 +458,45 @@ int oracle_kv_cache_append_int8(int64_t T, int64_t r, int64_t dr, const float* c
     return ORACLE_OK;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Standalone RMSNorm and RoPE (the prolog's steps 3 and 6 as operators).     */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The migration guide ships RMSNorm and RoPE as kernels of their own next to
+ * the fused prolog (section "Directory layout"; a switch for each in its
+ * usage section); what they compute is the prolog's step 3 and step 6 above,
+ * applied row by row:
+ *   rms_norm: x [rows, n] -> y[j] = x[j] / sqrt(mean_j x[j]^2 + eps) * gamma[j]
+ *   rope:     x [T, heads, dr] -> every head row of token t rotated by pos[t]
+ * Inputs are the model-dtype values widened (exactly) to double; outputs are
+ * double, before the final rounding.
+ */
+int oracle_rms_norm(int64_t rows, int64_t n, const double* x, const double* gamma,
+                    double eps, double* y)
+{
+    if (rows < 0 || n <= 0 || (rows > 0 && (!x || !gamma || !y))) return ORACLE_BAD_ARG;
+    for (int64_t t = 0; t < rows; ++t) {
+        const double* xr = x + t * n;
+        const double inv = rms_inv(xr, n, eps);
+        for (int64_t j = 0; j < n; ++j) y[t * n + j] = xr[j] * inv * gamma[j];
+    }
+    return ORACLE_OK;
+}
+
+int oracle_rope(int64_t T, int64_t heads, int64_t dr, const double* x, const int32_t* pos,
+                double theta, double* y)
+{
+    if (T < 0 || heads <= 0 || dr <= 0 || (dr % 2) != 0 || (T > 0 && (!x || !pos || !y)))
+        return ORACLE_BAD_ARG;
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t h = 0; h < heads; ++h) {
+            const int64_t off = (t * heads + h) * dr;
+            step_rope(x + off, dr, pos[t], theta, y + off);
+        }
+    return ORACLE_OK;
+}
+
 /* Number of threads an OpenMP parallel region of this library uses. */
 int oracle_num_threads(int nthreads)
 {

@@ -253,3 +253,39 @@ def test_prolog_w8a8_cached_argument_errors():
     assert call_w8_cached(cache=FAKE, q=None, sc=None, wsb=16) == mla.MLA_ERR_WORKSPACE
     assert call_w8_cached(slots=0, slots_ptr=None, q=None, sc=None, wsb=16) == \
         mla.MLA_ERR_WORKSPACE
+
+
+def test_rms_norm_and_rope_argument_errors():
+    L = mla.lib()
+    rms = lambda rows=4, n=512, dt=1, eps=1e-6, p=(FAKE, FAKE, FAKE): L.mla_rms_norm(  # noqa: E731
+        p[0], p[1], rows, n, dt, eps, p[2], None)
+    for i in range(3):
+        p = [FAKE] * 3
+        p[i] = None
+        assert rms(p=p) == mla.MLA_ERR_INVALID_ARG, i
+        p[i] = FAKE + 8
+        assert rms(p=p) == mla.MLA_ERR_MISALIGNED, i
+    assert rms(rows=-1) == mla.MLA_ERR_INVALID_ARG
+    assert rms(dt=0) == mla.MLA_ERR_INVALID_ARG
+    assert rms(eps=-1.0) == mla.MLA_ERR_INVALID_ARG
+    assert rms(eps=float("nan")) == mla.MLA_ERR_INVALID_ARG
+    for n in (0, 4, 12, 8200, 16384):
+        assert rms(n=n) == mla.MLA_ERR_UNSUPPORTED, n
+    assert rms(rows=0, p=(None, None, None)) == mla.MLA_OK
+
+    rope = lambda T=4, heads=2, dr=64, dt=2, theta=1e4, p=(FAKE, FAKE, FAKE): L.mla_rope(  # noqa: E731
+        p[0], p[1], T, heads, dr, dt, theta, p[2], None)
+    for i in range(3):
+        p = [FAKE] * 3
+        p[i] = None
+        assert rope(p=p) == mla.MLA_ERR_INVALID_ARG, i
+        p[i] = FAKE + (2 if i == 1 else 8)
+        assert rope(p=p) == mla.MLA_ERR_MISALIGNED, i
+    assert rope(T=-1) == mla.MLA_ERR_INVALID_ARG
+    assert rope(T=(1 << 22) + 1) == mla.MLA_ERR_INVALID_ARG
+    assert rope(heads=0) == mla.MLA_ERR_INVALID_ARG
+    assert rope(heads=1025) == mla.MLA_ERR_INVALID_ARG
+    assert rope(dt=5) == mla.MLA_ERR_INVALID_ARG
+    assert rope(theta=0.0) == mla.MLA_ERR_INVALID_ARG
+    assert rope(dr=128) == mla.MLA_ERR_UNSUPPORTED
+    assert rope(T=0, p=(None, None, None)) == mla.MLA_OK
