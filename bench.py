@@ -22,6 +22,10 @@ cache; for the W8A8 workload the int8 cache with one scale per slot);
 --op prolog_then_append times the same work as two calls (the prolog, then
 the append), for comparison.
 
+--op rms_norm / rope time the standalone operators on the workload's shapes:
+RMSNorm over [T, 512] (the latent), RoPE over [T, heads, 64] (a rope key per
+head, the query-side shape).
+
 --op cache_append / cache_append_int8 times the paged KV-cache append
 instead (the step after "assemble"): the workload's T rows of
 compressed_kv and k_pe (seeded, model dtype) written into a cache by a slot
@@ -296,6 +300,111 @@ class CacheSets:
             raise RuntimeError(f"library call failed: {self.mla.mla_status_string(st)}")
 
 
+class ElemSets:
+    """Rotated inputs of the standalone RMSNorm / RoPE: n_sets of (x, out)
+    plus gamma / positions, same call interface as Sets."""
+
+    def __init__(self, op, T, heads, dtype, n_sets, dev, seed):
+        import numpy as np
+        import torch
+
+        import mla_attention_kv_amd as mla
+
+        self.mla = mla
+        tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+        code = mla.MLA_F16 if dtype == "f16" else mla.MLA_BF16
+        rng = np.random.default_rng(seed)
+        shape = (T, 512) if op == "rms_norm" else (T, heads, 64)
+        self.keep, self.args = [], []
+        for _ in range(n_sets):
+            x = torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(tdt).to(dev)
+            y = torch.empty_like(x)
+            if op == "rms_norm":
+                g = torch.from_numpy(rng.uniform(0.5, 1.5, 512).astype(np.float32)).to(tdt).to(dev)
+                a = (x.data_ptr(), g.data_ptr(), T, 512, code, 1e-6, y.data_ptr())
+            else:
+                g = torch.from_numpy(rng.integers(0, 32768, T).astype(np.int32)).to(dev)
+                a = (x.data_ptr(), g.data_ptr(), T, heads, 64, code, 1e4, y.data_ptr())
+            self.keep.append((x, y, g))
+            self.args.append(a)
+        self.fn = mla.lib().mla_rms_norm if op == "rms_norm" else mla.lib().mla_rope
+
+    def call(self, i, stream_ptr):
+        st = self.fn(*self.args[i % len(self.args)], ctypes.c_void_p(stream_ptr))
+        if st != 0:
+            raise RuntimeError(f"library call failed: {self.mla.mla_status_string(st)}")
+
+
+def elem_cpu_baseline(op, T, heads, dtype, seconds, seed):
+    """The CPU oracle of RMSNorm / RoPE on (a prefix of) the same shapes,
+    repeated for about `seconds`."""
+    import numpy as np
+
+    import oracle
+
+    rng = np.random.default_rng(seed)
+    rows = min(T, 1024)
+    if op == "rms_norm":
+        x = oracle.round_to_dtype(rng.standard_normal((rows, 512)), dtype)
+        g = oracle.round_to_dtype(rng.uniform(0.5, 1.5, 512), dtype)
+        f = lambda: oracle.rms_norm(x, g, 1e-6)  # noqa: E731
+    else:
+        x = oracle.round_to_dtype(rng.standard_normal((rows, heads, 64)), dtype)
+        pos = rng.integers(0, 32768, rows).astype(np.int32)
+        f = lambda: oracle.rope(x, pos, 1e4)  # noqa: E731
+    t0 = time.perf_counter()
+    f()
+    one = time.perf_counter() - t0
+    reps = max(1, min(100000, int(seconds / max(one, 1e-6))))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        f()
+    dt = time.perf_counter() - t0
+    return {"value": rows * reps / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} x the first {rows} token rows ({dt:.1f} s; single-threaded)"}
+
+
+def main_elem(args, cfg, w, dev):
+    import torch
+
+    op = args.op
+    heads = w.dims.nh
+    per_tok = 512 * 2 * 2 if op == "rms_norm" else heads * 64 * 2 * 2 + 4
+    alg_bytes = w.T * per_tok + (512 * 2 if op == "rms_norm" else 0)
+    n_sets = max(2, math.ceil(ROTATE_BYTES / alg_bytes))
+    log(f"{op}: T={w.T} heads={heads} bytes/step={alg_bytes} sets={n_sets}")
+    sets = ElemSets(op, w.T, heads, w.dtype, n_sets, dev, seed=1000 + args.config)
+    torch.cuda.synchronize()
+    steps, warmup = args.steps, args.warmup
+    ms = time_graph(sets, steps, warmup, dev)
+    ms_per_step = ms / steps
+    step_s = ms_per_step / 1e3
+    value = w.T * steps / (ms / 1e3)
+    log(f"{ms_per_step * 1e3:.2f} us/step, {value:.4g} tokens/s")
+    roof = {"bound": "hbm", "achieved": alg_bytes / step_s / 1e9, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "traffic": None,
+            "kernel": ("rms_norm_kernel" if op == "rms_norm" else "rope_kernel") +
+                      " (one launch per call)"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = elem_cpu_baseline(op, w.T, heads, w.dtype, args.cpu_seconds, 1000 + args.config)
+    shape = [w.T, 512] if op == "rms_norm" else [w.T, heads, 64]
+    out = {
+        "metric": f"MLA standalone {op} tokens/s + % HBM roofline",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded; no public dataset exists for this path)",
+        "config": {"workload": f"{cfg['name']}_{op}", "T": w.T, "shape": shape,
+                   "timing": "HIP graph replays", "rotated_sets": n_sets,
+                   "algorithmic_bytes_per_step": alg_bytes},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def cache_cpu_baseline(T, dtype, int8, seconds, seed):
     """The CPU oracle of the append on the same shapes, repeated for about
     `seconds`."""
@@ -374,7 +483,7 @@ def main():
     ap.add_argument("--path", type=int, default=-1, help="force kernel family 0/1 (A/B runs)")
     ap.add_argument("--op", default="prolog",
                     choices=["prolog", "prolog_cached", "prolog_then_append", "cache_append",
-                             "cache_append_int8"],
+                             "cache_append_int8", "rms_norm", "rope"],
                     help="what one step is (default: the prolog)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -401,6 +510,12 @@ def main():
         mla.mla_kv_prolog_force_path(args.path)
 
     cfg = workloads.CONFIGS[args.config]
+    if args.op in ("rms_norm", "rope"):
+        w = workloads.make_config(args.config)
+        if w.kind != "fp":  # the W8A8 workload's activations are bf16
+            w.dtype = "bf16"
+        main_elem(args, cfg, w, dev)
+        return
     if args.op.startswith("cache_append") and cfg["kind"] != "fp":
         print(f"--op {args.op} needs an fp16 / bf16 workload", file=sys.stderr)
         sys.exit(2)

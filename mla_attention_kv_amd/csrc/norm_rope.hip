@@ -71,45 +71,66 @@ __global__ __launch_bounds__(256) void rms_norm_kernel(const uint16_t* x,
 }
 
 // RoPE on rows of dr = 64 values, x [T, heads, 64], every head of token t
-// rotated by positions[t].  Eight rows per wave: lane l holds values
-// 8 (l % 8) .. + 7 of row l / 8, and its partner half sits in lane l ^ 4 of
-// the same row.  Per value the arithmetic is the prolog's (rope_cos_sin on
-// the frequency of index i mod 32, then rope_rotate).  A lane's store
-// depends on its own and its partner's loads, so y may be x.
-template <int E>
+// rotated by positions[t].  A wave owns 8 R consecutive rows, eight at a
+// time: lane l holds values 8 (l % 8) .. + 7 of row 8 i + l / 8, and its
+// partner half sits in lane l ^ 4 of the same row.  All R loads are issued
+// before any arithmetic.  Per value the arithmetic is the prolog's
+// (rope_cos_sin on the frequency of index i mod 32, then rope_rotate); the
+// cos / sin pairs of a lane depend only on the token, so they are computed
+// again only when a lane's row moves to another token (with many heads per
+// token, once per token instead of once per row).  A lane's stores depend
+// on its own and its partner's loads, so y may be x.
+template <int E, int R>
 __global__ __launch_bounds__(256) void rope_kernel(const uint16_t* x,
                                                    const int32_t* __restrict__ pos,
                                                    int64_t rows, int heads, RopeTab rt,
                                                    uint16_t* y) {
-    const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
     const int lane = threadIdx.x & 63;
     const int part = lane & 7;  // 8-value group of the row
+    const int64_t base = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (8 * R) + (lane >> 3);
     // rows past the end still take part in the shuffles (with zeros) and
     // then store nothing
-    const bool live = row < rows;
-    const u4_t v = live ? __builtin_nontemporal_load((const u4_t*)(x + row * kDR + 8 * part))
-                        : u4_t{0, 0, 0, 0};
-    const int pt = live ? pos[row / heads] : 0;
-    u4_t pv;
+    u4_t v[R];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) pv[w] = (uint32_t)__shfl_xor((int)v[w], 4, 64);
+    for (int i = 0; i < R; ++i) {
+        const int64_t row = base + 8 * i;
+        v[i] = row < rows ? __builtin_nontemporal_load((const u4_t*)(x + row * kDR + 8 * part))
+                          : u4_t{0, 0, 0, 0};
+    }
     const bool first = part < 4;
     const int f0 = 8 * (part & 3);
-    u4_t o;
+    int64_t tok_prev = -1;
+    float cs[8], sn[8];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        uint32_t packed = 0;
+    for (int i = 0; i < R; ++i) {
+        const int64_t row = base + 8 * i;
+        const bool live = row < rows;
+        const int64_t tok = live ? row / heads : tok_prev;
+        if (tok != tok_prev) {
+            const int pt = pos[tok];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const float a = ld_to_f32<E>((uint16_t)(h ? (v[w] >> 16) : (v[w] & 0xFFFFu)));
-            const float b = ld_to_f32<E>((uint16_t)(h ? (pv[w] >> 16) : (pv[w] & 0xFFFFu)));
-            float cs, sn;
-            rope_cos_sin(pt, rt.f[f0 + 2 * w + h], cs, sn);
-            packed |= (uint32_t)f32_to_st<E>(rope_rotate(a, b, cs, sn, first)) << (16 * h);
+            for (int j = 0; j < 8; ++j) rope_cos_sin(pt, rt.f[f0 + j], cs[j], sn[j]);
+            tok_prev = tok;
         }
-        o[w] = packed;
+        u4_t pv;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) pv[w] = (uint32_t)__shfl_xor((int)v[i][w], 4, 64);
+        u4_t o;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            uint32_t packed = 0;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const float a = ld_to_f32<E>((uint16_t)(h ? (v[i][w] >> 16) : (v[i][w] & 0xFFFFu)));
+                const float b = ld_to_f32<E>((uint16_t)(h ? (pv[w] >> 16) : (pv[w] & 0xFFFFu)));
+                packed |= (uint32_t)f32_to_st<E>(rope_rotate(a, b, cs[2 * w + h], sn[2 * w + h],
+                                                             first))
+                          << (16 * h);
+            }
+            o[w] = packed;
+        }
+        if (live) __builtin_nontemporal_store(o, (u4_t*)(y + row * kDR + 8 * part));
     }
-    if (live) __builtin_nontemporal_store(o, (u4_t*)(y + row * kDR + 8 * part));
 }
 
 hipError_t launch_rms_norm(int dt, const void* x, const void* gamma, int64_t rows, int n,
@@ -138,16 +159,27 @@ hipError_t launch_rms_norm(int dt, const void* x, const void* gamma, int64_t row
     return hipGetLastError();
 }
 
+template <int R>
+static void rope_launch(int dt, const void* x, const int32_t* pos, int64_t rows, int heads,
+                        const RopeTab& rt, void* y, hipStream_t st) {
+    const dim3 grid((unsigned)((rows + 32 * R - 1) / (32 * R))), blk(256);  // 32 R rows each
+    if (dt == kF16)
+        hipLaunchKernelGGL((rope_kernel<kF16, R>), grid, blk, 0, st, (const uint16_t*)x, pos, rows,
+                           heads, rt, (uint16_t*)y);
+    else
+        hipLaunchKernelGGL((rope_kernel<kBF16, R>), grid, blk, 0, st, (const uint16_t*)x, pos,
+                           rows, heads, rt, (uint16_t*)y);
+}
+
 hipError_t launch_rope(int dt, const void* x, const int32_t* pos, int64_t T, int heads,
                        const RopeTab& rt, void* y, hipStream_t st) {
     const int64_t rows = T * heads;
-    const dim3 grid((unsigned)((rows + 31) / 32)), blk(256);  // 32 rows per workgroup
-    if (dt == kF16)
-        hipLaunchKernelGGL(rope_kernel<kF16>, grid, blk, 0, st, (const uint16_t*)x, pos, rows,
-                           heads, rt, (uint16_t*)y);
-    else
-        hipLaunchKernelGGL(rope_kernel<kBF16>, grid, blk, 0, st, (const uint16_t*)x, pos, rows,
-                           heads, rt, (uint16_t*)y);
+    // rows per wave: as many as keep at least ~2048 workgroups in the grid
+    // (and one token's cos / sin reused over several of its heads)
+    if (rows >= (int64_t)2048 * 32 * 8) rope_launch<8>(dt, x, pos, rows, heads, rt, y, st);
+    else if (rows >= (int64_t)2048 * 32 * 4) rope_launch<4>(dt, x, pos, rows, heads, rt, y, st);
+    else if (rows >= (int64_t)2048 * 32 * 2) rope_launch<2>(dt, x, pos, rows, heads, rt, y, st);
+    else rope_launch<1>(dt, x, pos, rows, heads, rt, y, st);
     return hipGetLastError();
 }
 

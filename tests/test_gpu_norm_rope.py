@@ -101,3 +101,25 @@ def test_rope(dev, dtype, T, heads):
         y2 = mla.mla_rope(xt[:, 0].contiguous(), pt, 1e4)  # [T, 64] form
         torch.cuda.synchronize()
         assert torch.equal(y2.view(torch.int16), y[:, 0].view(torch.int16))
+
+
+@pytest.mark.parametrize("T,heads", [(1100, 128), (30001, 9), (4200, 128), (70001, 8)])
+def test_rope_many_rows_sampled(dev, T, heads):
+    # launches that give each wave 2, 4 or 8 row groups (the cos / sin reuse
+    # across a token's heads, tokens changing inside a wave's rows, a ragged
+    # last workgroup); all heads of sampled tokens are compared
+    import mla_attention_kv_amd as mla
+
+    print(f"[norm] rope bf16 T={T} heads={heads} sampled", flush=True)
+    rng = np.random.default_rng(T + heads)
+    xt, x = to_dev(rng.standard_normal((T, heads, 64)).astype(np.float32), "bf16", dev)
+    pos = rng.integers(0, 1 << 20, T).astype(np.int32)
+    pt = torch.from_numpy(pos).to(dev)
+    y = mla.mla_rope(xt, pt, 1e4)
+    torch.cuda.synchronize()
+    tok = np.unique(np.concatenate([rng.choice(T, 48, replace=False), [0, 1, T - 2, T - 1]]))
+    ref = oracle.rope(x[tok], pos[tok], 1e4)
+    xs = x[tok]
+    mag = np.abs(xs) + np.abs(np.concatenate([xs[..., 32:], xs[..., :32]], axis=-1))
+    check(y[torch.from_numpy(tok).to(dev)], ref, "bf16", extra=1e-6 * mag,
+          label=f"rope T{T} h{heads}")
