@@ -26,6 +26,11 @@ the append), for comparison.
 RMSNorm over [T, 512] (the latent), RoPE over [T, heads, 64] (a rope key per
 head, the query-side shape).
 
+--op graph_buckets times the library's captured decode buckets
+(mla_prolog_graphs_*): one graph set per rotated input set, one
+mla_prolog_graphs_launch per step issued from the host (the serving-loop
+cost, launch included), against direct calls on the same sets.
+
 --op cache_append / cache_append_int8 times the paged KV-cache append
 instead (the step after "assemble"): the workload's T rows of
 compressed_kv and k_pe (seeded, model dtype) written into a cache by a slot
@@ -210,6 +215,39 @@ def time_graph(sets, steps, warmup, dev):
     torch.cuda.synchronize()
     del graphs
     return e0.elapsed_time(e1)
+
+
+class GraphBucketSets:
+    """The library's own captured decode buckets (mla_prolog_graphs_*): one
+    graph set per rotated input set, each with buckets 1, 2, 4, ... up to the
+    first power of two >= T, over static buffers filled with that set's
+    inputs.  A step is one mla_prolog_graphs_launch (one hipGraphLaunch)."""
+
+    def __init__(self, sets, T):
+        import mla_attention_kv_amd as mla
+
+        self.mla = mla
+        buckets = [1]
+        while buckets[-1] < T:
+            buckets.append(buckets[-1] * 2)
+        self.buckets = tuple(buckets)
+        self.graphs = []
+        w = sets.w
+        for t, _outs, _ws in sets.keep:
+            weights = ((t["Wa"], t["gamma"], t["Wb"]) if w.kind == "fp" else
+                       (t["Wqa"], t["swa"], t["gamma"], t["Wqb"], t["swb"]))
+            g = mla.PrologGraphs(weights, self.buckets, w.eps, w.theta, w8a8=w.kind != "fp")
+            g.hidden[:T] = t["X"]
+            g.positions[:T] = t["pos"]
+            self.graphs.append(g)
+        self.T = T
+        self.launch = mla.lib().mla_prolog_graphs_launch
+
+    def call(self, i, stream_ptr):
+        g = self.graphs[i % len(self.graphs)]
+        st = self.launch(g._handle, self.T, ctypes.c_void_p(stream_ptr), None)
+        if st != 0:
+            raise RuntimeError(f"library call failed: {self.mla.mla_status_string(st)}")
 
 
 def time_eager(sets, steps, warmup, dev):
@@ -483,7 +521,7 @@ def main():
     ap.add_argument("--path", type=int, default=-1, help="force kernel family 0/1 (A/B runs)")
     ap.add_argument("--op", default="prolog",
                     choices=["prolog", "prolog_cached", "prolog_then_append", "cache_append",
-                             "cache_append_int8", "rms_norm", "rope"],
+                             "cache_append_int8", "rms_norm", "rope", "graph_buckets"],
                     help="what one step is (default: the prolog)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -547,7 +585,15 @@ def main():
         del src, dst
 
     steps, warmup = args.steps, args.warmup
-    if args.eager:
+    graph_buckets = None
+    if args.op == "graph_buckets":
+        # the library's captured buckets, one graph launch per step from the
+        # host, against direct calls on the same rotated sets
+        graph_buckets = GraphBucketSets(sets, w.T)
+        torch.cuda.synchronize()
+        ms = time_eager(graph_buckets, steps, warmup, dev)
+        eager_ms = time_eager(sets, min(steps, 2000), min(warmup, 200), dev) * steps / min(steps, 2000)
+    elif args.eager:
         ms = time_eager(sets, steps, warmup, dev)
         eager_ms = ms
     else:
@@ -568,7 +614,8 @@ def main():
         roof = {"bound": "mfma", "achieved": alg_flops / step_s / 1e12,
                 "peak": MFMA_PEAK_TFLOPS[dt], "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = load_traffic(cfg["name"]) if cache_mode is None else None
+    roof["traffic"] = (load_traffic(cfg["name"])
+                       if cache_mode is None and graph_buckets is None else None)
     roof["kernel"] = ("one library call = every launch of the step: " +
                       ("dec_kv_a + dec_fin_kv_b (finish fused into kv_b_proj)"
                        if (path == 0 and w.kind == "fp" and w.T <= 64 and w.dims.nh * ((w.T + 15) // 16) <= 64)
@@ -598,11 +645,14 @@ def main():
         "vs_baseline": None,
         "dtype": {"fp": w.dtype, "w8a8": "i8"}[w.kind],
         "data": "synthetic (seeded; no public dataset exists for this path)",
-        "config": {"workload": cfg["name"] + ("" if cache_mode is None else "_" + args.op),
+        "config": {"workload": cfg["name"] + ("" if cache_mode is None and graph_buckets is None
+                                              else "_" + args.op),
                    "T": w.T, "H": d.H, "kv_lora_rank": d.r,
                    "rope_dim": d.dr, "heads": d.nh, "dn": d.dn, "dv": d.dv,
                    "kernel_family": ["decode", "prefill"][path],
-                   "timing": "eager calls" if args.eager else "HIP graph replays",
+                   "timing": ("one mla_prolog_graphs_launch per step (buckets "
+                              f"{list(graph_buckets.buckets)})" if graph_buckets is not None
+                              else "eager calls" if args.eager else "HIP graph replays"),
                    "rotated_sets": n_sets, "eager_us_per_step": eager_ms / steps * 1e3,
                    "algorithmic_bytes_per_step": alg_bytes,
                    "algorithmic_flops_per_step": alg_flops},

@@ -257,6 +257,100 @@ mla_status_t mla_rms_norm(const void* x, const void* gamma, int64_t rows, int64_
 mla_status_t mla_rope(const void* x, const int32_t* positions, int64_t T, int64_t heads,
                       int64_t dr, mla_dtype_t dt, float theta, void* y, void* stream);
 
+/*
+ * Captured decode buckets.  The migration guide captures the fused prolog
+ * into a graph (aclgraph) because at decode sizes launch overhead dominates
+ * ("Background", "Performance comparison"), warming up and capturing each
+ * q_len bucket with layer-0 weights before serving ("Migration notes").
+ * Here a set holds one HIP graph per bucket of token counts, each the
+ * launch sequence of one prolog call over fixed ("static") buffers; a step
+ * is one graph launch.
+ *
+ * The descriptor names every buffer of the recorded call, exactly as the
+ * plain entry points take them:
+ *   w8a8 == 0: mla_kv_prolog_cached (dt, W_kv_a, gamma, W_kv_b; s_kv_a,
+ *              s_kv_b, kv_cache_q, kv_scale unused, NULL);
+ *   w8a8 == 1: mla_kv_prolog_w8a8_cached (W_kv_a / W_kv_b are the int8
+ *              weights, s_kv_a / s_kv_b their scales; dt unused).
+ *   num_slots == 0 records the plain prolog (no cache write).
+ * Per-token buffers (hidden, positions, the four outputs, slot_mapping) hold
+ * rows for the largest bucket; workspace_bytes covers every bucket
+ * (the *_workspace_size query of each).  All buffers stay owned by the
+ * caller and must outlive the set (or its next update).
+ */
+typedef struct {
+    int32_t w8a8;
+    mla_dims_t d;
+    mla_dtype_t dt;
+    float eps, theta;
+    const void* W_kv_a;
+    const float* s_kv_a;
+    const void* gamma;
+    const void* W_kv_b;
+    const float* s_kv_b;
+    const void* hidden;
+    const int32_t* positions;
+    void* k_nope;
+    void* value;
+    void* k_pe;
+    void* compressed_kv;
+    const int64_t* slot_mapping;
+    void* kv_cache;
+    int8_t* kv_cache_q;
+    float* kv_scale;
+    int64_t num_slots;
+    void* workspace;
+    size_t workspace_bytes;
+} mla_prolog_graph_desc_t;
+
+typedef struct mla_prolog_graphs mla_prolog_graphs;
+
+/*
+ * Capture one graph per bucket (buckets: n_buckets ascending token counts,
+ * 1 <= n_buckets <= 64, each in [1, MLA_MAX_TOKENS]) on the current device
+ * and return the set in *out.  Every argument check of every recorded call
+ * runs first; on failure nothing is captured, *out is NULL and the status
+ * is that of the failing check.  Capture launches nothing: the kernels run
+ * only when a graph is launched.  Not to be called while the calling
+ * thread is capturing a stream of its own.
+ */
+mla_status_t mla_prolog_graphs_create(const mla_prolog_graph_desc_t* desc,
+                                      const int64_t* buckets, int32_t n_buckets,
+                                      mla_prolog_graphs** out);
+
+/*
+ * One prolog step over the first T rows of the static buffers: launches the
+ * graph of the smallest bucket >= T on `stream` (a stream of the set's
+ * device; NULL = the default stream) and stores that bucket in
+ * *bucket_used (if not NULL).  Rows [T, bucket) are computed too, from
+ * whatever the static buffers hold there: they must be finite (zeros, or an
+ * earlier step's rows), and with a cache their slot_mapping entries must lie
+ * outside [0, num_slots) (e.g. -1) so that padding writes no slot.  T == 0
+ * launches nothing; T above the largest bucket, or a stream of another
+ * device, is MLA_ERR_INVALID_ARG.  Asynchronous; steps share the static
+ * buffers and workspace, so they must be ordered (one stream).
+ */
+mla_status_t mla_prolog_graphs_launch(mla_prolog_graphs* g, int64_t T, void* stream,
+                                      int64_t* bucket_used);
+
+/* The bucket a step of T tokens runs (0 if T < 1 or above the largest). */
+int64_t mla_prolog_graphs_bucket(const mla_prolog_graphs* g, int64_t T);
+
+/*
+ * Rebind the set to new buffers (say the next layer's weights and cache, or
+ * new static buffers): the graphs are re-recorded from desc and updated in
+ * place.  w8a8, dims and (for w8a8 == 0) dt must equal the set's
+ * (MLA_ERR_INVALID_ARG otherwise); eps, theta and every pointer may change.
+ * Checks run first: on a failed check the set is unchanged.  On
+ * MLA_ERR_HIP the set may be partly updated and should be destroyed.  Not
+ * to be called while a launch of the set is in flight.
+ */
+mla_status_t mla_prolog_graphs_update(mla_prolog_graphs* g, const mla_prolog_graph_desc_t* desc);
+
+/* Free the set's graphs (NULL is a no-op).  The caller first synchronises
+ * with any launch of the set in flight. */
+void mla_prolog_graphs_destroy(mla_prolog_graphs* g);
+
 /* The kernel family the dispatcher picks for T tokens: 0 = decode
  * (weight-streaming, small T), 1 = prefill (MFMA-tiled, large T). */
 int mla_kv_prolog_selected_path(int64_t T, mla_dims_t d);

@@ -41,6 +41,11 @@ EXPORTS = (
     "mla_kv_prolog_w8a8_cached",
     "mla_rms_norm",
     "mla_rope",
+    "mla_prolog_graphs_create",
+    "mla_prolog_graphs_launch",
+    "mla_prolog_graphs_bucket",
+    "mla_prolog_graphs_update",
+    "mla_prolog_graphs_destroy",
     "mla_kv_prolog_selected_path",
     "mla_kv_prolog_force_path",
     "mla_status_string",
@@ -50,6 +55,20 @@ EXPORTS = (
 class mla_dims_t(ctypes.Structure):
     _fields_ = [("H", ctypes.c_int32), ("r", ctypes.c_int32), ("dr", ctypes.c_int32),
                 ("nh", ctypes.c_int32), ("dn", ctypes.c_int32), ("dv", ctypes.c_int32)]
+
+
+class mla_prolog_graph_desc_t(ctypes.Structure):
+    _fields_ = [("w8a8", ctypes.c_int32), ("d", mla_dims_t), ("dt", ctypes.c_int),
+                ("eps", ctypes.c_float), ("theta", ctypes.c_float),
+                ("W_kv_a", ctypes.c_void_p), ("s_kv_a", ctypes.c_void_p),
+                ("gamma", ctypes.c_void_p), ("W_kv_b", ctypes.c_void_p),
+                ("s_kv_b", ctypes.c_void_p), ("hidden", ctypes.c_void_p),
+                ("positions", ctypes.c_void_p), ("k_nope", ctypes.c_void_p),
+                ("value", ctypes.c_void_p), ("k_pe", ctypes.c_void_p),
+                ("compressed_kv", ctypes.c_void_p), ("slot_mapping", ctypes.c_void_p),
+                ("kv_cache", ctypes.c_void_p), ("kv_cache_q", ctypes.c_void_p),
+                ("kv_scale", ctypes.c_void_p), ("num_slots", ctypes.c_int64),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
 @dataclass(frozen=True)
@@ -111,6 +130,19 @@ def lib() -> ctypes.CDLL:
     L.mla_rms_norm.restype = i32
     L.mla_rope.argtypes = [vp, vp, i64, i64, i64, i32, f32, vp, vp]
     L.mla_rope.restype = i32
+    gp = ctypes.c_void_p
+    L.mla_prolog_graphs_create.argtypes = [ctypes.POINTER(mla_prolog_graph_desc_t),
+                                           ctypes.POINTER(ctypes.c_int64), ctypes.c_int32,
+                                           ctypes.POINTER(gp)]
+    L.mla_prolog_graphs_create.restype = i32
+    L.mla_prolog_graphs_launch.argtypes = [gp, i64, vp, ctypes.POINTER(ctypes.c_int64)]
+    L.mla_prolog_graphs_launch.restype = i32
+    L.mla_prolog_graphs_bucket.argtypes = [gp, i64]
+    L.mla_prolog_graphs_bucket.restype = i64
+    L.mla_prolog_graphs_update.argtypes = [gp, ctypes.POINTER(mla_prolog_graph_desc_t)]
+    L.mla_prolog_graphs_update.restype = i32
+    L.mla_prolog_graphs_destroy.argtypes = [gp]
+    L.mla_prolog_graphs_destroy.restype = None
     L.mla_kv_prolog_selected_path.argtypes = [i64, mla_dims_t]
     L.mla_kv_prolog_selected_path.restype = i32
     L.mla_kv_prolog_force_path.argtypes = [i32]
@@ -478,3 +510,151 @@ def mla_rope(x, positions, theta: float = 10000.0, *, out=None, stream=None):
     if st != MLA_OK:
         raise MlaError(st, "mla_rope")
     return out
+
+
+# ---------------------------------------------------------------------------
+# captured decode buckets
+# ---------------------------------------------------------------------------
+
+class PrologGraphs:
+    """A set of captured prolog graphs, one per token-count bucket, over
+    static buffers this object allocates (zero-filled; slot_mapping -1).
+
+    weights: fp16/bf16 (W_kv_a, gamma, W_kv_b) or, with w8a8=True,
+    (Wq_kv_a, s_kv_a, gamma, Wq_kv_b, s_kv_b).  cache: None, an fp cache
+    tensor ([..., r+dr], the model dtype), or for W8A8 a bfloat16 cache or a
+    (kv_cache_q int8, kv_scale float32) pair.  A step: write the first T rows
+    of .hidden / .positions (/ .slot_mapping), call run(T), read the first T
+    rows of .k_nope / .value / .k_pe / .compressed_kv.  Steps and the static
+    buffers belong to one device; keep them on one stream."""
+
+    def __init__(self, weights, buckets, eps: float = 1e-6, theta: float = 10000.0, *,
+                 w8a8: bool = False, cache=None, dn: int = 128, dv: int = 128,
+                 device=None):
+        torch = _torch()
+        self.buckets = tuple(int(b) for b in buckets)
+        if not self.buckets or list(self.buckets) != sorted(set(self.buckets)):
+            raise ValueError("buckets: ascending distinct token counts expected")
+        self.w8a8 = bool(w8a8)
+        self.device = weights[0].device if device is None else torch.device(device)
+        self._handle = ctypes.c_void_p(None)
+        self._bind(weights, eps, theta, cache, dn, dv, create=True)
+
+    def _bind(self, weights, eps, theta, cache, dn, dv, create):
+        torch = _torch()
+        dev = self.device
+        if self.w8a8:
+            Wqa, swa, gamma, Wqb, swb = weights
+            dtype, code = torch.bfloat16, MLA_BF16
+            H = Wqa.shape[0]
+            d = Dims(H=H, nh=Wqb.shape[1] // (dn + dv), r=gamma.shape[0],
+                     dr=Wqa.shape[1] - gamma.shape[0], dn=dn, dv=dv)
+            N1, N2 = d.r + d.dr, d.nh * (d.dn + d.dv)
+            _check(Wqa, "Wq_kv_a", torch.int8, (H, N1), dev)
+            _check(swa, "s_kv_a", torch.float32, (N1,), dev)
+            _check(gamma, "gamma", torch.bfloat16, (d.r,), dev)
+            _check(Wqb, "Wq_kv_b", torch.int8, (d.r, N2), dev)
+            _check(swb, "s_kv_b", torch.float32, (N2,), dev)
+            ptrs = (Wqa, swa, gamma, Wqb, swb)
+        else:
+            Wa, gamma, Wb = weights
+            dtype = Wa.dtype
+            code = {torch.float16: MLA_F16, torch.bfloat16: MLA_BF16}.get(dtype)
+            if code is None:
+                raise ValueError(f"W_kv_a: dtype {dtype}, expected float16 or bfloat16")
+            H = Wa.shape[0]
+            d = Dims(H=H, nh=Wb.shape[1] // (dn + dv), r=gamma.shape[0],
+                     dr=Wa.shape[1] - gamma.shape[0], dn=dn, dv=dv)
+            _check(Wa, "W_kv_a", dtype, (H, d.r + d.dr), dev)
+            _check(gamma, "gamma", dtype, (d.r,), dev)
+            _check(Wb, "W_kv_b", dtype, (d.r, d.nh * (d.dn + d.dv)), dev)
+            ptrs = (Wa, None, gamma, Wb, None)
+        if not create and (d != self.dims or dtype != self.dtype):
+            raise ValueError("update: dims and dtype must stay those of the set")
+        Tm = self.buckets[-1]
+        if create:
+            self.dims, self.dtype = d, dtype
+            self.hidden = torch.zeros((Tm, d.H), dtype=dtype, device=dev)
+            self.positions = torch.zeros(Tm, dtype=torch.int32, device=dev)
+            self.slot_mapping = torch.full((Tm,), -1, dtype=torch.int64, device=dev)
+            self.k_nope = torch.empty((Tm, d.nh, d.dn), dtype=dtype, device=dev)
+            self.value = torch.empty((Tm, d.nh, d.dv), dtype=dtype, device=dev)
+            self.k_pe = torch.empty((Tm, d.dr), dtype=dtype, device=dev)
+            self.compressed_kv = torch.empty((Tm, d.r), dtype=dtype, device=dev)
+            if self.w8a8:
+                nb = max(mla_kv_prolog_w8a8_workspace_size(b, d) for b in self.buckets)
+            else:
+                nb = max(mla_kv_prolog_workspace_size(b, d, code) for b in self.buckets)
+            if nb == 0:
+                raise MlaError(MLA_ERR_UNSUPPORTED, "workspace size")
+            self.workspace = torch.empty(nb, dtype=torch.uint8, device=dev)
+        W = d.r + d.dr
+        kv_cache = kv_cache_q = kv_scale = None
+        nslots = 0
+        if cache is not None:
+            if isinstance(cache, (tuple, list)):
+                if not self.w8a8:
+                    raise ValueError("an int8 cache needs w8a8=True")
+                kv_cache_q, kv_scale = cache
+                if kv_cache_q.dtype != torch.int8 or kv_cache_q.shape[-1] != W \
+                        or not kv_cache_q.is_contiguous() or kv_cache_q.device != dev:
+                    raise ValueError(f"kv_cache_q: contiguous int8 [..., {W}] on {dev} expected")
+                nslots = kv_cache_q.numel() // W
+                _check(kv_scale, "kv_scale", torch.float32, (nslots,), dev)
+            else:
+                kv_cache = cache
+                if kv_cache.dtype != dtype or kv_cache.shape[-1] != W \
+                        or not kv_cache.is_contiguous() or kv_cache.device != dev:
+                    raise ValueError(f"kv_cache: contiguous {dtype} [..., {W}] on {dev} expected")
+                nslots = kv_cache.numel() // W
+
+        def p(t):
+            return t.data_ptr() if t is not None else None
+
+        desc = mla_prolog_graph_desc_t(
+            1 if self.w8a8 else 0, d.c(), code, float(eps), float(theta),
+            p(ptrs[0]), p(ptrs[1]), p(ptrs[2]), p(ptrs[3]), p(ptrs[4]),
+            self.hidden.data_ptr(), self.positions.data_ptr(), self.k_nope.data_ptr(),
+            self.value.data_ptr(), self.k_pe.data_ptr(), self.compressed_kv.data_ptr(),
+            self.slot_mapping.data_ptr() if nslots else None, p(kv_cache), p(kv_cache_q),
+            p(kv_scale), nslots, self.workspace.data_ptr(), self.workspace.numel())
+        arr = (ctypes.c_int64 * len(self.buckets))(*self.buckets)
+        with torch.cuda.device(dev):
+            if create:
+                st = lib().mla_prolog_graphs_create(ctypes.byref(desc), arr, len(self.buckets),
+                                                    ctypes.byref(self._handle))
+            else:
+                st = lib().mla_prolog_graphs_update(self._handle, ctypes.byref(desc))
+        if st != MLA_OK:
+            raise MlaError(st, "mla_prolog_graphs_create" if create else "mla_prolog_graphs_update")
+        # keep the bound tensors alive as long as the graphs refer to them
+        self._bound = (weights, cache)
+
+    def update(self, weights, eps: float = 1e-6, theta: float = 10000.0, *, cache=None,
+               dn: int = 128, dv: int = 128):
+        """Rebind the graphs to other weights (say the next layer's) and
+        cache; the static buffers stay."""
+        self._bind(weights, eps, theta, cache, dn, dv, create=False)
+
+    def bucket(self, T: int) -> int:
+        return int(lib().mla_prolog_graphs_bucket(self._handle, int(T)))
+
+    def run(self, T: int, *, stream=None) -> int:
+        """One step over the first T rows; returns the bucket it ran."""
+        used = ctypes.c_int64(0)
+        st = lib().mla_prolog_graphs_launch(self._handle, int(T), _stream_ptr(self.device, stream),
+                                            ctypes.byref(used))
+        if st != MLA_OK:
+            raise MlaError(st, "mla_prolog_graphs_launch")
+        return int(used.value)
+
+    def close(self):
+        if self._handle:
+            lib().mla_prolog_graphs_destroy(self._handle)
+            self._handle = ctypes.c_void_p(None)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmlaprolog.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "prolog_tiled.hip", "prolog_decode.hip", "kv_cache.hip", "norm_rope.hip"]
+SOURCES = ["api.cpp", "graphs.cpp", "prolog_tiled.hip", "prolog_decode.hip", "kv_cache.hip",
+           "norm_rope.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

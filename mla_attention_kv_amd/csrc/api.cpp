@@ -13,6 +13,7 @@ using namespace mla;
 namespace {
 
 std::atomic<int> g_force_path{-1};
+thread_local int t_validate_only = 0;
 
 // Token counts up to this many take the decode tiling (small M tiles,
 // split-K over the hidden dimension so that the weight stream is spread
@@ -137,6 +138,12 @@ size_t ws_w8_max(int64_t T, const mla_dims_t& d) {
 
 }  // namespace
 
+namespace mla {
+bool validate_only() { return t_validate_only > 0; }
+ValidateOnlyScope::ValidateOnlyScope() { ++t_validate_only; }
+ValidateOnlyScope::~ValidateOnlyScope() { --t_validate_only; }
+}  // namespace mla
+
 extern "C" {
 
 size_t mla_kv_prolog_workspace_size(int64_t T, mla_dims_t d, mla_dtype_t dt) {
@@ -194,6 +201,7 @@ mla_status_t prolog_fp(const void* hidden, const void* W_kv_a, const void* gamma
     if (!aligned16(workspace)) return MLA_ERR_MISALIGNED;
     const Plan plan = make_plan(T, d.H, false, select_path(T));
     if (workspace_bytes < ws_fp(T, plan).total) return MLA_ERR_WORKSPACE;
+    if (validate_only()) return MLA_OK;
     hipError_t e = launch_fp((int)dt, hidden, W_kv_a, gamma, W_kv_b, positions, T, d.H, d.nh,
                              eps, rope_table(theta), k_nope, value, k_pe, compressed_kv,
                              workspace, plan, co, (hipStream_t)stream);
@@ -248,6 +256,7 @@ mla_status_t prolog_w8(const void* hidden_bf16, const int8_t* Wq_kv_a,
     if (!aligned16(workspace)) return MLA_ERR_MISALIGNED;
     const Plan plan = make_plan(T, d.H, true, select_path(T));
     if (workspace_bytes < ws_w8(T, d.H, plan).total) return MLA_ERR_WORKSPACE;
+    if (validate_only()) return MLA_OK;
     hipError_t e = launch_w8a8(hidden_bf16, Wq_kv_a, s_kv_a, gamma_bf16, Wq_kv_b, s_kv_b,
                                positions, T, d.H, d.nh, eps, rope_table(theta), k_nope, value, k_pe,
                                compressed_kv, dbg_acc1, dbg_acc2, dbg_row_begin, dbg_rows,

@@ -269,6 +269,15 @@ hipError_t launch_kv_cache_append(int dt, const void* ckv, const void* kpe, cons
                                   int64_t T, int64_t num_slots, void* cache, int8_t* cache_q,
                                   float* scale, hipStream_t st);
 
+// While a ValidateOnlyScope is alive on the calling thread, the prolog
+// entry points run every argument check and return without launching (the
+// captured-graph sets use it to reject bad arguments before capturing).
+bool validate_only();
+struct ValidateOnlyScope {
+    ValidateOnlyScope();
+    ~ValidateOnlyScope();
+};
+
 hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa,
                        const void* gamma, const int8_t* Wqb, const float* swb,
                        const int32_t* pos, int64_t T, int H, int nh, float eps,

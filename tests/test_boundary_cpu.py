@@ -289,3 +289,72 @@ def test_rms_norm_and_rope_argument_errors():
     assert rope(theta=0.0) == mla.MLA_ERR_INVALID_ARG
     assert rope(dr=128) == mla.MLA_ERR_UNSUPPORTED
     assert rope(T=0, p=(None, None, None)) == mla.MLA_OK
+
+
+def graph_desc(**kw):
+    d = dict(w8a8=0, d=V2.c(), dt=mla.MLA_F16, eps=1e-6, theta=1e4, W_kv_a=FAKE, s_kv_a=None,
+             gamma=FAKE, W_kv_b=FAKE, s_kv_b=None, hidden=FAKE, positions=FAKE, k_nope=FAKE,
+             value=FAKE, k_pe=FAKE, compressed_kv=FAKE, slot_mapping=None, kv_cache=None,
+             kv_cache_q=None, kv_scale=None, num_slots=0, workspace=FAKE,
+             workspace_bytes=1 << 40)
+    d.update(kw)
+    return mla.mla_prolog_graph_desc_t(**d)
+
+
+def create(desc, buckets):
+    out = ctypes.c_void_p(None)
+    arr = (ctypes.c_int64 * max(1, len(buckets)))(*buckets)
+    st = mla.lib().mla_prolog_graphs_create(ctypes.byref(desc) if desc is not None else None,
+                                            arr if buckets else None, len(buckets),
+                                            ctypes.byref(out))
+    return st, out.value
+
+
+def test_graph_set_argument_errors():
+    L = mla.lib()
+    bad = mla.MLA_ERR_INVALID_ARG
+    # bucket lists: empty, zero, unsorted, repeated, too many, above the limit
+    for b in ([], [0], [4, 2], [2, 2], list(range(1, 66)), [mla.MLA_MAX_TOKENS + 1]):
+        assert create(graph_desc(), b) == (bad, None), b
+    assert create(None, [1]) == (bad, None)
+    assert L.mla_prolog_graphs_create(ctypes.byref(graph_desc()),
+                                      (ctypes.c_int64 * 1)(1), 1, None) == bad
+    # every check of the recorded call, for every bucket, before any capture
+    assert create(graph_desc(hidden=None), [1, 64])[0] == bad
+    assert create(graph_desc(k_pe=FAKE + 8), [1])[0] == mla.MLA_ERR_MISALIGNED
+    assert create(graph_desc(dt=7), [1])[0] == bad
+    assert create(graph_desc(eps=float("nan")), [1])[0] == bad
+    assert create(graph_desc(d=Dims(H=2048, nh=16, r=256).c()), [1])[0] == \
+        mla.MLA_ERR_UNSUPPORTED
+    assert create(graph_desc(w8a8=2), [1])[0] == bad
+    # a workspace that fits the small bucket but not the large one
+    small = mla.mla_kv_prolog_workspace_size(1, V2)
+    assert small < mla.mla_kv_prolog_workspace_size(4096, V2)
+    assert create(graph_desc(workspace_bytes=small), [1, 4096])[0] == mla.MLA_ERR_WORKSPACE
+    assert create(graph_desc(workspace=None), [1])[0] == mla.MLA_ERR_WORKSPACE
+    # a cache needs its slot mapping; W8A8 needs its scales and H % 128 == 0
+    assert create(graph_desc(num_slots=8, kv_cache=FAKE), [1])[0] == bad
+    w8 = dict(w8a8=1, s_kv_a=FAKE, s_kv_b=FAKE)
+    assert create(graph_desc(**dict(w8, s_kv_b=None)), [1])[0] == bad
+    assert create(graph_desc(**dict(w8, d=Dims(H=64, nh=1).c())), [1])[0] == \
+        mla.MLA_ERR_UNSUPPORTED
+    # handles: NULL is rejected or ignored
+    used = ctypes.c_int64(5)
+    assert L.mla_prolog_graphs_launch(None, 1, None, ctypes.byref(used)) == bad
+    assert used.value == 0
+    assert L.mla_prolog_graphs_bucket(None, 1) == 0
+    assert L.mla_prolog_graphs_update(None, ctypes.byref(graph_desc())) == bad
+    L.mla_prolog_graphs_destroy(None)
+
+
+def test_graph_set_checks_pass_before_capture():
+    # with arguments that pass every check, create reaches the runtime: on a
+    # machine without a GPU that is MLA_ERR_HIP, and nothing is returned
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: capture would run")
+    st, h = create(graph_desc(), [1, 2, 64, 128])
+    assert st == mla.MLA_ERR_HIP and h is None
+    st, h = create(graph_desc(w8a8=1, s_kv_a=FAKE, s_kv_b=FAKE, d=R1.c()), [4])
+    assert st == mla.MLA_ERR_HIP and h is None
