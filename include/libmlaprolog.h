@@ -258,10 +258,10 @@ mla_status_t mla_rope(const void* x, const int32_t* positions, int64_t T, int64_
                       int64_t dr, mla_dtype_t dt, float theta, void* y, void* stream);
 
 /*
- * Captured decode buckets.  The migration guide captures the fused prolog
- * into a graph (aclgraph) because at decode sizes launch overhead dominates
- * ("Background", "Performance comparison"), warming up and capturing each
- * q_len bucket with layer-0 weights before serving ("Migration notes").
+ * Captured decode buckets.  The migration guide runs the fused prolog in
+ * graph mode (aclgraph) to cut scheduling overhead ("Background"), warming
+ * it up at q_len 1 and 2 with the first layer's weights before serving
+ * ("Command-line parameters", notes 2-3; "Migration notes", item 3).
  * Here a set holds one HIP graph per bucket of token counts, each the
  * launch sequence of one prolog call over fixed ("static") buffers; a step
  * is one graph launch.

@@ -1,10 +1,10 @@
 // Captured decode buckets: the prolog recorded once per token-count bucket
 // as a HIP graph over fixed buffers, then replayed with one graph launch per
 // step.  This is the MI355X counterpart of the migration guide's aclgraph
-// use (sections "Background" and "Performance comparison": at decode sizes
-// the launch overhead is what a graph removes; "Migration notes": each
-// q_len bucket is warmed up and captured with layer-0 weights before
-// serving).
+// use: graph mode on top of the fused kernel to cut scheduling overhead
+// (section "Background"), with the kernel warmed up at q_len 1 and 2 on the
+// first layer's weights before serving (section "Command-line parameters",
+// notes 2-3; "Migration notes", item 3).
 //
 // A set holds one instantiated graph per bucket.  Each graph is the exact
 // launch sequence the plain entry point issues for that many tokens, so a
