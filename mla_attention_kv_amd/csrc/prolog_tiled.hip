@@ -880,12 +880,13 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP),
 // in double; sine / cosine of the reduced angle and the rotation run in fp32
 // (rope_cos_sin).
 // ---------------------------------------------------------------------------
-template <int E>
+template <int E, int B>
 __global__ __launch_bounds__(256) void finish_a_fp_kernel(
     const float* __restrict__ P, int S, int64_t T, const uint16_t* __restrict__ gamma,
     const int32_t* __restrict__ pos, float eps, RopeTab rt, uint16_t* __restrict__ ckv,
     uint16_t* __restrict__ kpe, CacheOut co) {
-    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    // one token per wave; one to four waves per workgroup
+    const int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (t >= T) return;
     const int lane = threadIdx.x & 63;
     const int pt = pos[t];
@@ -893,18 +894,33 @@ __global__ __launch_bounds__(256) void finish_a_fp_kernel(
     const u4_t g = *(const u4_t*)(gamma + 8 * lane);
     float c[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float p = 0.f;
-#pragma unroll 2
-    for (int s = 0; s < S; ++s) {
-        const float* row = P + ((int64_t)s * T + t) * kN1;
-        // partials are read once: streaming (non-temporal) loads
-        const f4_t v0 = __builtin_nontemporal_load((const f4_t*)(row + 8 * lane));
-        const f4_t v1 = __builtin_nontemporal_load((const f4_t*)(row + 8 * lane + 4));
+    // the split-K partials, B splits' loads in flight at a time (B is the
+    // smallest power of two >= S, at most 8, so a batch re-reads nothing
+    // unless S is not a power of two: splits past S re-read split S - 1 and
+    // are not added); summed in ascending split order
+    for (int s0 = 0; s0 < S; s0 += B) {
+        f4_t v0[B], v1[B];
+        float pv[B];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            c[i] += v0[i];
-            c[4 + i] += v1[i];
+        for (int j = 0; j < B; ++j) {
+            const int s = s0 + j < S ? s0 + j : S - 1;
+            const float* row = P + ((int64_t)s * T + t) * kN1;
+            // partials are read once: streaming (non-temporal) loads
+            v0[j] = __builtin_nontemporal_load((const f4_t*)(row + 8 * lane));
+            v1[j] = __builtin_nontemporal_load((const f4_t*)(row + 8 * lane + 4));
+            pv[j] = __builtin_nontemporal_load(row + kR + lane);
         }
-        p += __builtin_nontemporal_load(row + kR + lane);
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            if (s0 + j < S) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    c[i] += v0[j][i];
+                    c[4 + i] += v1[j][i];
+                }
+                p += pv[j];
+            }
+        }
     }
     float ss = 0.f;
 #pragma unroll
@@ -1016,6 +1032,7 @@ __global__ __launch_bounds__(256) void quant_rows_long_kernel(const uint16_t* __
 //   inv_t = 1/sqrt(sum(c^2)/512 + eps);  compressed_kv = bf16(z * inv_t)
 //   k_pe = RoPE(p)
 // ---------------------------------------------------------------------------
+template <int B>
 __global__ __launch_bounds__(256) void finish_a_w8_kernel(
     const int32_t* __restrict__ P, int S, int64_t T, const float* __restrict__ sx,
     const float* __restrict__ swa, const uint16_t* __restrict__ gamma,
@@ -1035,18 +1052,31 @@ __global__ __launch_bounds__(256) void finish_a_w8_kernel(
     const u4_t gm = *(const u4_t*)(gamma + 8 * lane);
     int a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     int ap = 0;
-#pragma unroll 2
-    for (int s = 0; s < S; ++s) {
-        const int32_t* row = P + ((int64_t)s * T + t) * kN1;
-        // partials are read once: streaming (non-temporal) loads
-        const i4_t v0 = __builtin_nontemporal_load((const i4_t*)(row + 8 * lane));
-        const i4_t v1 = __builtin_nontemporal_load((const i4_t*)(row + 8 * lane + 4));
+    // the split-K partials, B splits' loads in flight at a time (B as in
+    // finish_a_fp_kernel; splits past S re-read split S - 1 and are not added)
+    for (int s0 = 0; s0 < S; s0 += B) {
+        i4_t v0[B], v1[B];
+        int pv[B];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            a[i] += v0[i];
-            a[4 + i] += v1[i];
+        for (int j = 0; j < B; ++j) {
+            const int s = s0 + j < S ? s0 + j : S - 1;
+            const int32_t* row = P + ((int64_t)s * T + t) * kN1;
+            // partials are read once: streaming (non-temporal) loads
+            v0[j] = __builtin_nontemporal_load((const i4_t*)(row + 8 * lane));
+            v1[j] = __builtin_nontemporal_load((const i4_t*)(row + 8 * lane + 4));
+            pv[j] = __builtin_nontemporal_load(row + kR + lane);
         }
-        ap += __builtin_nontemporal_load(row + kR + lane);
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            if (s0 + j < S) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    a[i] += v0[j][i];
+                    a[4 + i] += v1[j][i];
+                }
+                ap += pv[j];
+            }
+        }
     }
     if (dbg != nullptr && t >= dbg_begin && t < dbg_begin + dbg_rows) {
         int32_t* d = dbg + (t - dbg_begin) * kN1;
@@ -1192,15 +1222,25 @@ static void gemm2_dispatch(int bm, int bn, const void* A, int64_t lda, const voi
 void launch_finish_fp(int dt, const float* P, int S, int64_t T, const void* gamma,
                       const int32_t* pos, float eps, const RopeTab& rt, void* ckv, void* kpe,
                       const CacheOut& co, hipStream_t st) {
-    const dim3 grid((unsigned)((T + 3) / 4)), blk(256);  // four tokens per workgroup
-    if (dt == kF16)
-        hipLaunchKernelGGL(finish_a_fp_kernel<kF16>, grid, blk, 0, st, P, S, T,
-                           (const uint16_t*)gamma, pos, eps, rt, (uint16_t*)ckv, (uint16_t*)kpe,
-                           co);
-    else
-        hipLaunchKernelGGL(finish_a_fp_kernel<kBF16>, grid, blk, 0, st, P, S, T,
-                           (const uint16_t*)gamma, pos, eps, rt, (uint16_t*)ckv, (uint16_t*)kpe,
-                           co);
+    // four tokens per workgroup, or one when that leaves most CUs idle
+    const int tpw = T >= 2048 ? 4 : 1;
+    const dim3 grid((unsigned)((T + tpw - 1) / tpw)), blk(64 * tpw);
+    const int b = S <= 1 ? 1 : S <= 2 ? 2 : S <= 4 ? 4 : 8;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, blk, 0, st, P, S, T, (const uint16_t*)gamma, pos, eps, rt,
+                           (uint16_t*)ckv, (uint16_t*)kpe, co);
+    };
+    if (dt == kF16) {
+        if (b == 1) go(finish_a_fp_kernel<kF16, 1>);
+        else if (b == 2) go(finish_a_fp_kernel<kF16, 2>);
+        else if (b == 4) go(finish_a_fp_kernel<kF16, 4>);
+        else go(finish_a_fp_kernel<kF16, 8>);
+    } else {
+        if (b == 1) go(finish_a_fp_kernel<kBF16, 1>);
+        else if (b == 2) go(finish_a_fp_kernel<kBF16, 2>);
+        else if (b == 4) go(finish_a_fp_kernel<kBF16, 4>);
+        else go(finish_a_fp_kernel<kBF16, 8>);
+    }
 }
 
 template <int E>
@@ -1289,10 +1329,18 @@ hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa, const
     else
         gemm1_dispatch<kI8>(plan.bm1, QX, (int64_t)H, Wqa, T, H / 128, plan.s1,
                             EpiPartialI32{P1, T}, st);
-    hipLaunchKernelGGL(finish_a_w8_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, P1,
-                       plan.s1, T, sx,
-                       swa, (const uint16_t*)gamma, pos, eps, rt, QZ, sz, inv,
-                       (uint16_t*)ckv, (uint16_t*)k_pe, dbg1, dbg_begin, dbg_rows, co);
+    {
+        const int S = plan.s1;
+        auto go = [&](auto kern) {
+            hipLaunchKernelGGL(kern, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, P1, S, T,
+                               sx, swa, (const uint16_t*)gamma, pos, eps, rt, QZ, sz, inv,
+                               (uint16_t*)ckv, (uint16_t*)k_pe, dbg1, dbg_begin, dbg_rows, co);
+        };
+        if (S <= 1) go(finish_a_w8_kernel<1>);
+        else if (S <= 2) go(finish_a_w8_kernel<2>);
+        else if (S <= 4) go(finish_a_w8_kernel<4>);
+        else go(finish_a_w8_kernel<8>);
+    }
     const int N2 = nh * kHeadW;
     gemm2_dispatch<kI8>(plan.bm2, plan.bn2, QZ, (int64_t)kR, Wqb, T, N2,
                         EpiKvW8{(uint16_t*)k_nope, (uint16_t*)value, nh, sz, inv, swb, dbg2,
