@@ -342,8 +342,12 @@ int64_t mla_prolog_graphs_bucket(const mla_prolog_graphs* g, int64_t T);
  * place.  w8a8, dims and (for w8a8 == 0) dt must equal the set's
  * (MLA_ERR_INVALID_ARG otherwise); eps, theta and every pointer may change.
  * Checks run first: on a failed check the set is unchanged.  On
- * MLA_ERR_HIP the set may be partly updated and should be destroyed.  Not
- * to be called while a launch of the set is in flight.
+ * MLA_ERR_HIP the set may be partly updated and should be destroyed.  The
+ * caller first synchronises with any launch of the set in flight.
+ *
+ * Launch and bucket may be called from several host threads at once (their
+ * steps still share the static buffers); update and destroy must not run
+ * concurrently with any other call on the same set.
  */
 mla_status_t mla_prolog_graphs_update(mla_prolog_graphs* g, const mla_prolog_graph_desc_t* desc);
 

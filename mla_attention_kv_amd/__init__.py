@@ -13,6 +13,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import sys
 from dataclasses import dataclass
 from typing import Optional
 
@@ -654,6 +655,10 @@ class PrologGraphs:
             self._handle = ctypes.c_void_p(None)
 
     def __del__(self):
+        # at interpreter exit the runtime may already be torn down: leave the
+        # graphs to the process end then
+        if sys.is_finalizing():
+            return
         try:
             self.close()
         except Exception:
