@@ -108,7 +108,7 @@ def test_v2lite_fp16_token_counts(dev, T, path):
 
 
 @pytest.mark.parametrize("path", [0, 1])
-@pytest.mark.parametrize("T", [1, 7, 64, 130])
+@pytest.mark.parametrize("T", [1, 2, 7, 64, 130])
 def test_bf16_token_counts(dev, T, path):
     d = Dims(H=1024, nh=8)
     w = workloads.make_custom(d, T, dtype="bf16", seed=200 + T, wstd=0.03)
@@ -190,6 +190,18 @@ def test_odd_head_count_multi_tile(dev, T):
     d = Dims(H=256, nh=3)
     w = workloads.make_custom(d, T, dtype="f16", seed=410 + T, wstd=0.05)
     check_full(w, dev, f"nh3_T{T}", path=0)
+
+
+@pytest.mark.parametrize("nh", [1, 3, 64])
+@pytest.mark.parametrize("T", [1, 2])
+def test_tiny_T_head_counts(dev, T, nh):
+    # one or two tokens through the fused finish + kv_b_proj launch: with 1
+    # or 3 heads some workgroups of the rounded-up grid have no slab but
+    # still finish their token, with 64 heads the launch holds 256
+    # workgroups (the most it runs fused)
+    d = Dims(H=512, nh=nh)
+    w = workloads.make_custom(d, T, dtype="f16", seed=430 + 10 * nh + T, wstd=0.04)
+    check_full(w, dev, f"tiny_nh{nh}_T{T}", path=0)
 
 
 def test_r1_shapes_small_T(dev):
