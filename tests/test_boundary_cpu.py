@@ -358,3 +358,14 @@ def test_graph_set_checks_pass_before_capture():
     assert st == mla.MLA_ERR_HIP and h is None
     st, h = create(graph_desc(w8a8=1, s_kv_a=FAKE, s_kv_b=FAKE, d=R1.c()), [4])
     assert st == mla.MLA_ERR_HIP and h is None
+
+
+def test_python_graph_set_checks_buckets():
+    import torch
+
+    w = torch.zeros((2048, 576), dtype=torch.float16)
+    g = torch.zeros(512, dtype=torch.float16)
+    wb = torch.zeros((512, 4096), dtype=torch.float16)
+    for b in ((), (4, 2), (2, 2)):
+        with pytest.raises(ValueError):
+            mla.PrologGraphs((w, g, wb), b)
