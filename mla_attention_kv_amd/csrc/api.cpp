@@ -105,10 +105,16 @@ Plan make_plan(int64_t T, int H, bool int8, int path) {
     return p;
 }
 
-RopeTab rope_table(float theta) {
-    RopeTab rt;
-    for (int i = 0; i < kDR / 2; ++i)
-        rt.f[i] = std::pow((double)theta, -2.0 * (double)i / (double)kDR);
+// The RoPE frequencies theta^(-2i/dr) in double; kept per host thread for
+// the last theta seen, since a serving loop passes the same theta every call.
+const RopeTab& rope_table(float theta) {
+    thread_local float last = 0.f;  // 0 is never a valid theta
+    thread_local RopeTab rt;
+    if (theta != last) {
+        for (int i = 0; i < kDR / 2; ++i)
+            rt.f[i] = std::pow((double)theta, -2.0 * (double)i / (double)kDR);
+        last = theta;
+    }
     return rt;
 }
 

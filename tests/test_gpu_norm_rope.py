@@ -123,3 +123,28 @@ def test_rope_many_rows_sampled(dev, T, heads):
     mag = np.abs(xs) + np.abs(np.concatenate([xs[..., 32:], xs[..., :32]], axis=-1))
     check(y[torch.from_numpy(tok).to(dev)], ref, "bf16", extra=1e-6 * mag,
           label=f"rope T{T} h{heads}")
+
+
+def test_rope_alternating_theta(dev):
+    # calls with different bases in a row (the frequencies of the last base
+    # are kept per host thread and must be recomputed when it changes),
+    # through the standalone RoPE and the prolog's k_pe
+    import mla_attention_kv_amd as mla
+    import workloads
+    from parity import compare, gpu_rows, run_oracle, upload
+
+    rng = np.random.default_rng(77)
+    xt, x = to_dev(rng.standard_normal((40, 4, 64)).astype(np.float32), "bf16", dev)
+    pos = rng.integers(0, 1 << 20, 40).astype(np.int32)
+    pt = torch.from_numpy(pos).to(dev)
+    w = workloads.make_custom(workloads.V2LITE, 5, dtype="f16", seed=78)
+    t = upload(w, dev)
+    mag = np.abs(x) + np.abs(np.concatenate([x[..., 32:], x[..., :32]], axis=-1))
+    for theta in (1e4, 5e5, 1e4, 10.0, 5e5):
+        print(f"[norm] rope theta={theta}", flush=True)
+        y = mla.mla_rope(xt, pt, theta)
+        outs = mla.mla_kv_prolog(t["X"], t["Wa"], t["gamma"], t["Wb"], t["pos"], w.eps, theta)
+        torch.cuda.synchronize()
+        check(y, oracle.rope(x, pos, theta), "bf16", extra=1e-6 * mag, label=f"theta {theta}")
+        w.theta = theta
+        compare(gpu_rows(outs), run_oracle(w), f"prolog theta {theta}")
