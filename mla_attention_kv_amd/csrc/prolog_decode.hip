@@ -169,15 +169,17 @@ __device__ __forceinline__ int xcd_item(int nitems) {
 }
 
 // ---------------------------------------------------------------------------
-// kv_a_proj partial of (split s, slab) over K rows [s KW, s KW + KW) for all
-// T <= 16 NT tokens; item = 9 s + slab, so each XCD reads a contiguous
-// range of X's columns.  grid = 8 ceil(9 S / 8), 256 threads.
+// kv_a_proj partial of (split s, slab, token group tg) over K rows
+// [s KW, s KW + KW) for tokens [16 NT tg, 16 NT (tg + 1)) of T; item =
+// NG (9 s + slab) + tg, so each XCD reads a contiguous range of X's columns
+// and the token groups of one weight block share an XCD (and its L2).
+// grid = 8 ceil(9 S NG / 8), 256 threads; NG = ceil(T / (16 NT)).
 // ---------------------------------------------------------------------------
 template <int E, int NT, int KW>
 __global__ __launch_bounds__(256) void dec_kv_a_kernel(const uint16_t* __restrict__ X,
                                                        const uint16_t* __restrict__ Wa, int T,
                                                        int H, int S, float* __restrict__ P,
-                                                       uint16_t* __restrict__ ckv) {
+                                                       uint16_t* __restrict__ ckv, int NG) {
     __shared__ __align__(16) uint16_t ldsW[KW * kPitch];
     __shared__ __align__(16) uint16_t ldsA[NT * 16 * ARows<NT, KW>::kPitchA];
     // compressed_kv rows start out as the "not written yet" pattern that the
@@ -185,16 +187,19 @@ __global__ __launch_bounds__(256) void dec_kv_a_kernel(const uint16_t* __restric
     for (int row = blockIdx.x; row < T; row += gridDim.x)
         if (threadIdx.x < kR / 8)
             *(u4_t*)(ckv + (int64_t)row * kR + 8 * threadIdx.x) = u4_t{~0u, ~0u, ~0u, ~0u};
-    const int item = xcd_item(kSlabsA * S);
+    const int item = xcd_item(kSlabsA * S * NG);
     if (item < 0) return;
-    const int s = item / kSlabsA, slab = item % kSlabsA;
+    const int tg = item % NG, blk = item / NG;
+    const int s = blk / kSlabsA, slab = blk % kSlabsA;
     const int k0 = s * KW;
+    const int t0 = tg * 16 * NT;
+    const int nt = T - t0 < 16 * NT ? T - t0 : 16 * NT;  // >= 1
     u4_t v[KW / 32];
     u4_t a[ARows<NT, KW>::kPer];
     stage_load<KW / 32>(v, Wa, kN1, k0, H, slab * kSlabW);
-    arows_load<NT, KW>(a, X, H, T, k0, H);
+    arows_load<NT, KW>(a, X + (int64_t)t0 * H, H, nt, k0, H);
     stage_store<KW / 32>(v, ldsW, k0, H);
-    arows_store<NT, KW>(a, ldsA, T, k0, H);
+    arows_store<NT, KW>(a, ldsA, nt, k0, H);
     __syncthreads();
     f4_t acc[NT];
 #pragma unroll
@@ -208,7 +213,7 @@ __global__ __launch_bounds__(256) void dec_kv_a_kernel(const uint16_t* __restric
     for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int t = tt * 16 + 4 * g + i;
+            const int t = t0 + tt * 16 + 4 * g + i;
             if (t < T) Ps[(int64_t)t * kN1] = acc[tt][i];
         }
 }
@@ -514,12 +519,12 @@ static inline int grid8(int nitems) { return 8 * ((nitems + 7) / 8); }
 
 template <int E, int NA>
 static void dec_kv_a_launch(const void* X, const void* Wa, int T, int H, float* P, int kw, int S,
-                            uint16_t* ckv, hipStream_t st) {
-    const dim3 ga(grid8(kSlabsA * S)), blk(256);
+                            uint16_t* ckv, int ng, hipStream_t st) {
+    const dim3 ga(grid8(kSlabsA * S * ng)), blk(256);
     const uint16_t* x = (const uint16_t*)X;
     const uint16_t* wa = (const uint16_t*)Wa;
 #define MLA_KVA(KW) \
-    hipLaunchKernelGGL((dec_kv_a_kernel<E, NA, KW>), ga, blk, 0, st, x, wa, T, H, S, P, ckv)
+    hipLaunchKernelGGL((dec_kv_a_kernel<E, NA, KW>), ga, blk, 0, st, x, wa, T, H, S, P, ckv, ng)
     switch (kw) {
         case 64: MLA_KVA(64); break;
         case 128: MLA_KVA(128); break;
@@ -539,11 +544,14 @@ static void dec_launch_t(const void* X, const void* Wa, const void* gamma, const
     const int nitems = (N2 / kSlabW) * ntile;
     const bool fused = nitems <= kFusedItems;
     uint16_t* y = (uint16_t*)ckv;
-    switch (ntile) {
-        case 1: dec_kv_a_launch<E, 1>(X, Wa, T, H, P, plan.kw, plan.s1, y, st); break;
-        case 2: dec_kv_a_launch<E, 2>(X, Wa, T, H, P, plan.kw, plan.s1, y, st); break;
-        case 3: dec_kv_a_launch<E, 3>(X, Wa, T, H, P, plan.kw, plan.s1, y, st); break;
-        default: dec_kv_a_launch<E, 4>(X, Wa, T, H, P, plan.kw, plan.s1, y, st); break;
+    // fewer than 128 weight blocks: the token tiles go to two workgroups per
+    // block, so that more CUs share the weight and activation fetch
+    const int ng = (kSlabsA * plan.s1 < 128 && ntile >= 2) ? 2 : 1;
+    switch ((ntile + ng - 1) / ng) {
+        case 1: dec_kv_a_launch<E, 1>(X, Wa, T, H, P, plan.kw, plan.s1, y, ng, st); break;
+        case 2: dec_kv_a_launch<E, 2>(X, Wa, T, H, P, plan.kw, plan.s1, y, ng, st); break;
+        case 3: dec_kv_a_launch<E, 3>(X, Wa, T, H, P, plan.kw, plan.s1, y, ng, st); break;
+        default: dec_kv_a_launch<E, 4>(X, Wa, T, H, P, plan.kw, plan.s1, y, ng, st); break;
     }
     if (fused) {
         hipLaunchKernelGGL(dec_fin_kv_b_kernel<E>, dim3(grid8(nitems)), dim3(256), 0, st,
