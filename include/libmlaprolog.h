@@ -308,8 +308,8 @@ typedef struct mla_prolog_graphs mla_prolog_graphs;
 /*
  * Capture one graph per bucket (buckets: n_buckets ascending token counts,
  * 1 <= n_buckets <= 64, each in [1, MLA_MAX_TOKENS]) on the current device
- * and return the set in *out.  Every argument check of every recorded call
- * runs first; on failure nothing is captured, *out is NULL and the status
+ * and return the set in *out (every buffer of the descriptor must live on
+ * that device).  Every argument check of every recorded call runs first; on failure nothing is captured, *out is NULL and the status
  * is that of the failing check.  Capture launches nothing: the kernels run
  * only when a graph is launched.  Not to be called while the calling
  * thread is capturing a stream of its own.

@@ -212,11 +212,12 @@ mla_status_t mla_prolog_graphs_launch(mla_prolog_graphs* g, int64_t T, void* str
 
 void mla_prolog_graphs_destroy(mla_prolog_graphs* g) {
     if (g == nullptr) return;
+    const int device = g->device;  // g is gone after release
     int prev = -1;
     const bool ok = hipGetDevice(&prev) == hipSuccess;
-    if (ok && prev != g->device) (void)hipSetDevice(g->device);
+    if (ok && prev != device) (void)hipSetDevice(device);
     release(g);
-    if (ok && prev != g->device) (void)hipSetDevice(prev);
+    if (ok && prev != device) (void)hipSetDevice(prev);
 }
 
 }  // extern "C"
