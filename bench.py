@@ -245,7 +245,7 @@ class GraphBucketSets:
 
     def call(self, i, stream_ptr):
         g = self.graphs[i % len(self.graphs)]
-        st = self.launch(g._handle, self.T, ctypes.c_void_p(stream_ptr), None)
+        st = self.launch(g.handle, self.T, ctypes.c_void_p(stream_ptr), None)
         if st != 0:
             raise RuntimeError(f"library call failed: {self.mla.mla_status_string(st)}")
 

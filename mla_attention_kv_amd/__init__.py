@@ -637,6 +637,11 @@ class PrologGraphs:
         cache; the static buffers stay."""
         self._bind(weights, eps, theta, cache, dn, dv, create=False)
 
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        """The C handle (mla_prolog_graphs *), for direct library calls."""
+        return self._handle
+
     def bucket(self, T: int) -> int:
         return int(lib().mla_prolog_graphs_bucket(self._handle, int(T)))
 
