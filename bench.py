@@ -31,6 +31,9 @@ head, the query-side shape).
 mla_prolog_graphs_launch per step issued from the host (the serving-loop
 cost, launch included), against direct calls on the same sets.
 
+--op vendor_gemm times the vendor library's GEMM (torch.matmul) on the two
+projections' shapes, as a reference for the MFMA fractions (not the prolog).
+
 --op cache_append / cache_append_int8 times the paged KV-cache append
 instead (the step after "assemble"): the workload's T rows of
 compressed_kv and k_pe (seeded, model dtype) written into a cache by a slot
@@ -248,6 +251,46 @@ class GraphBucketSets:
         st = self.launch(g.handle, self.T, ctypes.c_void_p(stream_ptr), None)
         if st != 0:
             raise RuntimeError(f"library call failed: {self.mla.mla_status_string(st)}")
+
+
+def vendor_gemm_reference(dev, steps):
+    """The vendor library's GEMM (torch.matmul, i.e. hipBLASLt) on the
+    prolog's two projections at the workloads' shapes: a reference point for
+    the MFMA fractions, not part of the prolog.  Rotates over buffer sets,
+    times with events on the current stream."""
+    import torch
+
+    shapes = [("v2lite_prefill_kv_b", 4096, 512, 4096, torch.float16),
+              ("v2lite_prefill_kv_a", 4096, 2048, 576, torch.float16),
+              ("r1_T256_kv_b", 256, 512, 32768, torch.bfloat16),
+              ("r1_T256_kv_a", 256, 7168, 576, torch.bfloat16),
+              ("r1_T12874_kv_b_bf16", 12874, 512, 32768, torch.bfloat16),
+              ("r1_T12874_kv_a_bf16", 12874, 7168, 576, torch.bfloat16)]
+    out = []
+    for name, M, K, N, dt in shapes:
+        nsets = max(2, min(8, int(512e6 // ((M * K + K * N + M * N) * 2))))
+        A = [torch.randn(M, K, device=dev).to(dt) for _ in range(nsets)]
+        B = [(torch.randn(K, N, device=dev) * 0.02).to(dt) for _ in range(nsets)]
+        C = [torch.empty(M, N, device=dev, dtype=dt) for _ in range(nsets)]
+        reps = max(10, min(steps, int(2e5 // max(1, M * N * K // 10**7))))
+        for i in range(10):
+            torch.matmul(A[i % nsets], B[i % nsets], out=C[i % nsets])
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            torch.matmul(A[i % nsets], B[i % nsets], out=C[i % nsets])
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        tf = 2.0 * M * K * N / us / 1e6
+        log(f"{name}: {us:.2f} us, {tf:.0f} TFLOP/s")
+        out.append({"gemm": name, "M": M, "K": K, "N": N, "dtype": str(dt).split(".")[-1],
+                    "us": us, "tflops": tf, "frac_of_2.5PF": tf / 2500.0})
+        del A, B, C
+    print(json.dumps({"metric": "vendor GEMM (torch.matmul) on the prolog's projection shapes",
+                      "unit": "us", "higher_is_better": False, "results": out}), flush=True)
 
 
 def time_eager(sets, steps, warmup, dev):
@@ -521,7 +564,8 @@ def main():
     ap.add_argument("--path", type=int, default=-1, help="force kernel family 0/1 (A/B runs)")
     ap.add_argument("--op", default="prolog",
                     choices=["prolog", "prolog_cached", "prolog_then_append", "cache_append",
-                             "cache_append_int8", "rms_norm", "rope", "graph_buckets"],
+                             "cache_append_int8", "rms_norm", "rope", "graph_buckets",
+                             "vendor_gemm"],
                     help="what one step is (default: the prolog)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -548,6 +592,9 @@ def main():
         mla.mla_kv_prolog_force_path(args.path)
 
     cfg = workloads.CONFIGS[args.config]
+    if args.op == "vendor_gemm":
+        vendor_gemm_reference(dev, args.steps)
+        return
     if args.op in ("rms_norm", "rope"):
         w = workloads.make_config(args.config)
         if w.kind != "fp":  # the W8A8 workload's activations are bf16
