@@ -5,8 +5,9 @@
 // once from HBM and by the latency of doing so, so the kernels are shaped
 // around the weight stream:
 //   dec_kv_a       kv_a_proj: W_kv_a cut into 64-column slabs x K ranges of
-//                  KW rows, one workgroup each, writing split-K partial sums
-//                  P[s][t][576]
+//                  KW rows, one workgroup each (two, each with half the
+//                  token tiles, when the blocks alone would leave most of the
+//                  chip idle), writing split-K partial sums P[s][t][576]
 //   dec_fin_kv_b   the finish (sum of the partials, RMSNorm -> compressed_kv,
 //                  RoPE -> k_pe) fused into kv_b_proj: items of (16-token
 //                  tile, 64-column slab of W_kv_b over the full K = 512), one
