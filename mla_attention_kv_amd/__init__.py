@@ -15,7 +15,6 @@ import ctypes
 import os
 import sys
 from dataclasses import dataclass
-from typing import Optional
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmlaprolog.so")

@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 import workloads
-from workloads import R1, V2LITE, Dims
+from workloads import V2LITE, Dims
 
 pytestmark = pytest.mark.gpu
 
