@@ -576,7 +576,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: the KV prolog needs no communication and "
-              f"this build runs on a single MI355X (asked for --gpus {args.gpus}, "
+              f"one MI355X runs a whole batch (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE={world}).", file=sys.stderr)
         sys.exit(2)
 
