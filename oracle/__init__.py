@@ -4,9 +4,9 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The product library never does, and
 this package never imports the product library.
 
-The arithmetic lives in ``oracle.c`` (plain C, fp64, built by
-``oracle/build_oracle.py``); this module only converts numpy arrays to the
-pointer form that file takes.  What each step computes, and from which
+The arithmetic lives in ``oracle.c`` (plain C, fp32 with fp32
+accumulators in ascending order, built by ``oracle/build_oracle.py``); this
+module only converts numpy arrays to the pointer form that file takes.  What each step computes, and from which
 passage of the pages, is documented in ``oracle.c``.
 """
 from __future__ import annotations
@@ -17,7 +17,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# MLA_ORACLE_LIB names another build of oracle.c (the mutation tests load
+# deliberately broken copies through it); by default the in-tree build.
+LIB_PATH = os.environ.get("MLA_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 _lib = None
 
@@ -67,6 +69,17 @@ def _c(a, dt):
     return np.ascontiguousarray(a, dtype=dt)
 
 
+def _f32(a):
+    """float32 copy of an array whose values must be exactly representable
+    in float32 (model-dtype values); raises if converting would round."""
+    a64 = np.asarray(a)
+    out = np.ascontiguousarray(a64, dtype=np.float32)
+    if a64.dtype != np.float32 and a64.size and not np.array_equal(
+            out.astype(np.float64), np.asarray(a64, np.float64), equal_nan=True):
+        raise ValueError("oracle inputs must be exactly representable in float32")
+    return out
+
+
 def round_to_dtype(x, dtype: str) -> np.ndarray:
     """Round float64 values to the nearest fp16 / bf16 value (ties to even);
     returns float64 holding the rounded values."""
@@ -84,23 +97,25 @@ def num_threads(n: int = 0) -> int:
 
 def kv_prolog_fp(X, Wa, gamma, Wb, pos, *, r, dr, nh, dn, dv, eps, theta,
                  dtype: str, nthreads: int = 0, want_kv: bool = True):
-    """fp16/bf16 KV prolog in fp64.  Inputs are arrays of the stored values
-    (any float dtype; they are widened exactly to float64).  Returns a dict of
-    float64 arrays k_nope [T,nh,dn], value [T,nh,dv], k_pe [T,dr],
-    ckv [T,r], all before the final rounding to the output dtype."""
-    X = _c(X, np.float64)
+    """fp16/bf16 KV prolog in fp32.  Inputs are arrays of the stored values
+    (any float dtype holding fp16 / bf16 values; they are widened exactly to
+    float32).  Returns a dict of float32 arrays k_nope [T,nh,dn],
+    value [T,nh,dv], k_pe [T,dr], ckv [T,r], all before the final rounding
+    to the output dtype."""
+    X = _f32(X)
     T, H = X.shape
-    Wa = _c(Wa, np.float64)
-    gamma = _c(gamma, np.float64)
-    Wb = _c(Wb, np.float64)
+    Wa = _f32(Wa)
+    gamma = _f32(gamma)
+    Wb = _f32(Wb)
     pos = _c(pos, np.int32)
     assert Wa.shape == (H, r + dr) and gamma.shape == (r,)
     assert Wb.shape == (r, nh * (dn + dv)) and pos.shape == (T,)
+    f = np.float32
     out = {
-        "k_nope": np.empty((T, nh, dn)) if want_kv else None,
-        "value": np.empty((T, nh, dv)) if want_kv else None,
-        "k_pe": np.empty((T, dr)),
-        "ckv": np.empty((T, r)),
+        "k_nope": np.empty((T, nh, dn), f) if want_kv else None,
+        "value": np.empty((T, nh, dv), f) if want_kv else None,
+        "k_pe": np.empty((T, dr), f),
+        "ckv": np.empty((T, r), f),
     }
     rc = _load().oracle_kv_prolog_fp(
         T, H, r, dr, nh, dn, dv, _ptr(X), _ptr(Wa), _ptr(gamma), _ptr(Wb),
@@ -117,7 +132,8 @@ def kv_prolog_w8a8(X, Wqa, swa, gamma, Wqb, swb, pos, *, r, dr, nh, dn, dv,
                    want_acc: bool = True, want_codes: bool = False):
     """W8A8 KV prolog.  X and gamma hold bf16 values (widened exactly to
     float32 here); Wqa/Wqb int8 with float32 per-output-column scales.
-    Returns float64 references plus the exact int32 accumulators."""
+    Returns float32 references (before the final rounding to bf16) plus the
+    exact int32 accumulators."""
     X = _c(X, np.float32)
     T, H = X.shape
     N1 = r + dr
@@ -130,11 +146,12 @@ def kv_prolog_w8a8(X, Wqa, swa, gamma, Wqb, swb, pos, *, r, dr, nh, dn, dv,
     pos = _c(pos, np.int32)
     assert Wqa.shape == (H, N1) and swa.shape == (N1,) and gamma.shape == (r,)
     assert Wqb.shape == (r, N2) and swb.shape == (N2,) and pos.shape == (T,)
+    f = np.float32
     out = {
-        "k_nope": np.empty((T, nh, dn)) if want_kv else None,
-        "value": np.empty((T, nh, dv)) if want_kv else None,
-        "k_pe": np.empty((T, dr)),
-        "ckv": np.empty((T, r)),
+        "k_nope": np.empty((T, nh, dn), f) if want_kv else None,
+        "value": np.empty((T, nh, dv), f) if want_kv else None,
+        "k_pe": np.empty((T, dr), f),
+        "ckv": np.empty((T, r), f),
         "acc1": np.empty((T, N1), np.int32) if want_acc else None,
         "acc2": np.empty((T, N2), np.int32) if (want_acc and want_kv) else None,
         "qx": np.empty((T, H), np.int8) if want_codes else None,
@@ -188,10 +205,10 @@ def kv_cache_append_int8(ckv, kpe, slots, cache_q, scale):
 
 
 def rms_norm(x, gamma, eps: float) -> np.ndarray:
-    """Standalone RMSNorm over the last axis of ``x`` (fp64, before the final
-    rounding)."""
-    x = _c(x, np.float64)
-    gamma = _c(gamma, np.float64)
+    """Standalone RMSNorm over the last axis of ``x`` (fp32, before the final
+    rounding).  ``x`` and ``gamma`` hold model-dtype values."""
+    x = _f32(x)
+    gamma = _f32(gamma)
     n = x.shape[-1]
     rows = x.size // n if n else 0
     y = np.empty_like(x)
@@ -203,8 +220,9 @@ def rms_norm(x, gamma, eps: float) -> np.ndarray:
 
 def rope(x, pos, theta: float) -> np.ndarray:
     """Standalone rotate-half RoPE of ``x`` [T, dr] or [T, heads, dr], every
-    head of token t rotated by ``pos[t]`` (fp64, before the final rounding)."""
-    x = _c(x, np.float64)
+    head of token t rotated by ``pos[t]`` (fp32 rotation of fp32-rounded
+    cos / sin of a double angle, before the final rounding)."""
+    x = _f32(x)
     pos = _c(pos, np.int32)
     T, dr = x.shape[0], x.shape[-1]
     heads = x.shape[1] if x.ndim == 3 else 1

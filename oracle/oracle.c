@@ -20,11 +20,16 @@
  * quantisation formula, so the scheme implemented here is the plain
  * symmetric per-row / per-column int8 one described at each function.
  *
- * Precision: every floating-point step runs in IEEE double, in the plain
- * order of the definition (sums ascending over the contracted index), except
- * where a floating-point result decides an integer (the W8A8 quantisation
- * codes): those steps run in IEEE single precision, because that is the
- * precision the GPU kernels take the same decisions in.
+ * Precision: every arithmetic step runs in IEEE single precision (fp32),
+ * round to nearest even, in the plain order of the definition: each sum is
+ * one fp32 accumulator running over the contracted index in ascending order
+ * (products of two fp16 or two bf16 values are exact in fp32, so only the
+ * additions round).  The one exception is the RoPE angle: the frequency
+ * theta^(-2i/dr), the angle pos * f and its cosine / sine are evaluated in
+ * double and rounded to fp32 before the rotation, because an fp32 angle
+ * would be off by up to ~3e-3 rad at positions near 32768.  Built with
+ * -ffp-contract=off, so no multiply-add is fused.  The W8A8 quantisation
+ * decisions run in the same fp32 operations as the GPU kernels take them.
  *
  * Parity pins: every function here is pinned by the CPU tests against
  * closed forms, invariants, special cases and exact integer brute force
@@ -97,47 +102,50 @@ int oracle_round_to_dtype(const double* in, double* out, int64_t n, int dtype)
 
 /* Step 1, kv_a_proj: A[n] = sum_k x[k] * Wa[k, n], with Wa stored [H, N1]
  * row-major (the weight is handed over already transposed, as in the
- * "Source-level principle" section).  Sum ascending in k. */
-static void step_kv_a_proj(const double* x, const double* Wa, int64_t H,
-                           int64_t N1, double* A)
+ * "Source-level principle" section).  One fp32 accumulator per output,
+ * running over k in ascending order. */
+static void step_kv_a_proj(const float* x, const float* Wa, int64_t H,
+                           int64_t N1, float* A)
 {
-    for (int64_t n = 0; n < N1; ++n) A[n] = 0.0;
+    for (int64_t n = 0; n < N1; ++n) A[n] = 0.0f;
     for (int64_t k = 0; k < H; ++k) {
-        const double xk = x[k];
-        const double* w = Wa + k * N1;
+        const float xk = x[k];
+        const float* w = Wa + k * N1;
         for (int64_t n = 0; n < N1; ++n) A[n] += xk * w[n];
     }
 }
 
 /* Step 3, RMSNorm over the r latent columns (mean over r only, eps inside
  * the square root, gamma applied after the normalisation):
- *   y[j] = c[j] / sqrt(mean_j c[j]^2 + eps) * gamma[j]                     */
-static double rms_inv(const double* c, int64_t r, double eps)
+ *   y[j] = (c[j] * inv) * gamma[j],  inv = 1 / sqrt(sum_j c[j]^2 / r + eps)
+ * The sum of squares is one fp32 accumulator, ascending in j. */
+static float rms_inv(const float* c, int64_t r, float eps)
 {
-    double ss = 0.0;
+    float ss = 0.0f;
     for (int64_t j = 0; j < r; ++j) ss += c[j] * c[j];
-    return 1.0 / sqrt(ss / (double)r + eps);
+    return 1.0f / sqrtf(ss / (float)r + eps);
 }
 
-/* Step 4, kv_b_proj: B[m] = sum_j y[j] * Wb[j, m], Wb stored [r, N2]. */
-static void step_kv_b_proj(const double* y, const double* Wb, int64_t r,
-                           int64_t N2, double* B)
+/* Step 4, kv_b_proj: B[m] = sum_j y[j] * Wb[j, m], Wb stored [r, N2]; one
+ * fp32 accumulator per output, ascending in j. */
+static void step_kv_b_proj(const float* y, const float* Wb, int64_t r,
+                           int64_t N2, float* B)
 {
-    for (int64_t m = 0; m < N2; ++m) B[m] = 0.0;
+    for (int64_t m = 0; m < N2; ++m) B[m] = 0.0f;
     for (int64_t j = 0; j < r; ++j) {
-        const double yj = y[j];
-        const double* w = Wb + j * N2;
+        const float yj = y[j];
+        const float* w = Wb + j * N2;
         for (int64_t m = 0; m < N2; ++m) B[m] += yj * w[m];
     }
 }
 
 /* Step 5, reshape [N2] -> [nh, dn+dv] and split each head's row into its
  * first dn entries (k_nope) and its last dv entries (value). */
-static void step_split_heads(const double* B, int64_t nh, int64_t dn,
-                             int64_t dv, double* k_nope, double* value)
+static void step_split_heads(const float* B, int64_t nh, int64_t dn,
+                             int64_t dv, float* k_nope, float* value)
 {
     for (int64_t h = 0; h < nh; ++h) {
-        const double* row = B + h * (dn + dv);
+        const float* row = B + h * (dn + dv);
         for (int64_t d = 0; d < dn; ++d) k_nope[h * dn + d] = row[d];
         for (int64_t e = 0; e < dv; ++e) value[h * dv + e] = row[dn + e];
     }
@@ -148,16 +156,17 @@ static void step_split_heads(const double* B, int64_t nh, int64_t dn,
  *   out[i]        = p[i] cos a - p[i + dr/2] sin a
  *   out[i + dr/2] = p[i + dr/2] cos a + p[i] sin a
  * i.e. out = p * cos + rotate_half(p) * sin with rotate_half(p) =
- * (-p[dr/2:], p[:dr/2]). */
-static void step_rope(const double* p, int64_t dr, int64_t pos, double theta,
-                      double* out)
+ * (-p[dr/2:], p[:dr/2]).  f_i, a, cos a and sin a in double, rounded to
+ * fp32; the rotation itself in fp32. */
+static void step_rope(const float* p, int64_t dr, int64_t pos, double theta,
+                      float* out)
 {
     const int64_t half = dr / 2;
     for (int64_t i = 0; i < half; ++i) {
-        double f = pow(theta, -2.0 * (double)i / (double)dr);
-        double a = (double)pos * f;
-        double cs = cos(a), sn = sin(a);
-        double lo = p[i], hi = p[i + half];
+        const double f = pow(theta, -2.0 * (double)i / (double)dr);
+        const double a = (double)pos * f;
+        const float cs = (float)cos(a), sn = (float)sin(a);
+        const float lo = p[i], hi = p[i + half];
         out[i] = lo * cs - hi * sn;
         out[i + half] = hi * cs + lo * sn;
     }
@@ -169,20 +178,20 @@ static void step_rope(const double* p, int64_t dr, int64_t pos, double theta,
 
 /*
  * X [T,H], Wa [H, r+dr], gamma [r], Wb [r, nh*(dn+dv)]: the fp16/bf16
- * tensors widened (exactly) to double.  pos [T].  dtype selects the storage
+ * tensors widened (exactly) to float.  pos [T].  dtype selects the storage
  * format of the normalised latent that kv_b_proj consumes (it is the
  * compressed_kv output, materialised in the model's dtype).
  *
- * Outputs, all double and before the final rounding to the output dtype:
+ * Outputs, fp32 values before the final rounding to the output dtype:
  *   k_nope [T, nh, dn], value [T, nh, dv], k_pe [T, dr], ckv [T, r].
  * Any output pointer may be NULL to skip it (k_nope and value together).
  */
 int oracle_kv_prolog_fp(int64_t T, int64_t H, int64_t r, int64_t dr,
                         int64_t nh, int64_t dn, int64_t dv,
-                        const double* X, const double* Wa, const double* gamma,
-                        const double* Wb, const int32_t* pos, double eps,
-                        double theta, int dtype, double* k_nope, double* value,
-                        double* k_pe, double* ckv, int nthreads)
+                        const float* X, const float* Wa, const float* gamma,
+                        const float* Wb, const int32_t* pos, double eps,
+                        double theta, int dtype, float* k_nope, float* value,
+                        float* k_pe, float* ckv, int nthreads)
 {
     if (T < 0 || H <= 0 || r <= 0 || dr < 0 || (dr % 2) != 0 || nh <= 0 ||
         dn < 0 || dv < 0)
@@ -190,6 +199,7 @@ int oracle_kv_prolog_fp(int64_t T, int64_t H, int64_t r, int64_t dr,
     if (T > 0 && (!X || !Wa || !gamma || !Wb || !pos)) return ORACLE_BAD_ARG;
     if (dtype != 1 && dtype != 2) return ORACLE_BAD_ARG;
     const int64_t N1 = r + dr, N2 = nh * (dn + dv);
+    const float epsf = (float)eps;
     int bad = 0;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
@@ -198,9 +208,9 @@ int oracle_kv_prolog_fp(int64_t T, int64_t H, int64_t r, int64_t dr,
 #endif
 #pragma omp parallel
     {
-        double* A = (double*)malloc(sizeof(double) * (size_t)N1);
-        double* y = (double*)malloc(sizeof(double) * (size_t)r);
-        double* B = (double*)malloc(sizeof(double) * (size_t)(N2 > 0 ? N2 : 1));
+        float* A = (float*)malloc(sizeof(float) * (size_t)N1);
+        float* y = (float*)malloc(sizeof(float) * (size_t)r);
+        float* B = (float*)malloc(sizeof(float) * (size_t)(N2 > 0 ? N2 : 1));
         if (!A || !y || !B) {
 #pragma omp atomic write
             bad = 1;
@@ -210,15 +220,15 @@ int oracle_kv_prolog_fp(int64_t T, int64_t H, int64_t r, int64_t dr,
                 /* 1. kv_a_proj */
                 step_kv_a_proj(X + t * H, Wa, H, N1, A);
                 /* 2. split: c = A[0:r], p = A[r:r+dr] */
-                const double* c = A;
-                const double* p = A + r;
+                const float* c = A;
+                const float* p = A + r;
                 /* 3. RMSNorm */
-                double inv = rms_inv(c, r, eps);
-                for (int64_t j = 0; j < r; ++j) y[j] = c[j] * inv * gamma[j];
+                const float inv = rms_inv(c, r, epsf);
+                for (int64_t j = 0; j < r; ++j) y[j] = (c[j] * inv) * gamma[j];
                 if (ckv)
                     for (int64_t j = 0; j < r; ++j) ckv[t * r + j] = y[j];
                 /* kv_b_proj consumes the stored (dtype) latent */
-                for (int64_t j = 0; j < r; ++j) y[j] = round_dtype(y[j], dtype);
+                for (int64_t j = 0; j < r; ++j) y[j] = (float)round_dtype((double)y[j], dtype);
                 /* 4. kv_b_proj, 5. reshape + split */
                 if (k_nope && value && N2 > 0) {
                     step_kv_b_proj(y, Wb, r, N2, B);
@@ -282,9 +292,9 @@ static float quantize_row(const float* v, int64_t n, int8_t* q)
  *   a3q z[j]         = c[j] * gamma[j]                   (fp32)
  *       qz, sz       = quantize_row(z)
  *   a4  acc2[m]      = sum_j qz[j] * Wqb[j,m]            (exact integer)
- *   a3  inv_t        = 1 / sqrt(mean_j c[j]^2 + eps)     (double)
+ *   a3  inv_t        = 1 / sqrt(sum_j c[j]^2 / r + eps)  (fp32, ascending j)
  *       ckv[j]       = z[j] * inv_t
- *       B[m]         = acc2[m] * sz * inv_t * swb[m]
+ *       B[m]         = (((float)acc2[m] * sz) * inv_t) * swb[m]
  *   a5  split B into k_nope / value;  a6  RoPE on p.
  *
  * Quantising z = c*gamma and applying the per-token RMS factor after the
@@ -293,16 +303,17 @@ static float quantize_row(const float* v, int64_t n, int8_t* q)
  * the rounding of the scaled values), and keeps every integer-deciding step
  * free of reduction order.
  *
- * Optional exports (each may be NULL): acc1 [T, r+dr], acc2 [T, N2],
- * qx [T,H], sx [T], qz [T,r], sz [T].
+ * Outputs are fp32 values before the final rounding to bf16.  Optional
+ * exports (each may be NULL): acc1 [T, r+dr], acc2 [T, N2], qx [T,H], sx [T],
+ * qz [T,r], sz [T].
  */
 int oracle_kv_prolog_w8a8(int64_t T, int64_t H, int64_t r, int64_t dr,
                           int64_t nh, int64_t dn, int64_t dv, const float* X,
                           const int8_t* Wqa, const float* swa,
                           const float* gamma, const int8_t* Wqb,
                           const float* swb, const int32_t* pos, double eps,
-                          double theta, double* k_nope, double* value,
-                          double* k_pe, double* ckv, int32_t* acc1_out,
+                          double theta, float* k_nope, float* value,
+                          float* k_pe, float* ckv, int32_t* acc1_out,
                           int32_t* acc2_out, int8_t* qx_out, float* sx_out,
                           int8_t* qz_out, float* sz_out, int nthreads)
 {
@@ -312,6 +323,7 @@ int oracle_kv_prolog_w8a8(int64_t T, int64_t H, int64_t r, int64_t dr,
     if (T > 0 && (!X || !Wqa || !swa || !gamma || !Wqb || !swb || !pos))
         return ORACLE_BAD_ARG;
     const int64_t N1 = r + dr, N2 = nh * (dn + dv);
+    const float epsf = (float)eps;
     int bad = 0;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
@@ -326,16 +338,15 @@ int oracle_kv_prolog_w8a8(int64_t T, int64_t H, int64_t r, int64_t dr,
         float* z = (float*)malloc(sizeof(float) * (size_t)r);
         int8_t* qz = (int8_t*)malloc((size_t)r);
         int64_t* acc2 = (int64_t*)malloc(sizeof(int64_t) * (size_t)(N2 > 0 ? N2 : 1));
-        double* pd = (double*)malloc(sizeof(double) * (size_t)(dr > 0 ? dr : 1));
-        double* B = (double*)malloc(sizeof(double) * (size_t)(N2 > 0 ? N2 : 1));
-        if (!qx || !acc1 || !A || !z || !qz || !acc2 || !pd || !B) {
+        float* B = (float*)malloc(sizeof(float) * (size_t)(N2 > 0 ? N2 : 1));
+        if (!qx || !acc1 || !A || !z || !qz || !acc2 || !B) {
 #pragma omp atomic write
             bad = 1;
         } else {
 #pragma omp for schedule(dynamic, 1)
             for (int64_t t = 0; t < T; ++t) {
                 /* a0: per-token activation quantisation */
-                float sx = quantize_row(X + t * H, H, qx);
+                const float sx = quantize_row(X + t * H, H, qx);
                 /* a1: integer kv_a_proj, then dequantisation */
                 for (int64_t n = 0; n < N1; ++n) acc1[n] = 0;
                 for (int64_t k = 0; k < H; ++k) {
@@ -352,7 +363,7 @@ int oracle_kv_prolog_w8a8(int64_t T, int64_t H, int64_t r, int64_t dr,
                 const float* p = A + r;
                 /* a3q: quantise z = c * gamma per token */
                 for (int64_t j = 0; j < r; ++j) z[j] = c[j] * gamma[j];
-                float sz = quantize_row(z, r, qz);
+                const float sz = quantize_row(z, r, qz);
                 /* a4: integer kv_b_proj */
                 if (N2 > 0) {
                     for (int64_t m = 0; m < N2; ++m) acc2[m] = 0;
@@ -362,23 +373,18 @@ int oracle_kv_prolog_w8a8(int64_t T, int64_t H, int64_t r, int64_t dr,
                         for (int64_t m = 0; m < N2; ++m) acc2[m] += qj * (int64_t)w[m];
                     }
                 }
-                /* a3: RMS factor from c (double) */
-                double ss = 0.0;
-                for (int64_t j = 0; j < r; ++j) ss += (double)c[j] * (double)c[j];
-                double inv_t = 1.0 / sqrt(ss / (double)r + eps);
+                /* a3: the RMS factor of c */
+                const float inv_t = rms_inv(c, r, epsf);
                 if (ckv)
-                    for (int64_t j = 0; j < r; ++j) ckv[t * r + j] = (double)z[j] * inv_t;
+                    for (int64_t j = 0; j < r; ++j) ckv[t * r + j] = z[j] * inv_t;
                 if (k_nope && value && N2 > 0) {
                     for (int64_t m = 0; m < N2; ++m)
-                        B[m] = (double)acc2[m] * (double)sz * inv_t * (double)swb[m];
+                        B[m] = (((float)(int32_t)acc2[m] * sz) * inv_t) * swb[m];
                     step_split_heads(B, nh, dn, dv, k_nope + t * nh * dn,
                                      value + t * nh * dv);
                 }
                 /* a6: RoPE */
-                if (k_pe && dr > 0) {
-                    for (int64_t i = 0; i < dr; ++i) pd[i] = (double)p[i];
-                    step_rope(pd, dr, pos[t], theta, k_pe + t * dr);
-                }
+                if (k_pe && dr > 0) step_rope(p, dr, pos[t], theta, k_pe + t * dr);
                 /* optional exports */
                 if (acc1_out)
                     for (int64_t n = 0; n < N1; ++n) acc1_out[t * N1 + n] = (int32_t)acc1[n];
@@ -390,7 +396,7 @@ int oracle_kv_prolog_w8a8(int64_t T, int64_t H, int64_t r, int64_t dr,
                 if (sz_out) sz_out[t] = sz;
             }
         }
-        free(qx); free(acc1); free(A); free(z); free(qz); free(acc2); free(pd); free(B);
+        free(qx); free(acc1); free(A); free(z); free(qz); free(acc2); free(B);
     }
     return bad ? ORACLE_NOMEM : ORACLE_OK;
 }
@@ -466,26 +472,27 @@ int oracle_kv_cache_append_int8(int64_t T, int64_t r, int64_t dr, const float* c
  * The migration guide ships RMSNorm and RoPE as kernels of their own next to
  * the fused prolog (section "Directory layout"; a switch for each in its
  * usage section); what they compute is the prolog's step 3 and step 6 above,
- * applied row by row:
- *   rms_norm: x [rows, n] -> y[j] = x[j] / sqrt(mean_j x[j]^2 + eps) * gamma[j]
+ * applied row by row, in the same fp32 arithmetic:
+ *   rms_norm: x [rows, n] -> y[j] = (x[j] * inv) * gamma[j],
+ *             inv = 1 / sqrt(sum_j x[j]^2 / n + eps)
  *   rope:     x [T, heads, dr] -> every head row of token t rotated by pos[t]
- * Inputs are the model-dtype values widened (exactly) to double; outputs are
- * double, before the final rounding.
+ * Inputs are the model-dtype values widened (exactly) to float; outputs are
+ * fp32, before the final rounding.
  */
-int oracle_rms_norm(int64_t rows, int64_t n, const double* x, const double* gamma,
-                    double eps, double* y)
+int oracle_rms_norm(int64_t rows, int64_t n, const float* x, const float* gamma,
+                    double eps, float* y)
 {
     if (rows < 0 || n <= 0 || (rows > 0 && (!x || !gamma || !y))) return ORACLE_BAD_ARG;
     for (int64_t t = 0; t < rows; ++t) {
-        const double* xr = x + t * n;
-        const double inv = rms_inv(xr, n, eps);
-        for (int64_t j = 0; j < n; ++j) y[t * n + j] = xr[j] * inv * gamma[j];
+        const float* xr = x + t * n;
+        const float inv = rms_inv(xr, n, (float)eps);
+        for (int64_t j = 0; j < n; ++j) y[t * n + j] = (xr[j] * inv) * gamma[j];
     }
     return ORACLE_OK;
 }
 
-int oracle_rope(int64_t T, int64_t heads, int64_t dr, const double* x, const int32_t* pos,
-                double theta, double* y)
+int oracle_rope(int64_t T, int64_t heads, int64_t dr, const float* x, const int32_t* pos,
+                double theta, float* y)
 {
     if (T < 0 || heads <= 0 || dr <= 0 || (dr % 2) != 0 || (T > 0 && (!x || !pos || !y)))
         return ORACLE_BAD_ARG;

@@ -3,7 +3,7 @@ the library through its Python binding, run the CPU oracle on the same
 inputs, and compare element by element.
 
 Tolerance (fp16 / bf16 outputs): |gpu - ref| <= 1e-2 + 1e-2 * |ref|, with
-ref the oracle's fp64 value before the final rounding -- the rtol = atol =
+ref the oracle's fp32 value before the final rounding -- the rtol = atol =
 1e-2 bar of the migration guide's golden test ("Precision verification"
 section).  W8A8 int32 accumulators must match bit for bit.
 """
@@ -72,7 +72,7 @@ def run_lib(w: Workload, t, dbg_rows=None, **kw):
 
 
 def run_oracle(w: Workload, rows=None, nthreads: int = 0):
-    """Oracle outputs (fp64, before the final rounding) for all rows or the
+    """Oracle outputs (fp32, before the final rounding) for all rows or the
     given subset of token rows."""
     sub = w if rows is None else w.rows(rows)
     d = w.dims

@@ -2,7 +2,7 @@
 
 Tolerance: both kernels compute in fp32 and round once to the model dtype,
 so each value must lie within one unit in the last place of the dtype
-(2^-10 relative for fp16, 2^-7 for bf16) of the oracle's fp64 value, plus,
+(2^-10 relative for fp16, 2^-7 for bf16) of the oracle's fp32 value, plus,
 for RoPE, 1e-6 of the inputs' magnitude for the fp32 rotation (cos and sin
 to about 1e-7); this is tighter than the prolog's 1e-2 + 1e-2 |ref|, which
 is asserted as well.  In-place calls must give the same bits.
