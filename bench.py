@@ -3,8 +3,12 @@
 
 One step = one call of the whole prolog (kv_a_proj, split, RMSNorm,
 kv_b_proj, reshape/split, RoPE, assemble) over one batch of seeded synthetic
-input.  Default workload: DeepSeek-V2-Lite shapes, fp16 decode of 32
-sequences x 2 query tokens (T = 64).
+input.  The headline workload is the largest single-GPU one: the
+DeepSeek-R1-sized W8A8 packed prefill of 8 sequences (T = 12,874 for its
+seed).  The same JSON line carries the four other workloads (V2-Lite fp16
+decode at T = 1 and 64, V2-Lite fp16 prefill at T = 4096, R1 bf16 decode at
+T = 256) under "configs", each with its time per call and roofline
+fraction; --config N makes workload N the headline and measures it alone.
 
 Timing: inputs, weights, outputs and workspace are replicated over enough
 distinct buffers (>= 512 MB in total) that the 256 MB last-level cache
@@ -12,6 +16,11 @@ cannot serve a repeated call; successive steps rotate through them.  The K
 timed steps are launched as HIP graph replays (launch overhead removed, as
 a serving loop would) on one stream and bracketed by synchronisation and
 HIP events on that stream.  value = T * K / elapsed (tokens/s).
+
+The binding roof of a workload is the one its algorithmic arithmetic
+intensity (operations per algorithmic byte) puts it under: HBM below the
+ridge point (peak operations / 8 TB/s), MFMA above; both fractions are
+reported.
 
 Prints ONE JSON line on stdout.
 
@@ -312,25 +321,35 @@ def time_eager(sets, steps, warmup, dev):
 
 def cpu_baseline(w, seconds):
     """The CPU oracle, as it stands, on a bounded sample of the same
-    workload: whole batches (or a prefix of token rows) repeated until about
-    `seconds` have elapsed."""
+    workload: whole batches (or the first 256 token rows) repeated until
+    about `seconds` have elapsed.  The inputs are widened to the oracle's
+    fp32 form once, outside the timed loop."""
     import numpy as np
 
     import oracle
-    from tests.parity import run_oracle
+    from workloads import widen
 
     nthreads = oracle.num_threads(0)
-    rows = None
-    if w.T > 256:
-        rows = np.arange(256)
-    ntok = w.T if rows is None else len(rows)
+    rows = None if w.T <= 256 else np.arange(256)
+    sub = w if rows is None else w.rows(rows)
+    d = w.dims
+    kw = dict(r=d.r, dr=d.dr, nh=d.nh, dn=d.dn, dv=d.dv, eps=w.eps, theta=w.theta)
+    if w.kind == "fp":
+        args = (widen(sub.X, w.dtype), widen(w.Wa, w.dtype), widen(w.gamma, w.dtype),
+                widen(w.Wb, w.dtype), sub.positions)
+        f = lambda: oracle.kv_prolog_fp(*args, dtype=w.dtype, **kw)  # noqa: E731
+    else:
+        args = (widen(sub.X, "bf16"), w.Wqa, w.swa, widen(w.gamma, "bf16"), w.Wqb, w.swb,
+                sub.positions)
+        f = lambda: oracle.kv_prolog_w8a8(*args, want_acc=False, **kw)  # noqa: E731
+    ntok = sub.T
     t0 = time.perf_counter()
-    run_oracle(w, rows)
+    f()
     one = time.perf_counter() - t0
     reps = max(1, min(100000, int(seconds / max(one, 1e-6))))
     t0 = time.perf_counter()
     for _ in range(reps):
-        run_oracle(w, rows)
+        f()
     dt = time.perf_counter() - t0
     sample = (f"{reps} x {'all ' if rows is None else 'the first '}{ntok} token rows of the "
               f"same seeded workload ({dt:.1f} s)")
@@ -554,12 +573,133 @@ def main_cache(args, cfg, w, dev):
     print(json.dumps(out), flush=True)
 
 
+def roofline(w, step_s, alg_bytes, alg_flops):
+    """Roofline of one call: the binding roof is HBM when the algorithmic
+    arithmetic intensity is below the ridge point of the workload's MFMA
+    dtype, MFMA above it; both fractions are given."""
+    dt = "i8" if w.kind == "w8a8" else w.dtype
+    hbm = alg_bytes / step_s / 1e9
+    mfma = alg_flops / step_s / 1e12
+    ridge = MFMA_PEAK_TFLOPS[dt] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    ai = alg_flops / alg_bytes
+    if ai < ridge:
+        roof = {"bound": "hbm", "achieved": hbm, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": mfma, "peak": MFMA_PEAK_TFLOPS[dt],
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["hbm_frac"] = hbm / HBM_PEAK_GBS
+    roof["mfma_frac"] = mfma / MFMA_PEAK_TFLOPS[dt]
+    roof["mfma_dtype"] = dt
+    roof["arith_intensity"] = ai
+    roof["ridge"] = ridge
+    return roof
+
+
+def kernel_names(w, path, cache_mode):
+    fused_decode = path == 0 and w.kind == "fp" and w.T <= 64
+    if fused_decode:
+        k = "dec_kv_a + dec_fin_kv_b (finish fused into kv_b_proj)"
+    elif w.kind == "w8a8":
+        k = "kv_a_proj GEMM + finish + kv_b_proj GEMM (+ activation quantiser)"
+    else:
+        k = "kv_a_proj GEMM + finish + kv_b_proj GEMM"
+    k = "one library call = every launch of the step: " + k
+    k += {None: "", "fused": "; paged-cache write fused into the finish",
+          "separate": "; then kv_cache_append"}[cache_mode]
+    if cache_mode is not None and w.kind != "fp":
+        k += " (int8 cache)"
+    return k
+
+
+def measure_prolog(idx, steps, warmup, dev, args, cache_mode=None, graph_buckets=False):
+    """Time one workload's prolog over rotated input sets; returns a dict of
+    the measurements (the workload is returned too, for the CPU baseline)."""
+    import torch
+
+    import mla_attention_kv_amd as mla
+    import workloads
+
+    cfg = workloads.CONFIGS[idx]
+    log(f"generating workload {cfg['name']}")
+    w = workloads.make_config(idx)
+    d = w.dims
+    alg_bytes = workloads.algorithmic_bytes(d, w.T, w.kind, w.dtype)
+    if cache_mode is not None:
+        # each token's cache slot (int8 codes + scale for W8A8) and its slot index
+        alg_bytes += w.T * ((d.r + d.dr) * (2 if w.kind == "fp" else 1) +
+                            (0 if w.kind == "fp" else 4) + 8)
+    alg_flops = workloads.algorithmic_flops(d, w.T)
+    n_sets = max(1, math.ceil(ROTATE_BYTES / alg_bytes))
+    log(f"T={w.T} algorithmic bytes/step={alg_bytes} flops/step={alg_flops} sets={n_sets}")
+    sets = Sets(w, n_sets, dev, cache_mode)
+    torch.cuda.synchronize()
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    buckets = None
+    eager_steps = min(steps, 2000)
+    if graph_buckets:
+        # the library's captured buckets, one graph launch per step from the
+        # host, against direct calls on the same rotated sets
+        buckets = GraphBucketSets(sets, w.T)
+        torch.cuda.synchronize()
+        ms = time_eager(buckets, steps, warmup, dev)
+        eager_ms = time_eager(sets, eager_steps, min(warmup, 200), dev) * steps / eager_steps
+    elif args.eager:
+        ms = time_eager(sets, steps, warmup, dev)
+        eager_ms = ms
+    else:
+        ms = time_graph(sets, steps, warmup, dev)
+        eager_ms = time_eager(sets, eager_steps, min(warmup, 200), dev) * steps / eager_steps
+    ms_per_step = ms / steps
+    value = w.T * steps / (ms / 1e3)
+    log(f"{cfg['name']}: {ms_per_step * 1e3:.2f} us/step, {value:.4g} tokens/s "
+        f"(eager {eager_ms / steps * 1e3:.2f} us/step)")
+    path = mla.mla_kv_prolog_selected_path(w.T, sets.dims)
+    roof = roofline(w, ms_per_step / 1e3, alg_bytes, alg_flops)
+    traffic = (load_traffic(cfg["name"]) if cache_mode is None and buckets is None else None)
+    roof["traffic"] = traffic
+    roof["traffic_source"] = (f"profiles/traffic_{cfg['name']}.json (rocprofv3 FETCH_SIZE / "
+                              "WRITE_SIZE of the same kernel sources)" if traffic else None)
+    roof["kernel"] = kernel_names(w, path, cache_mode)
+    timing = ("one mla_prolog_graphs_launch per step (buckets "
+              f"{list(buckets.buckets)})" if buckets is not None
+              else "eager calls" if args.eager else "HIP graph replays")
+    res = {"workload": cfg["name"] + ("" if cache_mode is None and buckets is None
+                                      else "_" + args.op),
+           "T": w.T, "H": d.H, "kv_lora_rank": d.r, "rope_dim": d.dr, "heads": d.nh,
+           "dn": d.dn, "dv": d.dv, "dtype": {"fp": w.dtype, "w8a8": "i8"}[w.kind],
+           "kernel_family": ["decode", "prefill"][path], "timing": timing,
+           "rotated_sets": n_sets, "steps": steps, "us_per_step": ms_per_step * 1e3,
+           "tokens_per_s": value, "eager_us_per_step": eager_ms / steps * 1e3,
+           "algorithmic_bytes_per_step": alg_bytes, "algorithmic_flops_per_step": alg_flops,
+           "roofline": roof}
+    del sets, buckets
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res, w
+
+
+# time per call of the workloads that ride along with the headline, steps
+# sized to ~20-50 ms of GPU time each
+SIDE_STEPS = {0: 4000, 1: 3000, 2: 600, 3: 1000, 4: 100}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=7000)
-    ap.add_argument("--warmup", type=int, default=700)
-    ap.add_argument("--config", type=int, default=1, help="workload index (default 1)")
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=None,
+                    help="measure only workload N (default: the R1 W8A8 prefill as the "
+                         "headline, the other four under 'configs')")
     ap.add_argument("--eager", action="store_true", help="time direct calls, not graph replays")
     ap.add_argument("--path", type=int, default=-1, help="force kernel family 0/1 (A/B runs)")
     ap.add_argument("--op", default="prolog",
@@ -591,12 +731,13 @@ def main():
     if args.path in (0, 1):
         mla.mla_kv_prolog_force_path(args.path)
 
-    cfg = workloads.CONFIGS[args.config]
+    headline = 4 if args.config is None else args.config
+    cfg = workloads.CONFIGS[headline]
     if args.op == "vendor_gemm":
         vendor_gemm_reference(dev, args.steps)
         return
     if args.op in ("rms_norm", "rope"):
-        w = workloads.make_config(args.config)
+        w = workloads.make_config(headline)
         if w.kind != "fp":  # the W8A8 workload's activations are bf16
             w.dtype = "bf16"
         main_elem(args, cfg, w, dev)
@@ -605,73 +746,21 @@ def main():
         print(f"--op {args.op} needs an fp16 / bf16 workload", file=sys.stderr)
         sys.exit(2)
     if args.op.startswith("cache_append"):
-        w = workloads.make_config(args.config)
+        w = workloads.make_config(headline)
         main_cache(args, cfg, w, dev)
         return
-    log(f"generating workload {cfg['name']}")
-    w = workloads.make_config(args.config)
-    d = w.dims
-    alg_bytes = workloads.algorithmic_bytes(d, w.T, w.kind, w.dtype)
     cache_mode = {"prolog_cached": "fused", "prolog_then_append": "separate"}.get(args.op)
-    if cache_mode is not None:
-        # each token's cache slot (int8 codes + scale for W8A8) and its slot index
-        alg_bytes += w.T * ((d.r + d.dr) * (2 if w.kind == "fp" else 1) +
-                            (0 if w.kind == "fp" else 4) + 8)
-    alg_flops = workloads.algorithmic_flops(d, w.T)
-    n_sets = max(1, math.ceil(ROTATE_BYTES / alg_bytes))
-    log(f"T={w.T} algorithmic bytes/step={alg_bytes} flops/step={alg_flops} sets={n_sets}")
-    sets = Sets(w, n_sets, dev, cache_mode)
-    torch.cuda.synchronize()
-
-    if args.copy_calibration:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    steps, warmup = args.steps, args.warmup
-    graph_buckets = None
-    if args.op == "graph_buckets":
-        # the library's captured buckets, one graph launch per step from the
-        # host, against direct calls on the same rotated sets
-        graph_buckets = GraphBucketSets(sets, w.T)
-        torch.cuda.synchronize()
-        ms = time_eager(graph_buckets, steps, warmup, dev)
-        eager_ms = time_eager(sets, min(steps, 2000), min(warmup, 200), dev) * steps / min(steps, 2000)
-    elif args.eager:
-        ms = time_eager(sets, steps, warmup, dev)
-        eager_ms = ms
-    else:
-        ms = time_graph(sets, steps, warmup, dev)
-        eager_ms = time_eager(sets, min(steps, 2000), min(warmup, 200), dev) * steps / min(steps, 2000)
-    ms_per_step = ms / steps
-    value = w.T * steps / (ms / 1e3)
-    log(f"{ms_per_step * 1e3:.2f} us/step, {value:.4g} tokens/s "
-        f"(eager {eager_ms / steps * 1e3:.2f} us/step)")
-
-    path = mla.mla_kv_prolog_selected_path(w.T, sets.dims)
-    step_s = ms_per_step / 1e3
-    if path == 0 or w.kind == "fp" and alg_flops / alg_bytes < 312:
-        roof = {"bound": "hbm", "achieved": alg_bytes / step_s / 1e9, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s"}
-    else:
-        dt = "i8" if w.kind == "w8a8" else w.dtype
-        roof = {"bound": "mfma", "achieved": alg_flops / step_s / 1e12,
-                "peak": MFMA_PEAK_TFLOPS[dt], "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = (load_traffic(cfg["name"])
-                       if cache_mode is None and graph_buckets is None else None)
-    roof["kernel"] = ("one library call = every launch of the step: " +
-                      ("dec_kv_a + dec_fin_kv_b (finish fused into kv_b_proj)"
-                       if (path == 0 and w.kind == "fp" and w.T <= 64 and w.dims.nh * ((w.T + 15) // 16) <= 64)
-                       else "dec_kv_a + dec_finish + dec_kv_b" if (path == 0 and w.kind == "fp" and w.T <= 64)
-                       else "kv_a_proj GEMM + finish + kv_b_proj GEMM" +
-                       (" (+ activation quantiser)" if w.kind == "w8a8" else "")) +
-                      {None: "", "fused": "; paged-cache write fused into the finish",
-                       "separate": "; then kv_cache_append"}[cache_mode] +
-                      ("" if cache_mode is None or w.kind == "fp" else " (int8 cache)"))
+    res, w = measure_prolog(headline, args.steps, args.warmup, dev, args, cache_mode,
+                            graph_buckets=args.op == "graph_buckets")
+    side = {}
+    if args.config is None and args.op == "prolog":
+        for idx in (0, 1, 2, 3):
+            r, _ = measure_prolog(idx, SIDE_STEPS[idx], max(20, SIDE_STEPS[idx] // 10), dev,
+                                  args)
+            side[r["workload"]] = {k: r[k] for k in (
+                "T", "dtype", "kernel_family", "us_per_step", "tokens_per_s", "steps",
+                "rotated_sets", "algorithmic_bytes_per_step", "algorithmic_flops_per_step",
+                "roofline")}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -679,31 +768,27 @@ def main():
         cpu = cpu_baseline(w, args.cpu_seconds)
         log(f"oracle: {cpu['value']:.4g} tokens/s on {cpu['cores']} threads")
 
+    config = {k: res[k] for k in ("workload", "T", "H", "kv_lora_rank", "rope_dim", "heads",
+                                  "dn", "dv", "kernel_family", "timing", "rotated_sets",
+                                  "eager_us_per_step", "algorithmic_bytes_per_step",
+                                  "algorithmic_flops_per_step")}
+    if side:
+        config["configs"] = side
     out = {
         "metric": "MLA KV prolog tokens/s + % HBM (decode) / % MFMA (prefill) roofline",
-        "value": value,
+        "value": res["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": steps,
-        "warmup": warmup,
-        "ms_per_step": ms_per_step,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["us_per_step"] / 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"fp": w.dtype, "w8a8": "i8"}[w.kind],
+        "dtype": res["dtype"],
         "data": "synthetic (seeded; no public dataset exists for this path)",
-        "config": {"workload": cfg["name"] + ("" if cache_mode is None and graph_buckets is None
-                                              else "_" + args.op),
-                   "T": w.T, "H": d.H, "kv_lora_rank": d.r,
-                   "rope_dim": d.dr, "heads": d.nh, "dn": d.dn, "dv": d.dv,
-                   "kernel_family": ["decode", "prefill"][path],
-                   "timing": ("one mla_prolog_graphs_launch per step (buckets "
-                              f"{list(graph_buckets.buckets)})" if graph_buckets is not None
-                              else "eager calls" if args.eager else "HIP graph replays"),
-                   "rotated_sets": n_sets, "eager_us_per_step": eager_ms / steps * 1e3,
-                   "algorithmic_bytes_per_step": alg_bytes,
-                   "algorithmic_flops_per_step": alg_flops},
-        "roofline": roof,
+        "config": config,
+        "roofline": res["roofline"],
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -364,6 +364,25 @@ int mla_kv_prolog_selected_path(int64_t T, mla_dims_t d);
  * the previous setting.  Not for concurrent use. */
 int mla_kv_prolog_force_path(int path);
 
+/* Test hooks for the decode family's one-launch finish + kv_b_proj (taken
+ * when the device holds that launch's whole grid at once).  Its workgroups
+ * wait, with a bounded number of polls, for latent rows that other
+ * workgroups of the same launch finish; a workgroup that runs out of polls
+ * rebuilds the rows itself from the split-K partials of the previous launch
+ * (the same arithmetic in the same order, so the output bits do not change)
+ * and counts one fallback.
+ *
+ * mla_debug_set_handoff_spin sets the bound on the polls for later calls in
+ * this process (0: never wait, every workgroup rebuilds its rows; a
+ * negative value restores the default) and returns the previous setting
+ * (-1 for the default).  Not for concurrent use.
+ *
+ * mla_debug_handoff_fallbacks returns the current device's count of such
+ * fallbacks since the last reset (synchronises with the device; -1 on a HIP
+ * error) and clears it when reset != 0. */
+int64_t mla_debug_set_handoff_spin(int64_t limit);
+int64_t mla_debug_handoff_fallbacks(int reset);
+
 /* Static, human-readable name of a status code. */
 const char* mla_status_string(mla_status_t s);
 

@@ -41,6 +41,8 @@ EXPORTS = (
     "mla_kv_prolog_w8a8_cached",
     "mla_rms_norm",
     "mla_rope",
+    "mla_debug_set_handoff_spin",
+    "mla_debug_handoff_fallbacks",
     "mla_prolog_graphs_create",
     "mla_prolog_graphs_launch",
     "mla_prolog_graphs_bucket",
@@ -149,6 +151,10 @@ def lib() -> ctypes.CDLL:
     L.mla_kv_prolog_force_path.restype = i32
     L.mla_status_string.argtypes = [i32]
     L.mla_status_string.restype = ctypes.c_char_p
+    L.mla_debug_set_handoff_spin.argtypes = [i64]
+    L.mla_debug_set_handoff_spin.restype = i64
+    L.mla_debug_handoff_fallbacks.argtypes = [i32]
+    L.mla_debug_handoff_fallbacks.restype = i64
     _lib = L
     return L
 
@@ -171,6 +177,19 @@ def mla_kv_prolog_selected_path(T: int, dims: Dims) -> int:
 
 def mla_kv_prolog_force_path(path: int) -> int:
     return int(lib().mla_kv_prolog_force_path(int(path)))
+
+
+def mla_debug_set_handoff_spin(limit: int) -> int:
+    """Test hook: bound on the decode hand-off's polls (0: every workgroup
+    rebuilds its rows itself; negative: the default); returns the previous
+    setting."""
+    return int(lib().mla_debug_set_handoff_spin(int(limit)))
+
+
+def mla_debug_handoff_fallbacks(reset: bool = False) -> int:
+    """Test hook: the current device's count of decode hand-off fallbacks
+    since the last reset (synchronises; clears it when reset)."""
+    return int(lib().mla_debug_handoff_fallbacks(1 if reset else 0))
 
 
 # ---------------------------------------------------------------------------

@@ -170,6 +170,10 @@ int mla_kv_prolog_force_path(int path) {
     return g_force_path.exchange(path);
 }
 
+int64_t mla_debug_set_handoff_spin(int64_t limit) { return decode_set_spin_limit(limit); }
+
+int64_t mla_debug_handoff_fallbacks(int reset) { return decode_handoff_fallbacks(reset != 0); }
+
 const char* mla_status_string(mla_status_t s) {
     switch (s) {
         case MLA_OK: return "MLA_OK";

@@ -269,6 +269,13 @@ hipError_t launch_kv_cache_append(int dt, const void* ckv, const void* kpe, cons
                                   int64_t T, int64_t num_slots, void* cache, int8_t* cache_q,
                                   float* scale, hipStream_t st);
 
+// The decode family's finish + kv_b_proj hand-off: set the bound on its
+// polls (negative: the default; returns the previous setting), and read
+// (optionally clearing) the current device's count of workgroups that ran
+// out of polls and rebuilt their rows themselves (-1 on a HIP error).
+int64_t decode_set_spin_limit(int64_t limit);
+int64_t decode_handoff_fallbacks(bool reset);
+
 // While a ValidateOnlyScope is alive on the calling thread, the prolog
 // entry points run every argument check and return without launching (the
 // captured-graph sets use it to reject bad arguments before capturing).

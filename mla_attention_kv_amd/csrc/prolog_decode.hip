@@ -27,6 +27,8 @@
 // Steps as in the DeepSeek-V2-Lite-Chat MLA KV Prolog migration guide
 // (dpshk.com), sections "Background" and "Source-level principle"; RoPE in
 // the rotate-half x*cos + x_rot*sin form of its "Precision verification".
+#include <atomic>
+
 #include "mla_common.h"
 
 namespace mla {
@@ -285,15 +287,11 @@ __device__ __forceinline__ void fin_add(const FinPart& r, int S, f4_t& c0, f4_t&
     }
 }
 
-// Finish of token t given the wave's partials of its first 16 splits, gamma,
-// the position and the RoPE frequency in r.  After the partials are summed,
-// wave 0 normalises the latent and wave 1 rotates the rope part.
-template <int E, bool COH>
-__device__ __forceinline__ void finish_token_from(FinPart& r, const float* __restrict__ P, int S,
-                                                  int T, int t, float eps,
-                                                  uint16_t* __restrict__ ckv,
-                                                  uint16_t* __restrict__ kpe, const CacheOut& co,
-                                                  float* fred) {
+// The partial sums of token t, wave w holding splits w, w + 4, ... (the
+// first 16 already loaded in r): each wave adds its splits, then leaves its
+// sums in its fred row; ends with a barrier.
+__device__ __forceinline__ void fin_reduce(FinPart& r, const float* __restrict__ P, int S, int T,
+                                           int t, float* fred) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     f4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
     float p = 0.f;
@@ -307,22 +305,43 @@ __device__ __forceinline__ void finish_token_from(FinPart& r, const float* __res
     *(f4_t*)&fw[8 * lane + 4] = c1;
     fw[kR + lane] = p;
     __syncthreads();
+}
+
+// The normalised latent of the token whose four wave sums are in fred, for
+// lane l's columns 8l .. 8l + 7 (wave 0 calls it): the sums added in a fixed
+// order, then RMSNorm and gamma, rounded to E.
+template <int E>
+__device__ __forceinline__ u4_t fin_latent(const float* fred, const u4_t gm, float eps) {
+    const int lane = threadIdx.x & 63;
     const float* f0 = fred;
     const float* f1 = fred + kFredPitch;
     const float* f2 = fred + 2 * kFredPitch;
     const float* f3 = fred + 3 * kFredPitch;
+    float c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        c[i] = (f0[8 * lane + i] + f1[8 * lane + i]) + (f2[8 * lane + i] + f3[8 * lane + i]);
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += c[i] * c[i];
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)kR + eps);
+    return rms_scale8<E>(c, inv, gm);
+}
+
+// Finish of token t given the wave's partials of its first 16 splits, gamma,
+// the position and the RoPE frequency in r.  After the partials are summed,
+// wave 0 normalises the latent and wave 1 rotates the rope part.
+template <int E, bool COH>
+__device__ __forceinline__ void finish_token_from(FinPart& r, const float* __restrict__ P, int S,
+                                                  int T, int t, float eps,
+                                                  uint16_t* __restrict__ ckv,
+                                                  uint16_t* __restrict__ kpe, const CacheOut& co,
+                                                  float* fred) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    fin_reduce(r, P, S, T, t, fred);
     if (wave == 0) {
-        const u4_t gm = r.gm;
-        float c[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            c[i] = (f0[8 * lane + i] + f1[8 * lane + i]) + (f2[8 * lane + i] + f3[8 * lane + i]);
-        float ss = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ss += c[i] * c[i];
-        ss = wave_sum(ss);
-        const float inv = 1.0f / sqrtf(ss / (float)kR + eps);
-        const u4_t o = rms_scale8<E>(c, inv, gm);
+        const u4_t o = fin_latent<E>(fred, r.gm, eps);
         uint16_t* dst = ckv + (int64_t)t * kR + 8 * lane;
         if constexpr (COH) {
             store_coherent64(dst, (uint64_t)o[0] | ((uint64_t)o[1] << 32));
@@ -333,6 +352,10 @@ __device__ __forceinline__ void finish_token_from(FinPart& r, const float* __res
         if (cache_slot_ok(co, r.slot))  // the paged cache: [latent | rope key] in the slot
             __builtin_nontemporal_store(o, (u4_t*)(co.cache + r.slot * (kR + kDR) + 8 * lane));
     } else if (wave == 1) {
+        const float* f0 = fred;
+        const float* f1 = fred + kFredPitch;
+        const float* f2 = fred + 2 * kFredPitch;
+        const float* f3 = fred + 3 * kFredPitch;
         float cs, sn;
         rope_cos_sin(r.pos, r.freq, cs, sn);
         const float q = (f0[kR + lane] + f1[kR + lane]) + (f2[kR + lane] + f3[kR + lane]);
@@ -415,21 +438,26 @@ __global__ __launch_bounds__(256) void dec_kv_b_kernel(const uint16_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Finish and kv_b_proj in one launch, for at most kFusedItems 16-token items
-// (all resident at once, one per CU).  Every workgroup first issues the loads
-// of its W_kv_b slab; workgroup b then finishes tokens b, b + G, ... (G =
-// grid size), writing each compressed_kv row with device-coherent 8-byte
-// stores.  The kv_a launch before it filled those rows with all-ones
-// halves, a NaN pattern that the finish of finite inputs never produces, so
-// a row chunk is known to be final once it holds no all-ones half (8-byte
-// coherent stores and loads are single-copy atomic).  Each workgroup stages
-// its slab, then reads its tile's rows with coherent loads, re-reading the
-// chunks that still hold the pattern, and runs the slab product.  No
-// workgroup waits before its own finish work is done, so every wait is on
-// work that is already running or done; the spin is bounded.
+// Finish and kv_b_proj in one launch, for grids that fit on the device at
+// once (the host checks the CU count and this kernel's occupancy).  Every
+// workgroup first issues the loads of its W_kv_b slab; workgroup b then
+// finishes tokens b, b + G, ... (G = grid size), writing each compressed_kv
+// row with device-coherent 8-byte stores.  The kv_a launch before it filled
+// those rows with all-ones halves, a NaN pattern that the finish of finite
+// inputs never produces, so a row chunk is known to be final once it holds
+// no all-ones half (8-byte coherent stores and loads are single-copy
+// atomic).  Each workgroup stages its slab, then reads its tile's rows with
+// coherent loads, re-reading the chunks that still hold the pattern.
+//
+// The wait is bounded by spin_limit polls.  If a row is still missing then
+// (its producer was not resident, say, because other work held CUs), the
+// workgroup rebuilds every row of its tile itself from the split-K partials
+// P, which the previous launch completed, with the producer's own arithmetic
+// in the producer's order: the result is the same bits, only later.  Each
+// such fallback adds one to g_handoff_fallbacks (a count the host can read).
 // ---------------------------------------------------------------------------
-constexpr int kFusedItems = 256;
-constexpr uint32_t kSpinLimit = 1u << 20;
+constexpr uint32_t kSpinDefault = 256;
+__device__ unsigned int g_handoff_fallbacks = 0;
 
 __device__ __forceinline__ bool has_unset_half(uint64_t x) {
     return ((x & 0xFFFFull) == 0xFFFFull) || (((x >> 16) & 0xFFFFull) == 0xFFFFull) ||
@@ -441,11 +469,11 @@ __global__ __launch_bounds__(256) void dec_fin_kv_b_kernel(
     const float* __restrict__ P, int S, int T, const uint16_t* __restrict__ gamma,
     const int32_t* __restrict__ pos, float eps, RopeTab rt, const uint16_t* __restrict__ Wb,
     int N2, uint16_t* ckv, uint16_t* __restrict__ kpe, uint16_t* __restrict__ k_nope,
-    uint16_t* __restrict__ value, CacheOut co) {
+    uint16_t* __restrict__ value, CacheOut co, uint32_t spin_limit) {
     constexpr int AP = ARows<1, kR>::kPitchA;
     __shared__ __align__(16) uint16_t ldsW[kR * kPitch];
-    __shared__ __align__(16) uint16_t ldsA[16 * AP];  // also the finish's reduction buffer
-    static_assert(sizeof(ldsA) >= 4 * kFredPitch * sizeof(float), "reduction buffer fits");
+    __shared__ __align__(16) uint16_t ldsA[16 * AP];
+    __shared__ __align__(16) float fred[4 * kFredPitch];  // the finish's reduction buffer
     const int nh = N2 / kHeadW;
     const int ntile = (T + 15) / 16;
     const int item = xcd_item((N2 / kSlabW) * ntile);
@@ -460,13 +488,13 @@ __global__ __launch_bounds__(256) void dec_fin_kv_b_kernel(
         fin_load(r, P, S, T, t1, threadIdx.x >> 6);
         fin_load_aux(r, gamma, pos, rt, co, t1);
         stage_load<kR / 32, false>(v, Wb, N2, 0, kR, n0);
-        finish_token_from<E, true>(r, P, S, T, t1, eps, ckv, kpe, co, (float*)ldsA);
+        finish_token_from<E, true>(r, P, S, T, t1, eps, ckv, kpe, co, fred);
     } else {
         stage_load<kR / 32, false>(v, Wb, N2, 0, kR, n0);
     }
     for (int t = t1 + (int)gridDim.x; t < T; t += gridDim.x) {
         __syncthreads();  // the reduction buffer is free again
-        finish_token<E, true>(P, S, T, t, gamma, pos, eps, rt, ckv, kpe, co, (float*)ldsA);
+        finish_token<E, true>(P, S, T, t, gamma, pos, eps, rt, ckv, kpe, co, fred);
     }
     if (item < 0) return;
     const int slab = item / ntile, t0 = (item % ntile) * 16;
@@ -481,7 +509,7 @@ __global__ __launch_bounds__(256) void dec_fin_kv_b_kernel(
         y[u] = 0ull;
         if (row < nrows) pend |= 1u << u;
     }
-    for (uint32_t it = 0; pend != 0u && it < kSpinLimit; ++it) {
+    for (uint32_t it = 0; pend != 0u && it < spin_limit; ++it) {
         if (it != 0) __builtin_amdgcn_s_sleep(1);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -492,11 +520,23 @@ __global__ __launch_bounds__(256) void dec_fin_kv_b_kernel(
         for (int u = 0; u < 8; ++u)
             if ((pend & (1u << u)) && !has_unset_half(y[u])) pend &= ~(1u << u);
     }
-    __syncthreads();  // every wave is past the finish's use of ldsA
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
         const int q = threadIdx.x + 256 * u, row = q >> 7, col = (q & 127) * 4;
         *(uint64_t*)(ldsA + row * AP + col) = y[u];
+    }
+    if (__syncthreads_or(pend != 0u)) {
+        // the hand-off ran out of polls: rebuild the tile's rows from P
+        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        if (threadIdx.x == 0) atomicAdd(&g_handoff_fallbacks, 1u);
+        const u4_t gm = *(const u4_t*)(gamma + 8 * lane);
+        for (int row = 0; row < nrows; ++row) {
+            FinPart r;
+            fin_load(r, P, S, T, t0 + row, wave);
+            fin_reduce(r, P, S, T, t0 + row, fred);
+            if (wave == 0) *(u4_t*)(ldsA + row * AP + 8 * lane) = fin_latent<E>(fred, gm, eps);
+            __syncthreads();  // fred is reused by the next row
+        }
     }
     __syncthreads();
     f4_t acc[1] = {f4_t{0.f, 0.f, 0.f, 0.f}};
@@ -535,6 +575,28 @@ static void dec_kv_a_launch(const void* X, const void* Wa, int T, int H, float* 
 #undef MLA_KVA
 }
 
+// How many dec_fin_kv_b workgroups the current device holds at once (CU
+// count times this kernel's occupancy per CU), cached per device and dtype.
+static std::atomic<int> g_fused_cap[2][64];
+static std::atomic<int64_t> g_spin_limit{-1};
+
+template <int E>
+static int fused_capacity() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    std::atomic<int>& slot = g_fused_cap[E == kF16 ? 0 : 1][dev];
+    int cap = slot.load(std::memory_order_relaxed);
+    if (cap > 0) return cap;
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, dec_fin_kv_b_kernel<E>, 256, 0) !=
+            hipSuccess)
+        return 0;
+    cap = cus * per;
+    slot.store(cap, std::memory_order_relaxed);
+    return cap;
+}
+
 template <int E>
 static void dec_launch_t(const void* X, const void* Wa, const void* gamma, const void* Wb,
                          const int32_t* pos, int T, int H, int nh, float eps, const RopeTab& rt,
@@ -543,7 +605,9 @@ static void dec_launch_t(const void* X, const void* Wa, const void* gamma, const
     const int ntile = (T + 15) / 16;
     const int N2 = nh * kHeadW;
     const int nitems = (N2 / kSlabW) * ntile;
-    const bool fused = nitems <= kFusedItems;
+    // one launch for finish + kv_b_proj only when its whole grid is resident
+    // at once; otherwise the finish and kv_b_proj run as two launches
+    const bool fused = grid8(nitems) <= fused_capacity<E>();
     uint16_t* y = (uint16_t*)ckv;
     // fewer than 128 weight blocks: the token tiles go to two workgroups per
     // block, so that more CUs share the weight and activation fetch
@@ -555,10 +619,12 @@ static void dec_launch_t(const void* X, const void* Wa, const void* gamma, const
         default: dec_kv_a_launch<E, 4>(X, Wa, T, H, P, plan.kw, plan.s1, y, ng, st); break;
     }
     if (fused) {
+        const int64_t sl = g_spin_limit.load(std::memory_order_relaxed);
+        const uint32_t spin = sl < 0 ? kSpinDefault : (uint32_t)(sl > 0xFFFFFFFFll ? 0xFFFFFFFFll : sl);
         hipLaunchKernelGGL(dec_fin_kv_b_kernel<E>, dim3(grid8(nitems)), dim3(256), 0, st,
                            (const float*)P, plan.s1, T, (const uint16_t*)gamma, pos, eps, rt,
                            (const uint16_t*)Wb, N2, (uint16_t*)ckv, (uint16_t*)k_pe,
-                           (uint16_t*)k_nope, (uint16_t*)value, co);
+                           (uint16_t*)k_nope, (uint16_t*)value, co, spin);
         return;
     }
     hipLaunchKernelGGL(dec_finish_kernel<E>, dim3(T), dim3(256), 0, st, (const float*)P, plan.s1,
@@ -581,6 +647,24 @@ hipError_t launch_fp_decode(int dt, const void* X, const void* Wa, const void* g
         dec_launch_t<kBF16>(X, Wa, gamma, Wb, pos, (int)T, H, nh, eps, rt, k_nope, value, k_pe,
                             ckv, P, plan, co, st);
     return hipGetLastError();
+}
+
+int64_t decode_set_spin_limit(int64_t limit) {
+    return g_spin_limit.exchange(limit < 0 ? -1 : limit);
+}
+
+int64_t decode_handoff_fallbacks(bool reset) {
+    unsigned int v = 0;
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_handoff_fallbacks), sizeof(v), 0,
+                            hipMemcpyDeviceToHost) != hipSuccess)
+        return -1;
+    if (reset) {
+        const unsigned int z = 0;
+        if (hipMemcpyToSymbol(HIP_SYMBOL(g_handoff_fallbacks), &z, sizeof(z), 0,
+                              hipMemcpyHostToDevice) != hipSuccess)
+            return -1;
+    }
+    return (int64_t)v;
 }
 
 }  // namespace mla

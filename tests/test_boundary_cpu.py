@@ -369,3 +369,14 @@ def test_python_graph_set_checks_buckets():
     for b in ((), (4, 2), (2, 2)):
         with pytest.raises(ValueError):
             mla.PrologGraphs((w, g, wb), b)
+
+
+def test_handoff_spin_hook_round_trip():
+    # setting the bound needs no GPU; the default reads back as -1
+    prev = mla.mla_debug_set_handoff_spin(5)
+    try:
+        assert mla.mla_debug_set_handoff_spin(0) == 5
+        assert mla.mla_debug_set_handoff_spin(-7) == 0
+        assert mla.mla_debug_set_handoff_spin(-1) == -1
+    finally:
+        mla.mla_debug_set_handoff_spin(prev)

@@ -81,32 +81,29 @@ def test_config_large_every_row(dev, idx):
 
 def test_config4_w8a8_every_row_and_exact_accumulators(dev):
     """The R1 W8A8 ragged prefill at full size (T = 12,874): every output row
-    of the production launch against the oracle, then a second launch with
-    the accumulator exports on, whose int32 accumulators of both projections
-    must equal the oracle's bit for bit on every row.  Compared in chunks of
-    rows to bound host memory."""
+    of the production launch against the oracle, and the int32 accumulators
+    of both projections, from a second launch with the accumulator exports
+    on, bit for bit on every row.  Compared in chunks of rows to bound host
+    memory; the oracle runs once per chunk."""
     w = workloads.make_config(4)
     print(f"[parity] config4 T={w.T} lens={list(w.seq_lens)} every row", flush=True)
     t = upload(w, dev)
     outs, _ = run_lib(w, t)
+    outs2, (d1, d2) = run_lib(w, t, dbg_rows=(0, w.T))
     torch.cuda.synchronize()
     chunk = 1024
     for b in range(0, w.T, chunk):
         rows = np.arange(b, min(w.T, b + chunk))
-        compare(gpu_rows(outs, rows), run_oracle(w, rows), f"config4 rows {b}..")
-    del outs
-    outs2, (d1, d2) = run_lib(w, t, dbg_rows=(0, w.T))
-    torch.cuda.synchronize()
-    for b in range(0, w.T, chunk):
-        rows = np.arange(b, min(w.T, b + chunk))
         ref = run_oracle(w, rows)
+        compare(gpu_rows(outs, rows), ref, f"config4 rows {b}..")
         np.testing.assert_array_equal(d1[b:b + len(rows)].cpu().numpy(), ref["acc1"],
                                       err_msg=f"acc1 rows {b}..")
         np.testing.assert_array_equal(d2[b:b + len(rows)].cpu().numpy(), ref["acc2"],
                                       err_msg=f"acc2 rows {b}..")
         if b == 0:
-            # the debug launch computes the same outputs
-            compare(gpu_rows(outs2, rows), ref, "config4 dbg launch")
+            # the launch with the exports on computes the same outputs
+            for x, y in zip(outs, outs2):
+                assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
 # ---------------------------------------------------------------------------
@@ -323,3 +320,49 @@ def test_decode_many_calls_one_workspace(dev, T):
         if it == 0 or it >= 57:
             torch.cuda.synchronize()
             compare(gpu_rows(outs), refs[i], f"repeat{it}")
+
+
+# ---------------------------------------------------------------------------
+# the decode family's finish + kv_b_proj hand-off
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [1, 2, 17, 64])
+def test_decode_handoff_normal_run_needs_no_fallback(dev, T):
+    """On a normal call every latent row arrives through the hand-off: the
+    fallback count stays at zero, and the outputs match the oracle."""
+    import mla_attention_kv_amd as mla
+
+    w = workloads.make_custom(V2LITE, T, dtype="f16", seed=600 + T)
+    t = upload(w, dev)
+    assert mla.mla_debug_handoff_fallbacks(reset=True) >= 0
+    outs, _ = run_lib(w, t)
+    torch.cuda.synchronize()
+    assert mla.mla_debug_handoff_fallbacks() == 0
+    compare(gpu_rows(outs), run_oracle(w), f"handoff_T{T}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 17, 64])
+def test_decode_handoff_fallback_rebuilds_rows(dev, T):
+    """With the poll bound set to 0 from the host, every kv_b_proj workgroup
+    of the one-launch finish rebuilds its tile's latent rows itself from the
+    split-K partials (no workgroup waits, every kernel exits normally).  The
+    outputs are the same bits as the hand-off's, and match the oracle."""
+    import mla_attention_kv_amd as mla
+
+    w = workloads.make_custom(V2LITE, T, dtype="f16", seed=610 + T)
+    t = upload(w, dev)
+    ref_outs, _ = run_lib(w, t)
+    torch.cuda.synchronize()
+    prev = mla.mla_debug_set_handoff_spin(0)
+    try:
+        mla.mla_debug_handoff_fallbacks(reset=True)
+        outs, _ = run_lib(w, t)
+        torch.cuda.synchronize()
+        n = mla.mla_debug_handoff_fallbacks(reset=True)
+    finally:
+        mla.mla_debug_set_handoff_spin(prev)
+    ntile = (T + 15) // 16
+    assert n == ntile * (V2LITE.N2 // 64), n   # every workgroup with a tile
+    for a, b in zip(ref_outs, outs):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    compare(gpu_rows(outs), run_oracle(w), f"handoff_fallback_T{T}")
