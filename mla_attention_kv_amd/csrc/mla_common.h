@@ -163,10 +163,22 @@ inline WsW8 ws_w8(int64_t T, int H, const Plan& p) {
     return w;
 }
 
+// The fp32 value v as it is, kept out of any fusion with the operation that
+// consumes it (an empty asm that claims to modify it).  Used before a
+// conversion to fp16: the compiler otherwise folds a product and the
+// conversion into one mixed-precision FMA (v_fma_mix: a single rounding,
+// straight to fp16) in some inlined copies and not in others, so two copies
+// that must agree bit for bit, or agree with "round to fp32, then to fp16",
+// would not.
+__device__ __forceinline__ float fp32_value(float v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
 // RMSNorm's last step on 8 consecutive values c (fp32): times the row's
 // inverse RMS, then times gamma (8 values of dtype E packed in g), rounded to
-// E and packed.  The prolog's finish kernels and the standalone RMSNorm share
-// it.
+// fp32 and then to E, and packed.  The prolog's finish kernels and the
+// standalone RMSNorm share it.
 template <int E>
 __device__ __forceinline__ u4_t rms_scale8(const float (&c)[8], float inv, const u4_t g) {
     u4_t o;
@@ -174,8 +186,8 @@ __device__ __forceinline__ u4_t rms_scale8(const float (&c)[8], float inv, const
     for (int w = 0; w < 4; ++w) {
         const float g0 = ld_to_f32<E>((uint16_t)(g[w] & 0xFFFFu));
         const float g1 = ld_to_f32<E>((uint16_t)(g[w] >> 16));
-        const uint32_t y0 = f32_to_st<E>((c[2 * w] * inv) * g0);
-        const uint32_t y1 = f32_to_st<E>((c[2 * w + 1] * inv) * g1);
+        const uint32_t y0 = f32_to_st<E>(fp32_value((c[2 * w] * inv) * g0));
+        const uint32_t y1 = f32_to_st<E>(fp32_value((c[2 * w + 1] * inv) * g1));
         o[w] = y0 | (y1 << 16);
     }
     return o;

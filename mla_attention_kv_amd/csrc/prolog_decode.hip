@@ -310,8 +310,11 @@ __device__ __forceinline__ void fin_reduce(FinPart& r, const float* __restrict__
 // The normalised latent of the token whose four wave sums are in fred, for
 // lane l's columns 8l .. 8l + 7 (wave 0 calls it): the sums added in a fixed
 // order, then RMSNorm and gamma, rounded to E.
+// No contraction, so that every inlined copy (the producer's and the
+// fallback's) is the same sequence of fp32 operations.
 template <int E>
 __device__ __forceinline__ u4_t fin_latent(const float* fred, const u4_t gm, float eps) {
+#pragma clang fp contract(off)
     const int lane = threadIdx.x & 63;
     const float* f0 = fred;
     const float* f1 = fred + kFredPitch;
