@@ -364,6 +364,31 @@ int mla_kv_prolog_selected_path(int64_t T, mla_dims_t d);
  * the previous setting.  Not for concurrent use. */
 int mla_kv_prolog_force_path(int path);
 
+/* The fp16 / bf16 prolog for callers that cannot allocate: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, checks, outputs and kernels as mla_kv_prolog, minus the
+ * workspace: its scratch memory is a device array inside this library, one
+ * per GPU (MLA_NOALLOC_SCRATCH_BYTES, held until the process ends).  The
+ * call itself allocates nothing.  Its first call on a device looks up that
+ * device's array address once (hipGetSymbolAddress).
+ *
+ * Limit: T whose mla_kv_prolog_workspace_size(T, d, dt) exceeds
+ * MLA_NOALLOC_SCRATCH_BYTES returns MLA_ERR_WORKSPACE and launches nothing
+ * (V2-Lite shapes: every decode batch and prefills of several thousand
+ * tokens fit).  MLA_ERR_HIP if the array's address cannot be obtained.
+ *
+ * Every call on a GPU uses that GPU's one array, so calls that overlap in
+ * time on one GPU (different streams, or different host threads without
+ * ordering) race and give undefined results: order them (one stream, or
+ * events).  The array needs no clearing: every call writes whatever it
+ * later reads. */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+mla_status_t mla_kv_prolog_noalloc(const void* hidden, const void* W_kv_a, const void* gamma,
+                                   const void* W_kv_b, const int32_t* positions, int64_t T,
+                                   mla_dims_t d, mla_dtype_t dt, float eps, float theta,
+                                   void* k_nope, void* value, void* k_pe, void* compressed_kv,
+                                   void* stream);
+
 /* Test hooks for the decode family's one-launch finish + kv_b_proj (taken
  * when the device holds that launch's whole grid at once).  Its workgroups
  * wait, with a bounded number of polls, for latent rows that other

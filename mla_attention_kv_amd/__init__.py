@@ -28,6 +28,7 @@ MLA_ERR_HIP = -5
 MLA_F16 = 1
 MLA_BF16 = 2
 MLA_MAX_TOKENS = 1 << 22
+MLA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # entry points declared in include/libmlaprolog.h
 EXPORTS = (
@@ -41,6 +42,7 @@ EXPORTS = (
     "mla_kv_prolog_w8a8_cached",
     "mla_rms_norm",
     "mla_rope",
+    "mla_kv_prolog_noalloc",
     "mla_debug_set_handoff_spin",
     "mla_debug_handoff_fallbacks",
     "mla_prolog_graphs_create",
@@ -151,6 +153,9 @@ def lib() -> ctypes.CDLL:
     L.mla_kv_prolog_force_path.restype = i32
     L.mla_status_string.argtypes = [i32]
     L.mla_status_string.restype = ctypes.c_char_p
+    L.mla_kv_prolog_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, mla_dims_t, i32, f32, f32,
+                                        vp, vp, vp, vp, vp]
+    L.mla_kv_prolog_noalloc.restype = i32
     L.mla_debug_set_handoff_spin.argtypes = [i64]
     L.mla_debug_set_handoff_spin.restype = i64
     L.mla_debug_handoff_fallbacks.argtypes = [i32]

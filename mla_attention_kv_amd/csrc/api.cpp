@@ -333,6 +333,63 @@ mla_status_t mla_kv_cache_append_int8(const void* compressed_kv, const void* k_p
     return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The entry point that allocates nothing: mla_kv_prolog with its workspace in
+// a file-scope device array of this library (one copy per GPU, held until
+// the process ends).  In host code `scratch` is only a stand-in for the
+// array: its device address comes from hipGetSymbolAddress, looked up once
+// per device (with that device current) and kept in g_scratch_ptr.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::atomic<void*> g_scratch_ptr[64];
+
+// Device address of this device's scratch array, or nullptr on a HIP error.
+void* scratch_ptr() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p != nullptr) return p;
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr)
+        return nullptr;
+    g_scratch_ptr[dev].store(q, std::memory_order_release);
+    return q;
+}
+}  // namespace
+
+extern "C" {
+
+mla_status_t mla_kv_prolog_noalloc(const void* hidden, const void* W_kv_a, const void* gamma,
+                                   const void* W_kv_b, const int32_t* positions, int64_t T,
+                                   mla_dims_t d, mla_dtype_t dt, float eps, float theta,
+                                   void* k_nope, void* value, void* k_pe, void* compressed_kv,
+                                   void* stream) {
+    // sizes beyond the scratch array are rejected before anything else runs
+    if (T > 0 && T <= MLA_MAX_TOKENS && dims_supported(d) && (dt == MLA_F16 || dt == MLA_BF16) &&
+        ws_fp_max(T, d) > (size_t)MLA_NOALLOC_SCRATCH_BYTES)
+        return MLA_ERR_WORKSPACE;
+    {
+        // every other argument check first, against a stand-in workspace
+        // address that is never dereferenced
+        ValidateOnlyScope checks_only;
+        const mla_status_t st = prolog_fp(
+            hidden, W_kv_a, gamma, W_kv_b, positions, T, d, dt, eps, theta, k_nope, value, k_pe,
+            compressed_kv, CacheOut{nullptr, nullptr, 0}, (void*)(uintptr_t)256,
+            (size_t)MLA_NOALLOC_SCRATCH_BYTES, stream);
+        if (st != MLA_OK || T == 0) return st;
+    }
+    if (validate_only()) return MLA_OK;
+    void* ws = scratch_ptr();
+    if (ws == nullptr) return MLA_ERR_HIP;
+    return prolog_fp(hidden, W_kv_a, gamma, W_kv_b, positions, T, d, dt, eps, theta, k_nope,
+                     value, k_pe, compressed_kv, CacheOut{nullptr, nullptr, 0}, ws,
+                     (size_t)MLA_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 mla_status_t mla_kv_prolog_cached(const void* hidden, const void* W_kv_a, const void* gamma,
                                   const void* W_kv_b, const int32_t* positions, int64_t T,
                                   mla_dims_t d, mla_dtype_t dt, float eps, float theta,

@@ -380,3 +380,42 @@ def test_handoff_spin_hook_round_trip():
         assert mla.mla_debug_set_handoff_spin(-1) == -1
     finally:
         mla.mla_debug_set_handoff_spin(prev)
+
+
+def call_noalloc(T=4, d=V2, ptrs=None, dt=1, eps=1e-6, theta=1e4):
+    p = [FAKE] * 9 if ptrs is None else ptrs
+    return mla.lib().mla_kv_prolog_noalloc(p[0], p[1], p[2], p[3], p[4], T, d.c(), dt, eps,
+                                           theta, p[5], p[6], p[7], p[8], None)
+
+
+def test_noalloc_argument_errors():
+    # every check runs before the library looks up its scratch array (which
+    # needs a GPU), so each error is reported here as it is on a GPU machine
+    for i in range(9):
+        p = [FAKE] * 9
+        p[i] = None
+        assert call_noalloc(ptrs=p) == mla.MLA_ERR_INVALID_ARG, i
+        p[i] = FAKE + 8
+        assert call_noalloc(ptrs=p) == mla.MLA_ERR_MISALIGNED, i
+    assert call_noalloc(T=-1) == mla.MLA_ERR_INVALID_ARG
+    assert call_noalloc(dt=9) == mla.MLA_ERR_INVALID_ARG
+    assert call_noalloc(eps=-1.0) == mla.MLA_ERR_INVALID_ARG
+    assert call_noalloc(d=Dims(H=2048, nh=16, r=256)) == mla.MLA_ERR_UNSUPPORTED
+    assert call_noalloc(T=0, ptrs=[None] * 9) == mla.MLA_OK
+
+
+def test_noalloc_rejects_token_counts_beyond_its_array():
+    # the largest V2-Lite token count whose workspace fits is accepted by the
+    # size check; the next token count that does not fit is rejected with
+    # MLA_ERR_WORKSPACE before anything else (no launch)
+    lim = mla.MLA_NOALLOC_SCRATCH_BYTES
+    T = 40000
+    assert mla.mla_kv_prolog_workspace_size(T, V2) > lim
+    assert call_noalloc(T=T) == mla.MLA_ERR_WORKSPACE
+    assert call_noalloc(T=T, ptrs=[None] * 9) == mla.MLA_ERR_WORKSPACE
+    fits = max(t for t in range(1, 30000, 97) if mla.mla_kv_prolog_workspace_size(t, V2) <= lim)
+    # a fitting size passes every host check (the bad pointer below is then
+    # what stops it, before any launch)
+    p = [FAKE] * 9
+    p[0] = None
+    assert call_noalloc(T=fits, ptrs=p) == mla.MLA_ERR_INVALID_ARG
