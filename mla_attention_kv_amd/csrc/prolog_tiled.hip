@@ -440,8 +440,10 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
 //   B stage: [KE k rows][BN columns] (64 rows of fp16 / bf16, 128 of
 //            int8); 16-byte chunk c of row k sits at
 //            c ^ (2 (k & 3) + 8 ((k >> 3) & 1)) (c ^ 2 (k & 3) when a row is
-//            not a multiple of 16 chunks; c ^ (k & 7) for int8).  The B
-//            operand (column n, 8 or 16 consecutive k) comes from two
+//            not a multiple of 16 chunks; c ^ (k & 7) for int8) of LDS row
+//            brow(k) (k itself, or k with its low bit(s) flipped where two
+//            lane groups of one half-wave would otherwise share banks).  The
+//            B operand (column n, 8 or 16 consecutive k) comes from two
 //            transposing reads: ds_read_b64_tr_b16 (4 rows x 4 columns per
 //            16-lane group) or ds_read_b64_tr_b8 (8 rows x 8 columns).
 // MFMA waves are laid out WAVES_M x WAVES_N, each owning a (BM / WAVES_M) x
@@ -514,6 +516,22 @@ __device__ __forceinline__ int bswz(int k) {
     else if constexpr (E == kI8) return (k >> 1) & 3;  // 12-chunk rows (BN = 192)
     else if constexpr (BRB % 256 == 0) return 2 * (k & 3) + 8 * ((k >> 3) & 1);
     else return 2 * (k & 3);
+}
+// LDS row of B row k: rows whose second lane group of a transposing read
+// would otherwise hit the first group's banks (the two groups of a half-wave
+// read rows 8 (16-bit) or 16 (int8) apart, and with 384-, 128- or 192-byte
+// rows those land on the same bank slots) swap places with a neighbour, which
+// moves them to the other half of the 256-byte bank span:
+//   16-bit, rows of 24 chunks: k ^ 1 when bit 3 of k is set;
+//   int8, 8-chunk rows: k ^ 1 when bit 4 is set; 12-chunk rows: k ^ 2.
+// An involution inside each slab (bits 3 and 4 are unchanged), so the copy
+// waves use it to find the source row of an LDS row as well.
+template <int E, int BRB>
+__device__ __forceinline__ int brow(int k) {
+    if constexpr (E == kI8 && BRB % 128 == 0) return k ^ ((k >> 4) & 1);
+    else if constexpr (E == kI8) return k ^ (2 * ((k >> 4) & 1));
+    else if constexpr (BRB % 256 == 0) return k;
+    else return k ^ ((k >> 3) & 1);
 }
 typedef int v2i_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint2 lds_tr8(const uint8_t* p) {
@@ -588,8 +606,10 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP),
         int64_t boff[B_PW];
 #pragma unroll
         for (int u = 0; u < B_PW; ++u) {
+            // the LDS row this lane fills holds B row k (brow is its own
+            // inverse), swizzled chunk pos
             const int byte = (p + NP * u) * 1024 + lane * 16;
-            const int k = byte / BRB, pos = (byte % BRB) / 16;
+            const int k = brow<E, BRB>(byte / BRB), pos = (byte % BRB) / 16;
             boff[u] = (int64_t)k * ldb + (pos ^ bswz<E, BRB>(k)) * 16;
         }
         const int64_t bstep = KE * ldb;  // bytes of B per slab
@@ -691,9 +711,10 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP),
                 const int k = ks * 32 + g * 8 + (l16 >> 2);
                 const int colb = (wn0 + j * 16 + 4 * (l16 & 3)) * 2;
                 const int c = colb >> 4, off = colb & 15;
-                const uint2 lo = lds_tr16(Bs + k * BRB + ((c ^ bswz<E, BRB>(k)) << 4) + off);
-                const uint2 hi =
-                    lds_tr16(Bs + (k + 4) * BRB + ((c ^ bswz<E, BRB>(k + 4)) << 4) + off);
+                const uint2 lo =
+                    lds_tr16(Bs + brow<E, BRB>(k) * BRB + ((c ^ bswz<E, BRB>(k)) << 4) + off);
+                const uint2 hi = lds_tr16(Bs + brow<E, BRB>(k + 4) * BRB +
+                                          ((c ^ bswz<E, BRB>(k + 4)) << 4) + off);
                 fb[buf][j] = u4_t{lo.x, lo.y, hi.x, hi.y};
             } else {
                 // lane (16 g + s): rows 64 ks + 16 g + s / 2 (+ 8), columns
@@ -702,9 +723,10 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP),
                 const int k = ks * 64 + g * 16 + (l16 >> 1);
                 const int colb = wn0 + j * 16 + 8 * (l16 & 1);
                 const int c = colb >> 4, off = colb & 15;
-                const uint2 lo = lds_tr8(Bs + k * BRB + ((c ^ bswz<E, BRB>(k)) << 4) + off);
-                const uint2 hi =
-                    lds_tr8(Bs + (k + 8) * BRB + ((c ^ bswz<E, BRB>(k + 8)) << 4) + off);
+                const uint2 lo =
+                    lds_tr8(Bs + brow<E, BRB>(k) * BRB + ((c ^ bswz<E, BRB>(k)) << 4) + off);
+                const uint2 hi = lds_tr8(Bs + brow<E, BRB>(k + 8) * BRB +
+                                         ((c ^ bswz<E, BRB>(k + 8)) << 4) + off);
                 fb[buf][j] = u4_t{lo.x, lo.y, hi.x, hi.y};
             }
         }
