@@ -40,6 +40,10 @@ head, the query-side shape).
 mla_prolog_graphs_launch per step issued from the host (the serving-loop
 cost, launch included), against direct calls on the same sets.
 
+--op graph_layers --layers L times a stack of L layers' prologs per step
+(V2-Lite decode by default): one multi-layer graph launch
+(mla_prolog_graphs_create_layers) against L direct calls, per layer.
+
 --op vendor_gemm times the vendor library's GEMM (torch.matmul) on the two
 projections' shapes, as a reference for the MFMA fractions (not the prolog).
 
@@ -260,6 +264,103 @@ class GraphBucketSets:
         st = self.launch(g.handle, self.T, ctypes.c_void_p(stream_ptr), None)
         if st != 0:
             raise RuntimeError(f"library call failed: {self.mla.mla_status_string(st)}")
+
+
+class LayerStack:
+    """n_models stand-ins of an L-layer model for one workload: each model
+    holds L layers' weights (copies of the workload's, at distinct
+    addresses) and one multi-layer graph set over them (one bucket, the
+    workload's T).  call() is one step of the stack: either one
+    mla_prolog_graphs_launch replaying all L prologs (graph=True), or L
+    direct prolog calls over the same buffers."""
+
+    def __init__(self, w, L, n_models, dev, graph):
+        import mla_attention_kv_amd as mla
+        from tests.parity import upload
+
+        self.mla, self.w, self.L, self.graph = mla, w, L, graph
+        base = upload(w, dev)
+        fp = w.kind == "fp"
+        names = ("Wa", "gamma", "Wb") if fp else ("Wqa", "swa", "gamma", "Wqb", "swb")
+        self.models = []
+        for _ in range(n_models):
+            layers = [tuple(base[n].clone() for n in names) for _ in range(L)]
+            g = mla.PrologGraphs(layers, (w.T,), w.eps, w.theta, w8a8=not fp)
+            g.hidden[:w.T] = base["X"]
+            g.positions[:w.T] = base["pos"]
+            self.models.append((g, layers))
+        d = w.dims
+        self.dims = mla.Dims(H=d.H, nh=d.nh).c()
+        self.code = mla.MLA_F16 if w.dtype == "f16" else mla.MLA_BF16
+        self.launch = mla.lib().mla_prolog_graphs_launch
+        self.fn = mla.lib().mla_kv_prolog if fp else mla.lib().mla_kv_prolog_w8a8
+        self.args = self.models  # the rotation (time_graph's cycle length)
+
+    def call(self, i, stream_ptr):
+        g, layers = self.models[i % len(self.models)]
+        sp = ctypes.c_void_p(stream_ptr)
+        if self.graph:
+            st = self.launch(g.handle, self.w.T, sp, None)
+        else:
+            st = 0
+            T = self.w.T
+            for l in range(self.L):
+                outs = (g.k_nope[l].data_ptr(), g.value[l].data_ptr(), g.k_pe[l].data_ptr(),
+                        g.compressed_kv[l].data_ptr())
+                if self.w.kind == "fp":
+                    Wa, gamma, Wb = layers[l]
+                    st = self.fn(g.hidden.data_ptr(), Wa.data_ptr(), gamma.data_ptr(),
+                                 Wb.data_ptr(), g.positions.data_ptr(), T, self.dims, self.code,
+                                 self.w.eps, self.w.theta, *outs, g.workspace.data_ptr(),
+                                 g.workspace.numel(), sp)
+                else:
+                    Wqa, swa, gamma, Wqb, swb = layers[l]
+                    st = self.fn(g.hidden.data_ptr(), Wqa.data_ptr(), swa.data_ptr(),
+                                 gamma.data_ptr(), Wqb.data_ptr(), swb.data_ptr(),
+                                 g.positions.data_ptr(), T, self.dims, self.w.eps, self.w.theta,
+                                 *outs, None, None, 0, 0, g.workspace.data_ptr(),
+                                 g.workspace.numel(), sp)
+                if st != 0:
+                    break
+        if st != 0:
+            raise RuntimeError(f"library call failed: {self.mla.mla_status_string(st)}")
+
+
+def main_layers(args, headline, dev):
+    """--op graph_layers: an L-layer stack of prologs per step, as one
+    multi-layer graph launch against L direct calls; reports time per layer."""
+    import torch
+
+    import workloads
+
+    cfg = workloads.CONFIGS[headline]
+    w = workloads.make_config(headline)
+    L = args.layers
+    per_layer = workloads.algorithmic_bytes(w.dims, w.T, w.kind, w.dtype)
+    n_models = max(2, math.ceil(ROTATE_BYTES / (L * per_layer)))
+    log(f"{cfg['name']}: {L} layers per step, {n_models} rotated models")
+    res = {}
+    for graph in (True, False):
+        stack = LayerStack(w, L, n_models, dev, graph)
+        torch.cuda.synchronize()
+        ms = time_eager(stack, args.steps, args.warmup, dev)
+        res["graph" if graph else "direct"] = ms / args.steps / L * 1e3
+        if not graph:
+            # the same direct calls captured into one replayed graph per rotation
+            res["direct_replayed"] = time_graph(stack, args.steps, args.warmup, dev) / args.steps / L * 1e3
+        del stack
+        torch.cuda.empty_cache()
+    log(f"per layer: one multi-layer graph launch {res['graph']:.2f} us, direct calls "
+        f"{res['direct']:.2f} us, direct calls replayed as a captured graph "
+        f"{res['direct_replayed']:.2f} us")
+    out = {"metric": "MLA KV prolog time per layer of an L-layer stack", "unit": "us",
+           "value": res["graph"], "higher_is_better": False, "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "data": "synthetic (seeded; no public dataset exists for this path)",
+           "config": {"workload": cfg["name"] + f"_{L}_layers", "T": w.T, "layers": L,
+                      "rotated_models": n_models,
+                      "timing": "events around K host-issued steps (launches included)"},
+           "us_per_layer": res}
+    print(json.dumps(out), flush=True)
 
 
 def vendor_gemm_reference(dev, steps):
@@ -705,8 +806,10 @@ def main():
     ap.add_argument("--op", default="prolog",
                     choices=["prolog", "prolog_cached", "prolog_then_append", "cache_append",
                              "cache_append_int8", "rms_norm", "rope", "graph_buckets",
-                             "vendor_gemm"],
+                             "graph_layers", "vendor_gemm"],
                     help="what one step is (default: the prolog)")
+    ap.add_argument("--layers", type=int, default=27,
+                    help="--op graph_layers: layers per step (default 27, V2-Lite's count)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -735,6 +838,9 @@ def main():
     cfg = workloads.CONFIGS[headline]
     if args.op == "vendor_gemm":
         vendor_gemm_reference(dev, args.steps)
+        return
+    if args.op == "graph_layers":
+        main_layers(args, 1 if args.config is None else args.config, dev)
         return
     if args.op in ("rms_norm", "rope"):
         w = workloads.make_config(headline)

@@ -319,6 +319,22 @@ mla_status_t mla_prolog_graphs_create(const mla_prolog_graph_desc_t* desc,
                                       mla_prolog_graphs** out);
 
 /*
+ * The same over n_layers layers (1 <= n_layers <= 256): descs[l] names layer
+ * l's weights, cache and buffers (the layers must agree in w8a8, dims and,
+ * for w8a8 == 0, dt; MLA_ERR_INVALID_ARG otherwise).  Each bucket's graph
+ * replays the prolog of every layer, in layer order, so one launch runs all
+ * n_layers prologs: the guide captures the whole model forward into one
+ * graph ("Command-line parameters", note 3), and a graph launch costs the
+ * host about as much as a few direct kernel launches, so it pays off over
+ * many layers.  Layers may share buffers (say one workspace: the replays of
+ * one graph are ordered).  mla_prolog_graphs_create is the case
+ * n_layers == 1.
+ */
+mla_status_t mla_prolog_graphs_create_layers(const mla_prolog_graph_desc_t* descs,
+                                             int32_t n_layers, const int64_t* buckets,
+                                             int32_t n_buckets, mla_prolog_graphs** out);
+
+/*
  * One prolog step over the first T rows of the static buffers: launches the
  * graph of the smallest bucket >= T on `stream` (a stream of the set's
  * device; NULL = the default stream) and stores that bucket in
@@ -337,9 +353,9 @@ mla_status_t mla_prolog_graphs_launch(mla_prolog_graphs* g, int64_t T, void* str
 int64_t mla_prolog_graphs_bucket(const mla_prolog_graphs* g, int64_t T);
 
 /*
- * Rebind the set to new buffers (say the next layer's weights and cache, or
- * new static buffers): the graphs are re-recorded from desc and updated in
- * place.  w8a8, dims and (for w8a8 == 0) dt must equal the set's
+ * Rebind a one-layer set to new buffers (say the next layer's weights and
+ * cache, or new static buffers): the graphs are re-recorded from desc and
+ * updated in place.  w8a8, dims and (for w8a8 == 0) dt must equal the set's
  * (MLA_ERR_INVALID_ARG otherwise); eps, theta and every pointer may change.
  * Checks run first: on a failed check the set is unchanged.  On
  * MLA_ERR_HIP the set may be partly updated and should be destroyed.  The
@@ -350,6 +366,16 @@ int64_t mla_prolog_graphs_bucket(const mla_prolog_graphs* g, int64_t T);
  * concurrently with any other call on the same set.
  */
 mla_status_t mla_prolog_graphs_update(mla_prolog_graphs* g, const mla_prolog_graph_desc_t* desc);
+
+/* Rebind every layer of a set made by mla_prolog_graphs_create_layers
+ * (n_layers must equal the set's; the same rules as mla_prolog_graphs_update
+ * per layer).  mla_prolog_graphs_update is the case n_layers == 1. */
+mla_status_t mla_prolog_graphs_update_layers(mla_prolog_graphs* g,
+                                             const mla_prolog_graph_desc_t* descs,
+                                             int32_t n_layers);
+
+/* The number of layers a set replays per launch (0 for NULL). */
+int32_t mla_prolog_graphs_layers(const mla_prolog_graphs* g);
 
 /* Free the set's graphs (NULL is a no-op).  The caller first synchronises
  * with any launch of the set in flight. */

@@ -46,6 +46,9 @@ EXPORTS = (
     "mla_debug_set_handoff_spin",
     "mla_debug_handoff_fallbacks",
     "mla_prolog_graphs_create",
+    "mla_prolog_graphs_create_layers",
+    "mla_prolog_graphs_update_layers",
+    "mla_prolog_graphs_layers",
     "mla_prolog_graphs_launch",
     "mla_prolog_graphs_bucket",
     "mla_prolog_graphs_update",
@@ -139,6 +142,15 @@ def lib() -> ctypes.CDLL:
                                            ctypes.POINTER(ctypes.c_int64), ctypes.c_int32,
                                            ctypes.POINTER(gp)]
     L.mla_prolog_graphs_create.restype = i32
+    L.mla_prolog_graphs_create_layers.argtypes = [ctypes.POINTER(mla_prolog_graph_desc_t), i32,
+                                                  ctypes.POINTER(ctypes.c_int64), i32,
+                                                  ctypes.POINTER(gp)]
+    L.mla_prolog_graphs_create_layers.restype = i32
+    L.mla_prolog_graphs_update_layers.argtypes = [gp, ctypes.POINTER(mla_prolog_graph_desc_t),
+                                                  i32]
+    L.mla_prolog_graphs_update_layers.restype = i32
+    L.mla_prolog_graphs_layers.argtypes = [gp]
+    L.mla_prolog_graphs_layers.restype = i32
     L.mla_prolog_graphs_launch.argtypes = [gp, i64, vp, ctypes.POINTER(ctypes.c_int64)]
     L.mla_prolog_graphs_launch.restype = i32
     L.mla_prolog_graphs_bucket.argtypes = [gp, i64]
@@ -550,7 +562,13 @@ class PrologGraphs:
     (kv_cache_q int8, kv_scale float32) pair.  A step: write the first T rows
     of .hidden / .positions (/ .slot_mapping), call run(T), read the first T
     rows of .k_nope / .value / .k_pe / .compressed_kv.  Steps and the static
-    buffers belong to one device; keep them on one stream."""
+    buffers belong to one device; keep them on one stream.
+
+    Several layers: weights is a list of per-layer weight tuples (and cache,
+    if given, a list of per-layer caches).  Each graph then replays every
+    layer's prolog in order with one launch; the layers read the same static
+    .hidden / .positions / .slot_mapping rows and write their own outputs,
+    .k_nope[l] / .value[l] / .k_pe[l] / .compressed_kv[l]."""
 
     def __init__(self, weights, buckets, eps: float = 1e-6, theta: float = 10000.0, *,
                  w8a8: bool = False, cache=None, dn: int = 128, dv: int = 128,
@@ -560,11 +578,18 @@ class PrologGraphs:
         if not self.buckets or list(self.buckets) != sorted(set(self.buckets)):
             raise ValueError("buckets: ascending distinct token counts expected")
         self.w8a8 = bool(w8a8)
-        self.device = weights[0].device if device is None else torch.device(device)
+        self.multi = isinstance(weights, list)
+        self.n_layers = len(weights) if self.multi else 1
+        if self.n_layers < 1:
+            raise ValueError("weights: at least one layer expected")
+        first = weights[0] if self.multi else weights
+        self.device = first[0].device if device is None else torch.device(device)
         self._handle = ctypes.c_void_p(None)
         self._bind(weights, eps, theta, cache, dn, dv, create=True)
 
-    def _bind(self, weights, eps, theta, cache, dn, dv, create):
+    def _layer_dims(self, weights, dn, dv):
+        """Dims, dtype, dtype code and the five weight pointers' tensors of
+        one layer, after checking its weights."""
         torch = _torch()
         dev = self.device
         if self.w8a8:
@@ -579,44 +604,27 @@ class PrologGraphs:
             _check(gamma, "gamma", torch.bfloat16, (d.r,), dev)
             _check(Wqb, "Wq_kv_b", torch.int8, (d.r, N2), dev)
             _check(swb, "s_kv_b", torch.float32, (N2,), dev)
-            ptrs = (Wqa, swa, gamma, Wqb, swb)
-        else:
-            Wa, gamma, Wb = weights
-            dtype = Wa.dtype
-            code = {torch.float16: MLA_F16, torch.bfloat16: MLA_BF16}.get(dtype)
-            if code is None:
-                raise ValueError(f"W_kv_a: dtype {dtype}, expected float16 or bfloat16")
-            H = Wa.shape[0]
-            d = Dims(H=H, nh=Wb.shape[1] // (dn + dv), r=gamma.shape[0],
-                     dr=Wa.shape[1] - gamma.shape[0], dn=dn, dv=dv)
-            _check(Wa, "W_kv_a", dtype, (H, d.r + d.dr), dev)
-            _check(gamma, "gamma", dtype, (d.r,), dev)
-            _check(Wb, "W_kv_b", dtype, (d.r, d.nh * (d.dn + d.dv)), dev)
-            ptrs = (Wa, None, gamma, Wb, None)
-        if not create and (d != self.dims or dtype != self.dtype):
-            raise ValueError("update: dims and dtype must stay those of the set")
-        Tm = self.buckets[-1]
-        if create:
-            self.dims, self.dtype = d, dtype
-            self.hidden = torch.zeros((Tm, d.H), dtype=dtype, device=dev)
-            self.positions = torch.zeros(Tm, dtype=torch.int32, device=dev)
-            self.slot_mapping = torch.full((Tm,), -1, dtype=torch.int64, device=dev)
-            self.k_nope = torch.empty((Tm, d.nh, d.dn), dtype=dtype, device=dev)
-            self.value = torch.empty((Tm, d.nh, d.dv), dtype=dtype, device=dev)
-            self.k_pe = torch.empty((Tm, d.dr), dtype=dtype, device=dev)
-            self.compressed_kv = torch.empty((Tm, d.r), dtype=dtype, device=dev)
-            if self.w8a8:
-                nb = max(mla_kv_prolog_w8a8_workspace_size(b, d) for b in self.buckets)
-            else:
-                nb = max(mla_kv_prolog_workspace_size(b, d, code) for b in self.buckets)
-            if nb == 0:
-                raise MlaError(MLA_ERR_UNSUPPORTED, "workspace size")
-            self.workspace = torch.empty(nb, dtype=torch.uint8, device=dev)
-        W = d.r + d.dr
+            return d, dtype, code, (Wqa, swa, gamma, Wqb, swb)
+        Wa, gamma, Wb = weights
+        dtype = Wa.dtype
+        code = {torch.float16: MLA_F16, torch.bfloat16: MLA_BF16}.get(dtype)
+        if code is None:
+            raise ValueError(f"W_kv_a: dtype {dtype}, expected float16 or bfloat16")
+        H = Wa.shape[0]
+        d = Dims(H=H, nh=Wb.shape[1] // (dn + dv), r=gamma.shape[0],
+                 dr=Wa.shape[1] - gamma.shape[0], dn=dn, dv=dv)
+        _check(Wa, "W_kv_a", dtype, (H, d.r + d.dr), dev)
+        _check(gamma, "gamma", dtype, (d.r,), dev)
+        _check(Wb, "W_kv_b", dtype, (d.r, d.nh * (d.dn + d.dv)), dev)
+        return d, dtype, code, (Wa, None, gamma, Wb, None)
+
+    def _cache_ptrs(self, cache, dtype, W):
+        torch = _torch()
+        dev = self.device
         kv_cache = kv_cache_q = kv_scale = None
         nslots = 0
         if cache is not None:
-            if isinstance(cache, (tuple, list)):
+            if isinstance(cache, tuple):
                 if not self.w8a8:
                     raise ValueError("an int8 cache needs w8a8=True")
                 kv_cache_q, kv_scale = cache
@@ -631,33 +639,84 @@ class PrologGraphs:
                         or not kv_cache.is_contiguous() or kv_cache.device != dev:
                     raise ValueError(f"kv_cache: contiguous {dtype} [..., {W}] on {dev} expected")
                 nslots = kv_cache.numel() // W
+        return kv_cache, kv_cache_q, kv_scale, nslots
+
+    def _bind(self, weights, eps, theta, cache, dn, dv, create):
+        torch = _torch()
+        dev = self.device
+        L = self.n_layers
+        wl = weights if self.multi else [weights]
+        if len(wl) != L:
+            raise ValueError(f"weights: {L} layers expected")
+        if cache is None:
+            cl = [None] * L
+        elif self.multi:
+            if not isinstance(cache, list) or len(cache) != L:
+                raise ValueError(f"cache: a list of {L} per-layer caches expected")
+            cl = cache
+        else:
+            cl = [tuple(cache) if isinstance(cache, list) else cache]
+        kinds = [self._layer_dims(w, dn, dv) for w in wl]
+        d, dtype, code, _ = kinds[0]
+        for dl, tl, _c, _p in kinds[1:]:
+            if dl != d or tl != dtype:
+                raise ValueError("every layer must have the same dims and dtype")
+        if not create and (d != self.dims or dtype != self.dtype):
+            raise ValueError("update: dims and dtype must stay those of the set")
+        Tm = self.buckets[-1]
+        if create:
+            self.dims, self.dtype = d, dtype
+            lead = (L,) if self.multi else ()
+            self.hidden = torch.zeros((Tm, d.H), dtype=dtype, device=dev)
+            self.positions = torch.zeros(Tm, dtype=torch.int32, device=dev)
+            self.slot_mapping = torch.full((Tm,), -1, dtype=torch.int64, device=dev)
+            self.k_nope = torch.empty(lead + (Tm, d.nh, d.dn), dtype=dtype, device=dev)
+            self.value = torch.empty(lead + (Tm, d.nh, d.dv), dtype=dtype, device=dev)
+            self.k_pe = torch.empty(lead + (Tm, d.dr), dtype=dtype, device=dev)
+            self.compressed_kv = torch.empty(lead + (Tm, d.r), dtype=dtype, device=dev)
+            if self.w8a8:
+                nb = max(mla_kv_prolog_w8a8_workspace_size(b, d) for b in self.buckets)
+            else:
+                nb = max(mla_kv_prolog_workspace_size(b, d, code) for b in self.buckets)
+            if nb == 0:
+                raise MlaError(MLA_ERR_UNSUPPORTED, "workspace size")
+            # one workspace for every layer: a graph's replays are ordered
+            self.workspace = torch.empty(nb, dtype=torch.uint8, device=dev)
+        W = d.r + d.dr
 
         def p(t):
             return t.data_ptr() if t is not None else None
 
-        desc = mla_prolog_graph_desc_t(
-            1 if self.w8a8 else 0, d.c(), code, float(eps), float(theta),
-            p(ptrs[0]), p(ptrs[1]), p(ptrs[2]), p(ptrs[3]), p(ptrs[4]),
-            self.hidden.data_ptr(), self.positions.data_ptr(), self.k_nope.data_ptr(),
-            self.value.data_ptr(), self.k_pe.data_ptr(), self.compressed_kv.data_ptr(),
-            self.slot_mapping.data_ptr() if nslots else None, p(kv_cache), p(kv_cache_q),
-            p(kv_scale), nslots, self.workspace.data_ptr(), self.workspace.numel())
+        descs = (mla_prolog_graph_desc_t * L)()
+        for l, ((_d, _t, _c, ptrs), c) in enumerate(zip(kinds, cl)):
+            kv_cache, kv_cache_q, kv_scale, nslots = self._cache_ptrs(c, dtype, W)
+            outs = ((self.k_nope[l], self.value[l], self.k_pe[l], self.compressed_kv[l])
+                    if self.multi else (self.k_nope, self.value, self.k_pe, self.compressed_kv))
+            descs[l] = mla_prolog_graph_desc_t(
+                1 if self.w8a8 else 0, d.c(), code, float(eps), float(theta),
+                p(ptrs[0]), p(ptrs[1]), p(ptrs[2]), p(ptrs[3]), p(ptrs[4]),
+                self.hidden.data_ptr(), self.positions.data_ptr(), outs[0].data_ptr(),
+                outs[1].data_ptr(), outs[2].data_ptr(), outs[3].data_ptr(),
+                self.slot_mapping.data_ptr() if nslots else None, p(kv_cache), p(kv_cache_q),
+                p(kv_scale), nslots, self.workspace.data_ptr(), self.workspace.numel())
         arr = (ctypes.c_int64 * len(self.buckets))(*self.buckets)
         with torch.cuda.device(dev):
             if create:
-                st = lib().mla_prolog_graphs_create(ctypes.byref(desc), arr, len(self.buckets),
-                                                    ctypes.byref(self._handle))
+                st = lib().mla_prolog_graphs_create_layers(descs, L, arr, len(self.buckets),
+                                                           ctypes.byref(self._handle))
             else:
-                st = lib().mla_prolog_graphs_update(self._handle, ctypes.byref(desc))
+                st = lib().mla_prolog_graphs_update_layers(self._handle, descs, L)
         if st != MLA_OK:
-            raise MlaError(st, "mla_prolog_graphs_create" if create else "mla_prolog_graphs_update")
+            raise MlaError(st, "mla_prolog_graphs_create_layers" if create
+                           else "mla_prolog_graphs_update_layers")
         # keep the bound tensors alive as long as the graphs refer to them
         self._bound = (weights, cache)
 
     def update(self, weights, eps: float = 1e-6, theta: float = 10000.0, *, cache=None,
                dn: int = 128, dv: int = 128):
-        """Rebind the graphs to other weights (say the next layer's) and
-        cache; the static buffers stay."""
+        """Rebind the graphs to other weights (say the next layer's, or for a
+        multi-layer set another list of layers) and caches; the static
+        buffers stay."""
         self._bind(weights, eps, theta, cache, dn, dv, create=False)
 
     @property

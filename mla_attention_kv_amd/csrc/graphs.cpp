@@ -7,10 +7,13 @@
 // notes 2-3; "Migration notes", item 3).
 //
 // A set holds one instantiated graph per bucket.  Each graph is the exact
-// launch sequence the plain entry point issues for that many tokens, so a
-// replay computes bit for bit what a direct call over the same buffers
-// computes.  The set holds no tensors of its own: every buffer is the
-// caller's (the graphs themselves are runtime objects).
+// launch sequence the plain entry point issues for that many tokens, once
+// per layer of the set in layer order (a set of L layers, each with its own
+// weights and buffers, replays all L prologs with one launch, as a
+// whole-model graph does), so a replay computes bit for bit what direct
+// calls over the same buffers compute.  The set holds no tensors of its
+// own: every buffer is the caller's (the graphs themselves are runtime
+// objects).
 #include <algorithm>
 #include <new>
 #include <vector>
@@ -20,7 +23,7 @@
 
 struct mla_prolog_graphs {
     int device = 0;
-    mla_prolog_graph_desc_t desc{};
+    std::vector<mla_prolog_graph_desc_t> layers;
     std::vector<int64_t> buckets;
     std::vector<hipGraphExec_t> execs;
 };
@@ -28,6 +31,7 @@ struct mla_prolog_graphs {
 namespace {
 
 constexpr int kMaxBuckets = 64;
+constexpr int kMaxLayers = 256;
 
 // The plain entry point the graphs record: the cached variants, which with
 // num_slots == 0 are the plain prolog.
@@ -53,24 +57,38 @@ bool buckets_ok(const int64_t* b, int32_t n) {
     return true;
 }
 
-// Every argument check of the recorded calls, for every bucket, without
-// touching the GPU.
-mla_status_t validate(const mla_prolog_graph_desc_t& d, const int64_t* b, int32_t n) {
-    if (d.w8a8 != 0 && d.w8a8 != 1) return MLA_ERR_INVALID_ARG;
-    mla::ValidateOnlyScope scope;
-    for (int32_t i = 0; i < n; ++i) {
-        const mla_status_t st = call_prolog(d, b[i], nullptr);
-        if (st != MLA_OK) return st;
+// Layers of one set record the same kind of call: same w8a8, dims and (fp
+// path) dtype.
+bool same_kind(const mla_prolog_graph_desc_t& a, const mla_prolog_graph_desc_t& o) {
+    return a.w8a8 == o.w8a8 && a.d.H == o.d.H && a.d.r == o.d.r && a.d.dr == o.d.dr &&
+           a.d.nh == o.d.nh && a.d.dn == o.d.dn && a.d.dv == o.d.dv &&
+           (a.w8a8 != 0 || a.dt == o.dt);
+}
+
+// Every argument check of the recorded calls, for every layer and bucket,
+// without touching the GPU.
+mla_status_t validate(const mla_prolog_graph_desc_t* d, int32_t nl, const int64_t* b, int32_t n) {
+    if (d == nullptr || nl < 1 || nl > kMaxLayers) return MLA_ERR_INVALID_ARG;
+    for (int32_t l = 0; l < nl; ++l) {
+        if (d[l].w8a8 != 0 && d[l].w8a8 != 1) return MLA_ERR_INVALID_ARG;
+        if (!same_kind(d[l], d[0])) return MLA_ERR_INVALID_ARG;
     }
+    mla::ValidateOnlyScope scope;
+    for (int32_t l = 0; l < nl; ++l)
+        for (int32_t i = 0; i < n; ++i) {
+            const mla_status_t st = call_prolog(d[l], b[i], nullptr);
+            if (st != MLA_OK) return st;
+        }
     return MLA_OK;
 }
 
-mla_status_t capture(const mla_prolog_graph_desc_t& d, int64_t T, hipStream_t s,
-                     hipGraph_t* out) {
+mla_status_t capture(const std::vector<mla_prolog_graph_desc_t>& layers, int64_t T,
+                     hipStream_t s, hipGraph_t* out) {
     *out = nullptr;
     if (hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal) != hipSuccess)
         return MLA_ERR_HIP;
-    const mla_status_t st = call_prolog(d, T, s);
+    mla_status_t st = MLA_OK;
+    for (size_t l = 0; l < layers.size() && st == MLA_OK; ++l) st = call_prolog(layers[l], T, s);
     hipGraph_t g = nullptr;
     const hipError_t e = hipStreamEndCapture(s, &g);
     if (st != MLA_OK || e != hipSuccess || g == nullptr) {
@@ -103,18 +121,20 @@ mla_status_t on_device(int device, F&& f) {
 
 extern "C" {
 
-mla_status_t mla_prolog_graphs_create(const mla_prolog_graph_desc_t* desc,
-                                      const int64_t* buckets, int32_t n_buckets,
-                                      mla_prolog_graphs** out) {
+mla_status_t mla_prolog_graphs_create_layers(const mla_prolog_graph_desc_t* descs,
+                                             int32_t n_layers, const int64_t* buckets,
+                                             int32_t n_buckets, mla_prolog_graphs** out) {
     if (out == nullptr) return MLA_ERR_INVALID_ARG;
     *out = nullptr;
-    if (desc == nullptr || !buckets_ok(buckets, n_buckets)) return MLA_ERR_INVALID_ARG;
-    mla_status_t st = validate(*desc, buckets, n_buckets);
+    if (descs == nullptr || n_layers < 1 || n_layers > kMaxLayers ||
+        !buckets_ok(buckets, n_buckets))
+        return MLA_ERR_INVALID_ARG;
+    mla_status_t st = validate(descs, n_layers, buckets, n_buckets);
     if (st != MLA_OK) return st;
 
     mla_prolog_graphs* g = new (std::nothrow) mla_prolog_graphs;
     if (g == nullptr) return MLA_ERR_HIP;
-    g->desc = *desc;
+    g->layers.assign(descs, descs + n_layers);
     g->buckets.assign(buckets, buckets + n_buckets);
     g->execs.assign(n_buckets, nullptr);
     if (hipGetDevice(&g->device) != hipSuccess) {
@@ -128,7 +148,7 @@ mla_status_t mla_prolog_graphs_create(const mla_prolog_graph_desc_t* desc,
     }
     for (int32_t i = 0; i < n_buckets && st == MLA_OK; ++i) {
         hipGraph_t graph = nullptr;
-        st = capture(g->desc, g->buckets[i], s, &graph);
+        st = capture(g->layers, g->buckets[i], s, &graph);
         if (st != MLA_OK) break;
         if (hipGraphInstantiate(&g->execs[i], graph, nullptr, nullptr, 0) != hipSuccess) {
             g->execs[i] = nullptr;
@@ -145,15 +165,22 @@ mla_status_t mla_prolog_graphs_create(const mla_prolog_graph_desc_t* desc,
     return MLA_OK;
 }
 
-mla_status_t mla_prolog_graphs_update(mla_prolog_graphs* g, const mla_prolog_graph_desc_t* desc) {
-    if (g == nullptr || desc == nullptr) return MLA_ERR_INVALID_ARG;
-    const mla_prolog_graph_desc_t& o = g->desc;
-    if (desc->w8a8 != o.w8a8 || desc->d.H != o.d.H || desc->d.r != o.d.r ||
-        desc->d.dr != o.d.dr || desc->d.nh != o.d.nh || desc->d.dn != o.d.dn ||
-        desc->d.dv != o.d.dv || (desc->w8a8 == 0 && desc->dt != o.dt))
+mla_status_t mla_prolog_graphs_create(const mla_prolog_graph_desc_t* desc,
+                                      const int64_t* buckets, int32_t n_buckets,
+                                      mla_prolog_graphs** out) {
+    return mla_prolog_graphs_create_layers(desc, 1, buckets, n_buckets, out);
+}
+
+mla_status_t mla_prolog_graphs_update_layers(mla_prolog_graphs* g,
+                                             const mla_prolog_graph_desc_t* descs,
+                                             int32_t n_layers) {
+    if (g == nullptr || descs == nullptr || n_layers != (int32_t)g->layers.size())
         return MLA_ERR_INVALID_ARG;
-    mla_status_t st = validate(*desc, g->buckets.data(), (int32_t)g->buckets.size());
+    for (int32_t l = 0; l < n_layers; ++l)
+        if (!same_kind(descs[l], g->layers[0])) return MLA_ERR_INVALID_ARG;
+    mla_status_t st = validate(descs, n_layers, g->buckets.data(), (int32_t)g->buckets.size());
     if (st != MLA_OK) return st;
+    const std::vector<mla_prolog_graph_desc_t> layers(descs, descs + n_layers);
     return on_device(g->device, [&]() -> mla_status_t {
         hipStream_t s = nullptr;
         if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return MLA_ERR_HIP;
@@ -161,7 +188,7 @@ mla_status_t mla_prolog_graphs_update(mla_prolog_graphs* g, const mla_prolog_gra
         std::vector<hipGraph_t> graphs(g->buckets.size(), nullptr);
         mla_status_t r = MLA_OK;
         for (size_t i = 0; i < graphs.size() && r == MLA_OK; ++i)
-            r = capture(*desc, g->buckets[i], s, &graphs[i]);
+            r = capture(layers, g->buckets[i], s, &graphs[i]);
         (void)hipStreamDestroy(s);
         if (r == MLA_OK) {
             for (size_t i = 0; i < graphs.size() && r == MLA_OK; ++i) {
@@ -180,12 +207,20 @@ mla_status_t mla_prolog_graphs_update(mla_prolog_graphs* g, const mla_prolog_gra
                 (void)hipGraphExecDestroy(g->execs[i]);
                 g->execs[i] = x;
             }
-            if (r == MLA_OK) g->desc = *desc;
+            if (r == MLA_OK) g->layers = layers;
         }
         for (hipGraph_t x : graphs)
             if (x != nullptr) (void)hipGraphDestroy(x);
         return r;
     });
+}
+
+mla_status_t mla_prolog_graphs_update(mla_prolog_graphs* g, const mla_prolog_graph_desc_t* desc) {
+    return mla_prolog_graphs_update_layers(g, desc, 1);
+}
+
+int32_t mla_prolog_graphs_layers(const mla_prolog_graphs* g) {
+    return g == nullptr ? 0 : (int32_t)g->layers.size();
 }
 
 int64_t mla_prolog_graphs_bucket(const mla_prolog_graphs* g, int64_t T) {

@@ -419,3 +419,29 @@ def test_noalloc_rejects_token_counts_beyond_its_array():
     p = [FAKE] * 9
     p[0] = None
     assert call_noalloc(T=fits, ptrs=p) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_multi_layer_graph_set_argument_errors():
+    L = mla.lib()
+    bad = mla.MLA_ERR_INVALID_ARG
+
+    def create_layers(descs, buckets=(1, 64)):
+        out = ctypes.c_void_p(None)
+        arr = (mla.mla_prolog_graph_desc_t * max(1, len(descs)))(*descs)
+        b = (ctypes.c_int64 * len(buckets))(*buckets)
+        st = L.mla_prolog_graphs_create_layers(arr if descs else None, len(descs), b,
+                                               len(buckets), ctypes.byref(out))
+        return st, out.value
+
+    assert create_layers([]) == (bad, None)
+    assert create_layers([graph_desc()] * 257) == (bad, None)
+    # the layers must record the same kind of call
+    assert create_layers([graph_desc(), graph_desc(d=Dims(H=1024, nh=16).c())])[0] == bad
+    assert create_layers([graph_desc(), graph_desc(dt=2)])[0] == bad
+    assert create_layers([graph_desc(), graph_desc(w8a8=1, s_kv_a=FAKE, s_kv_b=FAKE)])[0] == bad
+    # every layer's checks run before any capture
+    assert create_layers([graph_desc(), graph_desc(hidden=None)])[0] == bad
+    assert create_layers([graph_desc(), graph_desc(k_pe=FAKE + 8)])[0] == mla.MLA_ERR_MISALIGNED
+    assert L.mla_prolog_graphs_layers(None) == 0
+    arr = (mla.mla_prolog_graph_desc_t * 2)(graph_desc(), graph_desc())
+    assert L.mla_prolog_graphs_update_layers(None, arr, 2) == bad

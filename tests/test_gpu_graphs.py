@@ -232,3 +232,59 @@ def test_graphs_launch_errors(dev):
         g.update((t["Wa"], t["gamma"][:256].contiguous(), t["Wb"]))
     g.close()
     g.close()
+
+
+def test_graphs_multi_layer(dev):
+    """One set over three layers, each with its own weights and cache: one
+    launch replays all three prologs in layer order.  Every layer's outputs
+    equal a direct call of that layer, bit for bit, and the oracle within
+    tolerance; its cache rows hold its own returned rows.  Then the set is
+    rebound to the layers in reverse order and checked again; every graph is
+    replayed several times with eager work in between."""
+    import mla_attention_kv_amd as mla
+
+    L = 3
+    ws = [workloads.make_custom(V2LITE, 64, dtype="f16", seed=1400 + i) for i in range(L)]
+    ts = [upload(w, dev) for w in ws]
+    # one shared hidden / positions input (the set's static rows): every
+    # layer reads layer 0's token rows
+    refs = [run_oracle(dataclasses_replace(ws[l], X=ws[0].X, positions=ws[0].positions))
+            for l in range(L)]
+    caches = [torch.full((64, 576), FILL, dtype=torch.float16, device=dev) for _ in range(L)]
+    weights = [(t["Wa"], t["gamma"], t["Wb"]) for t in ts]
+    g = mla.PrologGraphs(weights, (4, 16, 64), ws[0].eps, ws[0].theta, cache=caches)
+    assert mla.lib().mla_prolog_graphs_layers(g.handle) == L
+    assert tuple(g.k_nope.shape) == (L, 64, 16, 128)
+    order = list(range(L))
+    for step, T in enumerate((5, 64, 16, 64)):
+        if step == 2:
+            order = order[::-1]
+            g.update([weights[l] for l in order], cache=[caches[l] for l in order])
+        print(f"[graphs] {L} layers step={step} T={T} order={order}", flush=True)
+        g.hidden[:T] = ts[0]["X"][:T]
+        g.positions[:T] = ts[0]["pos"][:T]
+        g.slot_mapping[:T] = torch.arange(T, device=dev)
+        g.slot_mapping[T:] = -1
+        for rep in range(2):
+            b = g.run(T)
+            torch.cuda.synchronize()
+            for i, l in enumerate(order):
+                t = ts[l]
+                d = mla.mla_kv_prolog(g.hidden[:b].clone(), t["Wa"], t["gamma"], t["Wb"],
+                                      g.positions[:b].clone(), ws[l].eps, ws[l].theta)
+                torch.cuda.synchronize()
+                mine = (g.k_nope[i, :b], g.value[i, :b], g.k_pe[i, :b], g.compressed_kv[i, :b])
+                for x, y in zip(mine, d):
+                    assert torch.equal(bits(x), bits(y)), f"layer {l} T={T}"
+                compare(gpu_rows(tuple(m[:T] for m in mine)), head(refs[l], T),
+                        f"layer {l} T{T}")
+                row = torch.cat([g.compressed_kv[i, :T], g.k_pe[i, :T]], dim=1)
+                assert torch.equal(bits(caches[l][:T]), bits(row))
+            eager_noise(dev)
+    g.close()
+
+
+def dataclasses_replace(w, **kw):
+    import dataclasses
+
+    return dataclasses.replace(w, **kw)
