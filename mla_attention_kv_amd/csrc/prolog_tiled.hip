@@ -155,15 +155,25 @@ struct EpiKvW8 {
     static constexpr bool kDbg = true;
     static constexpr bool kScaleDma = true;
     // 16-byte source of lane group q (16 lanes, 64 values) for rows m.. and
-    // columns n..: column scales (q = 0, and 3 as filler), activation scales
-    // (q = 1), RMS factors (q = 2).  The two row arrays are padded to whole
+    // columns n.. of a wave tile WN columns wide.  WN = 64: column scales
+    // (q = 0, and 3 as filler), activation scales (q = 1), RMS factors
+    // (q = 2).  WN = 128: column scales (q = 0, 1), activation scales
+    // (q = 2), RMS factors (q = 3).  The two row arrays are padded to whole
     // 256-row tiles.
+    template <int WN>
     __device__ __forceinline__ const void* scale_src(int q, int m, int n) const {
-        // three addresses first, then a per-lane choice of value (a choice of
+        // the addresses first, then a per-lane choice of value (a choice of
         // member would make the compiler load the pointer per lane)
         const uintptr_t a = (uintptr_t)(sz + m), b = (uintptr_t)(inv_t + m), c = (uintptr_t)(swb + n);
-        const uintptr_t r = q == 1 ? a : c;
-        return (const void*)(q == 2 ? b : r);
+        if constexpr (WN == 128) {
+            const uintptr_t c1 = (uintptr_t)(swb + n + 64);
+            const uintptr_t r = q == 1 ? c1 : c;
+            const uintptr_t t = q == 2 ? a : r;
+            return (const void*)(q == 3 ? b : t);
+        } else {
+            const uintptr_t r = q == 1 ? a : c;
+            return (const void*)(q == 2 ? b : r);
+        }
     }
     __device__ __forceinline__ row_t row_scale2(float s, float i) const { return s * i; }
     uint16_t* k_nope;
@@ -559,11 +569,13 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP),
     constexpr int PW = A_PW + B_PW;           // copy instructions per copy wave per slab
     static_assert(STAGES >= 2 && (STAGES - 2) * PW < 64, "stages / vmcnt range");
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, TM = WM / 16, TN = WN / 16;
-    // 2-byte results are staged per wave (16 rows x 128 bytes) so that every
-    // store writes whole 128-byte lines
+    // 2-byte results are staged per wave (16 rows of the wave's WN columns:
+    // 128 or 256 bytes) so that every store writes whole 128-byte lines
     constexpr bool STAGE_OUT = sizeof(typename Epi::out_t) == 2;
-    static_assert(!STAGE_OUT || WN * 2 == 128, "one 128-byte row segment per wave");
-    constexpr int OUT_ST = STAGE_OUT ? NC * 2048 : 0;
+    static_assert(!STAGE_OUT || WN == 64 || WN == 128, "128- or 256-byte wave rows");
+    constexpr int RP = WN * 2;                    // staged row pitch (bytes)
+    constexpr int AREA = 16 * RP;                 // a wave's staging area
+    constexpr int OUT_ST = STAGE_OUT ? NC * AREA : 0;
     __shared__ __align__(1024) uint8_t smem[STAGES * STAGE + OUT_ST];
 
     // ---- work items: (tile, K split) pairs, split-major, so that an XCD's
@@ -632,10 +644,10 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP),
 #pragma unroll
                     for (int w = p; w < NC; w += NP) {
                         const int r4 = (lane & 15) * 4;
-                        dma16(epi.scale_src(lane >> 4, tm0 + (w / WAVES_N) * WM + r4,
-                                            tn0 + (w % WAVES_N) * WN + r4),
+                        dma16(epi.template scale_src<WN>(lane >> 4, tm0 + (w / WAVES_N) * WM + r4,
+                                                         tn0 + (w % WAVES_N) * WN + r4),
                               lds_addr(smem + STAGES * STAGE) +
-                                  (uint32_t)__builtin_amdgcn_readfirstlane(w * 2048));
+                                  (uint32_t)__builtin_amdgcn_readfirstlane(w * AREA));
                     }
                 }
             }
@@ -756,7 +768,8 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP),
         if constexpr (STAGE_OUT && Epi::kScaleDma) {
             // the copy waves brought this tile's scales into the staging
             // area (landed before the barrier this epilogue follows)
-            const uint8_t* sa = smem + STAGES * STAGE + wave * 2048;
+            // column scales first (WN floats), then the two row arrays
+            const uint8_t* sa = smem + STAGES * STAGE + wave * AREA;
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const f4_t c = *(const f4_t*)(sa + 64 * j + 16 * g);
@@ -765,8 +778,8 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP),
             }
 #pragma unroll
             for (int i = 0; i < TM; ++i)
-                rsv[i] = epi.row_scale2(((const float*)(sa + 256))[i * 16 + l16],
-                                        ((const float*)(sa + 512))[i * 16 + l16]);
+                rsv[i] = epi.row_scale2(((const float*)(sa + 4 * WN))[i * 16 + l16],
+                                        ((const float*)(sa + 4 * WN + 256))[i * 16 + l16]);
         } else {
 #pragma unroll
             for (int j = 0; j < TN; ++j)
@@ -791,12 +804,14 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP),
                 }
             }
             // per row of MFMA tiles: the lanes' 8-byte pieces go to this
-            // wave's 16 x 128-byte LDS area (16-byte chunk c of row r at
-            // c ^ (r & 7)), then come back as whole rows: lane l reads chunk
-            // l % 8 of rows l / 8 and l / 8 + 8 and stores 16 bytes each, so
-            // one store covers 8 full 128-byte lines.  LDS accesses of one
-            // wave complete in order, so the area is reused without waits.
-            uint8_t* ep = smem + STAGES * STAGE + wave * 2048;
+            // wave's 16-row LDS area (RP bytes a row; 16-byte chunk c of row
+            // r at c ^ (r & 7)), then come back as whole rows: lane l reads
+            // chunk l % CPR of rows l / CPR + (64 / CPR) h (CPR = chunks a
+            // row) and stores 16 bytes each, so one store covers whole
+            // 128-byte lines.  LDS accesses of one wave complete in order, so
+            // the area is reused without waits.
+            constexpr int CPR = RP / 16;
+            uint8_t* ep = smem + STAGES * STAGE + wave * AREA;
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -805,17 +820,17 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP),
 #pragma unroll
                     for (int v = 0; v < 4; ++v) f[v] = epi.valuef(acc[i][j][v], rsv[i], cs[j][v]);
                     const int ch = (2 * j + (g >> 1)) ^ (l16 & 7);
-                    *(u2_t*)(ep + l16 * 128 + ch * 16 + (g & 1) * 8) =
+                    *(u2_t*)(ep + l16 * RP + ch * 16 + (g & 1) * 8) =
                         u2_t{cvt_pk<Epi::kOut>(f[0], f[1]), cvt_pk<Epi::kOut>(f[2], f[3])};
                 }
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int r = (lane >> 3) + 8 * h;
-                    const u4_t v = *(const u4_t*)(ep + r * 128 + (((lane & 7) ^ (r & 7)) << 4));
+                for (int h = 0; h < CPR / 4; ++h) {
+                    const int r = lane / CPR + (64 / CPR) * h, c = lane % CPR;
+                    const u4_t v = *(const u4_t*)(ep + r * RP + ((c ^ (r & 7)) << 4));
                     const int grow = m0 + wm0 + i * 16 + r;
                     // written once, never re-read here: streaming stores
                     if (grow < M)
-                        __builtin_nontemporal_store(v, (u4_t*)epi.ptr(grow, n0 + wn0 + (lane & 7) * 8, sk));
+                        __builtin_nontemporal_store(v, (u4_t*)epi.ptr(grow, n0 + wn0 + c * 8, sk));
                 }
             }
         } else {
