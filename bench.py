@@ -94,9 +94,10 @@ def kernel_source_hash(files=None) -> str:
 
 
 def load_traffic(workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, or None
-    when they are absent or any source file of the kernels they measured
-    (listed in the file as "sources") has changed since."""
+    """HBM bytes per call and per kernel (launch order) from committed
+    rocprofv3 counter runs, or None when they are absent or any source file
+    of the kernels they measured (listed in the file as "sources") has
+    changed since."""
     p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(p):
         return None
@@ -104,7 +105,7 @@ def load_traffic(workload: str):
         t = json.load(f)
     if t.get("src_hash") != kernel_source_hash(t.get("sources")):
         return None
-    return t.get("hbm_bytes_per_launch")
+    return {"call": t.get("hbm_bytes_per_launch"), "kernels": t.get("kernel_hbm_bytes")}
 
 
 class Sets:
@@ -674,6 +675,68 @@ def main_cache(args, cfg, w, dev):
     print(json.dumps(out), flush=True)
 
 
+def kernel_parts(w, path, n_kernels):
+    """Names and algorithmic (bytes, operations) of the kernels one call
+    launches, in launch order: what each kernel must read and write at least
+    once as a stand-alone step (its inputs and its result; the kv_a_proj
+    result counted once in fp32, [T, 576]) and the multiply-adds it does
+    (2 operations each)."""
+    d, T = w.dims, w.T
+    D = 2
+    fp = w.kind == "fp"
+    wa = d.H * d.N1 * (D if fp else 1) + (0 if fp else 4 * d.N1)
+    wb = d.r * d.N2 * (D if fp else 1) + (0 if fp else 4 * d.N2)
+    xin = T * d.H * D + 4 * T
+    a_out = T * d.N1 * 4
+    fin_out = T * (d.r + d.dr) * D + (0 if fp else T * (d.r + 8))
+    kv_out = T * d.N2 * D
+    lat_in = T * d.r * (D if fp else 1) + (0 if fp else 8 * T)
+    f1, f2 = 2 * T * d.H * d.N1, 2 * T * d.r * d.N2
+    kv_a = ("kv_a_proj GEMM", (T * d.H * (D if fp else 1) + wa + a_out, f1))
+    finish = ("finish (split, RMSNorm, RoPE)", (a_out + d.r * D + 4 * T + fin_out, 0))
+    kv_b = ("kv_b_proj GEMM", (lat_in + wb + kv_out, f2))
+    if not fp:
+        quant = ("activation quantiser", (xin + T * d.H + 4 * T, 0))
+        return [quant, kv_a, finish, kv_b]
+    if path == 0 and n_kernels == 2:
+        return [("dec_kv_a (kv_a_proj, split-K)", (xin + wa + a_out, f1)),
+                ("dec_fin_kv_b (finish fused into kv_b_proj)",
+                 (a_out + d.r * D + 4 * T + fin_out + wb + kv_out, f2))]
+    if path == 0:
+        return [("dec_kv_a (kv_a_proj, split-K)", (xin + wa + a_out, f1)),
+                ("dec_finish", finish[1]), ("dec_kv_b", kv_b[1])]
+    return [kv_a, finish, kv_b]
+
+
+def kernel_times(sets, reps, dev):
+    """Average duration of each kernel of a call, live: events registered
+    with the library (mla_debug_set_launch_events) are recorded on the
+    call's stream right after each kernel it launches, one more before the
+    call; eager calls rotating over the input sets."""
+    import torch
+
+    L = sets.mla.lib()
+    sp = torch.cuda.current_stream(dev).cuda_stream
+    maxk = 8
+    sums, used = None, 0
+    for i in range(reps + 3):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(maxk + 1)]
+        for e in evs:
+            e.record()
+        torch.cuda.synchronize()
+        arr = (ctypes.c_void_p * maxk)(*[e.cuda_event for e in evs[1:]])
+        L.mla_debug_set_launch_events(arr, maxk)
+        evs[0].record()
+        sets.call(i, sp)
+        used = L.mla_debug_set_launch_events(None, 0)
+        torch.cuda.synchronize()
+        ms = [evs[k].elapsed_time(evs[k + 1]) for k in range(used)]
+        if i < 3:
+            continue  # warm-up calls
+        sums = ms if sums is None else [a + x for a, x in zip(sums, ms)]
+    return [s / reps * 1e3 for s in sums]  # microseconds
+
+
 def roofline(w, step_s, alg_bytes, alg_flops):
     """Roofline of one call: the binding roof is HBM when the algorithmic
     arithmetic intensity is below the ridge point of the workload's MFMA
@@ -764,12 +827,34 @@ def measure_prolog(idx, steps, warmup, dev, args, cache_mode=None, graph_buckets
     log(f"{cfg['name']}: {ms_per_step * 1e3:.2f} us/step, {value:.4g} tokens/s "
         f"(eager {eager_ms / steps * 1e3:.2f} us/step)")
     path = mla.mla_kv_prolog_selected_path(w.T, sets.dims)
-    roof = roofline(w, ms_per_step / 1e3, alg_bytes, alg_flops)
+    call_roof = roofline(w, ms_per_step / 1e3, alg_bytes, alg_flops)
     traffic = (load_traffic(cfg["name"]) if cache_mode is None and buckets is None else None)
-    roof["traffic"] = traffic
-    roof["traffic_source"] = (f"profiles/traffic_{cfg['name']}.json (rocprofv3 FETCH_SIZE / "
-                              "WRITE_SIZE of the same kernel sources)" if traffic else None)
-    roof["kernel"] = kernel_names(w, path, cache_mode)
+    call_roof["traffic"] = traffic["call"] if traffic else None
+    call_roof["traffic_source"] = (f"profiles/traffic_{cfg['name']}.json (rocprofv3 FETCH_SIZE / "
+                                   "WRITE_SIZE of the same kernel sources)" if traffic else None)
+    call_roof["kernel"] = kernel_names(w, path, cache_mode)
+    # the dominant kernel, timed live per kernel (eager calls)
+    kus = (kernel_times(sets, max(10, min(200, int(2e4 / max(ms_per_step * 1e3, 1.0)))), dev)
+           if cache_mode is None and buckets is None else [])
+    parts = kernel_parts(w, path, len(kus))
+    kernels = []
+    for k, ((name, (kb, kf)), us) in enumerate(zip(parts, kus)):
+        r = roofline(w, us * 1e-6, kb, max(kf, 1))
+        kernels.append({"kernel": name, "avg_us": us, "algorithmic_bytes": kb,
+                        "algorithmic_ops": kf, "hbm_frac": r["hbm_frac"],
+                        "mfma_frac": r["mfma_frac"] if kf else 0.0})
+    dom = max(range(len(kus)), key=lambda k: kus[k]) if kus else None
+    if dom is not None:
+        name, (kb, kf) = parts[dom]
+        roof = roofline(w, kus[dom] * 1e-6, kb, max(kf, 1))
+        roof["kernel"] = f"{name}: the call's longest kernel ({kus[dom]:.2f} us of " \
+                         f"{sum(kus):.2f} us of kernel time; live HIP events, eager calls)"
+        per_k = traffic.get("kernels") if traffic else None
+        roof["traffic"] = per_k[dom] if per_k and dom < len(per_k) else None
+        roof["traffic_source"] = call_roof["traffic_source"] if roof["traffic"] else None
+        roof["call"] = call_roof
+    else:
+        roof = call_roof
     timing = ("one mla_prolog_graphs_launch per step (buckets "
               f"{list(buckets.buckets)})" if buckets is not None
               else "eager calls" if args.eager else "HIP graph replays")
@@ -781,7 +866,7 @@ def measure_prolog(idx, steps, warmup, dev, args, cache_mode=None, graph_buckets
            "rotated_sets": n_sets, "steps": steps, "us_per_step": ms_per_step * 1e3,
            "tokens_per_s": value, "eager_us_per_step": eager_ms / steps * 1e3,
            "algorithmic_bytes_per_step": alg_bytes, "algorithmic_flops_per_step": alg_flops,
-           "roofline": roof}
+           "kernels": kernels, "roofline": roof}
     del sets, buckets
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -866,7 +951,7 @@ def main():
             side[r["workload"]] = {k: r[k] for k in (
                 "T", "dtype", "kernel_family", "us_per_step", "tokens_per_s", "steps",
                 "rotated_sets", "algorithmic_bytes_per_step", "algorithmic_flops_per_step",
-                "roofline")}
+                "kernels", "roofline")}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -877,7 +962,7 @@ def main():
     config = {k: res[k] for k in ("workload", "T", "H", "kv_lora_rank", "rope_dim", "heads",
                                   "dn", "dv", "kernel_family", "timing", "rotated_sets",
                                   "eager_us_per_step", "algorithmic_bytes_per_step",
-                                  "algorithmic_flops_per_step")}
+                                  "algorithmic_flops_per_step", "kernels")}
     if side:
         config["configs"] = side
     out = {

@@ -415,6 +415,19 @@ mla_status_t mla_kv_prolog_noalloc(const void* hidden, const void* W_kv_a, const
                                    void* k_nope, void* value, void* k_pe, void* compressed_kv,
                                    void* stream);
 
+/* Benchmark hook: per-kernel timing.  Registers, for the calling host
+ * thread, n events (hipEvent_t handles created and owned by the caller; the
+ * array is read at each launch, so it must stay valid until it is
+ * unregistered; NULL or n <= 0 unregisters).  Every later prolog call on
+ * this thread
+ * (mla_kv_prolog* entry points) then records the next registered event on
+ * its stream right after each kernel it launches, until the n events are
+ * used up; with an event recorded before the call, the elapsed times between
+ * consecutive events are the kernels' durations in launch order.  Returns
+ * how many events the previous registration had recorded.  Recording into a
+ * stream that is being captured adds the records to the graph. */
+int32_t mla_debug_set_launch_events(void* const* events, int32_t n);
+
 /* Test hooks for the decode family's one-launch finish + kv_b_proj (taken
  * when the device holds that launch's whole grid at once).  Its workgroups
  * wait, with a bounded number of polls, for latent rows that other

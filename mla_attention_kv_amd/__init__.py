@@ -43,6 +43,7 @@ EXPORTS = (
     "mla_rms_norm",
     "mla_rope",
     "mla_kv_prolog_noalloc",
+    "mla_debug_set_launch_events",
     "mla_debug_set_handoff_spin",
     "mla_debug_handoff_fallbacks",
     "mla_prolog_graphs_create",
@@ -168,6 +169,8 @@ def lib() -> ctypes.CDLL:
     L.mla_kv_prolog_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, mla_dims_t, i32, f32, f32,
                                         vp, vp, vp, vp, vp]
     L.mla_kv_prolog_noalloc.restype = i32
+    L.mla_debug_set_launch_events.argtypes = [vp, i32]
+    L.mla_debug_set_launch_events.restype = i32
     L.mla_debug_set_handoff_spin.argtypes = [i64]
     L.mla_debug_set_handoff_spin.restype = i64
     L.mla_debug_handoff_fallbacks.argtypes = [i32]

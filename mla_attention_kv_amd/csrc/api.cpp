@@ -144,7 +144,20 @@ size_t ws_w8_max(int64_t T, const mla_dims_t& d) {
 
 }  // namespace
 
+namespace {
+// events registered by mla_debug_set_launch_events on this host thread
+struct LaunchEvents {
+    void* const* ev = nullptr;
+    int32_t n = 0, used = 0;
+};
+thread_local LaunchEvents t_events;
+}  // namespace
+
 namespace mla {
+void launch_mark(hipStream_t st) {
+    LaunchEvents& e = t_events;
+    if (e.ev != nullptr && e.used < e.n) (void)hipEventRecord((hipEvent_t)e.ev[e.used++], st);
+}
 bool validate_only() { return t_validate_only > 0; }
 ValidateOnlyScope::ValidateOnlyScope() { ++t_validate_only; }
 ValidateOnlyScope::~ValidateOnlyScope() { --t_validate_only; }
@@ -168,6 +181,14 @@ int mla_kv_prolog_selected_path(int64_t T, mla_dims_t) { return select_path(T); 
 int mla_kv_prolog_force_path(int path) {
     if (path != 0 && path != 1) path = -1;
     return g_force_path.exchange(path);
+}
+
+int32_t mla_debug_set_launch_events(void* const* events, int32_t n) {
+    const int32_t used = t_events.used;
+    t_events.ev = (events != nullptr && n > 0) ? events : nullptr;
+    t_events.n = t_events.ev != nullptr ? n : 0;
+    t_events.used = 0;
+    return used;
 }
 
 int64_t mla_debug_set_handoff_spin(int64_t limit) { return decode_set_spin_limit(limit); }

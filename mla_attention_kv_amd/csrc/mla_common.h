@@ -288,6 +288,11 @@ hipError_t launch_kv_cache_append(int dt, const void* ckv, const void* kpe, cons
 int64_t decode_set_spin_limit(int64_t limit);
 int64_t decode_handoff_fallbacks(bool reset);
 
+// After each kernel a prolog call launches: records the next of the events
+// the calling thread registered (mla_debug_set_launch_events) on st, if any
+// are left; nothing otherwise.
+void launch_mark(hipStream_t st);
+
 // While a ValidateOnlyScope is alive on the calling thread, the prolog
 // entry points run every argument check and return without launching (the
 // captured-graph sets use it to reject bad arguments before capturing).

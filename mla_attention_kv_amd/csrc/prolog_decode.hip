@@ -621,6 +621,7 @@ static void dec_launch_t(const void* X, const void* Wa, const void* gamma, const
         case 3: dec_kv_a_launch<E, 3>(X, Wa, T, H, P, plan.kw, plan.s1, y, ng, st); break;
         default: dec_kv_a_launch<E, 4>(X, Wa, T, H, P, plan.kw, plan.s1, y, ng, st); break;
     }
+    launch_mark(st);
     if (fused) {
         const int64_t sl = g_spin_limit.load(std::memory_order_relaxed);
         const uint32_t spin = sl < 0 ? kSpinDefault : (uint32_t)(sl > 0xFFFFFFFFll ? 0xFFFFFFFFll : sl);
@@ -628,13 +629,16 @@ static void dec_launch_t(const void* X, const void* Wa, const void* gamma, const
                            (const float*)P, plan.s1, T, (const uint16_t*)gamma, pos, eps, rt,
                            (const uint16_t*)Wb, N2, (uint16_t*)ckv, (uint16_t*)k_pe,
                            (uint16_t*)k_nope, (uint16_t*)value, co, spin);
+        launch_mark(st);
         return;
     }
     hipLaunchKernelGGL(dec_finish_kernel<E>, dim3(T), dim3(256), 0, st, (const float*)P, plan.s1,
                        T, (const uint16_t*)gamma, pos, eps, rt, (uint16_t*)ckv, (uint16_t*)k_pe, co);
+    launch_mark(st);
     hipLaunchKernelGGL((dec_kv_b_kernel<E, 1>), dim3(grid8(nitems)), dim3(256), 0, st,
                        (const uint16_t*)ckv, (const uint16_t*)Wb, T, N2, (uint16_t*)k_nope,
                        (uint16_t*)value);
+    launch_mark(st);
 }
 
 hipError_t launch_fp_decode(int dt, const void* X, const void* Wa, const void* gamma,

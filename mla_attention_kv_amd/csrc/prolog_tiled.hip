@@ -907,6 +907,260 @@ __global__ __launch_bounds__(64 * (WAVES_M * WAVES_N + NP),
 }
 
 // ---------------------------------------------------------------------------
+// W8A8 kv_b_proj, weight-stationary.  A workgroup owns the 256 output
+// columns of one head (k_nope then value) and runs eight waves, two per
+// SIMD: wave w owns the 64 columns 64 (w % 4) .. and holds their int8
+// weights over all 512 latent dimensions in registers for the whole launch
+// (the MFMA operand fragments, read once through LDS with transposing
+// reads); the two waves of a column quarter split each block of 32 latent
+// rows into two halves of 16.  The workgroup streams its range of latent
+// rows, 32 at a time, through a ring of LDS stages that all eight waves fill
+// with direct global-to-LDS copies.  The results of block b are scaled,
+// rounded and stored while block b + 1's MFMAs run (two accumulator sets),
+// and the two waves of a SIMD overlap one's MFMAs with the other's vector
+// work.  Each 16-byte store carries 8 consecutive columns of a row: lanes
+// of neighbouring 16-lane rows swap packed pairs (v_permlane16_swap), so the
+// results need no LDS staging.
+// Work items are (row range, head) pairs: the row ranges split T so that
+// the items fill the device, and the workgroups of one XCD share a row
+// range, so the latent rows they read together stay in that XCD's L2.
+// ---------------------------------------------------------------------------
+namespace ws {
+constexpr int kRows = 32;                   // latent rows per block
+constexpr int kWaves = 8;
+constexpr int kStages = 8;                  // ring stages
+constexpr int kScaleOfs = kRows * kR;       // row scales after the codes
+constexpr int kStageBytes = 17 * 1024;      // 16 KB of codes + 256 B of scales
+constexpr int kSmem = kStages * kStageBytes;
+constexpr int kCopies = kRows * kR / 1024 / kWaves;  // 16-byte copies per wave and block
+static_assert(kSmem >= kR * 256, "the weight staging fits in the ring");
+static_assert(kScaleOfs + 256 <= kStageBytes, "stage layout");
+static_assert(kCopies * kWaves * 1024 == kRows * kR, "even copy split");
+}  // namespace ws
+
+// One 4-byte-per-lane copy from global memory into LDS (the wave's 64
+// lanes fill lds .. lds + 255), as dma16.
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %2, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "s"(lds), "v"(g)
+        : "memory");
+}
+// Wait until at most N of this wave's vector-memory operations (copies and
+// stores, which complete in issue order) are outstanding and its LDS reads
+// are complete, then barrier.
+template <int N>
+__device__ __forceinline__ void wait_vm_lds_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <bool DBG>
+__global__ __launch_bounds__(ws::kWaves * 64, 1) void kvb_w8_ws_kernel(
+    const int8_t* __restrict__ QZ, const float* __restrict__ sz, const float* __restrict__ inv,
+    const int8_t* __restrict__ Wqb, const float* __restrict__ swb, int T, int nh, int msplit,
+    int bps, uint16_t* __restrict__ k_nope, uint16_t* __restrict__ value_out,
+    int32_t* __restrict__ dbg, int64_t dbg_begin, int64_t dbg_rows) {
+    using namespace ws;
+    constexpr int BRB = 256;  // bytes of a staged weight row (the head's columns)
+    constexpr int NT = kWaves * 64;
+    __shared__ __align__(1024) uint8_t smem[kSmem];
+    const int items = nh * msplit, per = (items + 7) / 8;
+    const int xk = (int)(blockIdx.x >> 3), item = (int)(blockIdx.x & 7) * per + xk;
+    if (xk >= per || item >= items) return;
+    const int ms = item / nh, head = item - ms * nh;
+    const int nblk = (T + kRows - 1) / kRows, bfirst = ms * bps;
+    const int nb = min(bps, nblk - bfirst);
+    if (nb <= 0) return;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int cq = wave & 3, rh = wave >> 2;  // column quarter, row half
+    const int l16 = lane & 15, g = lane >> 4;
+    const int64_t N2 = (int64_t)nh * kHeadW;
+    const int col0 = head * kHeadW, wn0 = cq * 64;
+
+    // ---- the head's weights: row k of its 256 columns at LDS row brow(k),
+    // 16-byte chunk c at c ^ bswz(k); then each wave's operand fragments
+#pragma unroll 8
+    for (int it = 0; it < kR * BRB / 16 / NT; ++it) {
+        const int q = it * NT + tid, k = q >> 4, c = q & 15;
+        const u4_t v = *(const u4_t*)(Wqb + k * N2 + col0 + c * 16);
+        *(u4_t*)(smem + brow<kI8, BRB>(k) * BRB + ((c ^ bswz<kI8, BRB>(k)) << 4)) = v;
+    }
+    __syncthreads();
+    // fragment (ks, j): lane (16 g + s) receives column wn0 + 16 j + s, rows
+    // 64 ks + 16 g .. + 15 (two transposing reads of 8 rows)
+    u4_t fb[8][4];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int k = ks * 64 + g * 16 + (l16 >> 1);
+            const int colb = wn0 + j * 16 + 8 * (l16 & 1);
+            const int c = colb >> 4, off = colb & 15;
+            const uint2 lo = lds_tr8(smem + brow<kI8, BRB>(k) * BRB +
+                                     ((c ^ bswz<kI8, BRB>(k)) << 4) + off);
+            const uint2 hi = lds_tr8(smem + brow<kI8, BRB>(k + 8) * BRB +
+                                     ((c ^ bswz<kI8, BRB>(k + 8)) << 4) + off);
+            fb[ks][j] = u4_t{lo.x, lo.y, hi.x, hi.y};
+        }
+    }
+    // column scales of the lane's columns wn0 + 16 j + 4 g + v
+    float cs[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const f4_t c = *(const f4_t*)(swb + col0 + wn0 + j * 16 + g * 4);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) cs[j][v] = c[v];
+    }
+    // every load above complete and every fragment read before the ring
+    // reuses the staging memory
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // ---- ring.  Block bb (rows m_first + 32 bb ..) goes to stage
+    // bb % kStages: wave w copies rows 4 w .. 4 w + 3 (two rows of 512 bytes
+    // per instruction; chunk p of LDS row r holds chunk p ^ (r & 15)), wave
+    // 0 also the rows' two scale arrays.  Copies past the last block repeat
+    // it, so every wait below has the same number of later operations.
+    const int m_first = bfirst * kRows;
+    const uint32_t sbase =
+        lds_addr(smem) + (uint32_t)__builtin_amdgcn_readfirstlane(wave * kCopies * 1024);
+    const uint32_t scl = lds_addr(smem) + kScaleOfs;
+    auto issue = [&](int bb) {
+        const int m0 = m_first + min(bb, nb - 1) * kRows;
+        const uint32_t so = (uint32_t)((bb % kStages) * kStageBytes);
+#pragma unroll
+        for (int q = 0; q < kCopies; ++q) {
+            const int r = (wave * kCopies + q) * 2 + (lane >> 5), p = lane & 31;
+            dma16(QZ + (int64_t)min(m0 + r, T - 1) * kR + ((p ^ (r & 15)) << 4),
+                  sbase + so + q * 1024);
+        }
+        if (wave == 0) dma4(lane < 32 ? sz + m0 + lane : inv + m0 + (lane - 32), scl + so);
+    };
+    // stage b in place and the stage of block b - 1 free.  After block b's
+    // copies this wave issued kStages - 2 later groups of copies (kCopies,
+    // wave 0 one more instruction) and, from block kStages on, kStages - 1
+    // groups of 2 stores; before that it counts the copies only (it waits
+    // for more).
+    auto wait_stage = [&](int b) {
+        constexpr int D = kStages, C = kCopies;
+        if (b < D) {
+            if (wave == 0) wait_vm_lds_barrier<(C + 1) * (D - 2)>();
+            else wait_vm_lds_barrier<C * (D - 2)>();
+        } else {
+            if (wave == 0) wait_vm_lds_barrier<(C + 1) * (D - 2) + 2 * (D - 1)>();
+            else wait_vm_lds_barrier<C * (D - 2) + 2 * (D - 1)>();
+        }
+    };
+    typedef i4_t acc_t;
+    // MFMAs of the wave's 16 rows of block b (operands swapped, C^T = B^T
+    // A^T: lane l then holds row l % 16 and columns 4 (l / 16) .. + 3 of
+    // each 16-column tile).  The A fragment of K step ks + 2 is read while
+    // step ks multiplies.
+    const int arow = (rh * 16 + l16) * kR;
+    auto mma_block = [&](acc_t(&acc)[4], int b) {
+        const uint8_t* s = smem + (b % kStages) * kStageBytes + arow;
+        u4_t fa[3];
+        auto rd = [&](int ks) { fa[ks % 3] = *(const u4_t*)(s + (((ks * 4 + g) ^ l16) << 4)); };
+        rd(0);
+        rd(1);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            if (ks + 2 < 8) rd(ks + 2);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[j] = mfma16<kI8>(fb[ks][j], fa[ks % 3], ks == 0 ? acc_t{0, 0, 0, 0} : acc[j]);
+        }
+    };
+    // the factor (activation scale times RMS factor) of the lane's row of
+    // block b
+    auto read_rs = [&](int b) {
+        const float* s = (const float*)(smem + (b % kStages) * kStageBytes + kScaleOfs);
+        return s[rh * 16 + l16] * s[32 + rh * 16 + l16];
+    };
+    uint16_t* const dst0 = (cq < 2 ? k_nope : value_out) + (int64_t)head * kDN + (cq & 1) * 64;
+    const int64_t rstride = (int64_t)nh * kDN;
+    // results of block b: ((acc * row factor) * column scale) rounded to
+    // bf16; lanes of even 16-lane rows end with 8 columns of tile 2p, odd
+    // ones with 8 columns of tile 2p + 1.  GUARD: rows past T are skipped
+    // (only the last block has any).
+    auto epi_block = [&](const acc_t(&acc)[4], float rs, int b, auto guard) {
+        const int row = m_first + b * kRows + rh * 16 + l16;
+        uint32_t P[4][2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float f[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) f[v] = ((float)acc[j][v] * rs) * cs[j][v];
+            P[j][0] = cvt_pk<kBF16>(f[0], f[1]);
+            P[j][1] = cvt_pk<kBF16>(f[2], f[3]);
+        }
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const auto s0 = __builtin_amdgcn_permlane16_swap(P[2 * p][0], P[2 * p + 1][0], false, false);
+            const auto s1 = __builtin_amdgcn_permlane16_swap(P[2 * p][1], P[2 * p + 1][1], false, false);
+            const u4_t v = u4_t{s0[0], s1[0], s0[1], s1[1]};
+            const int col = 32 * p + ((g & 1) ? 16 + 4 * (g - 1) : 4 * g);
+            uint16_t* d = dst0 + row * rstride + col;
+            if constexpr (decltype(guard)::value) {
+                if (row < T) __builtin_nontemporal_store(v, (u4_t*)d);
+            } else {
+                __builtin_nontemporal_store(v, (u4_t*)d);
+            }
+        }
+        if constexpr (DBG) {
+            if (row < T && row >= dbg_begin && row < dbg_begin + dbg_rows) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        dbg[(row - dbg_begin) * N2 + col0 + wn0 + j * 16 + g * 4 + v] = acc[j][v];
+            }
+        }
+    };
+    typedef std::integral_constant<bool, false> NoGuard;
+    typedef std::integral_constant<bool, true> Guard;
+
+    acc_t accA[4], accB[4];
+    float rsA, rsB;
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s) issue(s);
+    wait_stage(0);
+    issue(kStages - 1);
+    rsA = read_rs(0);
+    mma_block(accA, 0);
+    int b = 1;
+    for (; b + 1 < nb; b += 2) {
+        wait_stage(b);
+        issue(b + kStages - 1);
+        rsB = read_rs(b);
+        mma_block(accB, b);
+        epi_block(accA, rsA, b - 1, NoGuard{});
+        wait_stage(b + 1);
+        issue(b + kStages);
+        rsA = read_rs(b + 1);
+        mma_block(accA, b + 1);
+        epi_block(accB, rsB, b, NoGuard{});
+    }
+    if (b < nb) {
+        wait_stage(b);
+        rsB = read_rs(b);
+        mma_block(accB, b);
+        epi_block(accA, rsA, b - 1, NoGuard{});
+        epi_block(accB, rsB, b, Guard{});
+    } else {
+        epi_block(accA, rsA, b - 1, Guard{});
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Per-token finish of kv_a_proj, fp16/bf16 path.  One wave per token, four
 // tokens per workgroup: lane l owns latent columns 8l..8l+7 and rope column
 // l.  Every load (position, gamma, partials) is issued before the first use.
@@ -1202,6 +1456,10 @@ static void gemm_launch(const void* A, int64_t lda, const void* B, int64_t ldb, 
 }
 
 constexpr int64_t kPersistentGrid = 256;  // MI355X compute units
+// W8A8 calls from this many tokens on use the weight-stationary kv_b_proj
+// kernel (each workgroup's 128 KB weight load is then spread over enough
+// latent rows)
+constexpr int64_t kWsMinTokens = 2048;
 
 // K is split S ways (S must divide K's slab count); split s writes its
 // partial through epi.ptr(row, col, s).  WGPC workgroups share a CU (their
@@ -1256,6 +1514,26 @@ static void gemm2_dispatch(int bm, int bn, const void* A, int64_t lda, const voi
     }
 }
 
+// W8A8 kv_b_proj, weight-stationary kernel: (row range, head) items, the
+// row ranges as few as fill the device.
+static void kvb_w8_ws_launch(const int8_t* QZ, const int8_t* Wqb, int64_t T, int nh,
+                             const EpiKvW8& e, hipStream_t st) {
+    const int nblk = (int)((T + ws::kRows - 1) / ws::kRows);
+    int msplit = std::min<int>(nblk, std::max<int>(1, (int)(kPersistentGrid / nh)));
+    const int bps = (nblk + msplit - 1) / msplit;
+    msplit = (nblk + bps - 1) / bps;  // no empty range
+    const int items = nh * msplit, per = (items + 7) / 8;
+    const dim3 grid((unsigned)(8 * per)), blk(ws::kWaves * 64);
+    if (e.dbg != nullptr)
+        hipLaunchKernelGGL(kvb_w8_ws_kernel<true>, grid, blk, 0, st, QZ, e.sz, e.inv_t, Wqb, e.swb,
+                           (int)T, nh, msplit, bps, e.k_nope, e.value_out, e.dbg, e.dbg_begin,
+                           e.dbg_rows);
+    else
+        hipLaunchKernelGGL(kvb_w8_ws_kernel<false>, grid, blk, 0, st, QZ, e.sz, e.inv_t, Wqb,
+                           e.swb, (int)T, nh, msplit, bps, e.k_nope, e.value_out, e.dbg,
+                           e.dbg_begin, e.dbg_rows);
+}
+
 void launch_finish_fp(int dt, const float* P, int S, int64_t T, const void* gamma,
                       const int32_t* pos, float eps, const RopeTab& rt, void* ckv, void* kpe,
                       const CacheOut& co, hipStream_t st) {
@@ -1300,10 +1578,13 @@ static hipError_t launch_fp_t(const void* X, const void* Wa, const void* gamma, 
     else
         gemm1_dispatch<E>(plan.bm1, X, (int64_t)H * 2, Wa, T, kslabs1, plan.s1,
                           EpiPartialF32{P1, T}, st);
+    launch_mark(st);
     launch_finish_fp(E, P1, plan.s1, T, gamma, pos, eps, rt, ckv, k_pe, co, st);
+    launch_mark(st);
     const int N2 = nh * kHeadW;
     gemm2_dispatch<E>(plan.bm2, plan.bn2, ckv, (int64_t)kR * 2, Wb, T, N2,
                       EpiKvFp<E>{(uint16_t*)k_nope, (uint16_t*)value, nh}, st);
+    launch_mark(st);
     return hipGetLastError();
 }
 
@@ -1354,6 +1635,7 @@ hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa, const
                 break;
         }
     }
+    launch_mark(st);
     if (plan.dma1 && plan.bm1 == 160)
         gemm_lds_launch<kI8, 160, 192, 2, 4, 4, 3>(QX, (int64_t)H, Wqa, (int64_t)kN1, T, kN1, H,
                                                    plan.s1, EpiPartialI32{P1, T}, st);
@@ -1366,6 +1648,7 @@ hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa, const
     else
         gemm1_dispatch<kI8>(plan.bm1, QX, (int64_t)H, Wqa, T, H / 128, plan.s1,
                             EpiPartialI32{P1, T}, st);
+    launch_mark(st);
     {
         const int S = plan.s1;
         auto go = [&](auto kern) {
@@ -1378,11 +1661,13 @@ hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa, const
         else if (S <= 4) go(finish_a_w8_kernel<4>);
         else go(finish_a_w8_kernel<8>);
     }
+    launch_mark(st);
     const int N2 = nh * kHeadW;
-    gemm2_dispatch<kI8>(plan.bm2, plan.bn2, QZ, (int64_t)kR, Wqb, T, N2,
-                        EpiKvW8{(uint16_t*)k_nope, (uint16_t*)value, nh, sz, inv, swb, dbg2,
-                                dbg_begin, dbg_rows},
-                        st);
+    const EpiKvW8 e2{(uint16_t*)k_nope, (uint16_t*)value, nh, sz, inv, swb, dbg2, dbg_begin,
+                     dbg_rows};
+    if (T >= kWsMinTokens) kvb_w8_ws_launch(QZ, Wqb, T, nh, e2, st);
+    else gemm2_dispatch<kI8>(plan.bm2, plan.bn2, QZ, (int64_t)kR, Wqb, T, N2, e2, st);
+    launch_mark(st);
     return hipGetLastError();
 }
 

@@ -382,6 +382,20 @@ def test_handoff_spin_hook_round_trip():
         mla.mla_debug_set_handoff_spin(prev)
 
 
+def test_launch_event_hook_records_nothing_for_rejected_calls():
+    # a call that fails validation launches nothing, so it records none of
+    # the registered events (the handles are never touched)
+    L = mla.lib()
+    evs = (ctypes.c_void_p * 4)(FAKE, FAKE, FAKE, FAKE)
+    assert L.mla_debug_set_launch_events(evs, 4) == 0
+    try:
+        assert call_fp(T=4, dt=7) != 0
+        assert call_w8(T=4, d=Dims(H=100, nh=16)) != 0
+    finally:
+        assert L.mla_debug_set_launch_events(None, 0) == 0
+    assert L.mla_debug_set_launch_events(None, -3) == 0
+
+
 def call_noalloc(T=4, d=V2, ptrs=None, dt=1, eps=1e-6, theta=1e4):
     p = [FAKE] * 9 if ptrs is None else ptrs
     return mla.lib().mla_kv_prolog_noalloc(p[0], p[1], p[2], p[3], p[4], T, d.c(), dt, eps,

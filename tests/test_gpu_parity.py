@@ -166,6 +166,31 @@ def test_tall_kv_a_tiles(dev, kind):
         check_full(w, dev, "f16_T12000", path=1)
 
 
+@pytest.mark.parametrize("nh,T", [(16, 5000), (3, 2049), (5, 3001), (1, 2080)])
+def test_w8a8_weight_stationary_kv_b(dev, nh, T):
+    # token counts that take the weight-stationary kv_b_proj kernel: row
+    # ranges of more blocks than its ring has stages (nh = 16: 10 blocks of
+    # 32 rows each), odd and single head counts, ragged last blocks (5000 =
+    # 156 x 32 + 8, 2049, 3001), an odd and an even block count per range.
+    # The production launch against the oracle on every row, then a launch
+    # with the accumulator exports: bit-exact int32 accumulators and the same
+    # outputs.
+    d = Dims(H=512, nh=nh)
+    w = workloads.make_custom(d, T, kind="w8a8", dtype="bf16", seed=490 + nh, wstd=0.02,
+                              max_pos=8192)
+    print(f"[parity] w8a8 weight-stationary kv_b nh={nh} T={T}", flush=True)
+    t = upload(w, dev)
+    outs, _ = run_lib(w, t)
+    outs2, (d1, d2) = run_lib(w, t, dbg_rows=(0, w.T))
+    torch.cuda.synchronize()
+    ref = run_oracle(w)
+    compare(gpu_rows(outs), ref, f"w8a8_ws_nh{nh}_T{T}")
+    np.testing.assert_array_equal(d1.cpu().numpy(), ref["acc1"])
+    np.testing.assert_array_equal(d2.cpu().numpy(), ref["acc2"])
+    for x, y in zip(outs, outs2):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
 @pytest.mark.parametrize("H,T", [(640, 7), (8320, 6)])
 def test_w8a8_hidden_sizes_exact(dev, H, T):
     # the activation quantiser: H = 640 leaves lanes with a partial last chunk
