@@ -712,7 +712,10 @@ def kernel_times(sets, reps, dev):
     """Average duration of each kernel of a call, live: events registered
     with the library (mla_debug_set_launch_events) are recorded on the
     call's stream right after each kernel it launches, one more before the
-    call; eager calls rotating over the input sets."""
+    call; eager calls rotating over the input sets.  Each call is queued
+    behind a ~40 us device-side spin, so that the host has submitted the
+    whole call before its first event fires and the intervals hold device
+    time only."""
     import torch
 
     L = sets.mla.lib()
@@ -726,6 +729,7 @@ def kernel_times(sets, reps, dev):
         torch.cuda.synchronize()
         arr = (ctypes.c_void_p * maxk)(*[e.cuda_event for e in evs[1:]])
         L.mla_debug_set_launch_events(arr, maxk)
+        torch.cuda._sleep(100_000)
         evs[0].record()
         sets.call(i, sp)
         used = L.mla_debug_set_launch_events(None, 0)

@@ -155,7 +155,9 @@ inline WsW8 ws_w8(int64_t T, int H, const Plan& p) {
     w.qx = o; o += align256((size_t)T * H);
     w.sx = o; o += align256((size_t)T * 4);
     w.p1 = o; o += align256((size_t)p.s1 * (size_t)T * kN1 * 4);
-    w.qz = o; o += align256((size_t)T * kR);
+    // the quantised latent, padded to whole blocks of 32 rows for the
+    // weight-stationary kv_b_proj kernel's copies
+    w.qz = o; o += align256((size_t)((T + 31) / 32) * 32 * kR);
     const size_t tpad = (size_t)((T + 255) / 256) * 256;
     w.sz = o; o += tpad * 4;
     w.inv = o; o += tpad * 4;

@@ -952,6 +952,32 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
         : "s"(lds), "v"(g)
         : "memory");
 }
+// The same copies from a wave-uniform base plus a 32-bit per-lane byte
+// offset (the scalar-base form: no per-lane address arithmetic).
+__device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t lds) {
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "s"(lds), "v"(voff), "s"(base)
+        : "memory");
+}
+__device__ __forceinline__ void dma4s(const void* base, uint32_t voff, uint32_t lds) {
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %2, %3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "s"(lds), "v"(voff), "s"(base)
+        : "memory");
+}
 // Wait until at most N of this wave's vector-memory operations (copies and
 // stores, which complete in issue order) are outstanding and its LDS reads
 // are complete, then barrier.
@@ -963,7 +989,7 @@ __device__ __forceinline__ void wait_vm_lds_barrier() {
 
 template <bool DBG>
 __global__ __launch_bounds__(ws::kWaves * 64, 1) void kvb_w8_ws_kernel(
-    const int8_t* __restrict__ QZ, const float* __restrict__ sz, const float* __restrict__ inv,
+    const int8_t* __restrict__ QZ, const float* __restrict__ sz, uint32_t inv_ofs,
     const int8_t* __restrict__ Wqb, const float* __restrict__ swb, int T, int nh, int msplit,
     int bps, uint16_t* __restrict__ k_nope, uint16_t* __restrict__ value_out,
     int32_t* __restrict__ dbg, int64_t dbg_begin, int64_t dbg_rows) {
@@ -1027,22 +1053,28 @@ __global__ __launch_bounds__(ws::kWaves * 64, 1) void kvb_w8_ws_kernel(
     // ---- ring.  Block bb (rows m_first + 32 bb ..) goes to stage
     // bb % kStages: wave w copies rows 4 w .. 4 w + 3 (two rows of 512 bytes
     // per instruction; chunk p of LDS row r holds chunk p ^ (r & 15)), wave
-    // 0 also the rows' two scale arrays.  Copies past the last block repeat
-    // it, so every wait below has the same number of later operations.
+    // 0 also the rows' two scale arrays (inv_t lies inv_ofs bytes after sz).
+    // The latent is padded to whole blocks, so the last block's copies stay
+    // in bounds.  Copies past the last block repeat it, so every wait below
+    // has the same number of later operations.
     const int m_first = bfirst * kRows;
     const uint32_t sbase =
         lds_addr(smem) + (uint32_t)__builtin_amdgcn_readfirstlane(wave * kCopies * 1024);
     const uint32_t scl = lds_addr(smem) + kScaleOfs;
+    uint32_t aoff[kCopies];
+#pragma unroll
+    for (int q = 0; q < kCopies; ++q) {
+        const int r = (wave * kCopies + q) * 2 + (lane >> 5), p = lane & 31;
+        aoff[q] = (uint32_t)(r * kR + ((p ^ (r & 15)) << 4));
+    }
+    const uint32_t soff = lane < 32 ? (uint32_t)lane * 4 : inv_ofs + (uint32_t)(lane - 32) * 4;
     auto issue = [&](int bb) {
         const int m0 = m_first + min(bb, nb - 1) * kRows;
         const uint32_t so = (uint32_t)((bb % kStages) * kStageBytes);
+        const int8_t* qb = QZ + (int64_t)m0 * kR;
 #pragma unroll
-        for (int q = 0; q < kCopies; ++q) {
-            const int r = (wave * kCopies + q) * 2 + (lane >> 5), p = lane & 31;
-            dma16(QZ + (int64_t)min(m0 + r, T - 1) * kR + ((p ^ (r & 15)) << 4),
-                  sbase + so + q * 1024);
-        }
-        if (wave == 0) dma4(lane < 32 ? sz + m0 + lane : inv + m0 + (lane - 32), scl + so);
+        for (int q = 0; q < kCopies; ++q) dma16s(qb, aoff[q], sbase + so + q * 1024);
+        if (wave == 0) dma4s(sz + m0, soff, scl + so);
     };
     // stage b in place and the stage of block b - 1 free.  After block b's
     // copies this wave issued kStages - 2 later groups of copies (kCopies,
@@ -1064,11 +1096,13 @@ __global__ __launch_bounds__(ws::kWaves * 64, 1) void kvb_w8_ws_kernel(
     // A^T: lane l then holds row l % 16 and columns 4 (l / 16) .. + 3 of
     // each 16-column tile).  The A fragment of K step ks + 2 is read while
     // step ks multiplies.
-    const int arow = (rh * 16 + l16) * kR;
+    uint32_t aro[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) aro[ks] = (uint32_t)((rh * 16 + l16) * kR + (((ks * 4 + g) ^ l16) << 4));
     auto mma_block = [&](acc_t(&acc)[4], int b) {
-        const uint8_t* s = smem + (b % kStages) * kStageBytes + arow;
+        const uint8_t* s = smem + (b % kStages) * kStageBytes;
         u4_t fa[3];
-        auto rd = [&](int ks) { fa[ks % 3] = *(const u4_t*)(s + (((ks * 4 + g) ^ l16) << 4)); };
+        auto rd = [&](int ks) { fa[ks % 3] = *(const u4_t*)(s + aro[ks]); };
         rd(0);
         rd(1);
 #pragma unroll
@@ -1087,12 +1121,19 @@ __global__ __launch_bounds__(ws::kWaves * 64, 1) void kvb_w8_ws_kernel(
     };
     uint16_t* const dst0 = (cq < 2 ? k_nope : value_out) + (int64_t)head * kDN + (cq & 1) * 64;
     const int64_t rstride = (int64_t)nh * kDN;
+    // byte offset of the lane's 16-byte pieces from its 16-row group's
+    // first row (row l16, columns of piece p)
+    uint32_t doff[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+        doff[p] = (uint32_t)((l16 * rstride + 32 * p + ((g & 1) ? 16 + 4 * (g - 1) : 4 * g)) * 2);
     // results of block b: ((acc * row factor) * column scale) rounded to
     // bf16; lanes of even 16-lane rows end with 8 columns of tile 2p, odd
     // ones with 8 columns of tile 2p + 1.  GUARD: rows past T are skipped
     // (only the last block has any).
     auto epi_block = [&](const acc_t(&acc)[4], float rs, int b, auto guard) {
-        const int row = m_first + b * kRows + rh * 16 + l16;
+        const int row0 = m_first + b * kRows + rh * 16, row = row0 + l16;
+        uint8_t* const drow = (uint8_t*)(dst0 + row0 * rstride);
         uint32_t P[4][2];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -1107,8 +1148,7 @@ __global__ __launch_bounds__(ws::kWaves * 64, 1) void kvb_w8_ws_kernel(
             const auto s0 = __builtin_amdgcn_permlane16_swap(P[2 * p][0], P[2 * p + 1][0], false, false);
             const auto s1 = __builtin_amdgcn_permlane16_swap(P[2 * p][1], P[2 * p + 1][1], false, false);
             const u4_t v = u4_t{s0[0], s1[0], s0[1], s1[1]};
-            const int col = 32 * p + ((g & 1) ? 16 + 4 * (g - 1) : 4 * g);
-            uint16_t* d = dst0 + row * rstride + col;
+            uint8_t* d = drow + doff[p];
             if constexpr (decltype(guard)::value) {
                 if (row < T) __builtin_nontemporal_store(v, (u4_t*)d);
             } else {
@@ -1524,12 +1564,14 @@ static void kvb_w8_ws_launch(const int8_t* QZ, const int8_t* Wqb, int64_t T, int
     msplit = (nblk + bps - 1) / bps;  // no empty range
     const int items = nh * msplit, per = (items + 7) / 8;
     const dim3 grid((unsigned)(8 * per)), blk(ws::kWaves * 64);
+    // the workspace places the RMS factors after the activation scales
+    const uint32_t inv_ofs = (uint32_t)((const uint8_t*)e.inv_t - (const uint8_t*)e.sz);
     if (e.dbg != nullptr)
-        hipLaunchKernelGGL(kvb_w8_ws_kernel<true>, grid, blk, 0, st, QZ, e.sz, e.inv_t, Wqb, e.swb,
-                           (int)T, nh, msplit, bps, e.k_nope, e.value_out, e.dbg, e.dbg_begin,
-                           e.dbg_rows);
+        hipLaunchKernelGGL(kvb_w8_ws_kernel<true>, grid, blk, 0, st, QZ, e.sz, inv_ofs, Wqb,
+                           e.swb, (int)T, nh, msplit, bps, e.k_nope, e.value_out, e.dbg,
+                           e.dbg_begin, e.dbg_rows);
     else
-        hipLaunchKernelGGL(kvb_w8_ws_kernel<false>, grid, blk, 0, st, QZ, e.sz, e.inv_t, Wqb,
+        hipLaunchKernelGGL(kvb_w8_ws_kernel<false>, grid, blk, 0, st, QZ, e.sz, inv_ofs, Wqb,
                            e.swb, (int)T, nh, msplit, bps, e.k_nope, e.value_out, e.dbg,
                            e.dbg_begin, e.dbg_rows);
 }
@@ -1665,7 +1707,7 @@ hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa, const
     const int N2 = nh * kHeadW;
     const EpiKvW8 e2{(uint16_t*)k_nope, (uint16_t*)value, nh, sz, inv, swb, dbg2, dbg_begin,
                      dbg_rows};
-    if (T >= kWsMinTokens) kvb_w8_ws_launch(QZ, Wqb, T, nh, e2, st);
+    if (T >= kWsMinTokens && inv > sz) kvb_w8_ws_launch(QZ, Wqb, T, nh, e2, st);
     else gemm2_dispatch<kI8>(plan.bm2, plan.bn2, QZ, (int64_t)kR, Wqb, T, N2, e2, st);
     launch_mark(st);
     return hipGetLastError();
