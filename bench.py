@@ -709,32 +709,27 @@ def kernel_parts(w, path, n_kernels):
 
 
 def kernel_times(sets, reps, dev):
-    """Average duration of each kernel of a call, live: events registered
-    with the library (mla_debug_set_launch_events) are recorded on the
-    call's stream right after each kernel it launches, one more before the
-    call; eager calls rotating over the input sets.  Each call is queued
-    behind a ~40 us device-side spin, so that the host has submitted the
-    whole call before its first event fires and the intervals hold device
-    time only."""
+    """Average duration of each kernel of a call, live: pairs of events
+    registered with the library (mla_debug_set_launch_events) are recorded
+    at each kernel's own start and end (its dispatch timestamps); eager
+    calls rotating over the input sets."""
     import torch
 
     L = sets.mla.lib()
     sp = torch.cuda.current_stream(dev).cuda_stream
     maxk = 8
-    sums, used = None, 0
+    sums = None
     for i in range(reps + 3):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(maxk + 1)]
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * maxk)]
         for e in evs:
             e.record()
         torch.cuda.synchronize()
-        arr = (ctypes.c_void_p * maxk)(*[e.cuda_event for e in evs[1:]])
-        L.mla_debug_set_launch_events(arr, maxk)
-        torch.cuda._sleep(100_000)
-        evs[0].record()
+        arr = (ctypes.c_void_p * (2 * maxk))(*[e.cuda_event for e in evs])
+        L.mla_debug_set_launch_events(arr, 2 * maxk)
         sets.call(i, sp)
         used = L.mla_debug_set_launch_events(None, 0)
         torch.cuda.synchronize()
-        ms = [evs[k].elapsed_time(evs[k + 1]) for k in range(used)]
+        ms = [evs[2 * k].elapsed_time(evs[2 * k + 1]) for k in range(used // 2)]
         if i < 3:
             continue  # warm-up calls
         sums = ms if sums is None else [a + x for a, x in zip(sums, ms)]
@@ -852,7 +847,7 @@ def measure_prolog(idx, steps, warmup, dev, args, cache_mode=None, graph_buckets
         name, (kb, kf) = parts[dom]
         roof = roofline(w, kus[dom] * 1e-6, kb, max(kf, 1))
         roof["kernel"] = f"{name}: the call's longest kernel ({kus[dom]:.2f} us of " \
-                         f"{sum(kus):.2f} us of kernel time; live HIP events, eager calls)"
+                         f"{sum(kus):.2f} us of kernel time; HIP events at its dispatch start and end, eager calls)"
         per_k = traffic.get("kernels") if traffic else None
         roof["traffic"] = per_k[dom] if per_k and dom < len(per_k) else None
         roof["traffic_source"] = call_roof["traffic_source"] if roof["traffic"] else None

@@ -416,16 +416,16 @@ mla_status_t mla_kv_prolog_noalloc(const void* hidden, const void* W_kv_a, const
                                    void* stream);
 
 /* Benchmark hook: per-kernel timing.  Registers, for the calling host
- * thread, n events (hipEvent_t handles created and owned by the caller; the
- * array is read at each launch, so it must stay valid until it is
- * unregistered; NULL or n <= 0 unregisters).  Every later prolog call on
- * this thread
- * (mla_kv_prolog* entry points) then records the next registered event on
- * its stream right after each kernel it launches, until the n events are
- * used up; with an event recorded before the call, the elapsed times between
- * consecutive events are the kernels' durations in launch order.  Returns
- * how many events the previous registration had recorded.  Recording into a
- * stream that is being captured adds the records to the graph. */
+ * thread, n events (hipEvent_t handles created with timing enabled and owned
+ * by the caller; the array is read at each launch, so it must stay valid
+ * until it is unregistered; NULL or n <= 0 unregisters).  Every later prolog
+ * call on this thread (mla_kv_prolog* entry points) then takes the next two
+ * events for each kernel it launches, while at least two are left, and the
+ * launch records them at that kernel's own start and end (the dispatch's
+ * timestamps, hipExtLaunchKernel), so the elapsed time between events 2k
+ * and 2k + 1 is the duration of the call's k-th kernel.  Returns how many
+ * events the previous registration had recorded (twice the kernels it
+ * timed).  Not for calls that are being captured into a graph. */
 int32_t mla_debug_set_launch_events(void* const* events, int32_t n);
 
 /* Test hooks for the decode family's one-launch finish + kv_b_proj (taken

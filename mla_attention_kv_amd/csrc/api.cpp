@@ -154,9 +154,15 @@ thread_local LaunchEvents t_events;
 }  // namespace
 
 namespace mla {
-void launch_mark(hipStream_t st) {
+void launch_events(hipEvent_t* start, hipEvent_t* stop) {
     LaunchEvents& e = t_events;
-    if (e.ev != nullptr && e.used < e.n) (void)hipEventRecord((hipEvent_t)e.ev[e.used++], st);
+    if (e.ev != nullptr && e.used + 2 <= e.n) {
+        *start = (hipEvent_t)e.ev[e.used];
+        *stop = (hipEvent_t)e.ev[e.used + 1];
+        e.used += 2;
+    } else {
+        *start = *stop = nullptr;
+    }
 }
 bool validate_only() { return t_validate_only > 0; }
 ValidateOnlyScope::ValidateOnlyScope() { ++t_validate_only; }

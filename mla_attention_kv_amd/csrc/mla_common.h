@@ -2,6 +2,7 @@
 // libmlaprolog.  Not a public header.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -290,10 +291,23 @@ hipError_t launch_kv_cache_append(int dt, const void* ckv, const void* kpe, cons
 int64_t decode_set_spin_limit(int64_t limit);
 int64_t decode_handoff_fallbacks(bool reset);
 
-// After each kernel a prolog call launches: records the next of the events
-// the calling thread registered (mla_debug_set_launch_events) on st, if any
-// are left; nothing otherwise.
-void launch_mark(hipStream_t st);
+// The next pair of the events the calling thread registered
+// (mla_debug_set_launch_events), or two nulls when none are left.
+void launch_events(hipEvent_t* start, hipEvent_t* stop);
+
+// Kernel launch of the prolog entry points.  With events registered, the
+// launch records the next pair at the kernel's own start and end (the
+// dispatch's timestamps); otherwise it is a plain launch.
+template <typename F, typename... Args>
+inline void launch_k(F kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t st,
+                     Args... args) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    launch_events(&e0, &e1);
+    if (e0 != nullptr)
+        hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, e0, e1, 0u, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, shmem, st, args...);
+}
 
 // While a ValidateOnlyScope is alive on the calling thread, the prolog
 // entry points run every argument check and return without launching (the

@@ -568,7 +568,7 @@ static void dec_kv_a_launch(const void* X, const void* Wa, int T, int H, float* 
     const uint16_t* x = (const uint16_t*)X;
     const uint16_t* wa = (const uint16_t*)Wa;
 #define MLA_KVA(KW) \
-    hipLaunchKernelGGL((dec_kv_a_kernel<E, NA, KW>), ga, blk, 0, st, x, wa, T, H, S, P, ckv, ng)
+    launch_k((dec_kv_a_kernel<E, NA, KW>), ga, blk, 0, st, x, wa, T, H, S, P, ckv, ng)
     switch (kw) {
         case 64: MLA_KVA(64); break;
         case 128: MLA_KVA(128); break;
@@ -621,24 +621,20 @@ static void dec_launch_t(const void* X, const void* Wa, const void* gamma, const
         case 3: dec_kv_a_launch<E, 3>(X, Wa, T, H, P, plan.kw, plan.s1, y, ng, st); break;
         default: dec_kv_a_launch<E, 4>(X, Wa, T, H, P, plan.kw, plan.s1, y, ng, st); break;
     }
-    launch_mark(st);
     if (fused) {
         const int64_t sl = g_spin_limit.load(std::memory_order_relaxed);
         const uint32_t spin = sl < 0 ? kSpinDefault : (uint32_t)(sl > 0xFFFFFFFFll ? 0xFFFFFFFFll : sl);
-        hipLaunchKernelGGL(dec_fin_kv_b_kernel<E>, dim3(grid8(nitems)), dim3(256), 0, st,
-                           (const float*)P, plan.s1, T, (const uint16_t*)gamma, pos, eps, rt,
-                           (const uint16_t*)Wb, N2, (uint16_t*)ckv, (uint16_t*)k_pe,
-                           (uint16_t*)k_nope, (uint16_t*)value, co, spin);
-        launch_mark(st);
+        launch_k(dec_fin_kv_b_kernel<E>, dim3(grid8(nitems)), dim3(256), 0, st,
+                 (const float*)P, plan.s1, T, (const uint16_t*)gamma, pos, eps, rt,
+                 (const uint16_t*)Wb, N2, (uint16_t*)ckv, (uint16_t*)k_pe,
+                 (uint16_t*)k_nope, (uint16_t*)value, co, spin);
         return;
     }
-    hipLaunchKernelGGL(dec_finish_kernel<E>, dim3(T), dim3(256), 0, st, (const float*)P, plan.s1,
-                       T, (const uint16_t*)gamma, pos, eps, rt, (uint16_t*)ckv, (uint16_t*)k_pe, co);
-    launch_mark(st);
-    hipLaunchKernelGGL((dec_kv_b_kernel<E, 1>), dim3(grid8(nitems)), dim3(256), 0, st,
-                       (const uint16_t*)ckv, (const uint16_t*)Wb, T, N2, (uint16_t*)k_nope,
-                       (uint16_t*)value);
-    launch_mark(st);
+    launch_k(dec_finish_kernel<E>, dim3(T), dim3(256), 0, st, (const float*)P, plan.s1,
+             T, (const uint16_t*)gamma, pos, eps, rt, (uint16_t*)ckv, (uint16_t*)k_pe, co);
+    launch_k((dec_kv_b_kernel<E, 1>), dim3(grid8(nitems)), dim3(256), 0, st,
+             (const uint16_t*)ckv, (const uint16_t*)Wb, T, N2, (uint16_t*)k_nope,
+             (uint16_t*)value);
 }
 
 hipError_t launch_fp_decode(int dt, const void* X, const void* Wa, const void* gamma,

@@ -1490,9 +1490,9 @@ static void gemm_launch(const void* A, int64_t lda, const void* B, int64_t ldb, 
     const int per = (kslabs + S - 1) / S;
     const int64_t tiles = ((M + BM - 1) / BM) * (N / BN) * (int64_t)S;
     const int64_t grid = ((tiles + 7) / 8) * 8;
-    hipLaunchKernelGGL((gemm_tiled_kernel<E, BM, BN, WM, WN, GM, Epi>), dim3((unsigned)grid),
-                       dim3(256), 0, st, (const uint8_t*)A, lda, (const uint8_t*)B, ldb, (int)M,
-                       N / BN, S, per, kslabs, epi);
+    launch_k((gemm_tiled_kernel<E, BM, BN, WM, WN, GM, Epi>), dim3((unsigned)grid),
+             dim3(256), 0, st, (const uint8_t*)A, lda, (const uint8_t*)B, ldb, (int)M,
+             N / BN, S, per, kslabs, epi);
 }
 
 constexpr int64_t kPersistentGrid = 256;  // MI355X compute units
@@ -1511,10 +1511,10 @@ static void gemm_lds_launch(const void* A, int64_t lda, const void* B, int64_t l
     constexpr int GM = 4;
     const int64_t tiles = ((M + BM - 1) / BM) * (N / BN) * S;
     const int64_t grid = std::min<int64_t>(((tiles + 7) / 8) * 8, kPersistentGrid * WGPC);
-    hipLaunchKernelGGL((gemm_lds_kernel<E, BM, BN, WAVES_M, WAVES_N, NP, STAGES, GM, WGPC, Epi>),
-                       dim3((unsigned)grid), dim3(64 * (WAVES_M * WAVES_N + NP)), 0, st,
-                       (const uint8_t*)A, lda, (const uint8_t*)B, ldb, (int)M, N / BN,
-                       K * (E == kI8 ? 1 : 2) / 128 / S, S, epi);
+    launch_k((gemm_lds_kernel<E, BM, BN, WAVES_M, WAVES_N, NP, STAGES, GM, WGPC, Epi>),
+             dim3((unsigned)grid), dim3(64 * (WAVES_M * WAVES_N + NP)), 0, st,
+             (const uint8_t*)A, lda, (const uint8_t*)B, ldb, (int)M, N / BN,
+             K * (E == kI8 ? 1 : 2) / 128 / S, S, epi);
 }
 
 // kv_a_proj tiles: BN = 64 always (576 = 9 x 64)
@@ -1567,13 +1567,13 @@ static void kvb_w8_ws_launch(const int8_t* QZ, const int8_t* Wqb, int64_t T, int
     // the workspace places the RMS factors after the activation scales
     const uint32_t inv_ofs = (uint32_t)((const uint8_t*)e.inv_t - (const uint8_t*)e.sz);
     if (e.dbg != nullptr)
-        hipLaunchKernelGGL(kvb_w8_ws_kernel<true>, grid, blk, 0, st, QZ, e.sz, inv_ofs, Wqb,
-                           e.swb, (int)T, nh, msplit, bps, e.k_nope, e.value_out, e.dbg,
-                           e.dbg_begin, e.dbg_rows);
+        launch_k(kvb_w8_ws_kernel<true>, grid, blk, 0, st, QZ, e.sz, inv_ofs, Wqb,
+                 e.swb, (int)T, nh, msplit, bps, e.k_nope, e.value_out, e.dbg,
+                 e.dbg_begin, e.dbg_rows);
     else
-        hipLaunchKernelGGL(kvb_w8_ws_kernel<false>, grid, blk, 0, st, QZ, e.sz, inv_ofs, Wqb,
-                           e.swb, (int)T, nh, msplit, bps, e.k_nope, e.value_out, e.dbg,
-                           e.dbg_begin, e.dbg_rows);
+        launch_k(kvb_w8_ws_kernel<false>, grid, blk, 0, st, QZ, e.sz, inv_ofs, Wqb,
+                 e.swb, (int)T, nh, msplit, bps, e.k_nope, e.value_out, e.dbg,
+                 e.dbg_begin, e.dbg_rows);
 }
 
 void launch_finish_fp(int dt, const float* P, int S, int64_t T, const void* gamma,
@@ -1584,8 +1584,8 @@ void launch_finish_fp(int dt, const float* P, int S, int64_t T, const void* gamm
     const dim3 grid((unsigned)((T + tpw - 1) / tpw)), blk(64 * tpw);
     const int b = S <= 1 ? 1 : S <= 2 ? 2 : S <= 4 ? 4 : 8;
     auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, grid, blk, 0, st, P, S, T, (const uint16_t*)gamma, pos, eps, rt,
-                           (uint16_t*)ckv, (uint16_t*)kpe, co);
+        launch_k(kern, grid, blk, 0, st, P, S, T, (const uint16_t*)gamma, pos, eps, rt,
+                 (uint16_t*)ckv, (uint16_t*)kpe, co);
     };
     if (dt == kF16) {
         if (b == 1) go(finish_a_fp_kernel<kF16, 1>);
@@ -1620,13 +1620,10 @@ static hipError_t launch_fp_t(const void* X, const void* Wa, const void* gamma, 
     else
         gemm1_dispatch<E>(plan.bm1, X, (int64_t)H * 2, Wa, T, kslabs1, plan.s1,
                           EpiPartialF32{P1, T}, st);
-    launch_mark(st);
     launch_finish_fp(E, P1, plan.s1, T, gamma, pos, eps, rt, ckv, k_pe, co, st);
-    launch_mark(st);
     const int N2 = nh * kHeadW;
     gemm2_dispatch<E>(plan.bm2, plan.bn2, ckv, (int64_t)kR * 2, Wb, T, N2,
                       EpiKvFp<E>{(uint16_t*)k_nope, (uint16_t*)value, nh}, st);
-    launch_mark(st);
     return hipGetLastError();
 }
 
@@ -1665,19 +1662,17 @@ hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa, const
         const uint16_t* x = (const uint16_t*)X;
         switch ((H + 511) / 512) {
 #define MLA_QUANT_WAVE(n)                                                                     \
-    case n: hipLaunchKernelGGL(quant_rows_wave_kernel<n>, g4, blk, 0, st, x, H, T, QX, sx); break;
+    case n: launch_k(quant_rows_wave_kernel<n>, g4, blk, 0, st, x, H, T, QX, sx); break;
             MLA_QUANT_WAVE(1) MLA_QUANT_WAVE(2) MLA_QUANT_WAVE(3) MLA_QUANT_WAVE(4)
             MLA_QUANT_WAVE(5) MLA_QUANT_WAVE(6) MLA_QUANT_WAVE(7) MLA_QUANT_WAVE(8)
             MLA_QUANT_WAVE(9) MLA_QUANT_WAVE(10) MLA_QUANT_WAVE(11) MLA_QUANT_WAVE(12)
             MLA_QUANT_WAVE(13) MLA_QUANT_WAVE(14) MLA_QUANT_WAVE(15) MLA_QUANT_WAVE(16)
 #undef MLA_QUANT_WAVE
             default:
-                hipLaunchKernelGGL(quant_rows_long_kernel, dim3((unsigned)T), blk, 0, st, x, H, QX,
-                                   sx);
+                launch_k(quant_rows_long_kernel, dim3((unsigned)T), blk, 0, st, x, H, QX, sx);
                 break;
         }
     }
-    launch_mark(st);
     if (plan.dma1 && plan.bm1 == 160)
         gemm_lds_launch<kI8, 160, 192, 2, 4, 4, 3>(QX, (int64_t)H, Wqa, (int64_t)kN1, T, kN1, H,
                                                    plan.s1, EpiPartialI32{P1, T}, st);
@@ -1690,26 +1685,23 @@ hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa, const
     else
         gemm1_dispatch<kI8>(plan.bm1, QX, (int64_t)H, Wqa, T, H / 128, plan.s1,
                             EpiPartialI32{P1, T}, st);
-    launch_mark(st);
     {
         const int S = plan.s1;
         auto go = [&](auto kern) {
-            hipLaunchKernelGGL(kern, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, P1, S, T,
-                               sx, swa, (const uint16_t*)gamma, pos, eps, rt, QZ, sz, inv,
-                               (uint16_t*)ckv, (uint16_t*)k_pe, dbg1, dbg_begin, dbg_rows, co);
+            launch_k(kern, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, P1, S, T,
+                     sx, swa, (const uint16_t*)gamma, pos, eps, rt, QZ, sz, inv,
+                     (uint16_t*)ckv, (uint16_t*)k_pe, dbg1, dbg_begin, dbg_rows, co);
         };
         if (S <= 1) go(finish_a_w8_kernel<1>);
         else if (S <= 2) go(finish_a_w8_kernel<2>);
         else if (S <= 4) go(finish_a_w8_kernel<4>);
         else go(finish_a_w8_kernel<8>);
     }
-    launch_mark(st);
     const int N2 = nh * kHeadW;
     const EpiKvW8 e2{(uint16_t*)k_nope, (uint16_t*)value, nh, sz, inv, swb, dbg2, dbg_begin,
                      dbg_rows};
     if (T >= kWsMinTokens && inv > sz) kvb_w8_ws_launch(QZ, Wqb, T, nh, e2, st);
     else gemm2_dispatch<kI8>(plan.bm2, plan.bn2, QZ, (int64_t)kR, Wqb, T, N2, e2, st);
-    launch_mark(st);
     return hipGetLastError();
 }
 

@@ -1,7 +1,8 @@
 """The per-kernel timing hook (mla_debug_set_launch_events) on the GPU: a
-registered call records one event after each kernel it launches, in launch
-order, and leaves the outputs bit for bit as an unregistered call makes
-them; the intervals between the events add up to the call's duration."""
+registered call records a pair of events at the start and end of each
+kernel it launches, in launch order, and leaves the outputs bit for bit as
+an unregistered call makes them; every kernel ends before the next starts
+(one stream) and their durations fit in the call's span."""
 import ctypes
 
 import pytest
@@ -44,25 +45,26 @@ def test_launch_events_one_per_kernel(dev, case):
     torch.cuda.synchronize()
     L = mla.lib()
     maxk = 8
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(maxk + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * maxk)]
     for e in evs:
         e.record()
     torch.cuda.synchronize()
-    arr = (ctypes.c_void_p * maxk)(*[e.cuda_event for e in evs[1:]])
-    assert L.mla_debug_set_launch_events(arr, maxk) == 0
+    arr = (ctypes.c_void_p * (2 * maxk))(*[e.cuda_event for e in evs])
+    assert L.mla_debug_set_launch_events(arr, 2 * maxk) == 0
     try:
-        evs[0].record()
         got, _ = run_lib(w, t)
     finally:
         used = L.mla_debug_set_launch_events(None, 0)
     torch.cuda.synchronize()
-    assert used == nk
+    assert used == 2 * nk
     for a, b in zip(ref, got):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
-    spans = [evs[k].elapsed_time(evs[k + 1]) for k in range(used)]
-    assert all(s >= 0.0 for s in spans)
-    total = evs[0].elapsed_time(evs[used])
-    assert abs(sum(spans) - total) <= 1e-3 + 1e-3 * total
+    durs = [evs[2 * k].elapsed_time(evs[2 * k + 1]) for k in range(nk)]
+    gaps = [evs[2 * k + 1].elapsed_time(evs[2 * k + 2]) for k in range(nk - 1)]
+    assert all(d > 0.0 for d in durs), durs
+    assert all(x >= -1e-3 for x in gaps), gaps
+    span = evs[0].elapsed_time(evs[2 * nk - 1])
+    assert sum(durs) <= span + 1e-3
     # an unregistered call records nothing more
     run_lib(w, t)
     torch.cuda.synchronize()
