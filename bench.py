@@ -829,8 +829,9 @@ def measure_prolog(idx, steps, warmup, dev, args, cache_mode=None, graph_buckets
     call_roof = roofline(w, ms_per_step / 1e3, alg_bytes, alg_flops)
     traffic = (load_traffic(cfg["name"]) if cache_mode is None and buckets is None else None)
     call_roof["traffic"] = traffic["call"] if traffic else None
-    call_roof["traffic_source"] = (f"profiles/traffic_{cfg['name']}.json (rocprofv3 FETCH_SIZE / "
-                                   "WRITE_SIZE of the same kernel sources)" if traffic else None)
+    call_roof["traffic_source"] = (f"profiles/traffic_{cfg['name']}.json: rocprofv3 FETCH_SIZE / "
+                                   "WRITE_SIZE of the same kernel sources from a separate profiling "
+                                   "run, not measured in this run" if traffic else None)
     call_roof["kernel"] = kernel_names(w, path, cache_mode)
     # the dominant kernel, timed live per kernel (eager calls)
     kus = (kernel_times(sets, max(10, min(200, int(2e4 / max(ms_per_step * 1e3, 1.0)))), dev)
