@@ -783,9 +783,17 @@ def measure_prolog(idx, steps, warmup, dev, args, cache_mode=None, graph_buckets
     import mla_attention_kv_amd as mla
     import workloads
 
-    cfg = workloads.CONFIGS[idx]
-    log(f"generating workload {cfg['name']}")
-    w = workloads.make_config(idx)
+    cfg = dict(workloads.CONFIGS[idx])
+    if getattr(args, "tokens", None):
+        # the configuration's model, dtype and value distributions at another
+        # token count (positions uniform over [0, 32768))
+        cfg["name"] = f"{cfg['name']}_at_T{args.tokens}"
+        log(f"generating workload {cfg['name']}")
+        w = workloads.make_custom(cfg["dims"], args.tokens, kind=cfg["kind"], dtype=cfg["dtype"],
+                                  seed=1000 + idx, wstd=cfg["wstd"], max_pos=32768)
+    else:
+        log(f"generating workload {cfg['name']}")
+        w = workloads.make_config(idx)
     d = w.dims
     alg_bytes = workloads.algorithmic_bytes(d, w.T, w.kind, w.dtype)
     if cache_mode is not None:
@@ -895,6 +903,9 @@ def main():
                     help="what one step is (default: the prolog)")
     ap.add_argument("--layers", type=int, default=27,
                     help="--op graph_layers: layers per step (default 27, V2-Lite's count)")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="with --config: that configuration's model and distributions at this "
+                         "token count (a side measurement, not a headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -924,6 +935,9 @@ def main():
     if args.op == "vendor_gemm":
         vendor_gemm_reference(dev, args.steps)
         return
+    if args.tokens is not None and (args.config is None or args.tokens < 1):
+        print("--tokens needs --config and a positive count", file=sys.stderr)
+        sys.exit(2)
     if args.op == "graph_layers":
         main_layers(args, 1 if args.config is None else args.config, dev)
         return

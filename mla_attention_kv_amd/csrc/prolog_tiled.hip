@@ -1201,6 +1201,192 @@ __global__ __launch_bounds__(ws::kWaves * 64, 1) void kvb_w8_ws_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// fp16 / bf16 kv_b_proj, weight-stationary: the same scheme with 2-byte
+// weights.  A workgroup owns one head's 256 columns; wave w (eight waves,
+// two per SIMD) owns the 32 columns 32 w .. and holds their weights over all
+// 512 latent dimensions in registers (the operand fragments of 16 K steps
+// of 32; the staging goes through LDS in two halves of K, 128 KB each), and
+// multiplies all 32 rows of each latent block.  Blocks of 32 latent rows
+// (32 KB) stream through a ring of 4 LDS stages; each wave copies 4 rows
+// (one 1 KB row per instruction, 16-byte chunk p of LDS row r holding chunk
+// p ^ (r & 15)), rows past T repeat row T - 1.  The results of block b are
+// rounded and stored while block b + 1's MFMAs run; one 16-byte store per
+// lane writes 16 rows x 64 bytes (the wave's 32 columns).
+// ---------------------------------------------------------------------------
+namespace wsf {
+constexpr int kRows = 32;
+constexpr int kWaves = 8;
+constexpr int kStages = 4;
+constexpr int kStageBytes = kRows * kR * 2;          // 32 KB
+constexpr int kSmem = kStages * kStageBytes;         // 128 KB, also one weight half
+constexpr int kCopies = kRows / kWaves;              // one row per copy instruction
+static_assert(kSmem >= (kR / 2) * 512, "a half of the weight staging fits");
+}  // namespace wsf
+
+template <int E>
+__global__ __launch_bounds__(wsf::kWaves * 64, 1) void kvb_fp_ws_kernel(
+    const uint16_t* __restrict__ Y, const uint16_t* __restrict__ Wb, int T, int nh, int msplit,
+    int bps, uint16_t* __restrict__ k_nope, uint16_t* __restrict__ value_out) {
+    using namespace wsf;
+    constexpr int BRB = 512;  // bytes of a staged weight row (the head's 256 columns)
+    constexpr int NT = kWaves * 64;
+    __shared__ __align__(1024) uint8_t smem[kSmem];
+    const int items = nh * msplit, per = (items + 7) / 8;
+    const int xk = (int)(blockIdx.x >> 3), item = (int)(blockIdx.x & 7) * per + xk;
+    if (xk >= per || item >= items) return;
+    const int ms = item / nh, head = item - ms * nh;
+    const int nblk = (T + kRows - 1) / kRows, bfirst = ms * bps;
+    const int nb = min(bps, nblk - bfirst);
+    if (nb <= 0) return;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g = lane >> 4;
+    const int64_t N2 = (int64_t)nh * kHeadW;
+    const int col0 = head * kHeadW, wn0 = wave * 32;
+
+    // ---- the head's weights, K in two halves: row k of its 256 columns at
+    // LDS row k - k0, 16-byte chunk c at c ^ bswz(k); then each wave's
+    // fragments of the half's 8 K steps.  Fragment (ks, j): lane (16 g + s)
+    // receives column wn0 + 16 j + s, rows 32 ks + 8 g .. + 7 (two
+    // transposing reads of 4 rows).
+    u4_t fb[16][2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int k0 = half * (kR / 2);
+#pragma unroll 8
+        for (int it = 0; it < (kR / 2) * BRB / 16 / NT; ++it) {
+            const int q = it * NT + tid, kk = q >> 5, c = q & 31, k = k0 + kk;
+            const u4_t v = *(const u4_t*)((const uint8_t*)Wb + (k * N2 + col0) * 2 + c * 16);
+            *(u4_t*)(smem + brow<E, BRB>(kk) * BRB + ((c ^ bswz<E, BRB>(kk)) << 4)) = v;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kq = 0; kq < 8; ++kq) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int kk = kq * 32 + g * 8 + (l16 >> 2);
+                const int colb = (wn0 + j * 16 + 4 * (l16 & 3)) * 2;
+                const int c = colb >> 4, off = colb & 15;
+                const uint2 lo = lds_tr16(smem + brow<E, BRB>(kk) * BRB +
+                                          ((c ^ bswz<E, BRB>(kk)) << 4) + off);
+                const uint2 hi = lds_tr16(smem + brow<E, BRB>(kk + 4) * BRB +
+                                          ((c ^ bswz<E, BRB>(kk + 4)) << 4) + off);
+                fb[half * 8 + kq][j] = u4_t{lo.x, lo.y, hi.x, hi.y};
+            }
+        }
+        // every load and fragment read done before the memory is reused
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    // ---- ring
+    const int m_first = bfirst * kRows;
+    const uint32_t sbase =
+        lds_addr(smem) + (uint32_t)__builtin_amdgcn_readfirstlane(wave * kCopies * kR * 2);
+    uint32_t aoff[kCopies];
+#pragma unroll
+    for (int q = 0; q < kCopies; ++q) {
+        const int r = wave * kCopies + q;
+        aoff[q] = (uint32_t)((lane ^ (r & 15)) << 4);
+    }
+    auto issue = [&](int bb) {
+        const int m0 = m_first + min(bb, nb - 1) * kRows;
+        const uint32_t so = (uint32_t)((bb % kStages) * kStageBytes);
+#pragma unroll
+        for (int q = 0; q < kCopies; ++q) {
+            const int row = min(m0 + wave * kCopies + q, T - 1);
+            dma16s(Y + (int64_t)row * kR, aoff[q], sbase + so + q * kR * 2);
+        }
+    };
+    // after block b's copies this wave issued kStages - 2 later groups of
+    // kCopies copies and, from block kStages on, kStages - 1 groups of 2
+    // stores; before that it counts the copies only (it waits for more)
+    auto wait_stage = [&](int b) {
+        constexpr int D = kStages;
+        if (b < D) wait_vm_lds_barrier<kCopies * (D - 2)>();
+        else wait_vm_lds_barrier<kCopies * (D - 2) + 2 * (D - 1)>();
+    };
+    uint32_t aro[16][2];
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            aro[ks][i] = (uint32_t)((16 * i + l16) * kR * 2 + (((ks * 4 + g) ^ l16) << 4));
+    typedef f4_t acc_t;
+    auto mma_block = [&](acc_t(&acc)[2][2], int b) {
+        const uint8_t* s = smem + (b % kStages) * kStageBytes;
+        u4_t fa[3][2];
+        auto rd = [&](int ks) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) fa[ks % 3][i] = *(const u4_t*)(s + aro[ks][i]);
+        };
+        rd(0);
+        rd(1);
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+            if (ks + 2 < 16) rd(ks + 2);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = mfma16<E>(fb[ks][j], fa[ks % 3][i],
+                                          ks == 0 ? acc_t{0.f, 0.f, 0.f, 0.f} : acc[i][j]);
+        }
+    };
+    uint16_t* const dst0 = (wave < 4 ? k_nope : value_out) + (int64_t)head * kDN + (wave & 3) * 32;
+    const int64_t rstride = (int64_t)nh * kDN;
+    const uint32_t doff =
+        (uint32_t)((l16 * rstride + ((g & 1) ? 16 + 4 * (g - 1) : 4 * g)) * 2);
+    auto epi_block = [&](const acc_t(&acc)[2][2], int b, auto guard) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int row0 = m_first + b * kRows + 16 * i, row = row0 + l16;
+            const uint32_t p00 = cvt_pk<E>(acc[i][0][0], acc[i][0][1]);
+            const uint32_t p01 = cvt_pk<E>(acc[i][0][2], acc[i][0][3]);
+            const uint32_t p10 = cvt_pk<E>(acc[i][1][0], acc[i][1][1]);
+            const uint32_t p11 = cvt_pk<E>(acc[i][1][2], acc[i][1][3]);
+            const auto s0 = __builtin_amdgcn_permlane16_swap(p00, p10, false, false);
+            const auto s1 = __builtin_amdgcn_permlane16_swap(p01, p11, false, false);
+            const u4_t v = u4_t{s0[0], s1[0], s0[1], s1[1]};
+            uint8_t* d = (uint8_t*)(dst0 + row0 * rstride) + doff;
+            if constexpr (decltype(guard)::value) {
+                if (row < T) __builtin_nontemporal_store(v, (u4_t*)d);
+            } else {
+                __builtin_nontemporal_store(v, (u4_t*)d);
+            }
+        }
+    };
+    typedef std::integral_constant<bool, false> NoGuard;
+    typedef std::integral_constant<bool, true> Guard;
+
+    acc_t accA[2][2], accB[2][2];
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s) issue(s);
+    wait_stage(0);
+    issue(kStages - 1);
+    mma_block(accA, 0);
+    int b = 1;
+    for (; b + 1 < nb; b += 2) {
+        wait_stage(b);
+        issue(b + kStages - 1);
+        mma_block(accB, b);
+        epi_block(accA, b - 1, NoGuard{});
+        wait_stage(b + 1);
+        issue(b + kStages);
+        mma_block(accA, b + 1);
+        epi_block(accB, b, NoGuard{});
+    }
+    if (b < nb) {
+        wait_stage(b);
+        mma_block(accB, b);
+        epi_block(accA, b - 1, NoGuard{});
+        epi_block(accB, b, Guard{});
+    } else {
+        epi_block(accA, b - 1, Guard{});
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Per-token finish of kv_a_proj, fp16/bf16 path.  One wave per token, four
 // tokens per workgroup: lane l owns latent columns 8l..8l+7 and rope column
 // l.  Every load (position, gamma, partials) is issued before the first use.
@@ -1496,10 +1682,12 @@ static void gemm_launch(const void* A, int64_t lda, const void* B, int64_t ldb, 
 }
 
 constexpr int64_t kPersistentGrid = 256;  // MI355X compute units
-// W8A8 calls from this many tokens on use the weight-stationary kv_b_proj
-// kernel (each workgroup's 128 KB weight load is then spread over enough
-// latent rows)
+// Prefill calls from this many tokens on use the weight-stationary kv_b_proj
+// kernels (each workgroup's 128 or 256 KB weight load is then spread over
+// enough latent rows)
 constexpr int64_t kWsMinTokens = 2048;
+// and the fp16 / bf16 kernel only when each row range holds this many rows
+constexpr int64_t kWsFpMinRows = 2048;
 
 // K is split S ways (S must divide K's slab count); split s writes its
 // partial through epi.ptr(row, col, s).  WGPC workgroups share a CU (their
@@ -1576,6 +1764,30 @@ static void kvb_w8_ws_launch(const int8_t* QZ, const int8_t* Wqb, int64_t T, int
                  e.dbg_begin, e.dbg_rows);
 }
 
+// fp16 / bf16 kv_b_proj, weight-stationary kernel: as kvb_w8_ws_launch.
+// Worth it only when each row range is long: a workgroup's 256 KB weight
+// load should be small next to the latent rows it then streams.
+static int kvb_ws_ranges(int64_t T, int nh, int rows) {
+    const int nblk = (int)((T + rows - 1) / rows);
+    const int msplit = std::min<int>(nblk, std::max<int>(1, (int)(kPersistentGrid / nh)));
+    const int bps = (nblk + msplit - 1) / msplit;
+    return (nblk + bps - 1) / bps;
+}
+static bool kvb_fp_ws_pays(int64_t T, int nh) {
+    return T >= kWsMinTokens && T / kvb_ws_ranges(T, nh, wsf::kRows) >= kWsFpMinRows;
+}
+template <int E>
+static void kvb_fp_ws_launch(const void* Y, const void* Wb, int64_t T, int nh, void* k_nope,
+                             void* value, hipStream_t st) {
+    const int nblk = (int)((T + wsf::kRows - 1) / wsf::kRows);
+    const int msplit = kvb_ws_ranges(T, nh, wsf::kRows);
+    const int bps = (nblk + msplit - 1) / msplit;
+    const int items = nh * msplit, per = (items + 7) / 8;
+    launch_k(kvb_fp_ws_kernel<E>, dim3((unsigned)(8 * per)), dim3(wsf::kWaves * 64), 0, st,
+             (const uint16_t*)Y, (const uint16_t*)Wb, (int)T, nh, msplit, bps,
+             (uint16_t*)k_nope, (uint16_t*)value);
+}
+
 void launch_finish_fp(int dt, const float* P, int S, int64_t T, const void* gamma,
                       const int32_t* pos, float eps, const RopeTab& rt, void* ckv, void* kpe,
                       const CacheOut& co, hipStream_t st) {
@@ -1622,8 +1834,11 @@ static hipError_t launch_fp_t(const void* X, const void* Wa, const void* gamma, 
                           EpiPartialF32{P1, T}, st);
     launch_finish_fp(E, P1, plan.s1, T, gamma, pos, eps, rt, ckv, k_pe, co, st);
     const int N2 = nh * kHeadW;
-    gemm2_dispatch<E>(plan.bm2, plan.bn2, ckv, (int64_t)kR * 2, Wb, T, N2,
-                      EpiKvFp<E>{(uint16_t*)k_nope, (uint16_t*)value, nh}, st);
+    if (plan.path == 1 && kvb_fp_ws_pays(T, nh))
+        kvb_fp_ws_launch<E>(ckv, Wb, T, nh, k_nope, value, st);
+    else
+        gemm2_dispatch<E>(plan.bm2, plan.bn2, ckv, (int64_t)kR * 2, Wb, T, N2,
+                          EpiKvFp<E>{(uint16_t*)k_nope, (uint16_t*)value, nh}, st);
     return hipGetLastError();
 }
 

@@ -191,6 +191,18 @@ def test_w8a8_weight_stationary_kv_b(dev, nh, T):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
+@pytest.mark.parametrize("dtype,nh,T", [("f16", 128, 4100), ("bf16", 257, 2049)])
+def test_fp_weight_stationary_kv_b(dev, dtype, nh, T):
+    # fp16 / bf16 prefills that take the weight-stationary kv_b_proj kernel
+    # (row ranges of at least 2048 rows): two ranges of 2050 rows at R1's
+    # head count with a ragged 4-row last block; an odd head count above the
+    # CU count (more workgroups than fit at once) with one range and a
+    # 1-row last block.  Every row against the oracle.
+    d = Dims(H=512, nh=nh)
+    w = workloads.make_custom(d, T, dtype=dtype, seed=520 + nh, wstd=0.03, max_pos=8192)
+    check_full(w, dev, f"{dtype}_ws_nh{nh}_T{T}", path=1)
+
+
 @pytest.mark.parametrize("H,T", [(640, 7), (8320, 6)])
 def test_w8a8_hidden_sizes_exact(dev, H, T):
     # the activation quantiser: H = 640 leaves lanes with a partial last chunk
