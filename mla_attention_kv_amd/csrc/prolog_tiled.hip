@@ -1549,52 +1549,17 @@ __global__ __launch_bounds__(256) void quant_rows_long_kernel(const uint16_t* __
 //   inv_t = 1/sqrt(sum(c^2)/512 + eps);  compressed_kv = bf16(z * inv_t)
 //   k_pe = RoPE(p)
 // ---------------------------------------------------------------------------
-template <int B>
-__global__ __launch_bounds__(256) void finish_a_w8_kernel(
-    const int32_t* __restrict__ P, int S, int64_t T, const float* __restrict__ sx,
-    const float* __restrict__ swa, const uint16_t* __restrict__ gamma,
-    const int32_t* __restrict__ pos, float eps, RopeTab rt, int8_t* __restrict__ QZ,
+// The finish of token t once lane l holds the token's int32 kv_a_proj sums of
+// latent columns 8l .. 8l + 7 (a) and of rope column l (ap): dequantise,
+// RMSNorm, quantise z = c * gamma, RoPE, and the writes.  One wave; the sums
+// are exact integers, so how the splits were added does not matter.
+__device__ __forceinline__ void w8_finish_token(
+    const int (&a)[8], int ap, int64_t t, int pt, int64_t slot, float sxt, f4_t wa0, f4_t wa1,
+    float wap, u4_t gm, float eps, const RopeTab& rt, int8_t* __restrict__ QZ,
     float* __restrict__ sz, float* __restrict__ inv_out, uint16_t* __restrict__ ckv,
     uint16_t* __restrict__ kpe, int32_t* __restrict__ dbg, int64_t dbg_begin, int64_t dbg_rows,
-    CacheOut co) {
-    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
+    const CacheOut& co) {
     const int lane = threadIdx.x & 63;
-    // every load before the first use
-    const int pt = pos[t];
-    const int64_t slot = co.slots != nullptr ? co.slots[t] : -1;
-    const float sxt = sx[t];
-    const f4_t wa0 = *(const f4_t*)(swa + 8 * lane), wa1 = *(const f4_t*)(swa + 8 * lane + 4);
-    const float wap = swa[kR + lane];
-    const u4_t gm = *(const u4_t*)(gamma + 8 * lane);
-    int a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    int ap = 0;
-    // the split-K partials, B splits' loads in flight at a time (B as in
-    // finish_a_fp_kernel; splits past S re-read split S - 1 and are not added)
-    for (int s0 = 0; s0 < S; s0 += B) {
-        i4_t v0[B], v1[B];
-        int pv[B];
-#pragma unroll
-        for (int j = 0; j < B; ++j) {
-            const int s = s0 + j < S ? s0 + j : S - 1;
-            const int32_t* row = P + ((int64_t)s * T + t) * kN1;
-            // partials are read once: streaming (non-temporal) loads
-            v0[j] = __builtin_nontemporal_load((const i4_t*)(row + 8 * lane));
-            v1[j] = __builtin_nontemporal_load((const i4_t*)(row + 8 * lane + 4));
-            pv[j] = __builtin_nontemporal_load(row + kR + lane);
-        }
-#pragma unroll
-        for (int j = 0; j < B; ++j) {
-            if (s0 + j < S) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    a[i] += v0[j][i];
-                    a[4 + i] += v1[j][i];
-                }
-                ap += pv[j];
-            }
-        }
-    }
     if (dbg != nullptr && t >= dbg_begin && t < dbg_begin + dbg_rows) {
         int32_t* d = dbg + (t - dbg_begin) * kN1;
 #pragma unroll
@@ -1664,6 +1629,127 @@ __global__ __launch_bounds__(256) void finish_a_w8_kernel(
             if (lane == 0) co.scale[slot] = (am > 0.f) ? (am / 127.0f) : 0.f;
         }
     }
+}
+
+template <int B>
+__global__ __launch_bounds__(256) void finish_a_w8_kernel(
+    const int32_t* __restrict__ P, int S, int64_t T, const float* __restrict__ sx,
+    const float* __restrict__ swa, const uint16_t* __restrict__ gamma,
+    const int32_t* __restrict__ pos, float eps, RopeTab rt, int8_t* __restrict__ QZ,
+    float* __restrict__ sz, float* __restrict__ inv_out, uint16_t* __restrict__ ckv,
+    uint16_t* __restrict__ kpe, int32_t* __restrict__ dbg, int64_t dbg_begin, int64_t dbg_rows,
+    CacheOut co) {
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const int lane = threadIdx.x & 63;
+    // every load before the first use
+    const int pt = pos[t];
+    const int64_t slot = co.slots != nullptr ? co.slots[t] : -1;
+    const float sxt = sx[t];
+    const f4_t wa0 = *(const f4_t*)(swa + 8 * lane), wa1 = *(const f4_t*)(swa + 8 * lane + 4);
+    const float wap = swa[kR + lane];
+    const u4_t gm = *(const u4_t*)(gamma + 8 * lane);
+    int a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int ap = 0;
+    // the split-K partials, B splits' loads in flight at a time (B as in
+    // finish_a_fp_kernel; splits past S re-read split S - 1 and are not added)
+    for (int s0 = 0; s0 < S; s0 += B) {
+        i4_t v0[B], v1[B];
+        int pv[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            const int s = s0 + j < S ? s0 + j : S - 1;
+            const int32_t* row = P + ((int64_t)s * T + t) * kN1;
+            // partials are read once: streaming (non-temporal) loads
+            v0[j] = __builtin_nontemporal_load((const i4_t*)(row + 8 * lane));
+            v1[j] = __builtin_nontemporal_load((const i4_t*)(row + 8 * lane + 4));
+            pv[j] = __builtin_nontemporal_load(row + kR + lane);
+        }
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            if (s0 + j < S) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    a[i] += v0[j][i];
+                    a[4 + i] += v1[j][i];
+                }
+                ap += pv[j];
+            }
+        }
+    }
+    w8_finish_token(a, ap, t, pt, slot, sxt, wa0, wa1, wap, gm, eps, rt, QZ, sz, inv_out, ckv, kpe,
+                    dbg, dbg_begin, dbg_rows, co);
+}
+
+// The same finish for calls with many K splits and few tokens: one
+// workgroup per token, wave w adding splits w, w + 4, ... with all of its
+// NPW loads in flight at once (those past S re-read split S - 1 and are not
+// added); the four wave sums meet in LDS and wave 0 finishes the token.
+template <int NPW>
+__global__ __launch_bounds__(256) void finish_w8_wide_kernel(
+    const int32_t* __restrict__ P, int S, int64_t T, const float* __restrict__ sx,
+    const float* __restrict__ swa, const uint16_t* __restrict__ gamma,
+    const int32_t* __restrict__ pos, float eps, RopeTab rt, int8_t* __restrict__ QZ,
+    float* __restrict__ sz, float* __restrict__ inv_out, uint16_t* __restrict__ ckv,
+    uint16_t* __restrict__ kpe, int32_t* __restrict__ dbg, int64_t dbg_begin, int64_t dbg_rows,
+    CacheOut co) {
+    __shared__ __align__(16) int red[3][64 * 9];
+    const int64_t t = blockIdx.x;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    int pt = 0;
+    int64_t slot = -1;
+    float sxt = 0.f, wap = 0.f;
+    f4_t wa0 = {0.f, 0.f, 0.f, 0.f}, wa1 = wa0;
+    u4_t gm = {0u, 0u, 0u, 0u};
+    if (wave == 0) {
+        pt = pos[t];
+        slot = co.slots != nullptr ? co.slots[t] : -1;
+        sxt = sx[t];
+        wa0 = *(const f4_t*)(swa + 8 * lane);
+        wa1 = *(const f4_t*)(swa + 8 * lane + 4);
+        wap = swa[kR + lane];
+        gm = *(const u4_t*)(gamma + 8 * lane);
+    }
+    i4_t v0[NPW], v1[NPW];
+    int pv[NPW];
+#pragma unroll
+    for (int j = 0; j < NPW; ++j) {
+        const int s = wave + 4 * j < S ? wave + 4 * j : S - 1;
+        const int32_t* row = P + ((int64_t)s * T + t) * kN1;
+        v0[j] = __builtin_nontemporal_load((const i4_t*)(row + 8 * lane));
+        v1[j] = __builtin_nontemporal_load((const i4_t*)(row + 8 * lane + 4));
+        pv[j] = __builtin_nontemporal_load(row + kR + lane);
+    }
+    int a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int ap = 0;
+#pragma unroll
+    for (int j = 0; j < NPW; ++j) {
+        if (wave + 4 * j < S) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                a[i] += v0[j][i];
+                a[4 + i] += v1[j][i];
+            }
+            ap += pv[j];
+        }
+    }
+    if (wave > 0) {
+        int* r = red[wave - 1] + lane * 9;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r[i] = a[i];
+        r[8] = ap;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+        const int* r = red[w] + lane * 9;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] += r[i];
+        ap += r[8];
+    }
+    w8_finish_token(a, ap, t, pt, slot, sxt, wa0, wa1, wap, gm, eps, rt, QZ, sz, inv_out, ckv, kpe,
+                    dbg, dbg_begin, dbg_rows, co);
 }
 
 // ---------------------------------------------------------------------------
@@ -1907,9 +1993,19 @@ hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa, const
                      sx, swa, (const uint16_t*)gamma, pos, eps, rt, QZ, sz, inv,
                      (uint16_t*)ckv, (uint16_t*)k_pe, dbg1, dbg_begin, dbg_rows, co);
         };
+        // many splits: one workgroup per token, the splits over four waves
+        auto wide = [&](auto kern) {
+            launch_k(kern, dim3((unsigned)T), dim3(256), 0, st, P1, S, T, sx, swa,
+                     (const uint16_t*)gamma, pos, eps, rt, QZ, sz, inv, (uint16_t*)ckv,
+                     (uint16_t*)k_pe, dbg1, dbg_begin, dbg_rows, co);
+        };
         if (S <= 1) go(finish_a_w8_kernel<1>);
         else if (S <= 2) go(finish_a_w8_kernel<2>);
         else if (S <= 4) go(finish_a_w8_kernel<4>);
+        else if (S <= 8) go(finish_a_w8_kernel<8>);
+        else if (S <= 16) wide(finish_w8_wide_kernel<4>);
+        else if (S <= 32) wide(finish_w8_wide_kernel<8>);
+        else if (S <= 64) wide(finish_w8_wide_kernel<16>);
         else go(finish_a_w8_kernel<8>);
     }
     const int N2 = nh * kHeadW;

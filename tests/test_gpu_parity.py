@@ -203,6 +203,20 @@ def test_fp_weight_stationary_kv_b(dev, dtype, nh, T):
     check_full(w, dev, f"{dtype}_ws_nh{nh}_T{T}", path=1)
 
 
+@pytest.mark.parametrize("H,T,path,nh", [(7168, 1, 0, 8), (7168, 5, 0, 8), (7168, 64, 0, 8),
+                                         (2304, 3, 0, 4), (12288, 1, 1, 2), (16384, 2, 1, 2)])
+def test_w8a8_many_splits_exact(dev, H, T, path, nh):
+    # W8A8 calls whose kv_a_proj is split over K more than 8 ways (9 to 64
+    # splits: H = 2304 on path 0 gives 9, R1's H = 7168 on path 0 gives 28,
+    # H = 12288 and 16384 on path 1 give 48 and 64): the finish sums the
+    # splits over four waves per token.  int32 accumulators of both
+    # projections bit-exact, outputs within tolerance, every row.
+    d = Dims(H=H, nh=nh)
+    w = workloads.make_custom(d, T, kind="w8a8", dtype="bf16", seed=530 + T + H % 97,
+                              wstd=0.01)
+    check_full(w, dev, f"w8a8_H{H}_T{T}_p{path}", path=path, dbg=True)
+
+
 @pytest.mark.parametrize("H,T", [(640, 7), (8320, 6)])
 def test_w8a8_hidden_sizes_exact(dev, H, T):
     # the activation quantiser: H = 640 leaves lanes with a partial last chunk
