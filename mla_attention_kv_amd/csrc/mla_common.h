@@ -283,6 +283,144 @@ hipError_t launch_rope(int dt, const void* x, const int32_t* pos, int64_t T, int
 hipError_t launch_kv_cache_append(int dt, const void* ckv, const void* kpe, const int64_t* slots,
                                   int64_t T, int64_t num_slots, void* cache, int8_t* cache_q,
                                   float* scale, hipStream_t st);
+// Device-coherent 8- and 4-byte accesses (single-copy atomic, seen by every
+// XCD): the hand-offs between workgroups of one launch.
+__device__ __forceinline__ void store_coherent64(void* p, uint64_t v) {
+    __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load_coherent64(const void* p) {
+    return __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent32(void* p, uint32_t v) {
+    __hip_atomic_store((uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_coherent32(const void* p) {
+    return __hip_atomic_load((const uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// W8A8: the latent of one token from its exact int32 kv_a_proj sums, lane l
+// holding latent columns 8l .. 8l + 7 (one wave):
+//   c = (acc * sx) * s_a,  z = c * gamma,
+//   inv = 1 / sqrt(sum(c^2) / 512 + eps)   (the RMS factor of c),
+//   codes = rint(z * 127 / amax(z)) clamped to +-127, scale = amax(z) / 127.
+// No contraction, so every inlined copy (the finish kernels', a hand-off
+// producer's and its fallback's) is the same sequence of fp32 operations.
+struct W8Latent {
+    float z[8];
+    u2_t q;
+    float sz, inv;
+};
+__device__ __forceinline__ W8Latent w8_latent(const int (&a)[8], float sxt, f4_t wa0, f4_t wa1,
+                                              u4_t gm, float eps) {
+#pragma clang fp contract(off)
+    W8Latent r;
+    float c[8];
+    float ss = 0.f, az = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float w = i < 4 ? wa0[i] : wa1[i - 4];
+        c[i] = ((float)a[i] * sxt) * w;
+        const uint16_t gb = (uint16_t)(gm[i >> 1] >> (16 * (i & 1)));
+        r.z[i] = c[i] * bf16_to_f32(gb);
+        ss += c[i] * c[i];
+        az = fmaxf(az, fabsf(r.z[i]));
+    }
+    ss = wave_sum(ss);
+    az = wave_max(az);
+    r.inv = 1.0f / sqrtf(ss / (float)kR + eps);
+    const float inv2 = (az > 0.f) ? (127.0f / az) : 0.f;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            float q = rintf(r.z[w * 4 + b] * inv2);
+            q = fminf(fmaxf(q, -127.f), 127.f);
+            packed |= ((uint32_t)(uint8_t)(int8_t)(int)q) << (8 * b);
+        }
+        r.q[w] = packed;
+    }
+    r.sz = (az > 0.f) ? (az / 127.0f) : 0.f;
+    return r;
+}
+
+// The W8A8 finish of token t once lane l holds the token's int32 kv_a_proj
+// sums of latent columns 8l .. 8l + 7 (a) and of rope column l (ap), one
+// wave: the latent codes and scales (with COH through device-coherent
+// stores, for a hand-off), compressed_kv = bf16(z * inv), k_pe, the paged
+// cache and the accumulator debug copy.
+template <bool COH>
+__device__ __forceinline__ void w8_finish_token(
+    const int (&a)[8], int ap, int64_t t, int pt, int64_t slot, float sxt, f4_t wa0, f4_t wa1,
+    float wap, u4_t gm, float eps, const RopeTab& rt, int8_t* __restrict__ QZ,
+    float* __restrict__ sz, float* __restrict__ inv_out, uint16_t* __restrict__ ckv,
+    uint16_t* __restrict__ kpe, int32_t* __restrict__ dbg, int64_t dbg_begin, int64_t dbg_rows,
+    const CacheOut& co) {
+    const int lane = threadIdx.x & 63;
+    if (dbg != nullptr && t >= dbg_begin && t < dbg_begin + dbg_rows) {
+        int32_t* d = dbg + (t - dbg_begin) * kN1;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d[8 * lane + i] = a[i];
+        d[kR + lane] = ap;
+    }
+    const W8Latent L = w8_latent(a, sxt, wa0, wa1, gm, eps);
+    const float p = ((float)ap * sxt) * wap;
+    u4_t o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+        o[w] = (uint32_t)f32_to_bf16(L.z[2 * w] * L.inv) |
+               ((uint32_t)f32_to_bf16(L.z[2 * w + 1] * L.inv) << 16);
+    if constexpr (COH) {
+        store_coherent64(QZ + t * kR + 8 * lane, (uint64_t)L.q[0] | ((uint64_t)L.q[1] << 32));
+        if (lane == 0) {
+            store_coherent32(sz + t, __builtin_bit_cast(uint32_t, L.sz));
+            store_coherent32(inv_out + t, __builtin_bit_cast(uint32_t, L.inv));
+        }
+    } else {
+        *(u2_t*)(QZ + t * kR + 8 * lane) = L.q;
+        if (lane == 0) {
+            sz[t] = L.sz;
+            inv_out[t] = L.inv;
+        }
+    }
+    *(u4_t*)(ckv + t * kR + 8 * lane) = o;
+    const float partner = __shfl_xor(p, 32, 64);
+    float cs, sn;
+    rope_cos_sin(pt, rt.f[lane & 31], cs, sn);
+    const float out = rope_rotate(p, partner, cs, sn, lane < 32);
+    const uint16_t ko = f32_to_bf16(out);
+    __builtin_nontemporal_store(ko, kpe + t * kDR + lane);
+    if (cache_slot_ok(co, slot)) {
+        // the paged cache, [latent | rope key] in the token's slot: the
+        // returned bf16 rows, or their int8 codes and the slot's scale
+        constexpr int W = kR + kDR;
+        if (co.cache_q == nullptr) {
+            uint16_t* row = co.cache + slot * W;
+            __builtin_nontemporal_store(o, (u4_t*)(row + 8 * lane));
+            __builtin_nontemporal_store(ko, row + kR + lane);
+        } else {
+            const float am = wave_max(fmaxf(absmax8_e<kBF16>(o, 0.f), fabsf(bf16_to_f32(ko))));
+            const float qi = (am > 0.f) ? (127.0f / am) : 0.f;
+            int8_t* row = co.cache_q + slot * W;
+            __builtin_nontemporal_store(codes8<kBF16>(o, qi), (u2_t*)(row + 8 * lane));
+            float rk = rintf(bf16_to_f32(ko) * qi);
+            rk = fminf(fmaxf(rk, -127.f), 127.f);
+            __builtin_nontemporal_store((int8_t)(int)rk, row + kR + lane);
+            if (lane == 0) co.scale[slot] = (am > 0.f) ? (am / 127.0f) : 0.f;
+        }
+    }
+}
+
+// W8A8 at decode sizes: whether the finish fused into kv_b_proj applies to
+// T tokens, nh heads and S kv_a_proj splits on the current device (its
+// grid resident at once), and its launch (prolog_decode.hip).
+bool w8_decode_fused_fits(int64_t T, int nh, int S);
+void launch_w8_fin_kv_b(const int32_t* P, int S, int64_t T, const float* sx, const float* swa,
+                        const void* gamma, const int32_t* pos, float eps, const RopeTab& rt,
+                        const int8_t* Wqb, const float* swb, int nh, int8_t* QZ, float* sz,
+                        float* inv, void* ckv, void* k_pe, void* k_nope, void* value,
+                        int32_t* dbg1, int32_t* dbg2, int64_t dbg_begin, int64_t dbg_rows,
+                        const CacheOut& co, hipStream_t st);
 
 // The decode family's finish + kv_b_proj hand-off: set the bound on its
 // polls (negative: the default; returns the previous setting), and read

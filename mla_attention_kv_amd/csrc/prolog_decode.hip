@@ -231,12 +231,6 @@ __global__ __launch_bounds__(256) void dec_kv_a_kernel(const uint16_t* __restric
 // (through to memory), for workgroups on other XCDs that read it in the same
 // launch.  fred: 4 x (576 + 4) floats of LDS.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void store_coherent64(void* p, uint64_t v) {
-    __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t load_coherent64(const void* p) {
-    return __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 constexpr int kFredPitch = kN1 + 4;
 
@@ -557,6 +551,268 @@ __global__ __launch_bounds__(256) void dec_fin_kv_b_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// W8A8 at decode sizes (up to 16 tokens, one token tile): the finish fused
+// into kv_b_proj, as dec_fin_kv_b_kernel.  Items are 64-column slabs of the
+// int8 W_kv_b over K = 512 (32 KB each).  Workgroup b < T first finishes
+// token b: its four waves add the int32 split-K partials (splits w, w + 4,
+// ...; exact in any order) and wave 0 forms the latent codes, their scale
+// and the RMS factor (w8_latent), compressed_kv, k_pe and the cache, the
+// codes and both scales through device-coherent stores.  The activation
+// quantiser of the same call filled every code row with 0x80 bytes (a code
+// the quantisers never produce) and both scales with all-ones words, so an
+// 8-byte chunk of codes or a scale is final once it holds no such byte or
+// word.  Every workgroup stages its slab, polls its tile's codes and scales
+// with coherent loads (bounded), multiplies with v_mfma_i32_16x16x64_i8
+// (tokens as M; wave w owns slab columns 16 w .. 16 w + 15, weight operands
+// from two transposing LDS reads), and writes ((acc * (sz * inv)) * s_b)
+// rounded to bf16.  A workgroup that runs out of polls rebuilds its tile's
+// codes and scales from the partials itself (the same operations, so the
+// same bits) and counts one fallback.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool has_0x80_byte(uint64_t x) {
+    const uint64_t y = x ^ 0x8080808080808080ull;  // a 0x80 byte becomes 0
+    return ((y - 0x0101010101010101ull) & ~y & 0x8080808080808080ull) != 0ull;
+}
+
+// int32 sums of token t's split-K partials: wave w adds splits w, w + 4,
+// ... (NPW loads in flight; those past S re-read split S - 1 and are not
+// added).  w8_parts_load issues the loads; w8_parts_sum adds them, waves
+// 1..3 leave theirs in red, and after the barrier wave 0 holds the total
+// (the caller synchronises before red is reused).
+template <int NPW>
+struct W8Parts {
+    i4_t v0[NPW], v1[NPW];
+    int pv[NPW];
+};
+template <int NPW>
+__device__ __forceinline__ void w8_parts_load(W8Parts<NPW>& r, const int32_t* __restrict__ P,
+                                              int S, int T, int t) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < NPW; ++j) {
+        const int s = wave + 4 * j < S ? wave + 4 * j : S - 1;
+        const int32_t* row = P + ((int64_t)s * T + t) * kN1;
+        r.v0[j] = __builtin_nontemporal_load((const i4_t*)(row + 8 * lane));
+        r.v1[j] = __builtin_nontemporal_load((const i4_t*)(row + 8 * lane + 4));
+        r.pv[j] = __builtin_nontemporal_load(row + kR + lane);
+    }
+}
+template <int NPW>
+__device__ __forceinline__ void w8_parts_sum(const W8Parts<NPW>& r, int S, int (*red)[64 * 9],
+                                             int (&a)[8], int& ap) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = 0;
+    ap = 0;
+#pragma unroll
+    for (int j = 0; j < NPW; ++j) {
+        if (wave + 4 * j < S) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                a[i] += r.v0[j][i];
+                a[4 + i] += r.v1[j][i];
+            }
+            ap += r.pv[j];
+        }
+    }
+    if (wave > 0) {
+        int* d = red[wave - 1] + lane * 9;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d[i] = a[i];
+        d[8] = ap;
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int w = 0; w < 3; ++w) {
+            const int* d = red[w] + lane * 9;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a[i] += d[i];
+            ap += d[8];
+        }
+    }
+}
+
+// Wave 0's per-token inputs of the W8A8 finish.
+struct W8Aux {
+    int pt;
+    int64_t slot;
+    float sxt, wap;
+    f4_t wa0, wa1;
+    u4_t gm;
+};
+__device__ __forceinline__ W8Aux w8_aux_load(const float* __restrict__ sx,
+                                             const float* __restrict__ swa,
+                                             const uint16_t* __restrict__ gamma,
+                                             const int32_t* __restrict__ pos, const CacheOut& co,
+                                             int t) {
+    const int lane = threadIdx.x & 63;
+    W8Aux x;
+    x.pt = pos[t];
+    x.slot = co.slots != nullptr ? co.slots[t] : -1;
+    x.sxt = sx[t];
+    x.wa0 = *(const f4_t*)(swa + 8 * lane);
+    x.wa1 = *(const f4_t*)(swa + 8 * lane + 4);
+    x.wap = swa[kR + lane];
+    x.gm = *(const u4_t*)(gamma + 8 * lane);
+    return x;
+}
+
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 lds_tr8_w(const int8_t* p) {
+    const v2i_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) v2i_t*)(p));
+    return __builtin_bit_cast(uint2, r);
+}
+
+__device__ unsigned int g_handoff_fallbacks_w8 = 0;
+
+template <int NPW>
+__global__ __launch_bounds__(256) void dec_fin_kv_b_w8_kernel(
+    const int32_t* __restrict__ P, int S, int T, const float* __restrict__ sx,
+    const float* __restrict__ swa, const uint16_t* __restrict__ gamma,
+    const int32_t* __restrict__ pos, float eps, RopeTab rt, const int8_t* __restrict__ Wqb,
+    const float* __restrict__ swb, int N2, int8_t* QZ, float* sz, float* inv,
+    uint16_t* __restrict__ ckv, uint16_t* __restrict__ kpe, uint16_t* __restrict__ k_nope,
+    uint16_t* __restrict__ value, int32_t* __restrict__ dbg1, int32_t* __restrict__ dbg2,
+    int64_t dbg_begin, int64_t dbg_rows, CacheOut co, uint32_t spin_limit) {
+    constexpr int WP = kSlabW + 16;  // LDS pitch of a staged slab row (bytes)
+    constexpr int AP = kR + 16;      // LDS pitch of a latent code row (bytes)
+    __shared__ __align__(16) int8_t ldsW[kR * WP];
+    __shared__ __align__(16) int8_t ldsA[16 * AP];
+    __shared__ __align__(16) int red[3][64 * 9];
+    __shared__ float lsz[16], linv[16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int nh = N2 / kHeadW;
+    const int item = xcd_item(N2 / kSlabW);
+    // the slab: rows k = (tid >> 2) + 64 u, 16-byte chunk tid & 3; requested
+    // after the finishing workgroup's partials, so that the finish does not
+    // wait for the slab (padding workgroups read slab 0)
+    const int n0 = (item >= 0 ? item : 0) * kSlabW;
+    u4_t v[8];
+    auto slab_load = [&]() {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            v[u] = __builtin_nontemporal_load(
+                (const u4_t*)(Wqb + (int64_t)((tid >> 2) + 64 * u) * N2 + n0 + 16 * (tid & 3)));
+    };
+    // tokens b, b + G, ... (G = grid size) are finished by workgroup b
+    const int t1 = blockIdx.x;
+    if (t1 < T) {
+        W8Aux x = {};
+        if (wave == 0) x = w8_aux_load(sx, swa, gamma, pos, co, t1);
+        W8Parts<NPW> r;
+        w8_parts_load(r, P, S, T, t1);
+        slab_load();
+        int a[8], ap;
+        w8_parts_sum(r, S, red, a, ap);
+        if (wave == 0)
+            w8_finish_token<true>(a, ap, t1, x.pt, x.slot, x.sxt, x.wa0, x.wa1, x.wap, x.gm, eps,
+                                  rt, QZ, sz, inv, ckv, kpe, dbg1, dbg_begin, dbg_rows, co);
+    } else {
+        slab_load();
+    }
+    for (int t = t1 + (int)gridDim.x; t < T; t += gridDim.x) {
+        __syncthreads();  // red is free again
+        W8Aux x = {};
+        if (wave == 0) x = w8_aux_load(sx, swa, gamma, pos, co, t);
+        W8Parts<NPW> r;
+        w8_parts_load(r, P, S, T, t);
+        int a[8], ap;
+        w8_parts_sum(r, S, red, a, ap);
+        if (wave == 0)
+            w8_finish_token<true>(a, ap, t, x.pt, x.slot, x.sxt, x.wa0, x.wa1, x.wap, x.gm, eps,
+                                  rt, QZ, sz, inv, ckv, kpe, dbg1, dbg_begin, dbg_rows, co);
+    }
+    if (item < 0) return;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+        *(u4_t*)(ldsW + ((tid >> 2) + 64 * u) * WP + 16 * (tid & 3)) = v[u];
+    // the tile's codes (16 rows x 64 eight-byte chunks) and scales
+    const int nrows = T < 16 ? T : 16;
+    uint64_t y[4];
+    uint32_t pend = 0, sc = 0u;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        y[u] = 0ull;
+        if (((tid + 256 * u) >> 6) < nrows) pend |= 1u << u;
+    }
+    const bool has_sc = tid < 32 && (tid & 15) < nrows;
+    if (has_sc) pend |= 1u << 4;
+    for (uint32_t it = 0; pend != 0u && it < spin_limit; ++it) {
+        if (it != 0) __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int q = tid + 256 * u;
+            if (pend & (1u << u)) y[u] = load_coherent64(QZ + (int64_t)(q >> 6) * kR + 8 * (q & 63));
+        }
+        if (pend & (1u << 4))
+            sc = load_coherent32((tid < 16 ? (const void*)(sz + tid) : (const void*)(inv + tid - 16)));
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if ((pend & (1u << u)) && !has_0x80_byte(y[u])) pend &= ~(1u << u);
+        if ((pend & (1u << 4)) && sc != ~0u) pend &= ~(1u << 4);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int q = tid + 256 * u;
+        *(uint64_t*)(ldsA + (q >> 6) * AP + 8 * (q & 63)) = y[u];
+    }
+    if (tid < 32) (tid < 16 ? lsz : linv)[tid & 15] = __builtin_bit_cast(float, sc);
+    if (__syncthreads_or(pend != 0u)) {
+        // the hand-off ran out of polls: rebuild the tile's codes and
+        // scales from the partials
+        if (tid == 0) atomicAdd(&g_handoff_fallbacks_w8, 1u);
+        const f4_t wa0 = *(const f4_t*)(swa + 8 * lane), wa1 = *(const f4_t*)(swa + 8 * lane + 4);
+        const u4_t gm = *(const u4_t*)(gamma + 8 * lane);
+        for (int row = 0; row < nrows; ++row) {
+            W8Parts<NPW> r;
+            w8_parts_load(r, P, S, T, row);
+            int a[8], ap;
+            w8_parts_sum(r, S, red, a, ap);
+            if (wave == 0) {
+                const W8Latent L = w8_latent(a, sx[row], wa0, wa1, gm, eps);
+                *(u2_t*)(ldsA + row * AP + 8 * lane) = L.q;
+                if (lane == 0) {
+                    lsz[row] = L.sz;
+                    linv[row] = L.inv;
+                }
+            }
+            __syncthreads();  // red is reused by the next row
+        }
+    }
+    __syncthreads();
+    // acc: tokens 4 g + i (rows of the tile) of slab column 16 wave + l16
+    i4_t acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int ks = 0; ks < kR / 64; ++ks) {
+        const u4_t fa = *(const u4_t*)(ldsA + l16 * AP + ks * 64 + 16 * g);
+        const int k = ks * 64 + g * 16 + (l16 >> 1);
+        const int colb = wave * 16 + 8 * (l16 & 1);
+        const uint2 lo = lds_tr8_w(ldsW + k * WP + colb);
+        const uint2 hi = lds_tr8_w(ldsW + (k + 8) * WP + colb);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i4_t, fa),
+                                                    __builtin_bit_cast(i4_t, u4_t{lo.x, lo.y, hi.x, hi.y}),
+                                                    acc, 0, 0, 0);
+    }
+    const int n = n0 + wave * 16 + l16;
+    const int h = n >> 8, sl = n & 255;
+    uint16_t* dst = ((sl < kDN) ? k_nope : value) + (int64_t)h * kDN + (sl & 127);
+    const float cs = swb[n];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int tok = 4 * g + i;
+        if (tok < nrows) {
+            const float f = ((float)acc[i] * (lsz[tok] * linv[tok])) * cs;
+            __builtin_nontemporal_store(f32_to_bf16(f), dst + (int64_t)tok * nh * kDN);
+            if (dbg2 != nullptr && tok >= dbg_begin && tok < dbg_begin + dbg_rows)
+                dbg2[(tok - dbg_begin) * (int64_t)N2 + n] = acc[i];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
 static inline int grid8(int nitems) { return 8 * ((nitems + 7) / 8); }
@@ -637,6 +893,52 @@ static void dec_launch_t(const void* X, const void* Wa, const void* gamma, const
              (uint16_t*)value);
 }
 
+// W8A8 decode: the fused finish + kv_b_proj for up to 16 tokens, when its
+// grid (one workgroup per 64-column slab) is resident at once.
+static std::atomic<int> g_fused_cap_w8[64];
+template <int NPW>
+static int fused_capacity_w8() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int cap = g_fused_cap_w8[dev].load(std::memory_order_relaxed);
+    if (cap > 0) return cap;
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, dec_fin_kv_b_w8_kernel<NPW>, 256, 0) !=
+            hipSuccess)
+        return 0;
+    cap = cus * per;
+    g_fused_cap_w8[dev].store(cap, std::memory_order_relaxed);
+    return cap;
+}
+
+bool w8_decode_fused_fits(int64_t T, int nh, int S) {
+    if (T < 1 || T > 16 || S < 1 || S > 32) return false;
+    // every NPW instance has the same LDS and register budget
+    return grid8(nh * kHeadW / kSlabW) <= fused_capacity_w8<8>();
+}
+
+void launch_w8_fin_kv_b(const int32_t* P, int S, int64_t T, const float* sx, const float* swa,
+                        const void* gamma, const int32_t* pos, float eps, const RopeTab& rt,
+                        const int8_t* Wqb, const float* swb, int nh, int8_t* QZ, float* sz,
+                        float* inv, void* ckv, void* k_pe, void* k_nope, void* value,
+                        int32_t* dbg1, int32_t* dbg2, int64_t dbg_begin, int64_t dbg_rows,
+                        const CacheOut& co, hipStream_t st) {
+    const int N2 = nh * kHeadW;
+    const int64_t sl = g_spin_limit.load(std::memory_order_relaxed);
+    const uint32_t spin = sl < 0 ? kSpinDefault : (uint32_t)(sl > 0xFFFFFFFFll ? 0xFFFFFFFFll : sl);
+    auto go = [&](auto kern) {
+        launch_k(kern, dim3(grid8(N2 / kSlabW)), dim3(256), 0, st, P, S, (int)T, sx, swa,
+                 (const uint16_t*)gamma, pos, eps, rt, Wqb, swb, N2, QZ, sz, inv, (uint16_t*)ckv,
+                 (uint16_t*)k_pe, (uint16_t*)k_nope, (uint16_t*)value, dbg1, dbg2, dbg_begin,
+                 dbg_rows, co, spin);
+    };
+    if (S <= 4) go(dec_fin_kv_b_w8_kernel<1>);
+    else if (S <= 8) go(dec_fin_kv_b_w8_kernel<2>);
+    else if (S <= 16) go(dec_fin_kv_b_w8_kernel<4>);
+    else go(dec_fin_kv_b_w8_kernel<8>);
+}
+
 hipError_t launch_fp_decode(int dt, const void* X, const void* Wa, const void* gamma,
                             const void* Wb, const int32_t* pos, int64_t T, int H, int nh,
                             float eps, const RopeTab& rt, void* k_nope, void* value, void* k_pe,
@@ -657,17 +959,21 @@ int64_t decode_set_spin_limit(int64_t limit) {
 }
 
 int64_t decode_handoff_fallbacks(bool reset) {
-    unsigned int v = 0;
+    unsigned int v = 0, v8 = 0;
     if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_handoff_fallbacks), sizeof(v), 0,
+                            hipMemcpyDeviceToHost) != hipSuccess ||
+        hipMemcpyFromSymbol(&v8, HIP_SYMBOL(g_handoff_fallbacks_w8), sizeof(v8), 0,
                             hipMemcpyDeviceToHost) != hipSuccess)
         return -1;
     if (reset) {
         const unsigned int z = 0;
         if (hipMemcpyToSymbol(HIP_SYMBOL(g_handoff_fallbacks), &z, sizeof(z), 0,
+                              hipMemcpyHostToDevice) != hipSuccess ||
+            hipMemcpyToSymbol(HIP_SYMBOL(g_handoff_fallbacks_w8), &z, sizeof(z), 0,
                               hipMemcpyHostToDevice) != hipSuccess)
             return -1;
     }
-    return (int64_t)v;
+    return (int64_t)v + (int64_t)v8;
 }
 
 }  // namespace mla

@@ -1496,12 +1496,18 @@ __device__ __forceinline__ float absmax8(const u4_t v, float amax) {
 
 // One wave per token row (four rows per workgroup), NCH 16-byte chunks per
 // lane (chunk lane + 64 u), all loaded before the first wait; the row maximum
-// is a wave reduction, so no LDS or barrier is involved.
+// is a wave reduction, so no LDS or barrier is involved.  With fill_q set,
+// the wave also writes the "not finished yet" pattern of the decode
+// hand-off into the token's latent code row (0x80 bytes, a code the
+// quantisers never produce) and its two latent scales (all-ones words).
 template <int NCH>
 __global__ __launch_bounds__(256) void quant_rows_wave_kernel(const uint16_t* __restrict__ X,
                                                               int H, int64_t T,
                                                               int8_t* __restrict__ Q,
-                                                              float* __restrict__ scale) {
+                                                              float* __restrict__ scale,
+                                                              int8_t* __restrict__ fill_q,
+                                                              uint32_t* __restrict__ fill_sz,
+                                                              uint32_t* __restrict__ fill_inv) {
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     const int lane = threadIdx.x & 63;
@@ -1521,6 +1527,13 @@ __global__ __launch_bounds__(256) void quant_rows_wave_kernel(const uint16_t* __
     for (int u = 0; u < NCH; ++u)
         if (lane + 64 * u < nch) *(u2_t*)(Q + t * H + 8 * (lane + 64 * u)) = quant8(v[u], inv);
     if (lane == 0) scale[t] = (amax > 0.f) ? (amax / 127.0f) : 0.f;
+    if (fill_q != nullptr) {
+        *(u2_t*)(fill_q + t * kR + 8 * lane) = u2_t{0x80808080u, 0x80808080u};
+        if (lane == 0) {
+            fill_sz[t] = ~0u;
+            fill_inv[t] = ~0u;
+        }
+    }
 }
 
 __global__ __launch_bounds__(256) void quant_rows_long_kernel(const uint16_t* __restrict__ X,
@@ -1549,88 +1562,6 @@ __global__ __launch_bounds__(256) void quant_rows_long_kernel(const uint16_t* __
 //   inv_t = 1/sqrt(sum(c^2)/512 + eps);  compressed_kv = bf16(z * inv_t)
 //   k_pe = RoPE(p)
 // ---------------------------------------------------------------------------
-// The finish of token t once lane l holds the token's int32 kv_a_proj sums of
-// latent columns 8l .. 8l + 7 (a) and of rope column l (ap): dequantise,
-// RMSNorm, quantise z = c * gamma, RoPE, and the writes.  One wave; the sums
-// are exact integers, so how the splits were added does not matter.
-__device__ __forceinline__ void w8_finish_token(
-    const int (&a)[8], int ap, int64_t t, int pt, int64_t slot, float sxt, f4_t wa0, f4_t wa1,
-    float wap, u4_t gm, float eps, const RopeTab& rt, int8_t* __restrict__ QZ,
-    float* __restrict__ sz, float* __restrict__ inv_out, uint16_t* __restrict__ ckv,
-    uint16_t* __restrict__ kpe, int32_t* __restrict__ dbg, int64_t dbg_begin, int64_t dbg_rows,
-    const CacheOut& co) {
-    const int lane = threadIdx.x & 63;
-    if (dbg != nullptr && t >= dbg_begin && t < dbg_begin + dbg_rows) {
-        int32_t* d = dbg + (t - dbg_begin) * kN1;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) d[8 * lane + i] = a[i];
-        d[kR + lane] = ap;
-    }
-    float c[8], z[8];
-    float ss = 0.f, az = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float w = i < 4 ? wa0[i] : wa1[i - 4];
-        c[i] = ((float)a[i] * sxt) * w;
-        const uint16_t gb = (uint16_t)(gm[i >> 1] >> (16 * (i & 1)));
-        z[i] = c[i] * bf16_to_f32(gb);
-        ss += c[i] * c[i];
-        az = fmaxf(az, fabsf(z[i]));
-    }
-    const float p = ((float)ap * sxt) * wap;
-    ss = wave_sum(ss);
-    az = wave_max(az);
-    const float inv_t = 1.0f / sqrtf(ss / (float)kR + eps);
-    const float inv2 = (az > 0.f) ? (127.0f / az) : 0.f;
-    u2_t q;
-    u4_t o;
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-        uint32_t packed = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            float r = rintf(z[w * 4 + b] * inv2);
-            r = fminf(fmaxf(r, -127.f), 127.f);
-            packed |= ((uint32_t)(uint8_t)(int8_t)(int)r) << (8 * b);
-        }
-        q[w] = packed;
-    }
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-        o[w] = (uint32_t)f32_to_bf16(z[2 * w] * inv_t) | ((uint32_t)f32_to_bf16(z[2 * w + 1] * inv_t) << 16);
-    *(u2_t*)(QZ + t * kR + 8 * lane) = q;
-    *(u4_t*)(ckv + t * kR + 8 * lane) = o;
-    if (lane == 0) {
-        sz[t] = (az > 0.f) ? (az / 127.0f) : 0.f;
-        inv_out[t] = inv_t;
-    }
-    const float partner = __shfl_xor(p, 32, 64);
-    float cs, sn;
-    rope_cos_sin(pt, rt.f[lane & 31], cs, sn);
-    const float out = rope_rotate(p, partner, cs, sn, lane < 32);
-    const uint16_t ko = f32_to_bf16(out);
-    __builtin_nontemporal_store(ko, kpe + t * kDR + lane);
-    if (cache_slot_ok(co, slot)) {
-        // the paged cache, [latent | rope key] in the token's slot: the
-        // returned bf16 rows, or their int8 codes and the slot's scale
-        constexpr int W = kR + kDR;
-        if (co.cache_q == nullptr) {
-            uint16_t* row = co.cache + slot * W;
-            __builtin_nontemporal_store(o, (u4_t*)(row + 8 * lane));
-            __builtin_nontemporal_store(ko, row + kR + lane);
-        } else {
-            const float am = wave_max(fmaxf(absmax8_e<kBF16>(o, 0.f), fabsf(bf16_to_f32(ko))));
-            const float qi = (am > 0.f) ? (127.0f / am) : 0.f;
-            int8_t* row = co.cache_q + slot * W;
-            __builtin_nontemporal_store(codes8<kBF16>(o, qi), (u2_t*)(row + 8 * lane));
-            float rk = rintf(bf16_to_f32(ko) * qi);
-            rk = fminf(fmaxf(rk, -127.f), 127.f);
-            __builtin_nontemporal_store((int8_t)(int)rk, row + kR + lane);
-            if (lane == 0) co.scale[slot] = (am > 0.f) ? (am / 127.0f) : 0.f;
-        }
-    }
-}
-
 template <int B>
 __global__ __launch_bounds__(256) void finish_a_w8_kernel(
     const int32_t* __restrict__ P, int S, int64_t T, const float* __restrict__ sx,
@@ -1677,8 +1608,8 @@ __global__ __launch_bounds__(256) void finish_a_w8_kernel(
             }
         }
     }
-    w8_finish_token(a, ap, t, pt, slot, sxt, wa0, wa1, wap, gm, eps, rt, QZ, sz, inv_out, ckv, kpe,
-                    dbg, dbg_begin, dbg_rows, co);
+    w8_finish_token<false>(a, ap, t, pt, slot, sxt, wa0, wa1, wap, gm, eps, rt, QZ, sz, inv_out, ckv,
+                           kpe, dbg, dbg_begin, dbg_rows, co);
 }
 
 // The same finish for calls with many K splits and few tokens: one
@@ -1748,8 +1679,8 @@ __global__ __launch_bounds__(256) void finish_w8_wide_kernel(
         for (int i = 0; i < 8; ++i) a[i] += r[i];
         ap += r[8];
     }
-    w8_finish_token(a, ap, t, pt, slot, sxt, wa0, wa1, wap, gm, eps, rt, QZ, sz, inv_out, ckv, kpe,
-                    dbg, dbg_begin, dbg_rows, co);
+    w8_finish_token<false>(a, ap, t, pt, slot, sxt, wa0, wa1, wap, gm, eps, rt, QZ, sz, inv_out, ckv,
+                           kpe, dbg, dbg_begin, dbg_rows, co);
 }
 
 // ---------------------------------------------------------------------------
@@ -1956,14 +1887,21 @@ hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa, const
     int8_t* QZ = (int8_t*)(base + w.qz);
     float* sz = (float*)(base + w.sz);
     float* inv = (float*)(base + w.inv);
+    // decode sizes: the finish fused into kv_b_proj when its launch fits on
+    // the device at once (the quantiser then also fills the hand-off's
+    // "not finished" pattern)
+    const bool fused = plan.path == 0 && H <= 8192 && w8_decode_fused_fits(T, nh, plan.s1);
     {
         // rows of up to 8192 elements: one wave per row; longer rows: one
         // workgroup per row, walked twice
         const dim3 g4((unsigned)((T + 3) / 4)), blk(256);
         const uint16_t* x = (const uint16_t*)X;
+        int8_t* fq = fused ? QZ : nullptr;
+        uint32_t* fs = fused ? (uint32_t*)sz : nullptr;
+        uint32_t* fi = fused ? (uint32_t*)inv : nullptr;
         switch ((H + 511) / 512) {
 #define MLA_QUANT_WAVE(n)                                                                     \
-    case n: launch_k(quant_rows_wave_kernel<n>, g4, blk, 0, st, x, H, T, QX, sx); break;
+    case n: launch_k(quant_rows_wave_kernel<n>, g4, blk, 0, st, x, H, T, QX, sx, fq, fs, fi); break;
             MLA_QUANT_WAVE(1) MLA_QUANT_WAVE(2) MLA_QUANT_WAVE(3) MLA_QUANT_WAVE(4)
             MLA_QUANT_WAVE(5) MLA_QUANT_WAVE(6) MLA_QUANT_WAVE(7) MLA_QUANT_WAVE(8)
             MLA_QUANT_WAVE(9) MLA_QUANT_WAVE(10) MLA_QUANT_WAVE(11) MLA_QUANT_WAVE(12)
@@ -1986,6 +1924,11 @@ hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa, const
     else
         gemm1_dispatch<kI8>(plan.bm1, QX, (int64_t)H, Wqa, T, H / 128, plan.s1,
                             EpiPartialI32{P1, T}, st);
+    if (fused) {
+        launch_w8_fin_kv_b(P1, plan.s1, T, sx, swa, gamma, pos, eps, rt, Wqb, swb, nh, QZ, sz,
+                           inv, ckv, k_pe, k_nope, value, dbg1, dbg2, dbg_begin, dbg_rows, co, st);
+        return hipGetLastError();
+    }
     {
         const int S = plan.s1;
         auto go = [&](auto kern) {

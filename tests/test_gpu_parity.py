@@ -417,3 +417,64 @@ def test_decode_handoff_fallback_rebuilds_rows(dev, T):
     for a, b in zip(ref_outs, outs):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     compare(gpu_rows(outs), run_oracle(w), f"handoff_fallback_T{T}")
+
+
+# W8A8 at decode sizes: the finish fused into kv_b_proj (up to 16 tokens)
+W8DEC = Dims(H=7168, nh=128)   # R1: 28 kv_a_proj splits, 512 kv_b_proj slabs
+
+
+@pytest.mark.parametrize("T", [1, 2, 7, 16])
+def test_w8a8_decode_fused_handoff_exact(dev, T):
+    """R1-shaped W8A8 calls of up to 16 tokens run the finish inside
+    kv_b_proj's launch and hand the latent codes and scales over between
+    workgroups.  On a normal call no workgroup falls back; the int32
+    accumulators of both projections are bit-exact and the outputs match
+    the oracle on every row; the launch with the accumulator exports gives
+    the same outputs."""
+    import mla_attention_kv_amd as mla
+
+    w = workloads.make_custom(W8DEC, T, kind="w8a8", dtype="bf16", seed=640 + T, wstd=0.01,
+                              max_pos=32768)
+    print(f"[parity] w8a8 decode fused T={T}", flush=True)
+    t = upload(w, dev)
+    assert mla.mla_debug_handoff_fallbacks(reset=True) >= 0
+    outs, _ = run_lib(w, t)
+    torch.cuda.synchronize()
+    assert mla.mla_debug_handoff_fallbacks() == 0
+    outs2, (d1, d2) = run_lib(w, t, dbg_rows=(0, w.T))
+    torch.cuda.synchronize()
+    ref = run_oracle(w)
+    compare(gpu_rows(outs), ref, f"w8a8_decode_T{T}")
+    np.testing.assert_array_equal(d1.cpu().numpy(), ref["acc1"])
+    np.testing.assert_array_equal(d2.cpu().numpy(), ref["acc2"])
+    for x, y in zip(outs, outs2):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+@pytest.mark.parametrize("dims,T", [(W8DEC, 1), (W8DEC, 16), (Dims(H=1024, nh=4), 5)])
+def test_w8a8_decode_fallback_rebuilds_codes(dev, dims, T):
+    """With the poll bound set to 0 from the host, every kv_b_proj workgroup
+    of the fused W8A8 launch rebuilds its tile's latent codes and scales from
+    the split-K partials (no workgroup waits).  The outputs and accumulators
+    are the same bits as the hand-off's, and match the oracle."""
+    import mla_attention_kv_amd as mla
+
+    w = workloads.make_custom(dims, T, kind="w8a8", dtype="bf16", seed=650 + T, wstd=0.01)
+    t = upload(w, dev)
+    ref_outs, (r1, r2) = run_lib(w, t, dbg_rows=(0, w.T))
+    torch.cuda.synchronize()
+    prev = mla.mla_debug_set_handoff_spin(0)
+    try:
+        mla.mla_debug_handoff_fallbacks(reset=True)
+        outs, (d1, d2) = run_lib(w, t, dbg_rows=(0, w.T))
+        torch.cuda.synchronize()
+        n = mla.mla_debug_handoff_fallbacks(reset=True)
+    finally:
+        mla.mla_debug_set_handoff_spin(prev)
+    assert n == dims.N2 // 64, n   # every slab's workgroup
+    for a, b in zip(ref_outs, outs):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(r2, d2) and torch.equal(r1, d1)
+    ref = run_oracle(w)
+    compare(gpu_rows(outs), ref, f"w8a8_decode_fallback_T{T}")
+    np.testing.assert_array_equal(d2.cpu().numpy(), ref["acc2"])
