@@ -697,9 +697,13 @@ def kernel_parts(w, path, n_kernels):
     kv_b = ("kv_b_proj GEMM", (lat_in + wb + kv_out, f2))
     if not fp:
         quant = ("activation quantiser", (xin + T * d.H + 4 * T, 0))
+        fused = ("finish fused into kv_b_proj (W8A8 decode)",
+                 (a_out + d.r * D + 4 * T + fin_out + wb + kv_out, f2))
+        if n_kernels == 2:  # up to 8 tokens: the quantiser folded into kv_a_proj too
+            return [("kv_a_proj with the activation quantiser folded in (W8A8 decode)",
+                     (xin + wa + a_out, f1)), fused]
         if n_kernels == 3:  # decode sizes: the finish fused into kv_b_proj
-            return [quant, kv_a, ("finish fused into kv_b_proj (W8A8 decode)",
-                                  (a_out + d.r * D + 4 * T + fin_out + wb + kv_out, f2))]
+            return [quant, kv_a, fused]
         return [quant, kv_a, finish, kv_b]
     if path == 0 and n_kernels == 2:
         return [("dec_kv_a (kv_a_proj, split-K)", (xin + wa + a_out, f1)),

@@ -298,6 +298,35 @@ __device__ __forceinline__ uint32_t load_coherent32(const void* p) {
     return __hip_atomic_load((const uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// W8A8 activation quantisation of 8 bf16 values with the token's factor
+// inv = 127 / amax: rint(x * inv) clamped to +-127 (ties to even), and the
+// running maximum of |x| over 8 values.
+__device__ __forceinline__ u2_t quant8(const u4_t v, float inv) {
+    u2_t q;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int e = w * 4 + b;
+            const uint32_t bits = (v[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+            float r = rintf(bf16_to_f32((uint16_t)bits) * inv);
+            r = fminf(fmaxf(r, -127.f), 127.f);
+            packed |= ((uint32_t)(uint8_t)(int8_t)(int)r) << (8 * b);
+        }
+        q[w] = packed;
+    }
+    return q;
+}
+__device__ __forceinline__ float absmax8(const u4_t v, float amax) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        amax = fmaxf(amax, fabsf(bf16_to_f32((uint16_t)(v[w] & 0xFFFFu))));
+        amax = fmaxf(amax, fabsf(bf16_to_f32((uint16_t)(v[w] >> 16))));
+    }
+    return amax;
+}
+
 // W8A8: the latent of one token from its exact int32 kv_a_proj sums, lane l
 // holding latent columns 8l .. 8l + 7 (one wave):
 //   c = (acc * sx) * s_a,  z = c * gamma,
@@ -415,6 +444,11 @@ __device__ __forceinline__ void w8_finish_token(
 // T tokens, nh heads and S kv_a_proj splits on the current device (its
 // grid resident at once), and its launch (prolog_decode.hip).
 bool w8_decode_fused_fits(int64_t T, int nh, int S);
+// and, for up to 8 tokens, kv_a_proj with the activation quantiser folded
+// in (it also fills the fused launch's hand-off pattern when fill_q is set)
+bool w8_decode_kva_fits(int64_t T, int H, int S);
+void launch_w8_kv_a(const void* X, const int8_t* Wqa, int64_t T, int H, int S, int32_t* P,
+                    float* sx, int8_t* fill_q, float* fill_sz, float* fill_inv, hipStream_t st);
 void launch_w8_fin_kv_b(const int32_t* P, int S, int64_t T, const float* sx, const float* swa,
                         const void* gamma, const int32_t* pos, float eps, const RopeTab& rt,
                         const int8_t* Wqb, const float* swb, int nh, int8_t* QZ, float* sz,

@@ -813,6 +813,130 @@ __global__ __launch_bounds__(256) void dec_fin_kv_b_w8_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// W8A8 kv_a_proj for a few tokens (T <= 8) with the activation quantiser
+// folded in.  Work items are (split s, 64-column slab of Wq_kv_a over the
+// split's kw <= KW rows), split-major as in dec_kv_a.  Each workgroup reads its
+// tokens' whole hidden rows (a few tens of KB, served from L2 after the
+// first workgroups) for their maxima, quantises its own K range of them
+// with the quantiser's operations (quant8: the same codes), stages the
+// codes and the weight slab in LDS and multiplies with
+// v_mfma_i32_16x16x64_i8 (tokens as M; wave w owns slab columns
+// 16 w .. 16 w + 15; weight operands from two transposing LDS reads),
+// writing int32 partials P[s][t][576].  Item 0 also writes the tokens'
+// activation scales and fills their latent code rows and scales with the
+// fused finish's "not finished" pattern.
+// ---------------------------------------------------------------------------
+template <int KW>
+__global__ __launch_bounds__(256) void dec_kv_a_w8_kernel(
+    const uint16_t* __restrict__ X, const int8_t* __restrict__ Wqa, int T, int H, int S, int kw,
+    int32_t* __restrict__ P, float* __restrict__ sx, int8_t* __restrict__ fill_q,
+    uint32_t* __restrict__ fill_sz, uint32_t* __restrict__ fill_inv) {
+    constexpr int WP = kSlabW + 16;  // LDS pitch of a staged slab row (bytes)
+    constexpr int AP = KW + 16;      // LDS pitch of a code row (bytes)
+    constexpr int NT = 8;            // tokens at most
+    constexpr int NCH = 4;           // 16-byte chunks per thread of a row (H <= 8192)
+    constexpr int KC = KW / 8;       // chunks of a token's K range
+    constexpr int KCT = (NT * KC + 255) / 256;
+    __shared__ __align__(16) int8_t ldsW[KW * WP];
+    __shared__ __align__(16) int8_t ldsA[16 * AP];
+    __shared__ float lmax[4][NT];
+    const int item = xcd_item(kSlabsA * S);
+    if (item < 0) return;
+    const int s = item / kSlabsA, slab = item % kSlabsA;
+    const int k0 = s * kw, kmax = min(H, k0 + kw);  // kw <= KW
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nch = H >> 3;
+    // every load first: the weight slab (rows past kmax read row kmax - 1
+    // and are zeroed when stored), the tokens' rows for the maxima and their
+    // chunks of this K range (rows past T read token T - 1, unused)
+    u4_t wv[KW / 64];
+#pragma unroll
+    for (int u = 0; u < KW / 64; ++u) {
+        const int k = min(k0 + (tid >> 2) + 64 * u, kmax - 1);
+        wv[u] = __builtin_nontemporal_load(
+            (const u4_t*)(Wqa + (int64_t)k * kN1 + slab * kSlabW + 16 * (tid & 3)));
+    }
+    u4_t xv[NT][NCH];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int u = 0; u < NCH; ++u)
+            xv[t][u] = *(const u4_t*)(X + (int64_t)min(t, T - 1) * H +
+                                      8 * min(tid + 256 * u, nch - 1));
+    u4_t kv[KCT];
+#pragma unroll
+    for (int u = 0; u < KCT; ++u) {
+        const int q = tid + 256 * u, t = q / KC, c = q % KC;
+        kv[u] = *(const u4_t*)(X + (int64_t)min(t, T - 1) * H + min(k0 + 8 * c, H - 8));
+    }
+    // the tokens' maxima (max is exact in any order)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        float am = 0.f;
+#pragma unroll
+        for (int u = 0; u < NCH; ++u)
+            if (tid + 256 * u < nch) am = absmax8(xv[t][u], am);
+        am = wave_max(am);
+        if (lane == 0) lmax[wave][t] = am;
+    }
+#pragma unroll
+    for (int u = 0; u < KW / 64; ++u) {
+        const int k = k0 + (tid >> 2) + 64 * u;
+        *(u4_t*)(ldsW + ((tid >> 2) + 64 * u) * WP + 16 * (tid & 3)) =
+            k < kmax ? wv[u] : u4_t{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+    // the codes of this K range: rows past T and columns past kmax are zero
+#pragma unroll
+    for (int u = 0; u < KCT; ++u) {
+        const int q = tid + 256 * u, t = q / KC, c = q % KC;
+        if (t < NT) {
+            const float am = fmaxf(fmaxf(lmax[0][t], lmax[1][t]), fmaxf(lmax[2][t], lmax[3][t]));
+            const float inv = (am > 0.f) ? (127.0f / am) : 0.f;
+            const bool ok = t < T && k0 + 8 * c < kmax;
+            *(u2_t*)(ldsA + t * AP + 8 * c) = ok ? quant8(kv[u], inv) : u2_t{0u, 0u};
+        }
+    }
+    // rows NT .. 15 of the token tile are zero
+    for (int q = tid; q < (16 - NT) * (KW / 8); q += 256)
+        *(u2_t*)(ldsA + (NT + q / (KW / 8)) * AP + 8 * (q % (KW / 8))) = u2_t{0u, 0u};
+    if (item == 0 && tid < T) {
+        const float am = fmaxf(fmaxf(lmax[0][tid], lmax[1][tid]), fmaxf(lmax[2][tid], lmax[3][tid]));
+        sx[tid] = (am > 0.f) ? (am / 127.0f) : 0.f;
+    }
+    if (item == 0 && fill_q != nullptr) {
+        for (int q = tid; q < T * (kR / 8); q += 256)
+            *(u2_t*)(fill_q + (int64_t)(q / (kR / 8)) * kR + 8 * (q % (kR / 8))) =
+                u2_t{0x80808080u, 0x80808080u};
+        if (tid < T) {
+            fill_sz[tid] = ~0u;
+            fill_inv[tid] = ~0u;
+        }
+    }
+    __syncthreads();
+    const int l16 = lane & 15, g = lane >> 4;
+    i4_t acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int ks = 0; ks < KW / 64; ++ks) {
+        const u4_t fa = *(const u4_t*)(ldsA + l16 * AP + ks * 64 + 16 * g);
+        const int k = ks * 64 + g * 16 + (l16 >> 1);
+        const int colb = wave * 16 + 8 * (l16 & 1);
+        const uint2 lo = lds_tr8_w(ldsW + k * WP + colb);
+        const uint2 hi = lds_tr8_w(ldsW + (k + 8) * WP + colb);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+            __builtin_bit_cast(i4_t, fa), __builtin_bit_cast(i4_t, u4_t{lo.x, lo.y, hi.x, hi.y}),
+            acc, 0, 0, 0);
+    }
+    // lane 16 g + c holds tokens 4 g + i of slab column 16 wave + c
+    int32_t* Ps = P + (int64_t)s * T * kN1 + slab * kSlabW + wave * 16 + l16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = 4 * g + i;
+        if (t < T) Ps[(int64_t)t * kN1] = acc[i];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
 static inline int grid8(int nitems) { return 8 * ((nitems + 7) / 8); }
@@ -910,6 +1034,25 @@ static int fused_capacity_w8() {
     cap = cus * per;
     g_fused_cap_w8[dev].store(cap, std::memory_order_relaxed);
     return cap;
+}
+
+// W8A8 kv_a_proj with the quantiser folded in, for up to 8 tokens: whether
+// it applies (H <= 8192 for the per-thread row chunks; a split of at most
+// 512 rows for the LDS slab) and its launch.
+bool w8_decode_kva_fits(int64_t T, int H, int S) {
+    const int ks = H / 128, per = (ks + S - 1) / S;
+    return T >= 1 && T <= 8 && H <= 8192 && per * S == ks && per <= 4;
+}
+void launch_w8_kv_a(const void* X, const int8_t* Wqa, int64_t T, int H, int S, int32_t* P,
+                    float* sx, int8_t* fill_q, float* fill_sz, float* fill_inv, hipStream_t st) {
+    const int kw = H / S;
+    auto go = [&](auto kern) {
+        launch_k(kern, dim3(grid8(kSlabsA * S)), dim3(256), 0, st, (const uint16_t*)X, Wqa,
+                 (int)T, H, S, kw, P, sx, fill_q, (uint32_t*)fill_sz, (uint32_t*)fill_inv);
+    };
+    if (kw <= 128) go(dec_kv_a_w8_kernel<128>);
+    else if (kw <= 256) go(dec_kv_a_w8_kernel<256>);
+    else go(dec_kv_a_w8_kernel<512>);
 }
 
 bool w8_decode_fused_fits(int64_t T, int nh, int S) {

@@ -1468,32 +1468,6 @@ __global__ __launch_bounds__(256) void finish_a_fp_kernel(
 // (quant_rows_wave_kernel); longer rows: one 256-thread workgroup per row
 // that walks it twice (quant_rows_long_kernel).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ u2_t quant8(const u4_t v, float inv) {
-    u2_t q;
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-        uint32_t packed = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int e = w * 4 + b;
-            const uint32_t bits = (v[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-            float r = rintf(bf16_to_f32((uint16_t)bits) * inv);
-            r = fminf(fmaxf(r, -127.f), 127.f);
-            packed |= ((uint32_t)(uint8_t)(int8_t)(int)r) << (8 * b);
-        }
-        q[w] = packed;
-    }
-    return q;
-}
-__device__ __forceinline__ float absmax8(const u4_t v, float amax) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        amax = fmaxf(amax, fabsf(bf16_to_f32((uint16_t)(v[w] & 0xFFFFu))));
-        amax = fmaxf(amax, fabsf(bf16_to_f32((uint16_t)(v[w] >> 16))));
-    }
-    return amax;
-}
-
 // One wave per token row (four rows per workgroup), NCH 16-byte chunks per
 // lane (chunk lane + 64 u), all loaded before the first wait; the row maximum
 // is a wave reduction, so no LDS or barrier is involved.  With fill_q set,
@@ -1891,7 +1865,12 @@ hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa, const
     // the device at once (the quantiser then also fills the hand-off's
     // "not finished" pattern)
     const bool fused = plan.path == 0 && H <= 8192 && w8_decode_fused_fits(T, nh, plan.s1);
-    {
+    // up to 8 tokens: kv_a_proj quantises the activations itself
+    const bool fold = plan.path == 0 && w8_decode_kva_fits(T, H, plan.s1);
+    if (fold) {
+        launch_w8_kv_a(X, Wqa, T, H, plan.s1, P1, sx, fused ? QZ : nullptr, fused ? sz : nullptr,
+                       fused ? inv : nullptr, st);
+    } else {
         // rows of up to 8192 elements: one wave per row; longer rows: one
         // workgroup per row, walked twice
         const dim3 g4((unsigned)((T + 3) / 4)), blk(256);
@@ -1911,19 +1890,19 @@ hipError_t launch_w8a8(const void* X, const int8_t* Wqa, const float* swa, const
                 launch_k(quant_rows_long_kernel, dim3((unsigned)T), blk, 0, st, x, H, QX, sx);
                 break;
         }
+        if (plan.dma1 && plan.bm1 == 160)
+            gemm_lds_launch<kI8, 160, 192, 2, 4, 4, 3>(QX, (int64_t)H, Wqa, (int64_t)kN1, T, kN1,
+                                                       H, plan.s1, EpiPartialI32{P1, T}, st);
+        else if (plan.dma1 && plan.bm1 == 128)
+            gemm_lds_launch<kI8, 128, 192, 2, 4, 4, 4>(QX, (int64_t)H, Wqa, (int64_t)kN1, T, kN1,
+                                                       H, plan.s1, EpiPartialI32{P1, T}, st);
+        else if (plan.dma1)
+            gemm_lds_launch<kI8, 64, 192, 2, 4, 4, 4>(QX, (int64_t)H, Wqa, (int64_t)kN1, T, kN1,
+                                                      H, plan.s1, EpiPartialI32{P1, T}, st);
+        else
+            gemm1_dispatch<kI8>(plan.bm1, QX, (int64_t)H, Wqa, T, H / 128, plan.s1,
+                                EpiPartialI32{P1, T}, st);
     }
-    if (plan.dma1 && plan.bm1 == 160)
-        gemm_lds_launch<kI8, 160, 192, 2, 4, 4, 3>(QX, (int64_t)H, Wqa, (int64_t)kN1, T, kN1, H,
-                                                   plan.s1, EpiPartialI32{P1, T}, st);
-    else if (plan.dma1 && plan.bm1 == 128)
-        gemm_lds_launch<kI8, 128, 192, 2, 4, 4, 4>(QX, (int64_t)H, Wqa, (int64_t)kN1, T, kN1, H,
-                                                   plan.s1, EpiPartialI32{P1, T}, st);
-    else if (plan.dma1)
-        gemm_lds_launch<kI8, 64, 192, 2, 4, 4, 4>(QX, (int64_t)H, Wqa, (int64_t)kN1, T, kN1, H,
-                                                  plan.s1, EpiPartialI32{P1, T}, st);
-    else
-        gemm1_dispatch<kI8>(plan.bm1, QX, (int64_t)H, Wqa, T, H / 128, plan.s1,
-                            EpiPartialI32{P1, T}, st);
     if (fused) {
         launch_w8_fin_kv_b(P1, plan.s1, T, sx, swa, gamma, pos, eps, rt, Wqb, swb, nh, QZ, sz,
                            inv, ckv, k_pe, k_nope, value, dbg1, dbg2, dbg_begin, dbg_rows, co, st);

@@ -478,3 +478,16 @@ def test_w8a8_decode_fallback_rebuilds_codes(dev, dims, T):
     ref = run_oracle(w)
     compare(gpu_rows(outs), ref, f"w8a8_decode_fallback_T{T}")
     np.testing.assert_array_equal(d2.cpu().numpy(), ref["acc2"])
+
+
+@pytest.mark.parametrize("H,T,nh", [(3456, 4, 4), (128, 3, 2), (7168, 8, 128)])
+def test_w8a8_decode_folded_quantiser_exact(dev, H, T, nh):
+    """W8A8 calls of up to 8 tokens quantise their activations inside
+    kv_a_proj: splits of 384 rows (H = 3456, 9 splits: a split narrower than
+    the kernel's LDS slab), of 128 rows (H = 128, one split) and R1's 256
+    rows at the largest such token count.  The int32 accumulators of both
+    projections are bit-exact on every row, the outputs match the oracle."""
+    d = Dims(H=H, nh=nh)
+    w = workloads.make_custom(d, T, kind="w8a8", dtype="bf16", seed=660 + H % 89 + T,
+                              wstd=0.01)
+    check_full(w, dev, f"w8a8_fold_H{H}_T{T}", path=0, dbg=True)
