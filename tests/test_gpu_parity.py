@@ -126,8 +126,10 @@ def test_bf16_token_counts(dev, T, path):
 
 
 @pytest.mark.parametrize("path", [0, 1])
-@pytest.mark.parametrize("T", [1, 5, 64, 131])
+@pytest.mark.parametrize("T", [1, 5, 8, 9, 16, 17, 64, 131])
 def test_w8a8_token_counts_exact(dev, T, path):
+    # on the decode family: the quantiser folded into kv_a_proj up to 8
+    # tokens, the finish fused into kv_b_proj up to 16, four launches beyond
     d = Dims(H=1024, nh=4)
     w = workloads.make_custom(d, T, kind="w8a8", dtype="bf16", seed=300 + T, wstd=0.02)
     check_full(w, dev, f"w8a8_T{T}", path=path, dbg=True)
