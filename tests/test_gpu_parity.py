@@ -289,6 +289,26 @@ def test_zero_tokens_is_noop(dev):
     assert all(o.shape[0] == 0 for o in outs)
 
 
+@pytest.mark.parametrize("path", [0, 1])
+@pytest.mark.parametrize("kind,dtype", [("fp", "f16"), ("fp", "bf16"), ("w8a8", "bf16")])
+def test_signed_gamma_and_wide_activations(dev, kind, dtype, path):
+    """gamma of both signs with exact zeros among its entries (the W8A8 path
+    quantises z = c * gamma, so a sign or a zero must reach the codes the
+    same way on both sides), and hidden rows whose scale spans 2^-6 .. 2^6
+    from token to token.  Every row against the oracle; W8A8 accumulators
+    bit-exact."""
+    d = Dims(H=1024, nh=4)
+    T = 40 if path == 0 else 200
+    w = workloads.make_custom(d, T, kind=kind, dtype=dtype, seed=700 + T + len(dtype), wstd=0.02)
+    rng = np.random.default_rng(701)
+    g = rng.uniform(-1.5, 1.5, d.r).astype(np.float32)
+    g[::37] = 0.0
+    w.gamma = workloads.to_storage(g, dtype)
+    x = workloads.widen(w.X, dtype) * np.exp2(rng.integers(-6, 7, (T, 1))).astype(np.float32)
+    w.X = workloads.to_storage(x, dtype)
+    check_full(w, dev, f"signed_gamma_{kind}_{dtype}_p{path}", path=path, dbg=(kind == "w8a8"))
+
+
 def test_zero_row_w8a8(dev):
     """A token whose hidden row is all zeros: codes 0, scale 0, outputs 0."""
     d = Dims(H=256, nh=2)
