@@ -1459,6 +1459,85 @@ __global__ __launch_bounds__(256) void finish_a_fp_kernel(
     }
 }
 
+// The same finish with one workgroup per token, for many splits and few
+// tokens: wave w sums splits w, w + 4, ... (NPW loads in flight, one batch),
+// waves 1..3 hand their sums to wave 0 through LDS, and wave 0 adds them in
+// wave order and finishes the token as above.  A single wave per token would
+// wait for its splits in several batches, one after another.
+template <int E, int NPW>
+__global__ __launch_bounds__(256) void finish_fp_wide_kernel(
+    const float* __restrict__ P, int S, int64_t T, const uint16_t* __restrict__ gamma,
+    const int32_t* __restrict__ pos, float eps, RopeTab rt, uint16_t* __restrict__ ckv,
+    uint16_t* __restrict__ kpe, CacheOut co) {
+    __shared__ float red[3][64 * 9];
+    const int64_t t = blockIdx.x;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    int pt = 0;
+    int64_t slot = -1;
+    u4_t g = {0u, 0u, 0u, 0u};
+    if (wave == 0) {
+        pt = pos[t];
+        slot = co.slots != nullptr ? co.slots[t] : -1;
+        g = *(const u4_t*)(gamma + 8 * lane);
+    }
+    f4_t v0[NPW], v1[NPW];
+    float pv[NPW];
+#pragma unroll
+    for (int j = 0; j < NPW; ++j) {
+        const int s = wave + 4 * j < S ? wave + 4 * j : S - 1;
+        const float* row = P + ((int64_t)s * T + t) * kN1;
+        v0[j] = __builtin_nontemporal_load((const f4_t*)(row + 8 * lane));
+        v1[j] = __builtin_nontemporal_load((const f4_t*)(row + 8 * lane + 4));
+        pv[j] = __builtin_nontemporal_load(row + kR + lane);
+    }
+    float c[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float p = 0.f;
+#pragma unroll
+    for (int j = 0; j < NPW; ++j) {
+        if (wave + 4 * j < S) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                c[i] += v0[j][i];
+                c[4 + i] += v1[j][i];
+            }
+            p += pv[j];
+        }
+    }
+    if (wave > 0) {
+        float* r = red[wave - 1] + lane * 9;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r[i] = c[i];
+        r[8] = p;
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+        const float* r = red[w] + lane * 9;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] += r[i];
+        p += r[8];
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += c[i] * c[i];
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)kR + eps);
+    const u4_t o = rms_scale8<E>(c, inv, g);
+    *(u4_t*)(ckv + t * kR + 8 * lane) = o;
+
+    const float partner = __shfl_xor(p, 32, 64);
+    float cs, sn;
+    rope_cos_sin(pt, rt.f[lane & 31], cs, sn);
+    const uint16_t ko = f32_to_st<E>(rope_rotate(p, partner, cs, sn, lane < 32));
+    __builtin_nontemporal_store(ko, kpe + t * kDR + lane);
+    if (cache_slot_ok(co, slot)) {
+        uint16_t* row = co.cache + slot * (kR + kDR);
+        __builtin_nontemporal_store(o, (u4_t*)(row + 8 * lane));
+        __builtin_nontemporal_store(ko, row + kR + lane);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // W8A8: per-token activation quantisation.
 //   amax = max |x|;  q = clamp(rint(x * (127/amax)), -127, 127);
@@ -1782,6 +1861,23 @@ static void kvb_fp_ws_launch(const void* Y, const void* Wb, int64_t T, int nh, v
 void launch_finish_fp(int dt, const float* P, int S, int64_t T, const void* gamma,
                       const int32_t* pos, float eps, const RopeTab& rt, void* ckv, void* kpe,
                       const CacheOut& co, hipStream_t st) {
+    // many splits and few tokens: one workgroup of four waves per token
+    if (S > 8 && S <= 64 && T < 2048) {
+        auto wide = [&](auto kern) {
+            launch_k(kern, dim3((unsigned)T), dim3(256), 0, st, P, S, T, (const uint16_t*)gamma,
+                     pos, eps, rt, (uint16_t*)ckv, (uint16_t*)kpe, co);
+        };
+        if (dt == kF16) {
+            if (S <= 16) wide(finish_fp_wide_kernel<kF16, 4>);
+            else if (S <= 32) wide(finish_fp_wide_kernel<kF16, 8>);
+            else wide(finish_fp_wide_kernel<kF16, 16>);
+        } else {
+            if (S <= 16) wide(finish_fp_wide_kernel<kBF16, 4>);
+            else if (S <= 32) wide(finish_fp_wide_kernel<kBF16, 8>);
+            else wide(finish_fp_wide_kernel<kBF16, 16>);
+        }
+        return;
+    }
     // four tokens per workgroup, or one when that leaves most CUs idle
     const int tpw = T >= 2048 ? 4 : 1;
     const dim3 grid((unsigned)((T + tpw - 1) / tpw)), blk(64 * tpw);

@@ -267,6 +267,18 @@ def test_tiny_T_head_counts(dev, T, nh):
     check_full(w, dev, f"tiny_nh{nh}_T{T}", path=0)
 
 
+@pytest.mark.parametrize("H,nh,T,dtype", [(7168, 8, 65, "bf16"), (7168, 8, 300, "f16"),
+                                           (20480, 2, 65, "bf16"), (2048, 16, 100, "f16")])
+def test_many_split_finish_prefill(dev, H, nh, T, dtype):
+    # prefill-family calls whose kv_a_proj is split over K more than 8 ways
+    # (16, 28 and 40 splits at these shapes) with under 2048 tokens: the
+    # finish sums the splits over four waves per token.  Every row.
+    d = Dims(H=H, nh=nh)
+    w = workloads.make_custom(d, T, dtype=dtype, seed=720 + T + H % 101, wstd=0.01,
+                              max_pos=32768)
+    check_full(w, dev, f"wide_finish_H{H}_T{T}_{dtype}", path=1)
+
+
 def test_r1_shapes_small_T(dev):
     w = workloads.make_custom(R1, 3, dtype="bf16", seed=401, wstd=0.01, max_pos=32768)
     check_full(w, dev, "r1_T3")
