@@ -1397,6 +1397,37 @@ __global__ __launch_bounds__(wsf::kWaves * 64, 1) void kvb_fp_ws_kernel(
 // in double; sine / cosine of the reduced angle and the rotation run in fp32
 // (rope_cos_sin).
 // ---------------------------------------------------------------------------
+// The end of the fp16/bf16 finish for token t, on one wave that holds the
+// token's summed partials (lane l: latent columns 8l..8l+7 in c, rope
+// column l in p) and gamma's columns 8l.. in g:
+//   y    = c / sqrt(sum(c^2)/512 + eps) * gamma      -> compressed_kv
+//   k_pe = rotate-half RoPE of p at position pt      -> k_pe (and the cache)
+template <int E>
+__device__ __forceinline__ void finish_fp_token(const float (&c)[8], float p, u4_t g, int64_t t,
+                                                int pt, int64_t slot, float eps,
+                                                const RopeTab& rt, uint16_t* __restrict__ ckv,
+                                                uint16_t* __restrict__ kpe, const CacheOut& co) {
+    const int lane = threadIdx.x & 63;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += c[i] * c[i];
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)kR + eps);
+    const u4_t o = rms_scale8<E>(c, inv, g);
+    *(u4_t*)(ckv + t * kR + 8 * lane) = o;
+
+    const float partner = __shfl_xor(p, 32, 64);
+    float cs, sn;
+    rope_cos_sin(pt, rt.f[lane & 31], cs, sn);
+    const uint16_t ko = f32_to_st<E>(rope_rotate(p, partner, cs, sn, lane < 32));
+    __builtin_nontemporal_store(ko, kpe + t * kDR + lane);
+    if (cache_slot_ok(co, slot)) {  // the paged cache: [latent | rope key] in the token's slot
+        uint16_t* row = co.cache + slot * (kR + kDR);
+        __builtin_nontemporal_store(o, (u4_t*)(row + 8 * lane));
+        __builtin_nontemporal_store(ko, row + kR + lane);
+    }
+}
+
 template <int E, int B>
 __global__ __launch_bounds__(256) void finish_a_fp_kernel(
     const float* __restrict__ P, int S, int64_t T, const uint16_t* __restrict__ gamma,
@@ -1439,24 +1470,7 @@ __global__ __launch_bounds__(256) void finish_a_fp_kernel(
             }
         }
     }
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ss += c[i] * c[i];
-    ss = wave_sum(ss);
-    const float inv = 1.0f / sqrtf(ss / (float)kR + eps);
-    const u4_t o = rms_scale8<E>(c, inv, g);
-    *(u4_t*)(ckv + t * kR + 8 * lane) = o;
-
-    const float partner = __shfl_xor(p, 32, 64);
-    float cs, sn;
-    rope_cos_sin(pt, rt.f[lane & 31], cs, sn);
-    const uint16_t ko = f32_to_st<E>(rope_rotate(p, partner, cs, sn, lane < 32));
-    __builtin_nontemporal_store(ko, kpe + t * kDR + lane);
-    if (cache_slot_ok(co, slot)) {  // the paged cache: [latent | rope key] in the token's slot
-        uint16_t* row = co.cache + slot * (kR + kDR);
-        __builtin_nontemporal_store(o, (u4_t*)(row + 8 * lane));
-        __builtin_nontemporal_store(ko, row + kR + lane);
-    }
+    finish_fp_token<E>(c, p, g, t, pt, slot, eps, rt, ckv, kpe, co);
 }
 
 // The same finish with one workgroup per token, for many splits and few
@@ -1518,24 +1532,7 @@ __global__ __launch_bounds__(256) void finish_fp_wide_kernel(
         for (int i = 0; i < 8; ++i) c[i] += r[i];
         p += r[8];
     }
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ss += c[i] * c[i];
-    ss = wave_sum(ss);
-    const float inv = 1.0f / sqrtf(ss / (float)kR + eps);
-    const u4_t o = rms_scale8<E>(c, inv, g);
-    *(u4_t*)(ckv + t * kR + 8 * lane) = o;
-
-    const float partner = __shfl_xor(p, 32, 64);
-    float cs, sn;
-    rope_cos_sin(pt, rt.f[lane & 31], cs, sn);
-    const uint16_t ko = f32_to_st<E>(rope_rotate(p, partner, cs, sn, lane < 32));
-    __builtin_nontemporal_store(ko, kpe + t * kDR + lane);
-    if (cache_slot_ok(co, slot)) {
-        uint16_t* row = co.cache + slot * (kR + kDR);
-        __builtin_nontemporal_store(o, (u4_t*)(row + 8 * lane));
-        __builtin_nontemporal_store(ko, row + kR + lane);
-    }
+    finish_fp_token<E>(c, p, g, t, pt, slot, eps, rt, ckv, kpe, co);
 }
 
 // ---------------------------------------------------------------------------
