@@ -279,6 +279,20 @@ def test_many_split_finish_prefill(dev, H, nh, T, dtype):
     check_full(w, dev, f"wide_finish_H{H}_T{T}_{dtype}", path=1)
 
 
+@pytest.mark.parametrize("dtype,T", [("bf16", 16), ("bf16", 64), ("f16", 33)])
+def test_r1_decode_family(dev, dtype, T):
+    # the decode family at R1 shape: the weight-streaming kv_a_proj over
+    # H = 7168 and the fused finish + kv_b_proj over 512 slabs of W_kv_b (two
+    # workgroups per CU when the device holds them all at once).  Every row
+    # against the oracle, and no workgroup runs out of polls.
+    import mla_attention_kv_amd as mla
+
+    w = workloads.make_custom(R1, T, dtype=dtype, seed=740 + T, wstd=0.01, max_pos=32768)
+    assert mla.mla_debug_handoff_fallbacks(reset=True) >= 0
+    check_full(w, dev, f"r1_decode_{dtype}_T{T}", path=0)
+    assert mla.mla_debug_handoff_fallbacks() == 0
+
+
 def test_r1_shapes_small_T(dev):
     w = workloads.make_custom(R1, 3, dtype="bf16", seed=401, wstd=0.01, max_pos=32768)
     check_full(w, dev, "r1_T3")
