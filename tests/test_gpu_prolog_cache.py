@@ -246,8 +246,10 @@ def check_c8(outs, cq, cs, slots, num_slots, ref, rows):
 
 
 @pytest.mark.parametrize("q8", [False, True])
-@pytest.mark.parametrize("T", [5, 131])
+@pytest.mark.parametrize("T", [5, 12, 40, 131])
 def test_prolog_w8a8_cached_small(dev, T, q8):
+    # T = 5: quantiser folded into kv_a_proj and finish fused into kv_b_proj;
+    # 12: the fused finish alone; 40: four launches; 131: the prefill family
     w = workloads.make_custom(Dims(H=1024, nh=8), T, kind="w8a8", dtype="bf16", seed=950 + T,
                               wstd=0.03)
     slots, n = workloads.paged_slot_mapping(w, block_size=16, seed=T)
