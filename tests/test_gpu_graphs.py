@@ -160,7 +160,8 @@ def test_graphs_w8a8_int8_cache(dev):
     g = mla.PrologGraphs(weights, (4, 16), w.eps, w.theta, w8a8=True, cache=(cq, cs))
     ref = run_oracle(w)
     sl = torch.from_numpy(slots).to(dev)
-    for T in (3, 16, 11):
+    # each bucket replayed twice, with eager work in between
+    for T in (3, 16, 11, 4):
         print(f"[graphs] w8a8 T={T}", flush=True)
         g.hidden[:T] = t["X"][:T]
         g.positions[:T] = t["pos"][:T]
