@@ -707,6 +707,9 @@ def kernel_parts(w, path, n_kernels):
         if n_kernels == 3:  # decode sizes: the finish fused into kv_b_proj
             return [quant, kv_a, fused]
         return [quant, kv_a, finish, kv_b]
+    if path == 1 and n_kernels == 2:  # the finish and kv_b_proj in one launch
+        return [kv_a, ("finish + kv_b_proj in one launch (latent staged in LDS)",
+                       (a_out + d.r * D + 4 * T + fin_out + wb + kv_out, f2))]
     if path == 0 and n_kernels == 2:
         return [("dec_kv_a (kv_a_proj, split-K)", (xin + wa + a_out, f1)),
                 ("dec_fin_kv_b (finish fused into kv_b_proj)",
@@ -920,6 +923,9 @@ def main():
                          "headline, the other four under 'configs')")
     ap.add_argument("--eager", action="store_true", help="time direct calls, not graph replays")
     ap.add_argument("--path", type=int, default=-1, help="force kernel family 0/1 (A/B runs)")
+    ap.add_argument("--prefill-fusion", type=int, default=-1,
+                    help="fp16/bf16 tiled path: finish and kv_b_proj in one launch (1), in two "
+                         "(0), or the dispatcher's choice (-1; A/B runs)")
     ap.add_argument("--op", default="prolog",
                     choices=["prolog", "prolog_cached", "prolog_then_append", "cache_append",
                              "cache_append_int8", "rms_norm", "rope", "graph_buckets",
@@ -953,6 +959,8 @@ def main():
     mla.lib()
     if args.path in (0, 1):
         mla.mla_kv_prolog_force_path(args.path)
+    if args.prefill_fusion in (0, 1):
+        mla.mla_debug_set_prefill_fusion(args.prefill_fusion)
 
     headline = 4 if args.config is None else args.config
     cfg = workloads.CONFIGS[headline]

@@ -51,7 +51,8 @@
  *   stream) and never synchronise.  Two calls that share a workspace must
  *   be ordered (same stream, or synchronised).
  * - The library holds no per-call state and is safe to call from several
- *   host threads (apart from mla_kv_prolog_force_path, a test hook).
+ *   host threads (apart from mla_kv_prolog_force_path and the mla_debug_set_*
+ *   calls, test hooks).
  */
 #ifndef LIBMLAPROLOG_H
 #define LIBMLAPROLOG_H
@@ -389,6 +390,18 @@ int mla_kv_prolog_selected_path(int64_t T, mla_dims_t d);
  * kernel family (0 or 1), or back to the dispatcher's choice (-1).  Returns
  * the previous setting.  Not for concurrent use. */
 int mla_kv_prolog_force_path(int path);
+
+/* Test / benchmark hook for the fp16 / bf16 MFMA-tiled kernels (the
+ * prefill family, and the decode family when forced past 64 tokens): run
+ * the finish (split, RMSNorm, RoPE) and kv_b_proj as one launch whose
+ * workgroups normalise a 64-row block's latent into LDS and feed kv_b_proj
+ * from there (1), as two launches through compressed_kv in memory (0), or
+ * as the dispatcher decides (-1: never, today).  Both give the same bits
+ * wherever the separate finish adds kv_a_proj's K splits in ascending
+ * order (up to 8 splits, or from 2048 tokens); elsewhere they differ by
+ * the rounding of that sum.  Returns the previous setting.  Not for
+ * concurrent use. */
+int mla_debug_set_prefill_fusion(int mode);
 
 /* The fp16 / bf16 prolog for callers that cannot allocate: code under HIP
  * graph capture, tight serving loops, harnesses that forbid allocation.

@@ -46,6 +46,7 @@ EXPORTS = (
     "mla_debug_set_launch_events",
     "mla_debug_set_handoff_spin",
     "mla_debug_handoff_fallbacks",
+    "mla_debug_set_prefill_fusion",
     "mla_prolog_graphs_create",
     "mla_prolog_graphs_create_layers",
     "mla_prolog_graphs_update_layers",
@@ -175,6 +176,8 @@ def lib() -> ctypes.CDLL:
     L.mla_debug_set_handoff_spin.restype = i64
     L.mla_debug_handoff_fallbacks.argtypes = [i32]
     L.mla_debug_handoff_fallbacks.restype = i64
+    L.mla_debug_set_prefill_fusion.argtypes = [i32]
+    L.mla_debug_set_prefill_fusion.restype = i32
     _lib = L
     return L
 
@@ -210,6 +213,13 @@ def mla_debug_handoff_fallbacks(reset: bool = False) -> int:
     """Test hook: the current device's count of decode hand-off fallbacks
     since the last reset (synchronises; clears it when reset)."""
     return int(lib().mla_debug_handoff_fallbacks(1 if reset else 0))
+
+
+def mla_debug_set_prefill_fusion(mode: int) -> int:
+    """Test hook: the fp16/bf16 prefill's finish and kv_b_proj as one launch
+    with the latent staged in LDS (1), as two launches (0), or the
+    dispatcher's choice (-1); returns the previous setting."""
+    return int(lib().mla_debug_set_prefill_fusion(int(mode)))
 
 
 # ---------------------------------------------------------------------------

@@ -13,6 +13,7 @@ using namespace mla;
 namespace {
 
 std::atomic<int> g_force_path{-1};
+std::atomic<int> g_prefill_fusion{-1};
 thread_local int t_validate_only = 0;
 
 // Token counts up to this many take the decode tiling (small M tiles,
@@ -37,6 +38,7 @@ Plan make_plan(int64_t T, int H, bool int8, int path) {
     p.stream = (!int8 && path == 0 && T <= kDecodeMaxT) ? 1 : 0;
     p.kw = 0;
     p.dma1 = 0;
+    p.fuse2 = int8 ? 0 : g_prefill_fusion.load(std::memory_order_relaxed);
     if (p.stream) {
         // weight-streaming kv_a_proj: 9 slabs x S splits of kw rows each;
         // wider splits once the split-K partials (S * T rows of 576 floats)
@@ -187,6 +189,11 @@ int mla_kv_prolog_selected_path(int64_t T, mla_dims_t) { return select_path(T); 
 int mla_kv_prolog_force_path(int path) {
     if (path != 0 && path != 1) path = -1;
     return g_force_path.exchange(path);
+}
+
+int mla_debug_set_prefill_fusion(int mode) {
+    if (mode != 0 && mode != 1) mode = -1;
+    return g_prefill_fusion.exchange(mode);
 }
 
 int32_t mla_debug_set_launch_events(void* const* events, int32_t n) {

@@ -97,6 +97,8 @@ struct Plan {
     int kw;         // streaming kv_a_proj: K rows per producer workgroup
     int bm2, bn2;   // kv_b_proj tile (tiled)
     int dma1;       // kv_a_proj by the direct-to-LDS pipelined GEMM (no split-K)
+    int fuse2;      // fp16/bf16 tiled path: finish and kv_b_proj in one launch
+                    // (-1: the dispatcher decides, 0: never, 1: whenever s1 <= 2)
 };
 
 // RoPE inverse frequencies theta^(-2i/dr), i < dr/2, evaluated once per call

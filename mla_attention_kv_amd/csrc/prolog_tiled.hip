@@ -1402,11 +1402,14 @@ __global__ __launch_bounds__(wsf::kWaves * 64, 1) void kvb_fp_ws_kernel(
 // column l in p) and gamma's columns 8l.. in g:
 //   y    = c / sqrt(sum(c^2)/512 + eps) * gamma      -> compressed_kv
 //   k_pe = rotate-half RoPE of p at position pt      -> k_pe (and the cache)
+// Returns the lane's 8 rounded latent values; with store false nothing is
+// written (a caller that needs only the latent).
 template <int E>
-__device__ __forceinline__ void finish_fp_token(const float (&c)[8], float p, u4_t g, int64_t t,
+__device__ __forceinline__ u4_t finish_fp_token(const float (&c)[8], float p, u4_t g, int64_t t,
                                                 int pt, int64_t slot, float eps,
                                                 const RopeTab& rt, uint16_t* __restrict__ ckv,
-                                                uint16_t* __restrict__ kpe, const CacheOut& co) {
+                                                uint16_t* __restrict__ kpe, const CacheOut& co,
+                                                bool store = true) {
     const int lane = threadIdx.x & 63;
     float ss = 0.f;
 #pragma unroll
@@ -1414,6 +1417,7 @@ __device__ __forceinline__ void finish_fp_token(const float (&c)[8], float p, u4
     ss = wave_sum(ss);
     const float inv = 1.0f / sqrtf(ss / (float)kR + eps);
     const u4_t o = rms_scale8<E>(c, inv, g);
+    if (!store) return o;
     *(u4_t*)(ckv + t * kR + 8 * lane) = o;
 
     const float partner = __shfl_xor(p, 32, 64);
@@ -1426,6 +1430,7 @@ __device__ __forceinline__ void finish_fp_token(const float (&c)[8], float p, u4
         __builtin_nontemporal_store(o, (u4_t*)(row + 8 * lane));
         __builtin_nontemporal_store(ko, row + kR + lane);
     }
+    return o;
 }
 
 template <int E, int B>
@@ -1533,6 +1538,274 @@ __global__ __launch_bounds__(256) void finish_fp_wide_kernel(
         p += r[8];
     }
     finish_fp_token<E>(c, p, g, t, pt, slot, eps, rt, ckv, kpe, co);
+}
+
+// ---------------------------------------------------------------------------
+// fp16 / bf16 prefill, the finish and kv_b_proj in one launch: the
+// normalised latent is staged in LDS and feeds kv_b_proj's MFMAs from there.
+// A workgroup owns a block of 64 token rows and a group of G heads.
+//   1. It sums its rows' split-K partials of kv_a_proj (split order
+//      ascending), normalises them (RMSNorm, gamma) and keeps the rounded
+//      latent [64][512] in LDS; the workgroup of the first head group also
+//      writes compressed_kv, k_pe and the cache rows (finish_fp_token, the
+//      same arithmetic as the separate finish kernels).
+//   2. For each of its heads it multiplies that latent by the head's 256
+//      W_kv_b columns, which stream through a ring of three LDS stages of
+//      64 K rows each (direct global-to-LDS copies, four per wave and
+//      stage; the first two stages are in flight during step 1).  Wave w
+//      owns columns 32 w .. 32 w + 31 of the head and all 64 rows; the
+//      K steps run in ascending order, as in the tiled kernel, so k_nope
+//      and value come out bit for bit as from the three-launch path.
+// LDS: latent rows of 1 KB, 16-byte chunk c of row r at c ^ (r % 16); ring
+// stages in the pipelined GEMM's B layout (rows of 512 bytes, swizzled
+// chunks, transposing reads).
+// ---------------------------------------------------------------------------
+namespace fb {
+constexpr int kRows = 64;                             // token rows per workgroup
+constexpr int kWaves = 8;
+constexpr int kStages = 3;                            // W_kv_b ring stages
+constexpr int kSlabK = 64;                            // K rows per stage
+constexpr int kBRB = kHeadW * 2;                      // bytes of a staged W row
+constexpr int kStageBytes = kSlabK * kBRB;            // 32 KB
+constexpr int kLatBytes = kRows * kR * 2;             // 64 KB
+constexpr int kCopies = kStageBytes / 1024 / kWaves;  // per wave and stage
+constexpr int kSlabsPerHead = kR / kSlabK;
+constexpr int kStores = 4;                            // per wave and head
+static_assert(kLatBytes + kStages * kStageBytes <= 160 * 1024, "LDS");
+static_assert(kCopies * kWaves * 1024 == kStageBytes, "even copy split");
+}  // namespace fb
+
+// Heads per workgroup of the fused finish + kv_b_proj launch: the smallest
+// divisor of nh that keeps the launch within 256 workgroups.
+inline int fin_kv_b_group(int64_t T, int nh) {
+    const int64_t nrb = (T + fb::kRows - 1) / fb::kRows;
+    for (int g = 1; g < nh; ++g)
+        if (nh % g == 0 && nrb * (nh / g) <= 256) return g;
+    return nh;
+}
+
+template <int E, int NS>
+__global__ __launch_bounds__(fb::kWaves * 64, 1) void fin_kv_b_fp_kernel(
+    const float* __restrict__ P, int S, int64_t T, const uint16_t* __restrict__ gamma,
+    const int32_t* __restrict__ pos, float eps, RopeTab rt, const uint16_t* __restrict__ Wb,
+    int nh, int G, uint16_t* __restrict__ ckv, uint16_t* __restrict__ kpe, CacheOut co,
+    uint16_t* __restrict__ k_nope, uint16_t* __restrict__ value_out) {
+    using namespace fb;
+    __shared__ __align__(1024) uint8_t smem[kLatBytes + kStages * kStageBytes];
+    uint8_t* const lat = smem;
+    uint8_t* const ring = smem + kLatBytes;
+    // work item (row block, head group): workgroup b runs on XCD b % 8,
+    // which owns a contiguous range of items, so the head groups of a row
+    // block share that XCD's L2 (their split-K partials are read there)
+    const int64_t nrb = (T + kRows - 1) / kRows;
+    const int ngrp = nh / G;
+    const int64_t items = nrb * ngrp, per = (items + 7) / 8;
+    const int64_t xk = blockIdx.x >> 3, item = (int64_t)(blockIdx.x & 7) * per + xk;
+    if (xk >= per || item >= items) return;
+    const int64_t rb = item / ngrp;
+    const int grp = (int)(item - rb * ngrp);
+    const int64_t m0 = rb * kRows;
+    const int head0 = grp * G;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g = lane >> 4;
+    const int64_t N2 = (int64_t)nh * kHeadW;
+
+    // ---- W_kv_b ring: slab n is K rows 64 (n % 8) .. of head head0 + n / 8,
+    // in stage n % 3.  Copy u of this wave fills stage bytes
+    // (kCopies wave + u) KB .. + 1 KB: B rows k, k + 1 of the slab, chunk pos
+    // of LDS row k holding global chunk pos ^ bswz(k).
+    const int nslab = G * kSlabsPerHead;
+    uint32_t woff[kCopies];
+#pragma unroll
+    for (int u = 0; u < kCopies; ++u) {
+        const int byte = (wave * kCopies + u) * 1024 + lane * 16;
+        const int k = brow<E, kBRB>(byte / kBRB), pp = (byte % kBRB) / 16;
+        woff[u] = (uint32_t)(k * N2 * 2 + ((pp ^ bswz<E, kBRB>(k)) << 4));
+    }
+    const uint32_t ring0 =
+        lds_addr(ring) + (uint32_t)__builtin_amdgcn_readfirstlane(wave * kCopies * 1024);
+    auto issue = [&](int n) {
+        const int h = head0 + n / kSlabsPerHead, kk = n % kSlabsPerHead;
+        const uint16_t* base = Wb + (int64_t)kk * kSlabK * N2 + (int64_t)h * kHeadW;
+        const uint32_t so = (uint32_t)((n % kStages) * kStageBytes);
+#pragma unroll
+        for (int u = 0; u < kCopies; ++u) dma16s(base, woff[u], ring0 + so + u * 1024);
+    };
+    issue(0);
+    if (nslab > 1) issue(1);
+
+    // ---- 1. finish rows 8 wave .. 8 wave + 7 into the LDS latent, four rows
+    // at a time, NS splits' partial loads in flight per row (rows past T load
+    // row T - 1 and store nothing; their latent rows are zero).  The splits
+    // are added in ascending order, as in the separate finish kernels.
+    const u4_t gm = *(const u4_t*)(gamma + 8 * lane);
+#pragma unroll
+    for (int q0 = 0; q0 < 8; q0 += 4) {
+        float c[4][8];
+        float p[4];
+        int ptv[4];
+        int64_t slv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t t = min(m0 + 8 * wave + q0 + r, T - 1);
+            ptv[r] = pos[t];
+            slv[r] = co.slots != nullptr ? co.slots[t] : -1;
+            p[r] = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) c[r][i] = 0.f;
+        }
+        for (int s0 = 0; s0 < S; s0 += NS) {
+            f4_t v0[4][NS], v1[4][NS];
+            float pv[4][NS];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t t = min(m0 + 8 * wave + q0 + r, T - 1);
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    const float* row = P + ((int64_t)min(s0 + s, S - 1) * T + t) * kN1;
+                    v0[r][s] = __builtin_nontemporal_load((const f4_t*)(row + 8 * lane));
+                    v1[r][s] = __builtin_nontemporal_load((const f4_t*)(row + 8 * lane + 4));
+                    pv[r][s] = __builtin_nontemporal_load(row + kR + lane);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    if (s0 + s < S) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            c[r][i] += v0[r][s][i];
+                            c[r][4 + i] += v1[r][s][i];
+                        }
+                        p[r] += pv[r][s];
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rr = 8 * wave + q0 + r;
+            const int64_t t = m0 + rr;
+            u4_t o = {0u, 0u, 0u, 0u};
+            if (t < T) o = finish_fp_token<E>(c[r], p[r], gm, t, ptv[r], slv[r], eps, rt, ckv,
+                                              kpe, co, grp == 0);
+            *(u4_t*)(lat + rr * (kR * 2) + ((lane ^ (rr & 15)) << 4)) = o;
+        }
+    }
+    // every partial load has been waited for, so the ring's first two
+    // stages (copied before them) have landed too; the latent rows are
+    // written
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    // ---- 2. kv_b_proj over the staged latent
+    typedef f4_t acc_t;
+    acc_t acc[4][2];
+    uint16_t* const dst_base = (wave < 4 ? k_nope : value_out) + (wave & 3) * 32;
+    const int64_t rstride = (int64_t)nh * kDN;
+    const uint32_t doff = (uint32_t)((l16 * rstride + ((g & 1) ? 16 + 4 * (g - 1) : 4 * g)) * 2);
+    for (int n = 0; n < nslab; ++n) {
+        // slab n landed and slab n - 1's stage free: after slab n's copies
+        // this wave issued slab n + 1's (unless it is the last) and, at a
+        // head boundary, one head's stores
+        if (n == 1) {
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        } else if (n >= 2) {
+            const bool more = n + 1 < nslab;
+            const bool st = n >= kSlabsPerHead && (n % kSlabsPerHead) < 2;
+            if (more && st) wait_vm_lds_barrier<kCopies + kStores>();
+            else if (more) wait_vm_lds_barrier<kCopies>();
+            else if (st) wait_vm_lds_barrier<kStores>();
+            else wait_vm_lds_barrier<0>();
+        }
+        if (n + kStages - 1 < nslab) issue(n + kStages - 1);
+        const uint8_t* Bs = ring + (n % kStages) * kStageBytes;
+        const int kk = n % kSlabsPerHead;
+        if (kk == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[i][j] = acc_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            u4_t fa[4], fbv[2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * i + l16;
+                const int ch = kk * 8 + ks * 4 + g;
+                fa[i] = *(const u4_t*)(lat + row * (kR * 2) + ((ch ^ l16) << 4));
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                // lane (16 g + s): K rows 32 ks + 8 g + s / 4 (+ 4), columns
+                // 32 wave + 16 j + 4 (s % 4) .. + 3
+                const int k = ks * 32 + g * 8 + (l16 >> 2);
+                const int colb = (32 * wave + 16 * j + 4 * (l16 & 3)) * 2;
+                const int c = colb >> 4, off = colb & 15;
+                const uint2 lo = lds_tr16(Bs + brow<E, kBRB>(k) * kBRB +
+                                          ((c ^ bswz<E, kBRB>(k)) << 4) + off);
+                const uint2 hi = lds_tr16(Bs + brow<E, kBRB>(k + 4) * kBRB +
+                                          ((c ^ bswz<E, kBRB>(k + 4)) << 4) + off);
+                fbv[j] = u4_t{lo.x, lo.y, hi.x, hi.y};
+            }
+            // operands swapped (C^T = B^T A^T): lane l holds row l % 16 of
+            // row tile i and columns 4 (l / 16) .. + 3 of column tile j
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = mfma16<E>(fbv[j], fa[i], acc[i][j]);
+        }
+        if (kk == kSlabsPerHead - 1) {
+            // the head's results, rounded; lanes of even 16-lane rows end with
+            // 8 columns of tile 0, odd ones with 8 columns of tile 1 (one
+            // 16-byte store per lane and row tile)
+            const int head = head0 + n / kSlabsPerHead;
+            uint8_t* const dh = (uint8_t*)(dst_base + (int64_t)head * kDN);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t row0 = m0 + 16 * i;
+                uint32_t P0[2], P1[2];
+                P0[0] = cvt_pk<E>(acc[i][0][0], acc[i][0][1]);
+                P0[1] = cvt_pk<E>(acc[i][0][2], acc[i][0][3]);
+                P1[0] = cvt_pk<E>(acc[i][1][0], acc[i][1][1]);
+                P1[1] = cvt_pk<E>(acc[i][1][2], acc[i][1][3]);
+                const auto s0 = __builtin_amdgcn_permlane16_swap(P0[0], P1[0], false, false);
+                const auto s1 = __builtin_amdgcn_permlane16_swap(P0[1], P1[1], false, false);
+                const u4_t v = u4_t{s0[0], s1[0], s0[1], s1[1]};
+                if (row0 + l16 < T)
+                    __builtin_nontemporal_store(v, (u4_t*)(dh + row0 * rstride * 2 + doff));
+            }
+        }
+    }
+}
+
+// Where the one-launch finish + kv_b_proj is taken by default: nowhere.  On
+// the V2-Lite prefill (T = 4096) it took ~40 us against ~24 us for the
+// finish and the tiled kv_b_proj it replaces: each row block's split sums
+// and RMSNorm are repeated by its four head groups (~15 us alone), and each
+// CU pulls 1 MB of W_kv_b through a ring two stages deep (the latent holds
+// the rest of LDS), ~31 us alone, against 768 KB per CU for the tiled
+// kernel's 256-row tiles.
+inline bool fin_kv_b_pays(int64_t, int) { return false; }
+
+template <int E>
+static void launch_fin_kv_b_fp(const float* P, int S, int64_t T, const void* gamma,
+                               const int32_t* pos, float eps, const RopeTab& rt, const void* Wb,
+                               int nh, void* ckv, void* kpe, const CacheOut& co, void* k_nope,
+                               void* value, hipStream_t st) {
+    const int G = fin_kv_b_group(T, nh);
+    const int64_t items = ((T + fb::kRows - 1) / fb::kRows) * (nh / G);
+    const dim3 grid((unsigned)(8 * ((items + 7) / 8))), blk(fb::kWaves * 64);
+    auto go = [&](auto kern) {
+        launch_k(kern, grid, blk, 0, st, P, S, T, (const uint16_t*)gamma, pos, eps, rt,
+                 (const uint16_t*)Wb, nh, G, (uint16_t*)ckv, (uint16_t*)kpe, co,
+                 (uint16_t*)k_nope, (uint16_t*)value);
+    };
+    if (S == 1) go(fin_kv_b_fp_kernel<E, 1>);
+    else go(fin_kv_b_fp_kernel<E, 2>);
 }
 
 // ---------------------------------------------------------------------------
@@ -1916,6 +2189,11 @@ static hipError_t launch_fp_t(const void* X, const void* Wa, const void* gamma, 
     else
         gemm1_dispatch<E>(plan.bm1, X, (int64_t)H * 2, Wa, T, kslabs1, plan.s1,
                           EpiPartialF32{P1, T}, st);
+    if (plan.fuse2 == 1 || (plan.fuse2 < 0 && plan.s1 <= 2 && fin_kv_b_pays(T, nh))) {
+        launch_fin_kv_b_fp<E>(P1, plan.s1, T, gamma, pos, eps, rt, Wb, nh, ckv, k_pe, co,
+                              k_nope, value, st);
+        return hipGetLastError();
+    }
     launch_finish_fp(E, P1, plan.s1, T, gamma, pos, eps, rt, ckv, k_pe, co, st);
     const int N2 = nh * kHeadW;
     if (plan.path == 1 && kvb_fp_ws_pays(T, nh))

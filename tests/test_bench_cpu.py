@@ -57,9 +57,11 @@ def test_roofline_picks_the_binding_roof(i, bound):
 
 # (workload index, kernel family, kernels per call) for every split the
 # library launches: fp decode (2 kernels, 3 for a separate finish), the
-# prefill family (3), W8A8 prefill (4) and W8A8 decode (3: finish fused into
-# kv_b_proj; 2: the quantiser folded into kv_a_proj as well)
-SPLITS = [(0, 0, 2), (1, 0, 2), (1, 0, 3), (2, 1, 3), (3, 1, 3), (4, 1, 4), (4, 0, 3), (4, 0, 2)]
+# prefill family (3; 2 with the finish and kv_b_proj in one launch), W8A8
+# prefill (4) and W8A8 decode (3: finish fused into kv_b_proj; 2: the
+# quantiser folded into kv_a_proj as well)
+SPLITS = [(0, 0, 2), (1, 0, 2), (1, 0, 3), (2, 1, 3), (2, 1, 2), (3, 1, 3), (4, 1, 4), (4, 0, 3),
+          (4, 0, 2)]
 
 
 @pytest.mark.parametrize("i,path,nk", SPLITS)

@@ -382,6 +382,17 @@ def test_handoff_spin_hook_round_trip():
         mla.mla_debug_set_handoff_spin(prev)
 
 
+def test_prefill_fusion_hook_round_trip():
+    # needs no GPU; out-of-range modes mean the dispatcher's choice (-1)
+    prev = mla.mla_debug_set_prefill_fusion(1)
+    try:
+        assert mla.mla_debug_set_prefill_fusion(0) == 1
+        assert mla.mla_debug_set_prefill_fusion(7) == 0
+        assert mla.mla_debug_set_prefill_fusion(-1) == -1
+    finally:
+        mla.mla_debug_set_prefill_fusion(prev)
+
+
 def test_launch_event_hook_records_nothing_for_rejected_calls():
     # a call that fails validation launches nothing, so it records none of
     # the registered events (the handles are never touched)
