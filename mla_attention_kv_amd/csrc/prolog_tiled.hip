@@ -1555,7 +1555,8 @@ __global__ __launch_bounds__(256) void finish_fp_wide_kernel(
 //      stage; the first two stages are in flight during step 1).  Wave w
 //      owns columns 32 w .. 32 w + 31 of the head and all 64 rows; the
 //      K steps run in ascending order, as in the tiled kernel, so k_nope
-//      and value come out bit for bit as from the three-launch path.
+//      and value come out bit for bit as from the three-launch path
+//      wherever its finish also adds the splits in ascending order.
 // LDS: latent rows of 1 KB, 16-byte chunk c of row r at c ^ (r % 16); ring
 // stages in the pipelined GEMM's B layout (rows of 512 bytes, swizzled
 // chunks, transposing reads).
