@@ -11,8 +11,9 @@ two launches through compressed_kv, and checks:
 
 Shapes: the V2-Lite prefill at full size (T = 4096), ragged last row blocks
 (T = 4100, 2050, 777, 100), bf16, head counts that give head groups of one
-(nh = 1, 3, 5), the decode family's tiling forced past 64 tokens, and the
-paged-cache write of the first head group's workgroups.
+(nh = 1, 3, 5), the decode family's tiling forced past 64 tokens, the
+paged-cache write of the first head group's workgroups, and replays of the
+call captured in a HIP graph.
 """
 import numpy as np
 import pytest
@@ -119,3 +120,36 @@ def test_one_launch_cached_write(dev):
     mine = torch.cat([res[1][0][3][rows], res[1][0][2][rows]], dim=1)
     assert torch.equal(got.view(torch.int16), mine.view(torch.int16)), "cache != returned rows"
     compare(gpu_rows(res[1][0]), run_oracle(w), "one launch cached")
+
+
+def test_one_launch_graph_replays(dev):
+    """The one-launch call captured in a HIP graph: three replays, with new
+    hidden rows and unrelated eager work between them, each give the bits of
+    an eager call on the same inputs (the launch records no memset and
+    allocates nothing)."""
+    import mla_attention_kv_amd as mla
+
+    w = workloads.make_custom(V2LITE, 4100, dtype="f16", seed=1170, max_pos=32768)
+    print(f"[prefill-fusion] graph replays T={w.T}", flush=True)
+    t = upload(w, dev)
+    mla.mla_debug_set_prefill_fusion(1)
+    x0 = t["X"].clone()
+    args = (t["X"], t["Wa"], t["gamma"], t["Wb"], t["pos"], w.eps, w.theta)
+    cap = torch.cuda.Stream(device=dev)
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        mla.mla_kv_prolog(*args)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        outs = mla.mla_kv_prolog(*args)
+    for i in range(3):
+        t["X"].copy_(x0 * (1.0 + 0.25 * i))
+        junk = torch.randn(1 << 20, device=dev).abs().sum()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = mla.mla_kv_prolog(*args)
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        _bit_equal(outs, ref, f"replay {i}")
